@@ -1,0 +1,219 @@
+"""Python binding of the fp4w4a16 C ABI (block-scaled 4-bit weights x bf16 activations on gfx950).
+
+Argument marshalling only: every function below checks tensor devices, dtypes and sizes,
+passes raw device pointers and the current HIP stream to the C entry point of the same
+name in libfp4w4a16.so, and raises RuntimeError on a negative status. All computation
+runs in the library's HIP kernels; there is no fallback path. Importing this package
+without the built library fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4w4a16.so")
+
+FORMATS = {"nvfp4": 1, "rocmfp4_dual": 2, "rocmfp4_fast": 3}
+BLOCK_BYTES = {"rocmfp4_dual": 18, "rocmfp4_fast": 17}
+GEMV_MAX_M = 16
+
+_c = ctypes.c_int
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_f = ctypes.c_float
+
+_SIGS = {
+    "fp4_abi_version": (_c, []),
+    "fp4_status_string": (ctypes.c_char_p, [_c]),
+    "fp4_layout_bytes": (_c, [_c, _i64, _i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "fp4_pack_layout": (_c, [_c, _i64, _i64, _p, _p, _p, _p, _p]),
+    "w4a16_gemv": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
+    "w4a16_gemm": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
+    "w4a16_matmul": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
+    "fp4_dequant_f32": (_c, [_c, _i64, _i64, _p, _p, _f, _p, _p]),
+    "fp4_quantize_nvfp4": (_c, [_i64, _i64, _p, _p, _p, _p, _p]),
+    "fp4_quantize_rocmfp4": (_c, [_c, _i64, _i64, _p, _p, _p, _p]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with block_scaled_fp4_w4a16_amd/build.py "
+                              "(or __graft_entry__.build())")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+lib()  # fail at import time when the HIP library is absent
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FORMATS)}")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"{what}: {lib().fp4_status_string(rc).decode()} (status {rc})")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def fp4_abi_version() -> int:
+    return lib().fp4_abi_version()
+
+
+def fp4_status_string(status: int) -> str:
+    return lib().fp4_status_string(status).decode()
+
+
+def fp4_layout_bytes(fmt, N: int, K: int) -> tuple[int, int]:
+    q = ctypes.c_size_t()
+    s = ctypes.c_size_t()
+    _check(lib().fp4_layout_bytes(_fmt(fmt), N, K, ctypes.byref(q), ctypes.byref(s)), "fp4_layout_bytes")
+    return q.value, s.value
+
+
+def fp4_pack_layout(fmt, N, K, src_q, src_s, dst_q, dst_s, stream=None):
+    _check(lib().fp4_pack_layout(_fmt(fmt), N, K, _ptr(src_q), _ptr(src_s), _ptr(dst_q), _ptr(dst_s),
+                                 _stream(stream)), "fp4_pack_layout")
+
+
+def _product(name, fmt, M, N, K, q, s, global_scale, x, y, stream):
+    if x.dtype != torch.bfloat16 or y.dtype != torch.float32:
+        raise TypeError("x must be bfloat16 and y float32")
+    if x.numel() < M * K or y.numel() < M * N:
+        raise ValueError("x or y is smaller than M x K / M x N")
+    _check(getattr(lib(), name)(_fmt(fmt), M, N, K, _ptr(q), _ptr(s), float(global_scale), _ptr(x), _ptr(y),
+                                _stream(stream)), name)
+
+
+def w4a16_gemv(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
+    _product("w4a16_gemv", fmt, M, N, K, q, s, global_scale, x, y, stream)
+
+
+def w4a16_gemm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
+    _product("w4a16_gemm", fmt, M, N, K, q, s, global_scale, x, y, stream)
+
+
+def w4a16_matmul(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
+    _product("w4a16_matmul", fmt, M, N, K, q, s, global_scale, x, y, stream)
+
+
+def fp4_dequant_f32(fmt, N, K, q, s, global_scale, w, stream=None):
+    if w.dtype != torch.float32 or w.numel() < N * K:
+        raise ValueError("w must be float32 with N x K elements")
+    _check(lib().fp4_dequant_f32(_fmt(fmt), N, K, _ptr(q), _ptr(s), float(global_scale), _ptr(w),
+                                 _stream(stream)), "fp4_dequant_f32")
+
+
+def fp4_quantize_nvfp4(N, K, w, wq, ws, g_out, stream=None):
+    if w.dtype != torch.float32 or g_out.dtype != torch.float32:
+        raise TypeError("w and g_out must be float32")
+    if w.numel() < N * K or wq.numel() < N * K // 2 or ws.numel() < N * K // 16 or g_out.numel() < 1:
+        raise ValueError("buffer too small")
+    _check(lib().fp4_quantize_nvfp4(N, K, _ptr(w), _ptr(wq), _ptr(ws), _ptr(g_out), _stream(stream)),
+           "fp4_quantize_nvfp4")
+
+
+def fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream=None):
+    if w.dtype != torch.float32 or (importance is not None and importance.dtype != torch.float32):
+        raise TypeError("w and importance must be float32")
+    f = _fmt(fmt)
+    bb = 18 if f == 2 else 17
+    if w.numel() < N * K or blocks.numel() < N * (K // 32) * bb:
+        raise ValueError("buffer too small")
+    _check(lib().fp4_quantize_rocmfp4(f, N, K, _ptr(w), _ptr(importance), _ptr(blocks), _stream(stream)),
+           "fp4_quantize_rocmfp4")
+
+
+# ----------------------------------------------------------------------------------------------
+# Convenience: a packed weight in kernel layout (allocation through torch, compute in the library)
+# ----------------------------------------------------------------------------------------------
+
+@dataclass
+class PackedWeight:
+    fmt: str
+    N: int
+    K: int
+    q: torch.Tensor          # nibble plane (uint8)
+    s: torch.Tensor          # scale plane (uint8)
+    global_scale: float
+
+    @staticmethod
+    def empty(fmt: str, N: int, K: int, global_scale: float = 1.0, device="cuda") -> "PackedWeight":
+        qb, sb = fp4_layout_bytes(fmt, N, K)
+        return PackedWeight(fmt, N, K, torch.empty(qb, dtype=torch.uint8, device=device),
+                            torch.empty(sb, dtype=torch.uint8, device=device), float(global_scale))
+
+    @staticmethod
+    def from_canonical(fmt: str, N: int, K: int, src_q: torch.Tensor, src_s: torch.Tensor | None,
+                       global_scale: float = 1.0, stream=None) -> "PackedWeight":
+        pw = PackedWeight.empty(fmt, N, K, global_scale, device=src_q.device)
+        fp4_pack_layout(fmt, N, K, src_q, src_s, pw.q, pw.s, stream)
+        return pw
+
+    @staticmethod
+    def quantize(fmt: str, w: torch.Tensor, importance: torch.Tensor | None = None, stream=None) -> "PackedWeight":
+        """Pack fp32 weights [N, K] on the GPU with the device packer, then repack to kernel layout."""
+        N, K = w.shape
+        w = w.contiguous()
+        if fmt == "nvfp4":
+            wq = torch.empty(N * K // 2, dtype=torch.uint8, device=w.device)
+            ws = torch.empty(N * K // 16, dtype=torch.uint8, device=w.device)
+            g = torch.empty(1, dtype=torch.float32, device=w.device)
+            fp4_quantize_nvfp4(N, K, w, wq, ws, g, stream)
+            gs = float(g.item())
+            return PackedWeight.from_canonical(fmt, N, K, wq, ws, gs, stream)
+        blocks = torch.empty(N * (K // 32) * BLOCK_BYTES[fmt], dtype=torch.uint8, device=w.device)
+        fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream)
+        return PackedWeight.from_canonical(fmt, N, K, blocks, None, 1.0, stream)
+
+    def matmul(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        M = x.shape[0]
+        if x.shape[-1] != self.K:
+            raise ValueError("x's last dimension must be K")
+        if out is None:
+            out = torch.empty(M, self.N, dtype=torch.float32, device=x.device)
+        w4a16_matmul(self.fmt, M, self.N, self.K, self.q, self.s, self.global_scale, x.contiguous(), out, stream)
+        return out
+
+    def dequant(self, stream=None) -> torch.Tensor:
+        w = torch.empty(self.N, self.K, dtype=torch.float32, device=self.q.device)
+        fp4_dequant_f32(self.fmt, self.N, self.K, self.q, self.s, self.global_scale, w, stream)
+        return w

@@ -1,0 +1,175 @@
+// Load-time repack (canonical -> kernel layout) and the FP32 dequantizer of the kernel layout.
+#include "common.h"
+#include "launch.h"
+#include "fp4w4a16.h"
+
+namespace fp4 {
+
+// One thread per 16-byte lane piece of the nibble plane, plus the scale bytes of its row.
+template <int F>
+__global__ void pack_layout_kernel(int N, int K, int nchunk, int64_t npieces,
+                                   const uint8_t* __restrict__ src_q, const uint8_t* __restrict__ src_s,
+                                   uint8_t* __restrict__ dst_q, uint8_t* __restrict__ dst_s) {
+  int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= npieces) return;
+  const int lane = (int)(p & 63);
+  const int64_t unit = p >> 6;            // tile * nchunk + chunk
+  const int chunk = (int)(unit % nchunk);
+  const int64_t tile = unit / nchunk;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t row = tile * TILE_N + n;
+  const bool row_ok = row < N;
+
+  uint8_t out[16];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) out[b] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int k = chunk * CHUNK_K + kmap(F, g, i);
+    uint32_t code = 0;
+    if (row_ok && k < K) {
+      if (F == NVFP4) {
+        uint8_t b = src_q[row * (K / 2) + k / 2];
+        code = (k & 1) ? (b >> 4) : (b & 15);
+      } else {
+        const int bb = (F == DUAL) ? 18 : 17, ns = (F == DUAL) ? 2 : 1;
+        const int blk = k >> 5, j = k & 31;
+        uint8_t b = src_q[(row * (K / 32) + blk) * bb + ns + (j & 15)];
+        code = (j >= 16) ? (b >> 4) : (b & 15);
+      }
+    }
+    out[nib_byte(F, i)] |= (uint8_t)(code << (4 * nib_high(F, i)));
+  }
+  u32x4 v;
+  __builtin_memcpy(&v, out, 16);
+  *reinterpret_cast<u32x4*>(dst_q + p * 16) = v;
+
+  // lane group 0 writes this row's scale bytes for the chunk
+  if (g == 0) {
+    constexpr int spr = scales_per_row_chunk(F);
+    uint8_t sb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < spr; ++j) {
+      const int k0 = chunk * CHUNK_K + j * group_size(F);
+      if (row_ok && k0 < K) {
+        if (F == NVFP4) {
+          sb[j] = src_s[row * (K / 16) + k0 / 16];
+        } else if (F == DUAL) {
+          sb[j] = src_q[(row * (K / 32) + (k0 >> 5)) * 18 + ((k0 >> 4) & 1)] & 0x7F;
+        } else {
+          sb[j] = src_q[(row * (K / 32) + (k0 >> 5)) * 17] & 0x7F;
+        }
+      }
+    }
+    uint8_t* d = dst_s + unit * unit_s(F) + n * spr;
+#pragma unroll
+    for (int j = 0; j < spr; ++j) d[j] = sb[j];
+  }
+}
+
+template <int F>
+__device__ __forceinline__ float level_of(uint32_t code) {
+  const uint32_t m = code & 7;
+  float mag;
+  if (F == NVFP4)  // E2M1: 0, .5, 1, 1.5, then 2, 3, 4, 6 = 2^((m>>1)-1) * (1 or 1.5)
+    mag = m < 4 ? 0.5f * (float)m : (float)((1u << (m >> 1)) >> 1) * ((m & 1) ? 1.5f : 1.0f);
+  else             // Codebook10: 0, 1, 2, 3, 4, 6, 8, 10
+    mag = m < 5 ? (float)m : (float)(m == 5 ? 6 : m == 6 ? 8 : 10);
+  return (code & 8) ? -mag : mag;
+}
+
+// One thread per 16-byte lane piece: 32 weights -> fl32(fl32(level*scale)*g).
+template <int F>
+__global__ void dequant_kernel(int N, int K, int nchunk, int64_t npieces, const uint8_t* __restrict__ q,
+                               const uint8_t* __restrict__ s, float gscale, float* __restrict__ w) {
+  int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= npieces) return;
+  const int lane = (int)(p & 63);
+  const int64_t unit = p >> 6;
+  const int chunk = (int)(unit % nchunk);
+  const int64_t tile = unit / nchunk;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t row = tile * TILE_N + n;
+  if (row >= N) return;
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(q + p * 16);
+  uint8_t qb[16];
+  __builtin_memcpy(qb, &qv, 16);
+  constexpr int spr = scales_per_row_chunk(F);
+  const uint8_t* srow = s + unit * unit_s(F) + n * spr;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int kk = kmap(F, g, i);
+    const int k = chunk * CHUNK_K + kk;
+    if (k >= K) continue;
+    const uint32_t code = (qb[nib_byte(F, i)] >> (4 * nib_high(F, i))) & 15u;
+    const float level = level_of<F>(code);
+    const uint32_t sbyte = srow[kk / group_size(F)];
+    const float sc = __builtin_amdgcn_cvt_f32_fp8(sbyte, 0);
+    const float prod = level * sc;  // exact: at most 3 + 4 significant bits
+    w[row * (int64_t)K + k] = prod * gscale;
+  }
+}
+
+}  // namespace fp4
+
+using namespace fp4;
+
+extern "C" int fp4_layout_bytes(int fmt, int64_t N, int64_t K, size_t* q_bytes, size_t* s_bytes) {
+  if (!fp4_valid_format(fmt) || !q_bytes || !s_bytes) return -1;
+  int rc = fp4_check_nk(fmt, N, K);
+  if (rc) return rc;
+  const int64_t tiles = (N + TILE_N - 1) / TILE_N, nchunk = (K + CHUNK_K - 1) / CHUNK_K;
+  *q_bytes = (size_t)(tiles * nchunk * UNIT_Q);
+  *s_bytes = (size_t)(tiles * nchunk * unit_s(fmt));
+  return 0;
+}
+
+extern "C" int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q, const void* src_s,
+                               void* dst_q, void* dst_s, void* stream) {
+  if (!fp4_valid_format(fmt) || !src_q || !dst_q || !dst_s) return -1;
+  if (fmt == NVFP4 && !src_s) return -1;
+  if (fmt != NVFP4 && src_s) return -1;
+  int rc = fp4_check_nk(fmt, N, K);
+  if (rc) return rc;
+  if (!fp4_aligned(dst_q, 16) || !fp4_aligned(dst_s, 16)) return -3;
+  const int64_t tiles = (N + TILE_N - 1) / TILE_N;
+  const int nchunk = (int)((K + CHUNK_K - 1) / CHUNK_K);
+  const int64_t npieces = tiles * nchunk * 64;
+  const int threads = 256;
+  const int64_t blocks = (npieces + threads - 1) / threads;
+  if (blocks > 0x7fffffffLL) return -4;
+  hipStream_t st = (hipStream_t)stream;
+  const uint8_t* sq = (const uint8_t*)src_q;
+  const uint8_t* ss = (const uint8_t*)src_s;
+  uint8_t* dq = (uint8_t*)dst_q;
+  uint8_t* ds = (uint8_t*)dst_s;
+  switch (fmt) {
+    case NVFP4: hipLaunchKernelGGL(pack_layout_kernel<NVFP4>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
+    case DUAL:  hipLaunchKernelGGL(pack_layout_kernel<DUAL>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
+    default:    hipLaunchKernelGGL(pack_layout_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
+  }
+  return fp4_launch_status();
+}
+
+extern "C" int fp4_dequant_f32(int fmt, int64_t N, int64_t K, const void* q, const void* s, float global_scale,
+                               float* w, void* stream) {
+  if (!fp4_valid_format(fmt) || !q || !s || !w) return -1;
+  int rc = fp4_check_nk(fmt, N, K);
+  if (rc) return rc;
+  if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(w, 4)) return -3;
+  const int64_t tiles = (N + TILE_N - 1) / TILE_N;
+  const int nchunk = (int)((K + CHUNK_K - 1) / CHUNK_K);
+  const int64_t npieces = tiles * nchunk * 64;
+  const int threads = 256;
+  const int64_t blocks = (npieces + threads - 1) / threads;
+  if (blocks > 0x7fffffffLL) return -4;
+  hipStream_t st = (hipStream_t)stream;
+  const uint8_t* qq = (const uint8_t*)q;
+  const uint8_t* sp = (const uint8_t*)s;
+  switch (fmt) {
+    case NVFP4: hipLaunchKernelGGL(dequant_kernel<NVFP4>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
+    case DUAL:  hipLaunchKernelGGL(dequant_kernel<DUAL>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
+    default:    hipLaunchKernelGGL(dequant_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
+  }
+  return fp4_launch_status();
+}

@@ -1,0 +1,250 @@
+// Device packers: fp32 weights -> canonical packed bytes.
+//
+// NVFP4, data-free round-to-nearest (Nanbeige4.2-3B-NVFP4A16 card, "Creation"; EdgeRock-4B-NVFP4
+// card, description): global amax -> g = fl32(amax / 2688); per 16-weight block an E4M3 scale,
+// rounded to nearest-even from blockmax / (6 g) in FP64; per weight the nearest E2M1 magnitude.
+//
+// ROCmFP4, exhaustive finite-UE4M3 MSE search (ROCmFP4 design page, section 03): one wave per
+// 32-weight block; for each scale group (two 16-weight halves for Dual, the whole block for
+// FAST) the 64 lanes score the 127 candidate codes, two each, in FP64 with the terms summed in
+// index order, then a wave reduction keeps the smallest error, breaking ties by distance to the
+// start code (E4M3 RNE of max|w| / 10) and then by the lower code.
+//
+// Every FP64 operation here is a separately rounded IEEE operation: contraction into fused
+// multiply-adds is switched off for this file, so the chosen codes do not depend on it.
+#include "common.h"
+#include "launch.h"
+#include "fp4w4a16.h"
+
+#pragma clang fp contract(off)
+
+namespace fp4 {
+
+// Nearest finite E4M3 code of v >= 0, ties to the even code, saturating at 0x7E (448).
+__device__ __forceinline__ int e4m3_rne(double v) {
+  if (!(v > 0.0)) return 0;
+  if (v >= 448.0) return 126;
+  if (v < 0.015625) {  // below 2^-6 the grid is k * 2^-9; code k (k = 8 is 2^-6, the first normal)
+    return (int)rint(v * 512.0);
+  }
+  int e;
+  const double f = frexp(v, &e);                  // v = f 2^e, f in [0.5, 1)
+  const int code = (e + 6) * 8 + (int)rint(16.0 * f - 8.0);  // exponent field e + 6, mantissa m
+  return code > 126 ? 126 : code;
+}
+
+// Value of a finite non-negative E4M3 / UE4M3 code (0..126), exact.
+__device__ __forceinline__ double e4m3_value(int c) {
+  const int e = c >> 3, m = c & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+// ---------------------------------------------------------------- NVFP4
+__global__ void nvfp4_zero_kernel(float* g) { g[0] = 0.f; }
+
+__global__ void nvfp4_amax_kernel(const float* __restrict__ w, int64_t count, float* g) {
+  float a = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    a = fmaxf(a, fabsf(w[i]));
+  for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(g), __float_as_uint(a));
+}
+
+// the global scale from amax: fl32(amax / 2688), or 0 when that is not positive
+__device__ __forceinline__ float nvfp4_global(float amax) {
+  return amax > 0.f ? (float)((double)amax / 2688.0) : 0.f;
+}
+
+// one thread per 16-weight block
+__global__ void nvfp4_pack_kernel(const float* __restrict__ w, int64_t nblocks, const float* __restrict__ gbuf,
+                                  uint8_t* __restrict__ wq, uint8_t* __restrict__ ws) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const float g = nvfp4_global(gbuf[0]);
+  float v[16];
+  const f32x4* src = reinterpret_cast<const f32x4*>(w + b * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 t = src[i];
+    v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+  }
+  uint8_t codes[16];
+  uint8_t sc = 0;
+  if (g > 0.f) {
+    double a = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmax(a, fabs((double)v[i]));
+    sc = (uint8_t)e4m3_rne(a / (6.0 * (double)g));
+    const double d = e4m3_value(sc) * (double)g;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double x = fabs((double)v[i]);
+      int c = 0;
+      if (d > 0.0) {
+        // E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6: midpoints .25 .75 1.25 1.75 2.5 3.5 5
+        const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+#pragma unroll
+        for (int j = 0; j < 7; ++j) c += (x > mid[j] * d) ? 1 : 0;
+        if (c < 7 && (c & 1) && x == mid[c] * d) ++c;   // exact tie -> even code
+      }
+      codes[i] = (uint8_t)(c | ((v[i] < 0.f && c != 0) ? 8 : 0));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) codes[i] = 0;
+  }
+  u32x2 packed = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) packed[i >> 2] |= (uint32_t)(codes[2 * i] | (codes[2 * i + 1] << 4)) << (8 * (i & 3));
+  *reinterpret_cast<u32x2*>(wq + b * 8) = packed;
+  ws[b] = sc;
+}
+
+__global__ void nvfp4_finish_kernel(float* g) {
+  const float gg = nvfp4_global(g[0]);
+  g[0] = gg > 0.f ? gg : 1.0f;
+}
+
+// ---------------------------------------------------------------- ROCmFP4
+// Codebook10 magnitude code of a / s: count midpoints * s below a, exact ties to the even code.
+__device__ __forceinline__ int cb10_nearest(double a, double s) {
+  if (s == 0.0) return 0;
+  const double mid[7] = {0.5, 1.5, 2.5, 3.5, 5.0, 7.0, 9.0};
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) c += (a > mid[j] * s) ? 1 : 0;
+  if (c < 7 && (c & 1) && a == mid[c] * s) ++c;
+  return c;
+}
+
+__device__ __forceinline__ double cb10_level(int c) {
+  return c < 5 ? (double)c : (c == 5 ? 6.0 : (c == 6 ? 8.0 : 10.0));
+}
+
+template <int G>
+__device__ __forceinline__ double group_error(const float* wv, const float* iv, double s) {
+  double e = 0.0;
+  for (int i = 0; i < G; ++i) {
+    const double a = fabs((double)wv[i]);
+    const double dlt = a - cb10_level(cb10_nearest(a, s)) * s;
+    double t = dlt * dlt;
+    if (iv) t = (double)iv[i] * t;
+    e = e + t;
+  }
+  return e;
+}
+
+// a better than b in the order (error, |code - start|, code)
+__device__ __forceinline__ bool better(double ea, int ca, double eb, int cb, int start) {
+  if (ea != eb) return ea < eb;
+  const int da = abs(ca - start), db = abs(cb - start);
+  if (da != db) return da < db;
+  return ca < cb;
+}
+
+template <int G>
+__device__ int search_group(const float* wv, const float* iv, int lane) {
+  double amax = 0.0;
+  for (int i = 0; i < G; ++i) amax = fmax(amax, fabs((double)wv[i]));
+  const int start = e4m3_rne(fmin(amax / 10.0, 448.0));
+  int bc = lane;
+  double be = group_error<G>(wv, iv, e4m3_value(lane));
+  if (lane + 64 < 127) {
+    const int c2 = lane + 64;
+    const double e2 = group_error<G>(wv, iv, e4m3_value(c2));
+    if (better(e2, c2, be, bc, start)) { be = e2; bc = c2; }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const double oe = __shfl_xor(be, off);
+    const int oc = __shfl_xor(bc, off);
+    if (better(oe, oc, be, bc, start)) { be = oe; bc = oc; }
+  }
+  return bc;
+}
+
+// one wave (64 threads) per 32-weight block
+template <int F>
+__global__ __launch_bounds__(256) void rocm_pack_kernel(const float* __restrict__ w, const float* __restrict__ imp,
+                                                        int64_t nblocks, uint8_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (blk >= nblocks) return;
+  float wv[32], iv[32];
+  const f32x4* src = reinterpret_cast<const f32x4*>(w + blk * 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 t = src[i];
+    wv[4 * i] = t[0]; wv[4 * i + 1] = t[1]; wv[4 * i + 2] = t[2]; wv[4 * i + 3] = t[3];
+  }
+  if (imp) {
+    const f32x4* isrc = reinterpret_cast<const f32x4*>(imp + blk * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 t = isrc[i];
+      iv[4 * i] = t[0]; iv[4 * i + 1] = t[1]; iv[4 * i + 2] = t[2]; iv[4 * i + 3] = t[3];
+    }
+  }
+  constexpr int BB = (F == DUAL) ? 18 : 17, NS = (F == DUAL) ? 2 : 1;
+  int sc[2];
+  if constexpr (F == DUAL) {
+    sc[0] = search_group<16>(wv, imp ? iv : nullptr, lane);
+    sc[1] = search_group<16>(wv + 16, imp ? iv + 16 : nullptr, lane);
+  } else {
+    sc[0] = search_group<32>(wv, imp ? iv : nullptr, lane);
+    sc[1] = sc[0];
+  }
+  uint8_t* ob = out + blk * BB;
+  if (lane < 16) {
+    const double s_lo = e4m3_value(sc[0]), s_hi = e4m3_value(sc[1]);
+    const int c_lo = cb10_nearest(fabs((double)wv[lane]), s_lo);
+    const int c_hi = cb10_nearest(fabs((double)wv[lane + 16]), s_hi);
+    const int n_lo = c_lo | ((wv[lane] < 0.f && c_lo) ? 8 : 0);
+    const int n_hi = c_hi | ((wv[lane + 16] < 0.f && c_hi) ? 8 : 0);
+    ob[NS + lane] = (uint8_t)(n_lo | (n_hi << 4));
+  }
+  if (lane == 0) {
+    ob[0] = (uint8_t)sc[0];
+    if (NS == 2) ob[1] = (uint8_t)sc[1];
+  }
+}
+
+}  // namespace fp4
+
+using namespace fp4;
+
+extern "C" int fp4_quantize_nvfp4(int64_t N, int64_t K, const float* w, void* wq, void* ws, float* g_out,
+                                  void* stream) {
+  if (!w || !wq || !ws || !g_out) return -1;
+  int rc = fp4_check_nk(NVFP4, N, K);
+  if (rc) return rc;
+  if (!fp4_aligned(w, 16) || !fp4_aligned(wq, 8) || !fp4_aligned(g_out, 4)) return -3;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t count = N * K, nblocks = count / 16;
+  hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(1), 0, st, g_out);
+  int grid = (int)((count + 255) / 256);
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(grid), dim3(256), 0, st, w, count, g_out);
+  hipLaunchKernelGGL(nvfp4_pack_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st, w, nblocks,
+                     (const float*)g_out, (uint8_t*)wq, (uint8_t*)ws);
+  hipLaunchKernelGGL(nvfp4_finish_kernel, dim3(1), dim3(1), 0, st, g_out);
+  return fp4_launch_status();
+}
+
+extern "C" int fp4_quantize_rocmfp4(int fmt, int64_t N, int64_t K, const float* w, const float* importance,
+                                    void* blocks, void* stream) {
+  if ((fmt != DUAL && fmt != FAST) || !w || !blocks) return -1;
+  int rc = fp4_check_nk(fmt, N, K);
+  if (rc) return rc;
+  if (!fp4_aligned(w, 16) || (importance && !fp4_aligned(importance, 16))) return -3;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t nblocks = N * K / 32;
+  const int64_t grid = (nblocks * 64 + 255) / 256;
+  if (grid > 0x7fffffffLL) return -4;
+  if (fmt == DUAL)
+    hipLaunchKernelGGL(rocm_pack_kernel<DUAL>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
+                       (uint8_t*)blocks);
+  else
+    hipLaunchKernelGGL(rocm_pack_kernel<FAST>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
+                       (uint8_t*)blocks);
+  return fp4_launch_status();
+}

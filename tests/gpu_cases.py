@@ -1,0 +1,51 @@
+"""Helpers shared by the GPU parity tests: seeded inputs, oracle packing, upload, comparison."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+from oracle import pack, ref
+
+FMTS = ("nvfp4", "rocmfp4_dual", "rocmfp4_fast")
+
+
+def canonical_tensors(fmt, packed, device="cuda"):
+    """Oracle-packed canonical bytes -> device tensors (src_q, src_s, g)."""
+    if fmt == "nvfp4":
+        wq, ws, g = packed
+        return (torch.from_numpy(np.ascontiguousarray(wq)).reshape(-1).to(device),
+                torch.from_numpy(np.ascontiguousarray(ws)).reshape(-1).to(device), float(g))
+    blocks, g = packed
+    return torch.from_numpy(np.ascontiguousarray(blocks)).reshape(-1).to(device), None, float(g)
+
+
+def upload(fmt, n, k, packed):
+    import block_scaled_fp4_w4a16_amd as fp4
+    q, s, g = canonical_tensors(fmt, packed)
+    pw = fp4.PackedWeight.from_canonical(fmt, n, k, q, s, g)
+    torch.cuda.synchronize()
+    return pw
+
+
+def make_case(fmt, n, k, *, dist="t", nu=5.0, outlier_frac=0.0, cfg=50, mat=0):
+    w = synth.weights(n, k, dist=dist, nu=nu, outlier_frac=outlier_frac, cfg=cfg, mat=mat)
+    return w, pack.pack(fmt, w)
+
+
+def x_tensor(x_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def check_product(fmt, packed, x_bits, y_gpu, cols=None, label=""):
+    """Compare y_gpu [M, N] (or the columns `cols`) with the FP64 oracle; assert the tolerance."""
+    sub = packed if cols is None else ref.rows(fmt, packed, cols)
+    w64 = ref.dequant(fmt, sub)
+    y_ref = ref.matmul(x_bits, w64)
+    b = ref.bound(x_bits, w64)
+    y = y_gpu.detach().cpu().numpy().astype(np.float64)
+    if cols is not None:
+        y = y[:, cols]
+    ok, worst = ref.check(y, y_ref, b)
+    assert ok, f"{label}: worst error / allowance = {worst}"
+    return worst

@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every declared entry point and rejects bad arguments before
+launching anything (runs without a GPU: every call here fails validation on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4w4a16.h")
+
+fp4 = pytest.importorskip("block_scaled_fp4_w4a16_amd")
+
+OK, ARG, SHAPE, ALIGN, UNSUP = 0, -1, -2, -3, -4
+FAKE = 1 << 20   # a 16-byte-aligned non-null address; never dereferenced by these calls
+NVFP4, DUAL, FAST = 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"fp4_pack_layout", "w4a16_gemv", "w4a16_gemm"} <= set(names)
+    h = ctypes.CDLL(fp4.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+
+
+def test_version_and_status_strings():
+    assert fp4.fp4_abi_version() == 1
+    for st in (OK, ARG, SHAPE, ALIGN, UNSUP, -6, 12345):
+        assert isinstance(fp4.fp4_status_string(st), str) and fp4.fp4_status_string(st)
+
+
+def test_layout_bytes():
+    # 16-row tiles x 128-wide chunks; 1 KiB of nibbles per unit; 8 (16-groups) or 4 (FAST) scale bytes per row
+    assert fp4.fp4_layout_bytes("nvfp4", 2048, 2048) == (2048 * 2048 // 2, 2048 * 2048 // 16)
+    assert fp4.fp4_layout_bytes("rocmfp4_dual", 4096, 4096) == (4096 * 4096 // 2, 4096 * 4096 // 16)
+    assert fp4.fp4_layout_bytes("rocmfp4_fast", 14336, 4096) == (14336 * 4096 // 2, 14336 * 4096 // 32)
+    # ragged: N = 17 -> 2 tiles, K = 160 -> 2 chunks
+    assert fp4.fp4_layout_bytes("rocmfp4_dual", 17, 160) == (2 * 2 * 1024, 2 * 2 * 128)
+    with pytest.raises(RuntimeError):
+        fp4.fp4_layout_bytes("rocmfp4_fast", 16, 48)     # K not a multiple of 32
+    with pytest.raises(RuntimeError):
+        fp4.fp4_layout_bytes("nvfp4", 0, 64)
+
+
+def test_layout_bytes_matches_weight_bytes_for_aligned_shapes():
+    # the kernel layout stores exactly the canonical weight + scale bytes when N % 16 == K % 128 == 0
+    from oracle import layouts
+    for fmt in ("nvfp4", "rocmfp4_dual", "rocmfp4_fast"):
+        q, s = fp4.fp4_layout_bytes(fmt, 256, 1024)
+        assert q + s == layouts.canonical_bytes(fmt, 256, 1024)
+
+
+def _raw():
+    return fp4.lib()
+
+
+@pytest.mark.parametrize("fn", ["w4a16_gemv", "w4a16_gemm", "w4a16_matmul"])
+def test_product_argument_errors(fn):
+    f = getattr(_raw(), fn)
+    good = dict(fmt=NVFP4, M=1, N=16, K=64, q=FAKE, s=FAKE, g=1.0, x=FAKE, y=FAKE, st=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["fmt"], a["M"], a["N"], a["K"], a["q"], a["s"], a["g"], a["x"], a["y"], a["st"])
+
+    assert call(fmt=7) == ARG
+    assert call(fmt=0) == ARG
+    assert call(q=None) == ARG
+    assert call(s=None) == ARG
+    assert call(x=None) == ARG
+    assert call(y=None) == ARG
+    assert call(K=40) == SHAPE                  # NVFP4 needs K % 16 == 0
+    assert call(fmt=DUAL, K=48) == SHAPE        # ROCmFP4 needs K % 32 == 0
+    assert call(N=0) == SHAPE
+    assert call(K=0) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(x=FAKE + 8) == ALIGN
+    assert call(q=FAKE + 4) == ALIGN
+    assert call(y=FAKE + 2) == ALIGN
+    assert call(M=0, q=None, x=None) == OK     # M = 0 is a no-op
+    assert call(N=1 << 31) == UNSUP
+    if fn == "w4a16_gemv":
+        assert call(M=17) == UNSUP
+
+
+def test_pack_layout_argument_errors():
+    f = _raw().fp4_pack_layout
+    assert f(NVFP4, 16, 64, FAKE, None, FAKE, FAKE, None) == ARG      # NVFP4 needs the scale plane
+    assert f(DUAL, 16, 64, FAKE, FAKE, FAKE, FAKE, None) == ARG       # ROCmFP4 carries scales in blocks
+    assert f(FAST, 16, 48, FAKE, None, FAKE, FAKE, None) == SHAPE
+    assert f(FAST, 16, 64, FAKE, None, FAKE + 4, FAKE, None) == ALIGN
+    assert f(9, 16, 64, FAKE, None, FAKE, FAKE, None) == ARG
+
+
+def test_dequant_and_quantize_argument_errors():
+    r = _raw()
+    assert r.fp4_dequant_f32(NVFP4, 16, 40, FAKE, FAKE, 1.0, FAKE, None) == SHAPE
+    assert r.fp4_dequant_f32(NVFP4, 16, 64, None, FAKE, 1.0, FAKE, None) == ARG
+    assert r.fp4_quantize_nvfp4(16, 40, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert r.fp4_quantize_nvfp4(16, 64, None, FAKE, FAKE, FAKE, None) == ARG
+    assert r.fp4_quantize_rocmfp4(NVFP4, 16, 64, FAKE, None, FAKE, None) == ARG
+    assert r.fp4_quantize_rocmfp4(DUAL, 16, 48, FAKE, None, FAKE, None) == SHAPE
+    assert r.fp4_quantize_rocmfp4(FAST, 16, 64, FAKE + 4, None, FAKE, None) == ALIGN
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        fp4._ptr(torch.zeros(4))

@@ -1,0 +1,245 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X; every call goes through the C ABI).
+
+Bars: dequantized weights bit-exact in FP32 (+0 == -0); products within
+|y - y_ref| <= 2e-3 * sum|x w| + 1e-6 elementwise; packers byte-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import layouts, pack, ref
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+fp4 = pytest.importorskip("block_scaled_fp4_w4a16_amd")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _announce(*a):
+    print("CASE", *a, flush=True)
+
+
+# ------------------------------------------------------------------ dequant (bit-exact)
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("n,k", [(16, 128), (37, 160), (64, 1024), (5, 32 * 7)])
+def test_dequant_bit_exact(fmt, n, k):
+    if fmt == "nvfp4" and k % 16:
+        pytest.skip()
+    _announce("dequant", fmt, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=51)
+    pw = gc.upload(fmt, n, k, packed)
+    got = pw.dequant().cpu().numpy()
+    want = ref.dequant_f32(fmt, packed)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)  # == treats +0 and -0 as equal
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+def test_dequant_all_codes_and_scales(fmt):
+    # every nibble code against every finite scale byte (and NaN scales for NVFP4)
+    _announce("dequant-all-codes", fmt)
+    rng = np.random.default_rng(8)
+    n, k = 128, 512
+    if fmt == "nvfp4":
+        wq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        ws = (np.arange(n * k // 16) % 256).astype(np.uint8).reshape(n, k // 16)
+        packed = (wq, ws, np.float32(0.37))
+    else:
+        bb = layouts.BLOCK_BYTES[fmt]
+        blocks = rng.integers(0, 256, size=(n, k // 32, bb), dtype=np.uint8)
+        ns = layouts.SCALES_PER_BLOCK[fmt]
+        blocks[:, :, :ns] = (np.arange(n * (k // 32) * ns) % 127).astype(np.uint8).reshape(n, k // 32, ns)
+        packed = (blocks, np.float32(1.0))
+    pw = gc.upload(fmt, n, k, packed)
+    got = pw.dequant().cpu().numpy()
+    want = ref.dequant_f32(fmt, packed)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+# ------------------------------------------------------------------ GEMV (M <= 16)
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16])
+def test_gemv_small_shapes(fmt, m):
+    for (n, k) in [(48, 256), (37, 160), (256, 1536)]:
+        _announce("gemv", fmt, m, n, k)
+        w, packed = gc.make_case(fmt, n, k, cfg=52, mat=n)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=52, mat=k)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        fp4.w4a16_gemv(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+        torch.cuda.synchronize()
+        gc.check_product(fmt, packed, x_bits, y, label=f"gemv {fmt} M={m} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+def test_gemv_one_hot_returns_weight_columns_exactly(fmt):
+    # x = e_k gives y[:, n] = W32[n, k] exactly (a single product, times g)
+    n, k = 64, 256
+    _announce("gemv-one-hot", fmt)
+    w, packed = gc.make_case(fmt, n, k, cfg=53)
+    pw = gc.upload(fmt, n, k, packed)
+    ks = np.arange(0, k, 17)[:16]
+    x_bits = np.zeros((len(ks), k), np.uint16)
+    x_bits[np.arange(len(ks)), ks] = 0x3F80
+    y = torch.empty((len(ks), n), device="cuda")
+    fp4.w4a16_gemv(fmt, len(ks), n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    want = ref.dequant_f32(fmt, packed)[:, ks].T
+    assert np.array_equal(y.cpu().numpy(), want)
+
+
+def test_gemv_canary_and_determinism():
+    fmt, m, n, k = "rocmfp4_dual", 3, 40, 512
+    _announce("gemv-canary", fmt)
+    w, packed = gc.make_case(fmt, n, k, cfg=54)
+    pw = gc.upload(fmt, n, k, packed)
+    x = gc.x_tensor(synth.activations(m, k, cfg=54))
+    buf = torch.full((m * n + 64,), 12345.0, device="cuda")
+    y1 = buf[32:32 + m * n]
+    fp4.w4a16_gemv(fmt, m, n, k, pw.q, pw.s, 1.0, x, y1)
+    torch.cuda.synchronize()
+    first = y1.clone()
+    for _ in range(3):
+        fp4.w4a16_gemv(fmt, m, n, k, pw.q, pw.s, 1.0, x, y1)
+    torch.cuda.synchronize()
+    assert torch.equal(first, y1)                         # bitwise repeatable
+    assert torch.all(buf[:32] == 12345.0) and torch.all(buf[32 + m * n:] == 12345.0)
+
+
+def test_gemv_m0_is_noop():
+    y = torch.full((4,), 7.0, device="cuda")
+    q = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    fp4.w4a16_gemv("nvfp4", 0, 16, 128, q, q, 1.0, torch.zeros(128, dtype=torch.bfloat16, device="cuda"), y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ------------------------------------------------------------------ GEMM
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("m", [1, 17, 63, 64, 100, 257])
+def test_gemm_shapes(fmt, m):
+    for (n, k) in [(200, 384), (37, 160)]:
+        _announce("gemm", fmt, m, n, k)
+        w, packed = gc.make_case(fmt, n, k, cfg=55, mat=n)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=55, mat=k)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+        torch.cuda.synchronize()
+        gc.check_product(fmt, packed, x_bits, y, label=f"gemm {fmt} M={m} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+def test_gemm_identity_returns_weights_exactly(fmt):
+    # x = I (M = K) gives y = W32^T exactly
+    n, k = 96, 256
+    _announce("gemm-identity", fmt)
+    w, packed = gc.make_case(fmt, n, k, cfg=56)
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = np.zeros((k, k), np.uint16)
+    x_bits[np.arange(k), np.arange(k)] = 0x3F80
+    y = torch.empty((k, n), device="cuda")
+    fp4.w4a16_gemm(fmt, k, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), ref.dequant_f32(fmt, packed).T)
+
+
+@pytest.mark.parametrize("m", [1, 16, 17, 64])
+def test_matmul_dispatch(m):
+    fmt, n, k = "nvfp4", 64, 256
+    _announce("matmul", m)
+    w, packed = gc.make_case(fmt, n, k, cfg=57)
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.activations(m, k, cfg=57)
+    y = pw.matmul(gc.x_tensor(x_bits))
+    torch.cuda.synchronize()
+    gc.check_product(fmt, packed, x_bits, y, label=f"matmul M={m}")
+
+
+# ------------------------------------------------------------------ device packers (byte-exact)
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("dist,outl", [("t", 0.0), ("t", 0.001), ("normal", 0.0)])
+def test_device_packer_matches_oracle(fmt, dist, outl):
+    n, k = 64, 512
+    _announce("quantize", fmt, dist, outl)
+    w = synth.weights(n, k, dist=dist, nu=4.0, outlier_frac=outl, cfg=58)
+    want = pack.pack(fmt, w)
+    wt = torch.from_numpy(w).cuda()
+    if fmt == "nvfp4":
+        wq = torch.empty(n * k // 2, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(n * k // 16, dtype=torch.uint8, device="cuda")
+        g = torch.empty(1, device="cuda")
+        fp4.fp4_quantize_nvfp4(n, k, wt, wq, ws, g)
+        torch.cuda.synchronize()
+        assert np.array_equal(wq.cpu().numpy().reshape(n, -1), want[0])
+        assert np.array_equal(ws.cpu().numpy().reshape(n, -1), want[1])
+        assert g.item() == want[2]
+    else:
+        bb = layouts.BLOCK_BYTES[fmt]
+        blocks = torch.empty(n * (k // 32) * bb, dtype=torch.uint8, device="cuda")
+        fp4.fp4_quantize_rocmfp4(fmt, n, k, wt, None, blocks)
+        torch.cuda.synchronize()
+        assert np.array_equal(blocks.cpu().numpy().reshape(n, k // 32, bb), want[0])
+
+
+@pytest.mark.parametrize("fmt", ["rocmfp4_dual", "rocmfp4_fast"])
+def test_device_packer_importance(fmt):
+    n, k = 16, 256
+    _announce("quantize-importance", fmt)
+    w = synth.weights(n, k, dist="t", nu=4.0, outlier_frac=0.01, cfg=59)
+    v = np.abs(synth.weights(n, k, dist="normal", sigma=1.0, cfg=59, mat=1)).astype(np.float32)
+    want = pack.pack(fmt, w, importance=v)
+    blocks = torch.empty(n * (k // 32) * layouts.BLOCK_BYTES[fmt], dtype=torch.uint8, device="cuda")
+    fp4.fp4_quantize_rocmfp4(fmt, n, k, torch.from_numpy(w).cuda(), torch.from_numpy(v).cuda(), blocks)
+    torch.cuda.synchronize()
+    assert np.array_equal(blocks.cpu().numpy().reshape(want[0].shape), want[0])
+
+
+def test_device_packer_edge_values():
+    # zeros, exact ties on every E2M1 / Codebook10 midpoint, a huge and a tiny block
+    n, k = 16, 128
+    w = np.zeros((n, k), np.float32)
+    w[0, :7] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * 448 / 6 * 2  # NVFP4 ties at d
+    w[1, :16] = 2688.0 * np.linspace(-1, 1, 16)
+    w[2, :32] = np.array([0.5, 1.5, 2.5, 3.5, 5, 7, 9] * 4 + [10, 11, 12, 13], np.float32)
+    w[3, :32] = 1e-6
+    w[4, 16:48] = -3e-3
+    for fmt in gc.FMTS:
+        _announce("quantize-edges", fmt)
+        want = pack.pack(fmt, w)
+        wt = torch.from_numpy(w).cuda()
+        if fmt == "nvfp4":
+            wq = torch.empty(n * k // 2, dtype=torch.uint8, device="cuda")
+            ws = torch.empty(n * k // 16, dtype=torch.uint8, device="cuda")
+            g = torch.empty(1, device="cuda")
+            fp4.fp4_quantize_nvfp4(n, k, wt, wq, ws, g)
+            torch.cuda.synchronize()
+            assert np.array_equal(wq.cpu().numpy().reshape(n, -1), want[0])
+            assert np.array_equal(ws.cpu().numpy().reshape(n, -1), want[1])
+            assert g.item() == want[2]
+        else:
+            bb = layouts.BLOCK_BYTES[fmt]
+            blocks = torch.empty(n * (k // 32) * bb, dtype=torch.uint8, device="cuda")
+            fp4.fp4_quantize_rocmfp4(fmt, n, k, wt, None, blocks)
+            torch.cuda.synchronize()
+            assert np.array_equal(blocks.cpu().numpy().reshape(n, k // 32, bb), want[0])
+    # all-zero matrix: g = 1 and zero codes
+    wq = torch.empty(n * k // 2, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(n * k // 16, dtype=torch.uint8, device="cuda")
+    g = torch.empty(1, device="cuda")
+    fp4.fp4_quantize_nvfp4(n, k, torch.zeros(n, k, device="cuda"), wq, ws, g)
+    torch.cuda.synchronize()
+    assert g.item() == 1.0 and not wq.any() and not ws.any()

@@ -1,0 +1,64 @@
+"""Parity at the benchmark workloads' full sizes, through the same entry points and dispatch
+the benchmark times. Weights are drawn by synth and packed by the CPU oracle; outputs are
+checked against the FP64 oracle on every column (or, for the prefill GEMM, on sampled
+columns over all rows)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import pack
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+fp4 = pytest.importorskip("block_scaled_fp4_w4a16_amd")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(fmt, cfg, mat, m, cols=None):
+    wl = synth.WORKLOADS[cfg]
+    n, k = wl["shapes"][mat]
+    print("CASE workload", wl["name"], fmt, n, k, "M", m, flush=True)
+    w = synth.workload_weights(cfg, mat)
+    packed = pack.pack(fmt, w)
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.workload_activations(cfg, mat, m)
+    y = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_matmul(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    return gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"{wl['name']} {fmt} M={m}")
+
+
+def test_nvfp4_2048x2048_m1():
+    _run("nvfp4", 0, 0, 1)
+
+
+def test_dual_4096x4096_m1():
+    _run("rocmfp4_dual", 1, 0, 1)
+
+
+def test_decode_sweep_one_layer():
+    # the seven shapes of one 4B-class layer (the sweep repeats them 36 times)
+    for mat in range(7):
+        _run("nvfp4", 2, mat, 1)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "rocmfp4_dual", "rocmfp4_fast"])
+@pytest.mark.parametrize("m", [1, 9, 16])
+def test_spec_verify(fmt, m):
+    for mat in range(2):
+        _run(fmt, 3, mat, m)
+
+
+@pytest.mark.parametrize("fmt", ["rocmfp4_fast", "nvfp4"])
+def test_prefill_m2048(fmt):
+    rng = np.random.default_rng(60)
+    n = synth.WORKLOADS[4]["shapes"][0][0]
+    cols = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, n - 1], rng.choice(n, 57, replace=False)]))
+    _run(fmt, 4, 0, 2048, cols=cols)
