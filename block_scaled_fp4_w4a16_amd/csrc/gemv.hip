@@ -10,10 +10,10 @@
 #include "common.h"
 #include "launch.h"
 #include "fp4w4a16.h"
+#include <stdlib.h>
 
 namespace fp4 {
 
-constexpr int GEMV_UNROLL = 4;  // chunks whose weight loads a wave issues back to back
 
 template <int F>
 struct WeightRegs {
@@ -99,69 +99,119 @@ __device__ __forceinline__ void unit_mac(f32x4& acc, const WeightRegs<F>& w, con
   }
 }
 
-// x fragments of one chunk for this lane: 8 x 4 bf16 (16-groups) or 4 x 8 bf16 (FAST).
-template <int F>
-__device__ __forceinline__ void load_x(uint32_t (&xa)[16], const uint16_t* __restrict__ xr, bool xrow, int kc,
-                                       int g, int K) {
-  if constexpr (F == FAST) {
+// x staging. Each wave copies the x columns of the chunks it is about to process into its own LDS
+// region, in per-lane fragment order: for chunk slot u, lane group g and x row m, the 32 bf16 that lane
+// (m, g) feeds to the MFMAs of that chunk sit as 64 contiguous bytes. The copy is one coalesced
+// 16-byte global load per piece (a chunk row of x is 16 pieces), issued before the wave's weight
+// loads so that it does not queue behind them; no workgroup barrier is involved.
+template <int F, int U>
+__device__ __forceinline__ void stage_x_wave(uint8_t* xs, const uint16_t* __restrict__ x, int M, int K, int c0, int W,
+                                             int nchunk, int lane) {
+  const int pieces = U * M * 16;
+  for (int p0 = 0; p0 < pieces; p0 += 64 * 4) {
+    u32x4 v[4];
+    int dst[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = kc + 32 * j + 8 * g;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (xrow && k < K) v = *reinterpret_cast<const u32x4*>(xr + k);
-      xa[4 * j] = v[0]; xa[4 * j + 1] = v[1]; xa[4 * j + 2] = v[2]; xa[4 * j + 3] = v[3];
+    for (int i = 0; i < 4; ++i) {       // up to four loads in flight per lane before the writes
+      const int p = p0 + 64 * i + lane;
+      dst[i] = -1;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (p < pieces) {
+        const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
+        const int c = c0 + u * W;
+        const int k = c * CHUNK_K + 8 * qq;
+        if (c < nchunk && k < K) v[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k);
+        dst[i] = (u * 4 * M + m) * 64 + ((F == FAST) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
+                                                        : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
+      }
     }
-  } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = kc + 16 * j + 4 * g;
-      u32x2 v = {0u, 0u};
-      if (xrow && k < K) v = *reinterpret_cast<const u32x2*>(xr + k);
-      xa[2 * j] = v[0]; xa[2 * j + 1] = v[1];
+    for (int i = 0; i < 4; ++i) {
+      if (dst[i] < 0) continue;
+      if constexpr (F == FAST) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
+        *reinterpret_cast<u32x4*>(xs + dst[i]) = v[i];
+      } else {                          // k = 16 j + 4 g + t: halves go to lane groups 2 (qq & 1) and +1
+        *reinterpret_cast<u32x2*>(xs + dst[i]) = u32x2{v[i][0], v[i][1]};
+        *reinterpret_cast<u32x2*>(xs + dst[i] + M * 64) = u32x2{v[i][2], v[i][3]};
+      }
     }
   }
 }
 
-template <int F, int T, int RU>
+template <int F, int T, int U>
+__device__ __forceinline__ void load_batch(WeightRegs<F> (&wr)[U][T], const uint8_t* __restrict__ qp,
+                                           const uint8_t* __restrict__ sp, int c0, int W, int nchunk, int tile0,
+                                           int ntiles, int lane, int n) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = c0 + u * W;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (c < nchunk && tile0 + t < ntiles) {
+        load_unit<F>(wr[u][t], qp, sp, (int64_t)(tile0 + t) * nchunk + c, lane, n);
+      } else {
+        wr[u][t].q = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < (F == FAST ? 1 : 2); ++i) wr[u][t].s[i] = 0u;
+      }
+    }
+  }
+}
+
+// Dynamic LDS: [W waves][U chunks][4 lane groups][M rows][64 B] of staged x, then the
+// cross-wave reduction buffer [W][T][64 lanes][4] floats.
+template <int F, int T, int RU, int U>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                                     const uint16_t* __restrict__ x, float* __restrict__ y,
                                                     int M, int N, int K, int ntiles, int nchunk, float gscale) {
-  extern __shared__ float red[];  // [W][T][64 lanes][4]
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  const int n = lane & 15, g = lane >> 4, m = lane & 15;
   const int tile0 = blockIdx.x * T;
-  const bool xrow = (lane & 15) < M;
-  const uint16_t* xr = x + (int64_t)(lane & 15) * K;
+  const bool xrow = m < M;
+  const size_t xw_bytes = (size_t)U * 4 * M * 64;
+  uint8_t* xs = smem + wave * xw_bytes;
+  float* red = reinterpret_cast<float*>(smem + W * xw_bytes);
 
   f32x4 acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = wave; c0 < nchunk; c0 += W * GEMV_UNROLL) {
-    WeightRegs<F> wr[GEMV_UNROLL][T];
+  WeightRegs<F> wr[U][T];
+  bool have = false;
+  for (int c0 = wave; c0 < nchunk; c0 += W * U) {
+    stage_x_wave<F, U>(xs, x, M, K, c0, W, nchunk, lane);     // x first: it must not wait behind weights
+    if (!have) load_batch<F, T, U>(wr, qp, sp, c0, W, nchunk, tile0, ntiles, lane, n);
+    // the next batch's weights go out before this batch is computed
+    WeightRegs<F> nx[U][T];
+    const int c1 = c0 + W * U;
+    have = c1 < nchunk;
+    if (have) load_batch<F, T, U>(nx, qp, sp, c1, W, nchunk, tile0, ntiles, lane, n);
 #pragma unroll
-    for (int u = 0; u < GEMV_UNROLL; ++u) {
-      const int c = c0 + u * W;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        if (c < nchunk && tile0 + t < ntiles) {
-          load_unit<F>(wr[u][t], qp, sp, (int64_t)(tile0 + t) * nchunk + c, lane, n);
-        } else {
-          wr[u][t].q = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int i = 0; i < (F == FAST ? 1 : 2); ++i) wr[u][t].s[i] = 0u;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < GEMV_UNROLL; ++u) {
-      const int c = c0 + u * W;
-      if (c < nchunk) {
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u * W < nchunk) {
+        // this lane's 32 x values of chunk slot u, read from the wave's staging area just before use
         uint32_t xa[16];
-        load_x<F>(xa, xr, xrow, c * CHUNK_K, g, K);
+        if (xrow) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(xs + ((u * 4 + g) * M + m) * 64);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const u32x4 w4 = src[v];
+            xa[4 * v] = w4[0]; xa[4 * v + 1] = w4[1]; xa[4 * v + 2] = w4[2]; xa[4 * v + 3] = w4[3];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xa[i] = 0u;
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) unit_mac<F, RU>(acc[t], wr[u][t], xa);
       }
+    }
+    if (have) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < T; ++t) wr[u][t] = nx[u][t];
     }
   }
 
@@ -185,11 +235,17 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* __restrict__ 
   }
 }
 
-template <int F, int T, int RU>
+constexpr int GEMV_LDS_MAX = 160 * 1024;
+
+template <int F, int T, int RU, int U>
 static void launch_gemv(int nwg, int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x,
                         float* y, int M, int N, int K, int ntiles, int nchunk, float g) {
-  const size_t lds = (size_t)W * T * 64 * 4 * sizeof(float);
-  hipLaunchKernelGGL((gemv_kernel<F, T, RU>), dim3(nwg), dim3(64 * W), lds, st, q, s, x, y, M, N, K, ntiles,
+  const size_t lds = (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float);
+  // allow more than 64 KiB of dynamic LDS for this instantiation (once; thread-safe static init)
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
+  (void)attr;
+  hipLaunchKernelGGL((gemv_kernel<F, T, RU, U>), dim3(nwg), dim3(64 * W), lds, st, q, s, x, y, M, N, K, ntiles,
                      nchunk, g);
 }
 
@@ -200,14 +256,16 @@ static void dispatch_gemv(int M, hipStream_t st, const uint8_t* q, const uint8_t
   const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const int T = (M > 4) ? 2 : 1;
   const int nwg = (ntiles + T - 1) / T;
-  int W = (2048 + nwg - 1) / nwg;  // aim for ~8 waves per CU across 256 CUs
-  if (W > 16) W = 16;
+  int W = (4096 + nwg - 1) / nwg;  // aim for ~16 waves per CU across 256 CUs
+  if (const char* e = getenv("FP4_GEMV_WAVES")) W = atoi(e);  // tuning override
+  const int wmax = (M > 4) ? 8 : 16;  // keep the staged x (W * U * M * 256 B) inside the LDS
+  if (W > wmax) W = wmax;
   if (W > nchunk) W = nchunk;
   if (W < 1) W = 1;
-  if (M == 1)      launch_gemv<F, 1, 1>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else if (M == 2) launch_gemv<F, 1, 2>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else if (M <= 4) launch_gemv<F, 1, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else             launch_gemv<F, 2, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  if (M == 1)      launch_gemv<F, 1, 1, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  else if (M == 2) launch_gemv<F, 1, 2, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  else if (M <= 4) launch_gemv<F, 1, 4, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  else             launch_gemv<F, 2, 4, 2>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
 }
 
 }  // namespace fp4
