@@ -1,23 +1,40 @@
 // Prefill-shaped W4A16 product (any M >= 1; intended for M >= 64).
 //
-// A workgroup computes a BM x BN tile of y. Per 128-wide K chunk it
-//   1. stages the x tile [BM][128] (bf16) into LDS, in the chunk's permuted k' order, and
-//   2. loads the packed weight units of its BN rows, dequantizes every weight once to
-//      exact bf16 level*scale (g deferred) and writes the tile [BN][128] into LDS, in the
-//      same k' order (the contraction only needs A and B to agree on the k order),
-// then its four waves run bf16 MFMA 16x16x32 over the chunk with FP32 accumulators.
-// The epilogue multiplies by g and stores fp32 y. Global loads of chunk c+1 are issued
-// before the MFMAs of chunk c so that memory latency hides under the matrix work.
+// A workgroup of 4 waves computes a 256 x 256 tile of y; wave w owns all 256 rows of the tile and weight rows
+// 64 w .. 64 w + 63, so every weight is dequantized exactly once per workgroup. The K loop runs over pipeline
+// stages of 64 positions: stage h is half hh = h % 2 of 128-wide chunk c = h / 2, i.e. lane pieces g = 2 hh
+// and 2 hh + 1 of every packed unit.
+//  * All global reads are buffer loads that write LDS directly (no registers), into a 3-deep ring, two
+//    stages ahead of use: the 256 x 64 x-values of the stage (natural k order over the stage's k subset,
+//    16-byte segments XOR-swizzled by row so the MFMA operand reads have no bank conflicts), each wave's
+//    packed weight bytes and scale bytes.
+//  * Each wave reads its packed weights back and dequantizes them straight into bf16 MFMA B operands as
+//    exact level * scale; x fragments are the A operands. bf16 MFMA 32x32x16, FP32 accumulators. The
+//    k-steps are software-pipelined: the next k-step's A reads and B dequantization are issued before the
+//    current k-step's MFMAs so that one wave per SIMD keeps the matrix core busy.
+//  * The epilogue multiplies by g and stores fp32 y.
+// Rows beyond M / N and columns beyond K come back as zeros from the buffer loads (raw buffers return zero
+// past num_records), so the loop has no bounds branches.
 #include "common.h"
 #include "launch.h"
 #include "fp4w4a16.h"
 
 namespace fp4 {
 
-constexpr int GM_BM = 128, GM_BN = 128, GM_THREADS = 256;
-constexpr int LDS_ROW = CHUNK_K * 2 + 16;        // bytes per LDS row (128 bf16 + pad)
-constexpr int X_PIECES = GM_BM * 16 / GM_THREADS;  // 16-byte x pieces per thread per chunk (8)
-constexpr int W_PIECES = (GM_BN / TILE_N) * 64 / GM_THREADS;  // lane pieces per thread (2)
+constexpr int GM_BM = 256, GM_BN = 256, GM_WAVES = 4, GM_THREADS = 64 * GM_WAVES;
+constexpr int GM_STAGE_K = 64;                        // positions per pipeline stage
+constexpr int GM_ROW_BYTES = GM_STAGE_K * 2;          // 128 bytes of x per row and stage
+constexpr int GM_X_BYTES = GM_BM * GM_ROW_BYTES;      // 32 KiB of x per stage
+constexpr int GM_W_BYTES = GM_WAVES * 4 * 512;        // per wave: 4 tiles x 2 lane pieces of 256 B
+constexpr int GM_S_BYTES = GM_WAVES * 4 * 128;        // per wave: 4 tiles x scale bytes (<= 128 each)
+constexpr int GM_STAGE_BYTES = GM_X_BYTES + GM_W_BYTES + GM_S_BYTES;  // 42 KiB
+constexpr int GM_RING = 3;
+constexpr int GM_LDS = GM_RING * GM_STAGE_BYTES;      // 126 KiB
+constexpr int GM_X_SLOTS = GM_BM * 8 / GM_THREADS;    // 16-byte x slots per thread per stage (8)
+// vector-memory instructions per thread per stage: x slots, 2 weight loads, scale loads (512 or 256 bytes)
+__host__ __device__ constexpr int gm_loads_per_stage(int f) { return GM_X_SLOTS + 2 + (f == FAST ? 1 : 2); }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // bf16 of two f32 values (exact here: level*scale has at most 7 significant bits)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -27,187 +44,313 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return u;
 }
 
-// 32 weights of one lane piece -> 16 dwords of bf16 pairs in lane-position order i = 0..31.
-template <int F>
-__device__ __forceinline__ void dequant_piece(const u32x4& q, const u32x2& s, uint32_t (&out)[16]) {
-  if constexpr (F == NVFP4) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      // positions 8d..8d+7; group of position i is i / 4 -> groups 2d (bytes 0,1) and 2d+1 (bytes 2,3)
-      const uint32_t sw = s[d >> 1];
-      const float s0 = (d & 1) ? e4m3_to_f32<2>(sw) : e4m3_to_f32<0>(sw);
-      const float s1 = (d & 1) ? e4m3_to_f32<3>(sw) : e4m3_to_f32<1>(sw);
-      const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[d], 1.0f, 0);
-      const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[d], 1.0f, 1);
-      const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[d], 1.0f, 2);
-      const f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[d], 1.0f, 3);
-      out[4 * d + 0] = pack_bf16x2(a[0] * s0, a[1] * s0);
-      out[4 * d + 1] = pack_bf16x2(b[0] * s0, b[1] * s0);
-      out[4 * d + 2] = pack_bf16x2(c[0] * s1, c[1] * s1);
-      out[4 * d + 3] = pack_bf16x2(e[0] * s1, e[1] * s1);
-    }
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x2& a, const f32x2& b, const f32x2& c, const f32x2& e, float sc) {
+  u32x4 v = {pack_bf16x2(a[0] * sc, a[1] * sc), pack_bf16x2(b[0] * sc, b[1] * sc), pack_bf16x2(c[0] * sc, c[1] * sc),
+             pack_bf16x2(e[0] * sc, e[1] * sc)};
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// Four Codebook10 nibbles (the low nibbles of the four bytes of w when HIGH is false, the high nibbles
+// otherwise) -> four E4M3 bytes.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t cb10_quad(uint32_t w) {
+  if constexpr (HIGH) {
+    return __builtin_amdgcn_perm(CB10_E4M3_HI, CB10_E4M3_LO, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
   } else {
+    return __builtin_amdgcn_perm(CB10_E4M3_HI, CB10_E4M3_LO, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  }
+}
+
+// B operand of k-step s for this lane: 8 consecutive positions of the stage's k subset (see the kernel),
+// dequantized to bf16 level * scale. w0 / w1 are this lane's two dwords of lane piece 2hh / 2hh + 1.
+template <int F, int S>
+__device__ __forceinline__ bf16x8 b_operand(const u32x2& w0, const u32x2& w1, float sc) {
+  if constexpr (F == FAST) {
+    // 8 positions = one dword: dword S / 2 of piece S % 2, positions in lane-piece order
+    const uint32_t w = (S & 1) ? w1[S >> 1] : w0[S >> 1];
+    const uint32_t lo = cb10_quad<false>(w), hi = cb10_quad<true>(w);
+    return to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true), sc);
+  } else if constexpr (F == DUAL) {
+    // 4 positions from piece 2hh (k 0..3 of the run) and 4 from piece 2hh + 1 (k 4..7): the low or high
+    // nibbles of dword S / 2 of each piece
+    const uint32_t a = cb10_quad<(S & 1) != 0>(w0[S >> 1]), b = cb10_quad<(S & 1) != 0>(w1[S >> 1]);
+    return to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(a, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(a, 1.0f, true),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b, 1.0f, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b, 1.0f, true), sc);
+  } else {
+    // NVFP4: 16-bit half S % 2 of dword S / 2 of each piece (4 nibbles each), joined into one dword
+    const uint32_t w = __builtin_amdgcn_perm(w1[S >> 1], w0[S >> 1], (S & 1) ? 0x07060302u : 0x05040100u);
+    return to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
+                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), sc);
+  }
+}
+
+// This lane's weight bytes for one stage, read back from LDS: for each of the wave's two 32-row column
+// tiles, dwords 2 kh and 2 kh + 1 of the row's two lane pieces, and the row's scale bytes of the chunk.
+struct WRegs {
+  u32x2 w[2][2];
+  u32x2 sc[2];
+};
+
+// Buffer descriptors (raw, stride 0): loads past num_records return zeros.
+struct GemmSrc {
+  __amdgpu_buffer_rsrc_t x, q, s;
+};
+
+// The descriptor must live in scalar registers; its inputs are wave-uniform, so read them from lane 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
+}
+
+// Stage k subset and its natural order (segment sigma = 16-byte group of 8 positions, 8 per stage):
+//   16-weight groups: sigma = j -> k = 16 sigma + 8 hh + u          (u = 0..7; group j of the chunk)
+//   FAST:             sigma = 2 j + b -> k = 32 j + 16 hh + 8 b + u (block j of the chunk)
+template <int F>
+__device__ __forceinline__ int stage_k(int c, int hh, int sigma) {
+  return c * CHUNK_K + (F == FAST ? 32 * (sigma >> 1) + 16 * hh + 8 * (sigma & 1) : 16 * sigma + 8 * hh);
+}
+
+// x of stage h: global -> LDS ring slot, one 16-byte direct load per slot. Slot S of the stage holds row
+// S / 8, physical segment S % 8 = sigma ^ (row % 8).
+template <int F, bool RAGGED>
+__device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h, int K, int wave, int lane) {
+  const int c = h >> 1, hh = h & 1;
+  uint8_t* base = ring + (h % GM_RING) * GM_STAGE_BYTES;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t lo, hi;
-      cb10_to_e4m3(q[d], lo, hi);
-      float s0, s1;
-      if constexpr (F == DUAL) {  // positions 8d..8d+3 -> group 2d, 8d+4..8d+7 -> group 2d+1
-        const uint32_t sw = s[d >> 1];
-        s0 = (d & 1) ? e4m3_to_f32<2>(sw) : e4m3_to_f32<0>(sw);
-        s1 = (d & 1) ? e4m3_to_f32<3>(sw) : e4m3_to_f32<1>(sw);
-      } else {                    // positions 8d..8d+7 -> block d
-        const uint32_t sw = s[0];
-        s0 = (d == 0) ? e4m3_to_f32<0>(sw) : (d == 1) ? e4m3_to_f32<1>(sw) : (d == 2) ? e4m3_to_f32<2>(sw)
-                                                                                    : e4m3_to_f32<3>(sw);
-        s1 = s0;
-      }
-      const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false);
-      const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true);
-      const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false);
-      const f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true);
-      out[4 * d + 0] = pack_bf16x2(a[0] * s0, a[1] * s0);
-      out[4 * d + 1] = pack_bf16x2(b[0] * s0, b[1] * s0);
-      out[4 * d + 2] = pack_bf16x2(c[0] * s1, c[1] * s1);
-      out[4 * d + 3] = pack_bf16x2(e[0] * s1, e[1] * s1);
-    }
+  for (int i = 0; i < GM_X_SLOTS; ++i) {
+    const int first = (wave * GM_X_SLOTS + i) * 64;          // first slot of this instruction (uniform)
+    const int slot = first + lane;
+    const int row = slot >> 3, sigma = (slot & 7) ^ (row & 7);
+    const int k = stage_k<F>(c, hh, sigma);
+    const uint32_t off = (!RAGGED || k < K) ? (uint32_t)(row * K + k) * 2u : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(base + first * 16),
+                                             16, off, 0, 0, 0);
+  }
+}
+
+// Weights of stage h: the two lane pieces 2 hh, 2 hh + 1 of a unit are 512 contiguous bytes, so the wave's four
+// tiles take 2 KiB (two 16-byte direct loads per lane), plus the scale bytes of the same four tiles.
+template <int F>
+__device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h, int nchunk, int wave, int lane) {
+  const int c = h >> 1, hh = h & 1;
+  uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const int tt = 2 * part + (lane >> 5);
+    const uint32_t off = (uint32_t)(tt * nchunk + c) * UNIT_Q + 512 * hh + (lane & 31) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16, off, 0,
+        0, 0);
+  }
+  constexpr int us = unit_s(F);                   // 128 (16-weight groups) or 64 (FAST) bytes per unit
+  constexpr int lanes_per_tile = us / 4;          // 4-byte loads
+  constexpr int parts = 4 * lanes_per_tile / 64;  // 2 or 1
+#pragma unroll
+  for (int part = 0; part < parts; ++part) {
+    const int idx = part * 64 + lane;
+    const int tt = idx / lanes_per_tile;
+    const uint32_t off = (uint32_t)(tt * nchunk + c) * us + (idx % lanes_per_tile) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256), 4,
+        off, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void read_w(WRegs& r, const uint8_t* stage, int F_spr, int F_us, int wave, int lane) {
+  const int kh = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rl = 32 * j + (lane & 31);
+    const int t = rl >> 4, n = rl & 15;
+    const uint8_t* wb = stage + GM_X_BYTES + wave * 2048 + t * 512 + n * 16 + 8 * kh;
+    r.w[j][0] = *reinterpret_cast<const u32x2*>(wb);
+    r.w[j][1] = *reinterpret_cast<const u32x2*>(wb + 256);
+    const uint8_t* sb = stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + t * F_us + n * F_spr;
+    if (F_spr == 4) r.sc[j] = u32x2{*reinterpret_cast<const uint32_t*>(sb), 0u};
+    else r.sc[j] = *reinterpret_cast<const u32x2*>(sb);
+  }
+}
+
+// Workgroup barrier without a memory fence; the "memory" clobber keeps the compiler from moving LDS
+// accesses across it. The waits that make the LDS data complete are explicit (wait_vmcnt).
+__device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt with only a vector-memory bound (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// B operands of k-step S for the wave's two column tiles.
+template <int F, int S>
+__device__ __forceinline__ void b_pair(bf16x8 (&b)[2], const WRegs& r, int kh) {
+  const int sigma = 4 * kh + S;
+  const int gi = (F == FAST) ? (sigma >> 1) : sigma;     // scale byte of this k-step
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t sw = (gi & 4) ? r.sc[j][1] : r.sc[j][0];
+    const float sc = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * (gi & 3)), 0);
+    b[j] = b_operand<F, S>(r.w[j][0], r.w[j][1], sc);
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void a_frags(bf16x8 (&a)[8], const uint8_t* stage, int lane) {
+  const int sigma = 4 * (lane >> 5) + S;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 32 * i + (lane & 31);
+    a[i] = *reinterpret_cast<const bf16x8*>(stage + row * GM_ROW_BYTES + 16 * (sigma ^ (row & 7)));
+  }
+}
+
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bf16x8 (&b)[2]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// MFMAs of one stage for the wave's 256 x 64 tile. k-step s, lane half kh = lane / 32 use segment
+// sigma = 4 kh + s: the x fragment is that segment of the lane's row, and the B operand is built from
+// dwords 2 kh + s / 2 of the two lane pieces (see b_operand), whose scale group is sigma (16-weight
+// groups) or block sigma / 2 (FAST). Software-pipelined: operands of k-step s + 1 are fetched and
+// dequantized before the MFMAs of k-step s are issued.
+// Scheduling of one k-step region: its 16 MFMAs (operands prepared in the previous region) interleaved with
+// the next k-step's 8 LDS reads (early, so their latency is covered) and its dequantization (VALU). With one
+// wave per SIMD and in-order issue, the instructions between two MFMAs run while the matrix core is busy.
+__device__ __forceinline__ void kstep_schedule() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
   }
 }
 
 template <int F>
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[8][2], const uint8_t* stage, int wave, int lane) {
+  WRegs r;
+  read_w(r, stage, scales_per_row_chunk(F), unit_s(F), wave, lane);
+  const int kh = lane >> 5;
+  bf16x8 a0[8], a1[8], b0[2], b1[2];
+  a_frags<0>(a0, stage, lane);
+  b_pair<F, 0>(b0, r, kh);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(acc, a0, b0);
+  a_frags<1>(a1, stage, lane);
+  b_pair<F, 1>(b1, r, kh);
+  kstep_schedule();
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(acc, a1, b1);
+  a_frags<2>(a0, stage, lane);
+  b_pair<F, 2>(b0, r, kh);
+  kstep_schedule();
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(acc, a0, b0);
+  a_frags<3>(a1, stage, lane);
+  b_pair<F, 3>(b1, r, kh);
+  kstep_schedule();
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(acc, a1, b1);
+}
+
+template <int F, bool RAGGED>
 __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restrict__ qp,
                                                           const uint8_t* __restrict__ sp,
                                                           const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                          int M, int N, int K, int ntiles, int nchunk,
-                                                          int tiles_m, float gscale) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[GM_BM * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[GM_BN * LDS_ROW];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                          int M, int N, int K, int nchunk, int tiles_m, float gscale) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave: keeps descriptors scalar
+  // consecutive workgroups go to different XCDs (block b runs on XCD b % 8); with tiles_m = 8 the
+  // workgroups of one XCD share an x tile in its L2
   const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
   const int m0 = bm * GM_BM, n0 = bn * GM_BN;
-  const int tile_base = n0 / TILE_N;
+  const int wrow0 = n0 + 64 * wave;            // this wave's 64 weight rows (4 tiles of 16)
+  const int ntiles = (N + TILE_N - 1) / TILE_N;
 
-  // ---- per-thread global load assignments ----
-  // x: piece p = tid + 256 * u  ->  row p / 16, 16-byte column p % 16 of the chunk
-  // w: piece p = tid + 256 * u  ->  tile p / 64 of the block, lane piece p % 64
-  u32x4 xr[X_PIECES];
-  u32x4 wq[W_PIECES];
-  u32x2 ws[W_PIECES];
+  GemmSrc src;
+  const int mrows = min(M - m0, GM_BM);
+  src.x = make_rsrc(x + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
+  const int tiles_here = max(0, min(ntiles - wrow0 / TILE_N, 4));
+  src.q = make_rsrc(qp + (int64_t)(wrow0 / TILE_N) * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
+  src.s = make_rsrc(sp + (int64_t)(wrow0 / TILE_N) * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
 
-  auto load_chunk = [&](int c) {
+  f32x16 acc[8][2];
 #pragma unroll
-    for (int u = 0; u < X_PIECES; ++u) {
-      const int p = tid + GM_THREADS * u;
-      const int row = m0 + (p >> 4);
-      const int k = c * CHUNK_K + 8 * (p & 15);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < M && k < K) v = *reinterpret_cast<const u32x4*>(x + (int64_t)row * K + k);
-      xr[u] = v;
-    }
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int u = 0; u < W_PIECES; ++u) {
-      const int p = tid + GM_THREADS * u;
-      const int tile = tile_base + (p >> 6), l = p & 63;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      u32x2 sv = {0u, 0u};
-      if (tile < ntiles) {
-        const int64_t unit = (int64_t)tile * nchunk + c;
-        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp + unit * UNIT_Q + l * 16));
-        const uint8_t* srow = sp + unit * unit_s(F) + (l & 15) * scales_per_row_chunk(F);
-        if constexpr (F == FAST) {
-          sv[0] = *reinterpret_cast<const uint32_t*>(srow);
-        } else {
-          sv = *reinterpret_cast<const u32x2*>(srow);
-        }
-      }
-      wq[u] = v;
-      ws[u] = sv;
-    }
-  };
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int u = 0; u < X_PIECES; ++u) {
-      const int p = tid + GM_THREADS * u;
-      const int r = p >> 4, q = p & 15;
-      uint8_t* rowp = lds_a + r * LDS_ROW;
-      if constexpr (F == FAST) {
-        // k = 8q + t -> k' = 32 (q % 4) + 8 (q / 4) + t
-        *reinterpret_cast<u32x4*>(rowp + 2 * (32 * (q & 3) + 8 * (q >> 2))) = xr[u];
-      } else {
-        // k = 8q + u -> k' = 64 (q % 2) + 4 (q / 2) + u (u < 4), + 32 more for u >= 4
-        const int kp = 64 * (q & 1) + 4 * (q >> 1);
-        *reinterpret_cast<u32x2*>(rowp + 2 * kp) = u32x2{xr[u][0], xr[u][1]};
-        *reinterpret_cast<u32x2*>(rowp + 2 * (kp + 32)) = u32x2{xr[u][2], xr[u][3]};
-      }
+  const int H = 2 * nchunk;
+  issue_x<F, RAGGED>(src, ring, 0, K, wave, lane);
+  issue_w<F>(src, ring, 0, nchunk, wave, lane);
+  if (1 < H) {
+    issue_x<F, RAGGED>(src, ring, 1, K, wave, lane);
+    issue_w<F>(src, ring, 1, nchunk, wave, lane);
+  }
+  for (int h = 0; h < H; ++h) {
+    // wait for this wave's loads of stage h (stage h + 1's may stay in flight), then a barrier: every
+    // wave's share of stage h is in LDS and stage h - 1, whose ring slot is refilled next, is finished
+    if (h + 1 < H) wait_vmcnt<gm_loads_per_stage(F)>();
+    else wait_vmcnt<0>();
+    workgroup_barrier();
+    if (h + 2 < H) {
+      issue_x<F, RAGGED>(src, ring, h + 2, K, wave, lane);
+      issue_w<F>(src, ring, h + 2, nchunk, wave, lane);
     }
-#pragma unroll
-    for (int u = 0; u < W_PIECES; ++u) {
-      const int p = tid + GM_THREADS * u;
-      const int t = p >> 6, l = p & 63;
-      const int row = TILE_N * t + (l & 15), g = l >> 4;
-      uint32_t out[16];
-      dequant_piece<F>(wq[u], ws[u], out);
-      uint8_t* dst = lds_b + row * LDS_ROW + 2 * 32 * g;
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *reinterpret_cast<u32x4*>(dst + 16 * v) = u32x4{out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]};
-    }
-  };
-
-  const int wm = wave & 1, wn = wave >> 1;  // 2 x 2 waves, 64 x 64 each
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load_chunk(0);
-  for (int c = 0; c < nchunk; ++c) {
-    __syncthreads();  // previous chunk's MFMAs are done with the LDS tiles
-    store_chunk();
-    __syncthreads();
-    if (c + 1 < nchunk) load_chunk(c + 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kb = 2 * (32 * ks + 8 * (lane >> 4));
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(lds_a + (64 * wm + 16 * i + (lane & 15)) * LDS_ROW + kb);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(lds_b + (64 * wn + 16 * j + (lane & 15)) * LDS_ROW + kb);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+    compute_stage<F>(acc, ring + (h % GM_RING) * GM_STAGE_BYTES, wave, lane);
   }
 
-  // epilogue: C[16 i + 4 (lane/16) + r][16 j + lane % 16]
+  // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
-        const int col = n0 + 64 * wn + 16 * j + (lane & 15);
-        if (row < M && col < N) y[(int64_t)row * N + col] = acc[i][j][r] * gscale;
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int col = wrow0 + 32 * j + (lane & 31);
+        if (row < M && col < N) y[(int64_t)row * N + col] = acc[i][j][e] * gscale;
       }
+}
+
+template <int F, bool RAGGED>
+static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
+                          int N, int K, float g) {
+  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
+  const int tiles_m = (M + GM_BM - 1) / GM_BM;
+  const int tiles_n = (N + GM_BN - 1) / GM_BN;
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, GM_LDS) == hipSuccess;
+  (void)attr;
+  hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(tiles_m * tiles_n), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M,
+                     N, K, nchunk, tiles_m, g);
 }
 
 template <int F>
 static void launch_gemm(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
                         int N, int K, float g) {
-  const int ntiles = (N + TILE_N - 1) / TILE_N;
-  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
-  const int tiles_m = (M + GM_BM - 1) / GM_BM;
-  const int tiles_n = (N + GM_BN - 1) / GM_BN;
-  hipLaunchKernelGGL(gemm_kernel<F>, dim3(tiles_m * tiles_n), dim3(GM_THREADS), 0, st, q, s, x, y, M, N, K, ntiles,
-                     nchunk, tiles_m, g);
+  if (K % CHUNK_K == 0) launch_gemm_t<F, false>(st, q, s, x, y, M, N, K, g);
+  else launch_gemm_t<F, true>(st, q, s, x, y, M, N, K, g);
 }
 
 }  // namespace fp4
@@ -222,6 +365,7 @@ extern "C" int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   if (rc) return rc;
   if (M == 0) return 0;
   if (M > (1LL << 30)) return -4;
+  if (K > (1LL << 22)) return -4;  // tile offsets are 32-bit buffer offsets: 256 rows x K x 2 bytes < 2^31
   if (!q || !s || !x_bf16 || !y) return -1;
   if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(x_bf16, 16) || !fp4_aligned(y, 4)) return -3;
   const int64_t grid = ((M + GM_BM - 1) / GM_BM) * ((N + GM_BN - 1) / GM_BN);
