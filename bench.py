@@ -179,18 +179,28 @@ def bench_gemm(fp4, torch, synth, fmt: str, steps: int, warmup: int):
     return dict(fmt=fmt, m=m, n=n, k=k, per_launch_s=per, tflops=flops / per / 1e12)
 
 
+def host_threads() -> int:
+    """Host cores this process may use (the affinity mask), at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(fmt: str, w_np: np.ndarray, x_bits: np.ndarray, y_gpu: np.ndarray, budget_s: float = 12.0):
     """The CPU oracle on a row sample of the same matrix: oracle-packed, exact dequant + FP64 product."""
     from threadpoolctl import threadpool_limits
 
     from oracle import pack, ref
+    threads = host_threads()
     rows = np.arange(0, w_np.shape[0], max(1, w_np.shape[0] // 512))[:512]
     sample_w = np.ascontiguousarray(w_np[rows])
     packed = pack.pack(fmt, sample_w)                       # input preparation, not timed
     n, k = sample_w.shape
     abytes = algorithmic_bytes(fmt, n, k)
     times = []
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t_end = time.perf_counter() + budget_s
         while time.perf_counter() < t_end or len(times) < 3:
             t0 = time.perf_counter()
@@ -200,10 +210,23 @@ def cpu_baseline(fmt: str, w_np: np.ndarray, x_bits: np.ndarray, y_gpu: np.ndarr
     med = float(np.median(times))
     b = ref.bound(x_bits, w64)
     ok, worst = ref.check(y_gpu[:, rows], y_ref, b)
-    return dict(value=abytes / med / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"{n} of {w_np.shape[0]} rows x K={k} ({fmt}, M={x_bits.shape[0]}), exact dequant + "
-                       f"FP64 product, median of {len(times)} runs, 1 thread",
+    return dict(value=abytes / med / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{n} of {w_np.shape[0]} rows x K={k} ({fmt}, M={x_bits.shape[0]}), exact dequant "
+                       f"(numpy, one thread) + FP64 product (BLAS, {threads} threads), median of "
+                       f"{len(times)} runs",
                 ms=med * 1e3, parity_on_sample=ok, worst_error_ratio=worst)
+
+
+def copy_calibration(torch, mib: int = 256, reps: int = 5):
+    """A plain device copy of known size, run so that rocprofv3 counters can be scaled to bytes."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 256)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "reps": reps}}), flush=True)
 
 
 def main():
@@ -215,6 +238,8 @@ def main():
     ap.add_argument("--gemm-steps", type=int, default=30)
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device copy (scale factor for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -228,6 +253,9 @@ def main():
 
     torch.cuda.set_device(0)
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     t0 = time.time()
     gv = bench_gemv(fp4, torch, synth, args.workload, args.steps, args.warmup)
     print(f"# gemv {args.workload}: {gv['per_launch_s'] * 1e6:.3f} us/launch, {gv['gbs']:.1f} GB/s "

@@ -54,10 +54,10 @@ __device__ __forceinline__ void unit_mac(f32x4& acc, const WeightRegs<F>& w, con
       const bf16x4 b1 = cat(e2m1x2_to_bf16<2>(word), e2m1x2_to_bf16<3>(word));
       const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xf[2 * d], b0, zero, 0, 0, 0);
       const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xf[2 * d + 1], b1, zero, 0, 0, 0);
-      const uint32_t sw = w.s[d >> 1];
-      float sc0, sc1;
-      if (d & 1) { sc0 = e4m3_to_f32<2>(sw); sc1 = e4m3_to_f32<3>(sw); }
-      else       { sc0 = e4m3_to_f32<0>(sw); sc1 = e4m3_to_f32<1>(sw); }
+      // the two scale bytes of groups 2d and 2d+1, converted together
+      const f32x2 sc = (d & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w.s[d >> 1], true)
+                               : __builtin_amdgcn_cvt_pk_f32_fp8(w.s[d >> 1], false);
+      const float sc0 = sc[0], sc1 = sc[1];
       fold<RU>(acc, p0, sc0);
       fold<RU>(acc, p1, sc1);
     }
@@ -71,10 +71,10 @@ __device__ __forceinline__ void unit_mac(f32x4& acc, const WeightRegs<F>& w, con
       const bf16x4 b1 = cat(e4m3x2_to_bf16<false>(hi), e4m3x2_to_bf16<true>(hi));
       const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xf[2 * d], b0, zero, 0, 0, 0);
       const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xf[2 * d + 1], b1, zero, 0, 0, 0);
-      const uint32_t sw = w.s[d >> 1];
-      float sc0, sc1;
-      if (d & 1) { sc0 = e4m3_to_f32<2>(sw); sc1 = e4m3_to_f32<3>(sw); }
-      else       { sc0 = e4m3_to_f32<0>(sw); sc1 = e4m3_to_f32<1>(sw); }
+      // the two scale bytes of groups 2d and 2d+1, converted together
+      const f32x2 sc = (d & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w.s[d >> 1], true)
+                               : __builtin_amdgcn_cvt_pk_f32_fp8(w.s[d >> 1], false);
+      const float sc0 = sc[0], sc1 = sc[1];
       fold<RU>(acc, p0, sc0);
       fold<RU>(acc, p1, sc1);
     }
