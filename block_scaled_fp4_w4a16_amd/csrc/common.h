@@ -75,6 +75,17 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
 }
 
+// Raw buffer descriptor (stride 0) over `bytes` bytes from `base`; loads past the end return zeros.
+// The descriptor must live in scalar registers; its inputs are wave-uniform, so read them from lane 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
+}
+
 __device__ __forceinline__ bf16x4 cat(bf16x2 a, bf16x2 b) { return bf16x4{a[0], a[1], b[0], b[1]}; }
 __device__ __forceinline__ bf16x8 cat(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};

@@ -105,16 +105,6 @@ struct GemmSrc {
   __amdgpu_buffer_rsrc_t x, q, s;
 };
 
-// The descriptor must live in scalar registers; its inputs are wave-uniform, so read them from lane 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
-}
-
 // Stage k subset and its natural order (segment sigma = 16-byte group of 8 positions, 8 per stage):
 //   16-weight groups: sigma = j -> k = 16 sigma + 8 hh + u          (u = 0..7; group j of the chunk)
 //   FAST:             sigma = 2 j + b -> k = 32 j + 16 hh + 8 b + u (block j of the chunk)

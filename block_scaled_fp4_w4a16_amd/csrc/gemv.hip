@@ -21,14 +21,22 @@ struct WeightRegs {
   uint32_t s[F == FAST ? 1 : 2];
 };
 
+// Buffer descriptors: the workgroup's tiles of both planes, and x. A load at an offset a descriptor
+// does not reach returns zeros, so no load needs a branch or a select; OOB is such an offset (every
+// descriptor here covers less than 2^31 bytes).
+constexpr uint32_t OOB = 0x80000000u;
+
+struct Srcs {
+  __amdgpu_buffer_rsrc_t q, s, x;
+};
+
 template <int F>
-__device__ __forceinline__ void load_unit(WeightRegs<F>& r, const uint8_t* __restrict__ qp,
-                                          const uint8_t* __restrict__ sp, int64_t unit, int lane, int n) {
-  r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp + unit * UNIT_Q + lane * 16));
+__device__ __forceinline__ void load_unit(WeightRegs<F>& r, const Srcs& src, uint32_t qoff, uint32_t soff) {
+  r.q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.q, qoff, 0, 2 /* nt */));
   if constexpr (F == FAST) {
-    r.s[0] = *reinterpret_cast<const uint32_t*>(sp + unit * unit_s(F) + n * 4);
+    r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(src.s, soff, 0, 0);
   } else {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(sp + unit * unit_s(F) + n * 8);
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(src.s, soff, 0, 0));
     r.s[0] = v[0];
     r.s[1] = v[1];
   }
@@ -101,74 +109,121 @@ __device__ __forceinline__ void unit_mac(f32x4& acc, const WeightRegs<F>& w, con
 
 // x staging. Each wave copies the x columns of the chunks it is about to process into its own LDS
 // region, in per-lane fragment order: for chunk slot u, lane group g and x row m, the 32 bf16 that lane
-// (m, g) feeds to the MFMAs of that chunk sit as 64 contiguous bytes. The copy is one coalesced
-// 16-byte global load per piece (a chunk row of x is 16 pieces), issued before the wave's weight
-// loads so that it does not queue behind them; no workgroup barrier is involved.
-template <int F, int U>
-__device__ __forceinline__ void stage_x_wave(uint8_t* xs, const uint16_t* __restrict__ x, int M, int K, int c0, int W,
-                                             int nchunk, int lane) {
+// (m, g) feeds to the MFMAs of that chunk sit as 64 contiguous bytes. The copy is split in two so that
+// the weight loads can be issued in between: `issue` starts coalesced 16-byte global loads (a chunk
+// row of x is 16 pieces) into registers, `commit` writes them to LDS. Loads complete in order, so
+// committing waits only for x, never for the weight loads issued after it; no workgroup barrier is
+// involved. MX bounds M, so NX = U * MX / 4 loads per lane cover every piece.
+template <int U, int MX>
+struct XStage {
+  static constexpr int NX = (U * MX * 16 + 63) / 64;
+  u32x4 v[NX];
+};
+
+// byte offset of x piece p (16 bytes: 8 consecutive k of one row) of the batch starting at chunk c0
+template <int U>
+__device__ __forceinline__ uint32_t x_piece_off(int p, int M, int K, int c0, int W, int nchunk) {
   const int pieces = U * M * 16;
-  for (int p0 = 0; p0 < pieces; p0 += 64 * 4) {
-    u32x4 v[4];
-    int dst[4];
+  const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
+  const int c = c0 + u * W;
+  const int k = c * CHUNK_K + 8 * qq;
+  return (p < pieces && c < nchunk && k < K) ? (uint32_t)(m * K + k) * 2u : OOB;
+}
+
+template <int F, int U, int MX>
+__device__ __forceinline__ void stage_x_issue(XStage<U, MX>& st, const Srcs& src, int M, int K, int c0, int W,
+                                              int nchunk, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {       // up to four loads in flight per lane before the writes
-      const int p = p0 + 64 * i + lane;
-      dst[i] = -1;
-      v[i] = u32x4{0u, 0u, 0u, 0u};
-      if (p < pieces) {
-        const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
-        const int c = c0 + u * W;
-        const int k = c * CHUNK_K + 8 * qq;
-        if (c < nchunk && k < K) v[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k);
-        dst[i] = (u * 4 * M + m) * 64 + ((F == FAST) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
-                                                        : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
-      }
-    }
+  for (int i = 0; i < XStage<U, MX>::NX; ++i) {
+    const uint32_t off = x_piece_off<U>(64 * i + lane, M, K, c0, W, nchunk);
+    st.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, off, 0, 0));
+  }
+}
+
+template <int F, int U, int MX>
+__device__ __forceinline__ void stage_x_commit(uint8_t* xs, const XStage<U, MX>& st, int M, int lane) {
+  const int pieces = U * M * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (dst[i] < 0) continue;
+  for (int i = 0; i < XStage<U, MX>::NX; ++i) {
+    const int p = 64 * i + lane;
+    if (p < pieces) {
+      const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
+      const int dst = (u * 4 * M + m) * 64 + ((F == FAST) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
+                                                           : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
       if constexpr (F == FAST) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
-        *reinterpret_cast<u32x4*>(xs + dst[i]) = v[i];
+        *reinterpret_cast<u32x4*>(xs + dst) = st.v[i];
       } else {                          // k = 16 j + 4 g + t: halves go to lane groups 2 (qq & 1) and +1
-        *reinterpret_cast<u32x2*>(xs + dst[i]) = u32x2{v[i][0], v[i][1]};
-        *reinterpret_cast<u32x2*>(xs + dst[i] + M * 64) = u32x2{v[i][2], v[i][3]};
+        *reinterpret_cast<u32x2*>(xs + dst) = u32x2{st.v[i][0], st.v[i][1]};
+        *reinterpret_cast<u32x2*>(xs + dst + M * 64) = u32x2{st.v[i][2], st.v[i][3]};
       }
     }
   }
 }
 
+// Loads and commits a batch's x in one go, four loads per lane in flight at a time (used when x has
+// too many rows to be held in registers across the weight loads).
+template <int F, int U>
+__device__ __forceinline__ void stage_x_now(uint8_t* xs, const Srcs& src, int M, int K, int c0, int W, int nchunk,
+                                            int lane) {
+  const int pieces = U * M * 16;
+  for (int p0 = 0; p0 < pieces; p0 += 64 * 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = x_piece_off<U>(p0 + 64 * i + lane, M, K, c0, W, nchunk);
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + 64 * i + lane;
+      if (p >= pieces) continue;
+      const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
+      const int dst = (u * 4 * M + m) * 64 + ((F == FAST) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
+                                                           : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
+      if constexpr (F == FAST) {
+        *reinterpret_cast<u32x4*>(xs + dst) = v[i];
+      } else {
+        *reinterpret_cast<u32x2*>(xs + dst) = u32x2{v[i][0], v[i][1]};
+        *reinterpret_cast<u32x2*>(xs + dst + M * 64) = u32x2{v[i][2], v[i][3]};
+      }
+    }
+  }
+}
+
+// Weight units of one batch: chunk c0 + u W of each of the T tiles. Units past the last chunk, or
+// of a tile past the last one (outside the descriptor), read as zeros.
 template <int F, int T, int U>
-__device__ __forceinline__ void load_batch(WeightRegs<F> (&wr)[U][T], const uint8_t* __restrict__ qp,
-                                           const uint8_t* __restrict__ sp, int c0, int W, int nchunk, int tile0,
-                                           int ntiles, int lane, int n) {
+__device__ __forceinline__ void load_batch(WeightRegs<F> (&wr)[U][T], const Srcs& src, int c0, int W, int nchunk,
+                                           int lane, int n) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = c0 + u * W;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      if (c < nchunk && tile0 + t < ntiles) {
-        load_unit<F>(wr[u][t], qp, sp, (int64_t)(tile0 + t) * nchunk + c, lane, n);
-      } else {
-        wr[u][t].q = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < (F == FAST ? 1 : 2); ++i) wr[u][t].s[i] = 0u;
-      }
+      const uint32_t unit = (uint32_t)(t * nchunk + c);
+      const bool ok = c < nchunk;
+      load_unit<F>(wr[u][t], src, ok ? unit * UNIT_Q + lane * 16 : OOB,
+                   ok ? unit * unit_s(F) + n * (unit_s(F) / TILE_N) : OOB);
     }
   }
 }
 
 // Dynamic LDS: [W waves][U chunks][4 lane groups][M rows][64 B] of staged x, then the
 // cross-wave reduction buffer [W][T][64 lanes][4] floats.
-template <int F, int T, int RU, int U>
+template <int F, int T, int RU, int U, int MX>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                                     const uint16_t* __restrict__ x, float* __restrict__ y,
                                                     int M, int N, int K, int ntiles, int nchunk, float gscale) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar branches
   const int n = lane & 15, g = lane >> 4, m = lane & 15;
   const int tile0 = blockIdx.x * T;
-  const bool xrow = m < M;
+  const int tiles_here = min(T, ntiles - tile0);
+  Srcs src;
+  src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
+  src.s = make_rsrc(sp + (int64_t)tile0 * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
+  src.x = make_rsrc(x, (uint32_t)(M * K) * 2u);
   const size_t xw_bytes = (size_t)U * 4 * M * 64;
   uint8_t* xs = smem + wave * xw_bytes;
   float* red = reinterpret_cast<float*>(smem + W * xw_bytes);
@@ -177,31 +232,47 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* __restrict__ 
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Rows m >= M of the MFMA A operand read x row M - 1: their products land in C rows that are never
+  // stored, and reading a valid row keeps every lane on one path with no zero fill.
+  const int xm = m < M ? m : M - 1;
   WeightRegs<F> wr[U][T];
-  bool have = false;
+  // With few x rows (XPF) a batch's x is loaded ahead of its weights and held in registers until
+  // they are issued, and the next batch's x is prefetched together with its weights. With many rows
+  // that would cost too many registers: x is then loaded and committed at the top of each batch.
+  constexpr bool XPF = XStage<U, MX>::NX <= 2;
+  XStage<U, XPF ? MX : 1> xst;
+  if constexpr (XPF) {
+    if (wave < nchunk) {
+      stage_x_issue<F, U, MX>(xst, src, M, K, wave, W, nchunk, lane);
+      load_batch<F, T, U>(wr, src, wave, W, nchunk, lane, n);
+    }
+  }
+  bool have = XPF;  // wr already holds this batch's weights
   for (int c0 = wave; c0 < nchunk; c0 += W * U) {
-    stage_x_wave<F, U>(xs, x, M, K, c0, W, nchunk, lane);     // x first: it must not wait behind weights
-    if (!have) load_batch<F, T, U>(wr, qp, sp, c0, W, nchunk, tile0, ntiles, lane, n);
-    // the next batch's weights go out before this batch is computed
+    if constexpr (XPF) {
+      stage_x_commit<F, U, MX>(xs, xst, M, lane);
+    } else {
+      stage_x_now<F, U>(xs, src, M, K, c0, W, nchunk, lane);
+      if (!have) load_batch<F, T, U>(wr, src, c0, W, nchunk, lane, n);
+    }
+    // the next batch (x first, then weights) goes out before this batch is computed
     WeightRegs<F> nx[U][T];
     const int c1 = c0 + W * U;
     have = c1 < nchunk;
-    if (have) load_batch<F, T, U>(nx, qp, sp, c1, W, nchunk, tile0, ntiles, lane, n);
+    if (have) {
+      if constexpr (XPF) stage_x_issue<F, U, MX>(xst, src, M, K, c1, W, nchunk, lane);
+      load_batch<F, T, U>(nx, src, c1, W, nchunk, lane, n);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (c0 + u * W < nchunk) {
         // this lane's 32 x values of chunk slot u, read from the wave's staging area just before use
         uint32_t xa[16];
-        if (xrow) {
-          const u32x4* src = reinterpret_cast<const u32x4*>(xs + ((u * 4 + g) * M + m) * 64);
+        const u32x4* src = reinterpret_cast<const u32x4*>(xs + ((u * 4 + g) * M + xm) * 64);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const u32x4 w4 = src[v];
-            xa[4 * v] = w4[0]; xa[4 * v + 1] = w4[1]; xa[4 * v + 2] = w4[2]; xa[4 * v + 3] = w4[3];
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xa[i] = 0u;
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 w4 = src[v];
+          xa[4 * v] = w4[0]; xa[4 * v + 1] = w4[1]; xa[4 * v + 2] = w4[2]; xa[4 * v + 3] = w4[3];
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) unit_mac<F, RU>(acc[t], wr[u][t], xa);
@@ -237,15 +308,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* __restrict__ 
 
 constexpr int GEMV_LDS_MAX = 160 * 1024;
 
-template <int F, int T, int RU, int U>
+template <int F, int T, int RU, int U, int MX>
 static void launch_gemv(int nwg, int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x,
                         float* y, int M, int N, int K, int ntiles, int nchunk, float g) {
   const size_t lds = (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float);
   // allow more than 64 KiB of dynamic LDS for this instantiation (once; thread-safe static init)
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U>),
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((gemv_kernel<F, T, RU, U>), dim3(nwg), dim3(64 * W), lds, st, q, s, x, y, M, N, K, ntiles,
+  hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX>), dim3(nwg), dim3(64 * W), lds, st, q, s, x, y, M, N, K, ntiles,
                      nchunk, g);
 }
 
@@ -256,16 +327,21 @@ static void dispatch_gemv(int M, hipStream_t st, const uint8_t* q, const uint8_t
   const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const int T = (M > 4) ? 2 : 1;
   const int nwg = (ntiles + T - 1) / T;
-  int W = (4096 + nwg - 1) / nwg;  // aim for ~16 waves per CU across 256 CUs
-  if (const char* e = getenv("FP4_GEMV_WAVES")) W = atoi(e);  // tuning override
+  // Waves per workgroup: the most (up to 16) that still give every wave at least two K chunks and
+  // keep the whole grid resident at once (about 20 waves per CU at this kernel's register use).
+  int W = 16;
+  while (W > 1 && (nchunk < 2 * W || nwg * W > 5120)) W >>= 1;
+  if (const char* e = getenv("FP4_GEMV_WAVES")) {  // tuning override, read at each call
+    if (atoi(e) > 0) W = atoi(e);
+  }
   const int wmax = (M > 4) ? 8 : 16;  // keep the staged x (W * U * M * 256 B) inside the LDS
   if (W > wmax) W = wmax;
   if (W > nchunk) W = nchunk;
   if (W < 1) W = 1;
-  if (M == 1)      launch_gemv<F, 1, 1, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else if (M == 2) launch_gemv<F, 1, 2, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else if (M <= 4) launch_gemv<F, 1, 4, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else             launch_gemv<F, 2, 4, 2>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  if (M == 1)      launch_gemv<F, 1, 1, 4, 1>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  else if (M == 2) launch_gemv<F, 1, 2, 4, 2>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  else if (M <= 4) launch_gemv<F, 1, 4, 4, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  else             launch_gemv<F, 2, 4, 2, 16>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
 }
 
 }  // namespace fp4
@@ -279,6 +355,7 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   if (M > 16) return -4;
   int rc = fp4_check_nk(fmt, N, K);
   if (rc) return rc;
+  if (K > (1 << 24)) return -4;  // 32-bit buffer offsets within a tile row of the planes and within x
   if (M == 0) return 0;
   if (!q || !s || !x_bf16 || !y) return -1;
   if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(x_bf16, 16) || !fp4_aligned(y, 4)) return -3;
