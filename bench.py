@@ -188,6 +188,61 @@ def host_threads() -> int:
     return max(1, min(16, n))
 
 
+def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int):
+    """The 4B-class decode sweep: 36 layers x {q, k, v, o, gate, up, down}, NVFP4, M = 1.
+
+    Weights are N(0, 0.02) drawn on the GPU (synth.device_weights) and packed by the library's NVFP4
+    packer; all 252 matrices (2.04 GB) stay resident, so each sweep streams them from HBM. A sweep is
+    launched per layer the way a decoder consumes it: one grouped launch for q|k|v (same x), one for
+    o, one grouped launch for gate|up (same x), one for down -- 144 launches. The same sweep with one
+    launch per matrix (252 launches) is timed beside it. Both are recorded as HIP graphs.
+    """
+    cfg = 2
+    layer = synth.DECODE_4B_LAYER
+    mats, total_bytes = [], 0
+    for li in range(36):
+        row = []
+        for pi, (_, n, k) in enumerate(layer):
+            w = synth.device_weights(n, k, cfg=cfg, mat=7 * li + pi)
+            pw = fp4.PackedWeight.quantize("nvfp4", w)
+            del w
+            row.append(pw)
+            total_bytes += algorithmic_bytes("nvfp4", n, k)
+        mats.append(row)
+    torch.cuda.synchronize()
+
+    def xb(k, mat):
+        return torch.from_numpy(synth.activations(1, k, cfg=cfg, mat=mat).view(np.int16)).view(torch.bfloat16).cuda()
+
+    xs = [dict(attn=xb(2560, 4 * li), o=xb(4096, 4 * li + 1), mlp=xb(2560, 4 * li + 2), down=xb(9728, 4 * li + 3))
+          for li in range(36)]
+    ys = [[torch.empty((1, n), dtype=torch.float32, device="cuda") for (_, n, _) in layer] for _ in range(36)]
+    which_x = ("attn", "attn", "attn", "o", "mlp", "mlp", "down")
+
+    def item(li, pi):
+        pw = mats[li][pi]
+        return (pw.q, pw.s, pw.global_scale, xs[li][which_x[pi]], ys[li][pi], pw.N, pw.K)
+
+    def sweep_grouped(_):
+        for li in range(36):
+            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 0), item(li, 1), item(li, 2)])
+            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 3)])
+            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 4), item(li, 5)])
+            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 6)])
+
+    def sweep_single(_):
+        for li in range(36):
+            for pi in range(7):
+                q, s_, g, x, y, n, k = item(li, pi)
+                fp4.w4a16_gemv("nvfp4", 1, n, k, q, s_, g, x, y)
+
+    out = dict(bytes=total_bytes)
+    for name, fn in (("grouped", sweep_grouped), ("single", sweep_single)):
+        secs = time_launches(torch, fn, 1, steps, warmup)
+        out[name] = secs / steps
+    return out
+
+
 def cpu_baseline(fmt: str, w_np: np.ndarray, x_bits: np.ndarray, y_gpu: np.ndarray, budget_s: float = 12.0):
     """The CPU oracle on a row sample of the same matrix: oracle-packed, exact dequant + FP64 product."""
     from threadpoolctl import threadpool_limits
@@ -238,6 +293,8 @@ def main():
     ap.add_argument("--gemm-steps", type=int, default=30)
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=50)
+    ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (scale factor for HBM byte counters)")
     args = ap.parse_args()
@@ -267,6 +324,15 @@ def main():
         gm = bench_gemm(fp4, torch, synth, "rocmfp4_fast", args.gemm_steps, 3)
         print(f"# gemm FAST M=2048: {gm['per_launch_s'] * 1e6:.1f} us/launch, {gm['tflops']:.1f} TFLOP/s "
               f"({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
+
+    sw = None
+    if not args.no_sweep:
+        t2 = time.time()
+        sw = bench_decode_sweep(fp4, torch, synth, args.sweep_steps, 3)
+        print(f"# decode sweep NVFP4 M=1 (252 matrices, {sw['bytes'] / 1e9:.3f} GB): grouped "
+              f"{sw['grouped'] * 1e6:.1f} us ({sw['bytes'] / sw['grouped'] / 1e9:.1f} GB/s), one launch per matrix "
+              f"{sw['single'] * 1e6:.1f} us ({sw['bytes'] / sw['single'] / 1e9:.1f} GB/s) ({time.time() - t2:.1f}s)",
+              file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -303,6 +369,17 @@ def main():
                                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                      "frac": round(gm["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
                                      "traffic": traffic_from_profiles("gemm.hip", "rocmfp4_fast_prefill_m2048")}}
+    if sw:
+        gbs = sw["bytes"] / sw["grouped"] / 1e9
+        line["decode_sweep"] = {
+            "workload": "nvfp4_4b_decode_sweep_m1 (36 layers x q,k,v,o,gate,up,down)",
+            "value": round(gbs, 2), "unit": "GB/s", "us_per_sweep": round(sw["grouped"] * 1e6, 2),
+            "launches_per_sweep": 144, "bytes_per_sweep": sw["bytes"],
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "one_launch_per_matrix": {"value": round(sw["bytes"] / sw["single"] / 1e9, 2),
+                                      "us_per_sweep": round(sw["single"] * 1e6, 2), "launches_per_sweep": 252},
+        }
     print(json.dumps(line), flush=True)
 
 

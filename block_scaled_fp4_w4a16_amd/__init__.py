@@ -26,12 +26,23 @@ _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 _f = ctypes.c_float
 
+GEMV_MAX_ITEMS = 32
+
+
+class GemvItem(ctypes.Structure):
+    """Mirror of `fp4_gemv_item` (one matrix of a w4a16_gemv_batched call)."""
+    _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("global_scale", ctypes.c_float)]
+
+
 _SIGS = {
     "fp4_abi_version": (_c, []),
     "fp4_status_string": (ctypes.c_char_p, [_c]),
     "fp4_layout_bytes": (_c, [_c, _i64, _i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "fp4_pack_layout": (_c, [_c, _i64, _i64, _p, _p, _p, _p, _p]),
     "w4a16_gemv": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
+    "w4a16_gemv_batched": (_c, [_c, _i64, _c, ctypes.POINTER(GemvItem), _p]),
     "w4a16_gemm": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "w4a16_matmul": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "fp4_dequant_f32": (_c, [_c, _i64, _i64, _p, _p, _f, _p, _p]),
@@ -125,6 +136,18 @@ def _product(name, fmt, M, N, K, q, s, global_scale, x, y, stream):
 
 def w4a16_gemv(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
     _product("w4a16_gemv", fmt, M, N, K, q, s, global_scale, x, y, stream)
+
+
+def w4a16_gemv_batched(fmt, M, items, stream=None):
+    """items: sequence of (q, s, global_scale, x, y, N, K), one per matrix; all share fmt and M."""
+    arr = (GemvItem * max(1, len(items)))()
+    for i, (q, s, g, x, y, n, k) in enumerate(items):
+        if x.dtype != torch.bfloat16 or y.dtype != torch.float32:
+            raise TypeError("x must be bfloat16 and y float32")
+        if x.numel() < M * k or y.numel() < M * n:
+            raise ValueError("x or y is smaller than M x K / M x N")
+        arr[i] = GemvItem(_ptr(q), _ptr(s), _ptr(x), _ptr(y), n, k, float(g))
+    _check(lib().w4a16_gemv_batched(_fmt(fmt), M, len(items), arr, _stream(stream)), "w4a16_gemv_batched")
 
 
 def w4a16_gemm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):

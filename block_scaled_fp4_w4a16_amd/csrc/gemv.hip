@@ -208,17 +208,47 @@ __device__ __forceinline__ void load_batch(WeightRegs<F> (&wr)[U][T], const Srcs
   }
 }
 
+// One matrix of a launch. A launch covers one or more matrices that share the format and M; the
+// grid is the concatenation of their workgroup ranges, matrix i owning workgroups [wg0, next wg0).
+struct GemvItem {
+  const uint8_t* q;
+  const uint8_t* s;
+  const uint16_t* x;
+  float* y;
+  int N, K, nchunk, wg0;
+  float g;
+  int pad;
+};
+
+template <int MAXI>
+struct GemvBatch {
+  int count;
+  GemvItem it[MAXI];
+};
+
 // Dynamic LDS: [W waves][U chunks][4 lane groups][M rows][64 B] of staged x, then the
 // cross-wave reduction buffer [W][T][64 lanes][4] floats.
-template <int F, int T, int RU, int U, int MX>
-__global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
-                                                    const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                    int M, int N, int K, int ntiles, int nchunk, float gscale) {
+template <int F, int T, int RU, int U, int MX, int MAXI>
+__global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch, int M) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // this workgroup's matrix (a uniform search over at most MAXI starts)
+  int item = 0;
+#pragma unroll
+  for (int i = 1; i < MAXI; ++i)
+    if (i < batch.count && (int)blockIdx.x >= batch.it[i].wg0) item = i;
+  const GemvItem& it = batch.it[item];
+  const uint8_t* __restrict__ qp = it.q;
+  const uint8_t* __restrict__ sp = it.s;
+  const uint16_t* __restrict__ x = it.x;
+  float* __restrict__ y = it.y;
+  const int N = it.N, K = it.K, nchunk = it.nchunk;
+  const float gscale = it.g;
+  const int ntiles = (N + TILE_N - 1) / TILE_N;
+
   const int lane = threadIdx.x & 63, W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar branches
   const int n = lane & 15, g = lane >> 4, m = lane & 15;
-  const int tile0 = blockIdx.x * T;
+  const int tile0 = ((int)blockIdx.x - it.wg0) * T;
   const int tiles_here = min(T, ntiles - tile0);
   Srcs src;
   src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
@@ -308,45 +338,69 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* __restrict__ 
 
 constexpr int GEMV_LDS_MAX = 160 * 1024;
 
-template <int F, int T, int RU, int U, int MX>
-static void launch_gemv(int nwg, int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x,
-                        float* y, int M, int N, int K, int ntiles, int nchunk, float g) {
+template <int F, int T, int RU, int U, int MX, int MAXI>
+static void launch_gemv(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
   const size_t lds = (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float);
   // allow more than 64 KiB of dynamic LDS for this instantiation (once; thread-safe static init)
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX>),
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX, MAXI>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX>), dim3(nwg), dim3(64 * W), lds, st, q, s, x, y, M, N, K, ntiles,
-                     nchunk, g);
+  hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX, MAXI>), dim3(nwg), dim3(64 * W), lds, st, b, M);
 }
 
-template <int F>
-static void dispatch_gemv(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
-                          int N, int K, float g) {
-  const int ntiles = (N + TILE_N - 1) / TILE_N;
-  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
+// Fills in the workgroup ranges, picks the wave count and launches. Every item has N, K >= 1.
+template <int F, int MAXI>
+static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   const int T = (M > 4) ? 2 : 1;
-  const int nwg = (ntiles + T - 1) / T;
+  int nwg = 0, min_chunks = 1 << 30;
+  for (int i = 0; i < b.count; ++i) {
+    GemvItem& it = b.it[i];
+    it.nchunk = (it.K + CHUNK_K - 1) / CHUNK_K;
+    it.wg0 = nwg;
+    const int ntiles = (it.N + TILE_N - 1) / TILE_N;
+    nwg += (ntiles + T - 1) / T;
+    min_chunks = min_chunks < it.nchunk ? min_chunks : it.nchunk;
+  }
   // Waves per workgroup: the most (up to 16) that still give every wave at least two K chunks and
   // keep the whole grid resident at once (about 20 waves per CU at this kernel's register use).
   int W = 16;
-  while (W > 1 && (nchunk < 2 * W || nwg * W > 5120)) W >>= 1;
+  while (W > 1 && (min_chunks < 2 * W || nwg * W > 5120)) W >>= 1;
   if (const char* e = getenv("FP4_GEMV_WAVES")) {  // tuning override, read at each call
     if (atoi(e) > 0) W = atoi(e);
   }
   const int wmax = (M > 4) ? 8 : 16;  // keep the staged x (W * U * M * 256 B) inside the LDS
   if (W > wmax) W = wmax;
-  if (W > nchunk) W = nchunk;
   if (W < 1) W = 1;
-  if (M == 1)      launch_gemv<F, 1, 1, 4, 1>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else if (M == 2) launch_gemv<F, 1, 2, 4, 2>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else if (M <= 4) launch_gemv<F, 1, 4, 4, 4>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
-  else             launch_gemv<F, 2, 4, 2, 16>(nwg, W, st, q, s, x, y, M, N, K, ntiles, nchunk, g);
+  if (M == 1)      launch_gemv<F, 1, 1, 4, 1, MAXI>(b, nwg, W, M, st);
+  else if (M == 2) launch_gemv<F, 1, 2, 4, 2, MAXI>(b, nwg, W, M, st);
+  else if (M <= 4) launch_gemv<F, 1, 4, 4, 4, MAXI>(b, nwg, W, M, st);
+  else             launch_gemv<F, 2, 4, 2, 16, MAXI>(b, nwg, W, M, st);
+}
+
+template <int MAXI>
+static void dispatch_fmt(int fmt, GemvBatch<MAXI>& b, int M, hipStream_t st) {
+  switch (fmt) {
+    case NVFP4: dispatch_gemv<NVFP4>(b, M, st); break;
+    case DUAL:  dispatch_gemv<DUAL>(b, M, st); break;
+    default:    dispatch_gemv<FAST>(b, M, st); break;
+  }
 }
 
 }  // namespace fp4
 
 using namespace fp4;
+
+// Checks one matrix of a GEMV call; 0 or a negative status.
+static int check_item(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s, const void* x,
+                      const float* y) {
+  int rc = fp4_check_nk(fmt, N, K);
+  if (rc) return rc;
+  if (K > (1 << 24)) return -4;  // 32-bit buffer offsets within a tile row of the planes and within x
+  (void)M;
+  if (!q || !s || !x || !y) return -1;
+  if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(x, 16) || !fp4_aligned(y, 4)) return -3;
+  return 0;
+}
 
 extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                           float global_scale, const void* x_bf16, float* y, void* stream) {
@@ -355,18 +409,39 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   if (M > 16) return -4;
   int rc = fp4_check_nk(fmt, N, K);
   if (rc) return rc;
-  if (K > (1 << 24)) return -4;  // 32-bit buffer offsets within a tile row of the planes and within x
+  if (K > (1 << 24)) return -4;
   if (M == 0) return 0;
-  if (!q || !s || !x_bf16 || !y) return -1;
-  if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(x_bf16, 16) || !fp4_aligned(y, 4)) return -3;
-  hipStream_t st = (hipStream_t)stream;
-  const uint8_t* qq = (const uint8_t*)q;
-  const uint8_t* ss = (const uint8_t*)s;
-  const uint16_t* xx = (const uint16_t*)x_bf16;
-  switch (fmt) {
-    case NVFP4: dispatch_gemv<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
-    case DUAL:  dispatch_gemv<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
-    default:    dispatch_gemv<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+  rc = check_item(fmt, M, N, K, q, s, x_bf16, y);
+  if (rc) return rc;
+  GemvBatch<1> b;
+  b.count = 1;
+  b.it[0] = GemvItem{(const uint8_t*)q, (const uint8_t*)s, (const uint16_t*)x_bf16, y, (int)N, (int)K, 0, 0,
+                     global_scale, 0};
+  dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
+  return fp4_launch_status();
+}
+
+extern "C" int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items, void* stream) {
+  if (!fp4_valid_format(fmt)) return -1;
+  if (M < 0) return -2;
+  if (M > 16) return -4;
+  if (count < 0) return -1;
+  if (count > FP4_GEMV_MAX_ITEMS) return -4;
+  if (count > 0 && !items) return -1;
+  if (M == 0 || count == 0) return 0;
+  for (int i = 0; i < count; ++i) {
+    const fp4_gemv_item& it = items[i];
+    const int rc = check_item(fmt, M, it.N, it.K, it.q, it.s, it.x_bf16, it.y);
+    if (rc) return rc;
   }
+  GemvBatch<FP4_GEMV_MAX_ITEMS> b;
+  b.count = count;
+  for (int i = 0; i < count; ++i) {
+    const fp4_gemv_item& it = items[i];
+    b.it[i] = GemvItem{(const uint8_t*)it.q, (const uint8_t*)it.s, (const uint16_t*)it.x_bf16, it.y, (int)it.N,
+                       (int)it.K, 0, 0, it.global_scale, 0};
+  }
+  for (int i = count; i < FP4_GEMV_MAX_ITEMS; ++i) b.it[i] = GemvItem{};
+  dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
   return fp4_launch_status();
 }

@@ -96,6 +96,30 @@ int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const vo
                float global_scale, const void* x_bf16, float* y, void* stream);
 
 /*
+ * Several decode-shaped products in one launch (next-step row f1: the per-launch cost dominates
+ * decode matrices of a few MB, Nanbeige4.2-3B-NVFP4A16 card, speed notes). Each item is one
+ * matrix with its own planes, x, y, N, K and global scale; all share fmt and M (1 <= M <= 16).
+ * Typical use: the q|k|v or gate|up projections of one token, which read the same x, or any
+ * list of independent products. Each y equals what w4a16_gemv would produce to within the
+ * product tolerance (the K split may differ, so the summation order can). `items` is a HOST
+ * array, read before the call returns; at most FP4_GEMV_MAX_ITEMS items. Each item is checked
+ * as w4a16_gemv checks its arguments; the first failing item's status is returned and nothing
+ * runs. M = 0 or count = 0 is a no-op. y buffers must not overlap each other or any input.
+ */
+#define FP4_GEMV_MAX_ITEMS 32
+typedef struct fp4_gemv_item {
+  const void* q;        /* fp4_pack_layout nibble plane (device) */
+  const void* s;        /* fp4_pack_layout scale plane (device) */
+  const void* x_bf16;   /* x[M][K], bf16 bit patterns (device) */
+  float* y;             /* y[M][N], fp32 (device) */
+  int64_t N;
+  int64_t K;
+  float global_scale;
+} fp4_gemv_item;
+
+int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items, void* stream);
+
+/*
  * Prefill-shaped product, any M >= 1, intended for M >= 64 (rows a7-a10): stages x tiles
  * and packed weight tiles, dequantizes each weight tile once into LDS as exact bf16
  * level*scale, contracts with bf16 MFMA in FP32 and multiplies by g in the epilogue.

@@ -58,6 +58,21 @@ def weights(n: int, k: int, *, dist: str = "normal", nu: float = 5.0, sigma: flo
     return w
 
 
+def device_weights(n: int, k: int, *, sigma: float = 0.02, cfg: int = 0, mat: int = 0, device="cuda"):
+    """N(0, sigma^2) fp32 weights W[n, k] drawn on a torch device (for benchmark-sized workloads).
+
+    Same recipe as ``weights(dist="normal")``, drawn by torch's generator for ``device`` seeded from
+    the (cfg, mat) weight stream, so a many-GB workload is generated in place in seconds. The values
+    differ from the numpy draw of the same (cfg, mat); tests that compare with the oracle use
+    ``weights``.
+    """
+    import torch
+    seed = int(np.random.SeedSequence(ROOT_SEED, spawn_key=(int(cfg), int(mat), STREAM_W)).generate_state(1)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((n, k), generator=g, device=device, dtype=torch.float32) * sigma
+
+
 def _f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 to the nearest bf16 (ties to even); returns the uint16 bit patterns."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)

@@ -114,3 +114,32 @@ def test_python_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         fp4._ptr(torch.zeros(4))
+
+
+def test_gemv_batched_argument_errors():
+    f = _raw().w4a16_gemv_batched
+    Item = fp4.GemvItem
+
+    def items(*specs):
+        arr = (Item * max(1, len(specs)))()
+        for i, kw in enumerate(specs):
+            a = dict(q=FAKE, s=FAKE, x_bf16=FAKE, y=FAKE, N=16, K=64, global_scale=1.0)
+            a.update(kw)
+            arr[i] = Item(a["q"], a["s"], a["x_bf16"], a["y"], a["N"], a["K"], a["global_scale"])
+        return arr
+
+    good = {}
+    assert f(7, 1, 1, items(good), None) == ARG
+    assert f(NVFP4, 17, 1, items(good), None) == UNSUP
+    assert f(NVFP4, -1, 1, items(good), None) == SHAPE
+    assert f(NVFP4, 1, -1, items(good), None) == ARG
+    assert f(NVFP4, 1, fp4.GEMV_MAX_ITEMS + 1, items(good), None) == UNSUP
+    assert f(NVFP4, 1, 1, None, None) == ARG
+    assert f(NVFP4, 1, 0, None, None) == OK                    # no items: no-op
+    assert f(NVFP4, 0, 2, items(good, dict(q=None)), None) == OK   # M = 0: no-op
+    # the first failing item decides the status
+    assert f(NVFP4, 1, 3, items(good, dict(K=40), dict(q=None)), None) == SHAPE
+    assert f(NVFP4, 1, 2, items(good, dict(y=FAKE + 2)), None) == ALIGN
+    assert f(DUAL, 1, 2, items(good, dict(K=48)), None) == SHAPE
+    assert f(NVFP4, 1, 2, items(good, dict(x_bf16=None)), None) == ARG
+    assert f(NVFP4, 1, 1, items(dict(K=1 << 25)), None) == UNSUP

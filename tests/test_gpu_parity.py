@@ -125,6 +125,63 @@ def test_gemv_m0_is_noop():
     assert torch.all(y == 7.0)
 
 
+# ------------------------------------------------------------------ batched GEMV
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("m", [1, 3, 9, 16])
+def test_gemv_batched_matches_oracle(fmt, m):
+    # matrices of different N and K (ragged tiles and chunks), two of them sharing one x, with
+    # canaries around every y
+    shapes = [(48, 256), (37, 160), (256, 1536), (16, 32 if fmt != "nvfp4" else 16), (130, 256)]
+    _announce("gemv-batched", fmt, m, shapes)
+    cases, items, bufs = [], [], []
+    shared_x = None
+    for i, (n, k) in enumerate(shapes):
+        w, packed = gc.make_case(fmt, n, k, cfg=58, mat=100 * i + n)
+        pw = gc.upload(fmt, n, k, packed)
+        if i == 4:                      # same K as item 0: reuse its x
+            x_bits = cases[0][2]
+            x = shared_x
+        else:
+            x_bits = synth.activations(m, k, cfg=58, mat=1000 * i + k)
+            x = gc.x_tensor(x_bits)
+        if i == 0:
+            shared_x = x
+        buf = torch.full((m * n + 64,), 12345.0, device="cuda")
+        y = buf[32:32 + m * n]
+        cases.append((packed, pw, x_bits, y, buf, n, k))
+        items.append((pw.q, pw.s, pw.global_scale, x, y, n, k))
+    fp4.w4a16_gemv_batched(fmt, m, items)
+    torch.cuda.synchronize()
+    for (packed, pw, x_bits, y, buf, n, k) in cases:
+        gc.check_product(fmt, packed, x_bits, y.view(m, n), label=f"batched {fmt} M={m} {n}x{k}")
+        assert torch.all(buf[:32] == 12345.0) and torch.all(buf[32 + m * n:] == 12345.0)
+
+
+def test_gemv_batched_many_items_and_repeatability():
+    # the full item count; every item a different matrix; outputs bitwise repeatable
+    fmt, m = "nvfp4", 2
+    _announce("gemv-batched-max", fmt, m)
+    items, cases = [], []
+    for i in range(fp4.GEMV_MAX_ITEMS):
+        n, k = 16 * (1 + i % 5), 128 * (1 + i % 3)
+        w, packed = gc.make_case(fmt, n, k, cfg=59, mat=i)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=59, mat=i)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        items.append((pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y, n, k))
+        cases.append((packed, x_bits, y))
+    fp4.w4a16_gemv_batched(fmt, m, items)
+    torch.cuda.synchronize()
+    first = [c[2].clone() for c in cases]
+    for packed, x_bits, y in cases:
+        gc.check_product(fmt, packed, x_bits, y, label="batched-max")
+    fp4.w4a16_gemv_batched(fmt, m, items)
+    torch.cuda.synchronize()
+    for f, (_, _, y) in zip(first, cases):
+        assert torch.equal(f, y)
+
+
 # ------------------------------------------------------------------ GEMM
 
 @pytest.mark.parametrize("fmt", gc.FMTS)
