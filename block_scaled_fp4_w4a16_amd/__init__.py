@@ -44,6 +44,7 @@ _SIGS = {
     "w4a16_gemv": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "w4a16_gemv_batched": (_c, [_c, _i64, _c, ctypes.POINTER(GemvItem), _p]),
     "w4a16_gemm": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
+    "w4a16_midm": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "w4a16_matmul": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "fp4_dequant_f32": (_c, [_c, _i64, _i64, _p, _p, _f, _p, _p]),
     "fp4_quantize_nvfp4": (_c, [_i64, _i64, _p, _p, _p, _p, _p]),
@@ -152,6 +153,10 @@ def w4a16_gemv_batched(fmt, M, items, stream=None):
 
 def w4a16_gemm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
     _product("w4a16_gemm", fmt, M, N, K, q, s, global_scale, x, y, stream)
+
+
+def w4a16_midm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
+    _product("w4a16_midm", fmt, M, N, K, q, s, global_scale, x, y, stream)
 
 
 def w4a16_matmul(fmt, M, N, K, q, s, global_scale, x, y, stream=None):

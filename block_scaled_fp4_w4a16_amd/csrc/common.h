@@ -91,4 +91,41 @@ __device__ __forceinline__ bf16x8 cat(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// bf16 of two f32 values (exact for level*scale, which has at most 7 significant bits)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  uint32_t u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x2& a, const f32x2& b, const f32x2& c, const f32x2& e, float sc) {
+  u32x4 v = {pack_bf16x2(a[0] * sc, a[1] * sc), pack_bf16x2(b[0] * sc, b[1] * sc), pack_bf16x2(c[0] * sc, c[1] * sc),
+             pack_bf16x2(e[0] * sc, e[1] * sc)};
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// Four Codebook10 nibbles (the low nibbles of the four bytes of w when HIGH is false, the high nibbles
+// otherwise) -> four E4M3 bytes.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t cb10_quad(uint32_t w) {
+  if constexpr (HIGH) {
+    return __builtin_amdgcn_perm(CB10_E4M3_HI, CB10_E4M3_LO, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+  } else {
+    return __builtin_amdgcn_perm(CB10_E4M3_HI, CB10_E4M3_LO, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  }
+}
+
+// Same with a separate scale for the first and the second four values.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x2& a, const f32x2& b, const f32x2& c, const f32x2& e, float s0,
+                                           float s1) {
+  u32x4 v = {pack_bf16x2(a[0] * s0, a[1] * s0), pack_bf16x2(b[0] * s0, b[1] * s0), pack_bf16x2(c[0] * s1, c[1] * s1),
+             pack_bf16x2(e[0] * s1, e[1] * s1)};
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
 }  // namespace fp4

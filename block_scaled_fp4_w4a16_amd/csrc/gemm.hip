@@ -36,33 +36,6 @@ __host__ __device__ constexpr int gm_loads_per_stage(int f) { return GM_X_SLOTS 
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// bf16 of two f32 values (exact here: level*scale has at most 7 significant bits)
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2 v = {(__bf16)a, (__bf16)b};
-  uint32_t u;
-  __builtin_memcpy(&u, &v, 4);
-  return u;
-}
-
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x2& a, const f32x2& b, const f32x2& c, const f32x2& e, float sc) {
-  u32x4 v = {pack_bf16x2(a[0] * sc, a[1] * sc), pack_bf16x2(b[0] * sc, b[1] * sc), pack_bf16x2(c[0] * sc, c[1] * sc),
-             pack_bf16x2(e[0] * sc, e[1] * sc)};
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
-
-// Four Codebook10 nibbles (the low nibbles of the four bytes of w when HIGH is false, the high nibbles
-// otherwise) -> four E4M3 bytes.
-template <bool HIGH>
-__device__ __forceinline__ uint32_t cb10_quad(uint32_t w) {
-  if constexpr (HIGH) {
-    return __builtin_amdgcn_perm(CB10_E4M3_HI, CB10_E4M3_LO, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
-  } else {
-    return __builtin_amdgcn_perm(CB10_E4M3_HI, CB10_E4M3_LO, w & 0x07070707u) | ((w << 4) & 0x80808080u);
-  }
-}
-
 // B operand of k-step s for this lane: 8 consecutive positions of the stage's k subset (see the kernel),
 // dequantized to bf16 level * scale. w0 / w1 are this lane's two dwords of lane piece 2hh / 2hh + 1.
 template <int F, int S>
@@ -375,5 +348,6 @@ extern "C" int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
 extern "C" int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                             float global_scale, const void* x_bf16, float* y, void* stream) {
   if (M >= 0 && M <= 16) return w4a16_gemv(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
+  if (M <= 64) return w4a16_midm(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
   return w4a16_gemm(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
 }

@@ -336,6 +336,121 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch,
   }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Mid-M product (17 <= M <= 64). Same layout, workgroup shape and K split as the GEMV (one 16-row
+// tile per workgroup, waves take chunks wave, wave + W, ...), but every unit's weights are decoded
+// once into bf16 MFMA operands that already carry the group scale (level * scale, exact in bf16) and
+// are reused by the MB = ceil(M / 16) blocks of 16 x rows, one 16x16x32 MFMA per 32 positions and
+// block accumulating straight into FP32. The waves' sums are reduced through LDS in a fixed order.
+//
+// B operand j (j = 0..3) of a unit is dword j of the lane's 16 bytes: positions 8 j .. 8 j + 7. For
+// 16-weight groups those are positions 4 t of group 2 j (first four) and of group 2 j + 1 (last four),
+// matching x fragments 2 j and 2 j + 1 of the staged row; for FAST they are block j.
+template <int F>
+__device__ __forceinline__ void decode_scaled(const WeightRegs<F>& w, bf16x8 (&b)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t d = w.q[j];
+    if constexpr (F == FAST) {
+      const float sc = (j == 0) ? e4m3_to_f32<0>(w.s[0]) : (j == 1) ? e4m3_to_f32<1>(w.s[0])
+                     : (j == 2) ? e4m3_to_f32<2>(w.s[0]) : e4m3_to_f32<3>(w.s[0]);
+      const uint32_t lo = cb10_quad<false>(d), hi = cb10_quad<true>(d);
+      b[j] = to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true),
+                       __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true), sc);
+    } else {
+      // scales of groups 2 j and 2 j + 1: half-word j % 2 of scale dword j / 2
+      const f32x2 sc = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w.s[j >> 1], true)
+                               : __builtin_amdgcn_cvt_pk_f32_fp8(w.s[j >> 1], false);
+      if constexpr (F == DUAL) {
+        const uint32_t lo = cb10_quad<false>(d), hi = cb10_quad<true>(d);
+        b[j] = to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true), sc[0], sc[1]);
+      } else {
+        b[j] = to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3), sc[0], sc[1]);
+      }
+    }
+  }
+}
+
+// Dynamic LDS: [W waves][4 lane groups][M rows][64 B] of staged x (one chunk per wave), then the
+// cross-wave reduction buffer [W][MB][64 lanes][4] floats.
+template <int F, int MB>
+__global__ __launch_bounds__(512) void midm_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
+                                                   const uint16_t* __restrict__ x, float* __restrict__ y, int M,
+                                                   int N, int K, int ntiles, int nchunk, float gscale) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63, W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4, m16 = lane & 15;
+  const int tile = blockIdx.x;
+  Srcs src;
+  src.q = make_rsrc(qp + (int64_t)tile * nchunk * UNIT_Q, (uint32_t)(nchunk * UNIT_Q));
+  src.s = make_rsrc(sp + (int64_t)tile * nchunk * unit_s(F), (uint32_t)(nchunk * unit_s(F)));
+  src.x = make_rsrc(x, (uint32_t)(M * K) * 2u);
+  const size_t xw_bytes = (size_t)4 * M * 64;
+  uint8_t* xs = smem + wave * xw_bytes;
+  float* red = reinterpret_cast<float*>(smem + W * xw_bytes);
+  const uint32_t soff_lane = n * (unit_s(F) / TILE_N);
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // x of the wave's next chunk is loaded into registers (all of it at once) together with the next
+  // weights while the current chunk is computed, then committed to LDS at the top of the next chunk.
+  XStage<1, 16 * MB> xst;
+  WeightRegs<F> wr;
+  if (wave < nchunk) {
+    stage_x_issue<F, 1, 16 * MB>(xst, src, M, K, wave, W, nchunk, lane);
+    load_unit<F>(wr, src, (uint32_t)wave * UNIT_Q + lane * 16, (uint32_t)wave * unit_s(F) + soff_lane);
+  }
+  for (int c = wave; c < nchunk; c += W) {
+    stage_x_commit<F, 1, 16 * MB>(xs, xst, M, lane);
+    WeightRegs<F> nx;                  // next unit of this wave, in flight during this one
+    const int c1 = c + W;
+    if (c1 < nchunk) {
+      stage_x_issue<F, 1, 16 * MB>(xst, src, M, K, c1, W, nchunk, lane);
+      load_unit<F>(nx, src, (uint32_t)c1 * UNIT_Q + lane * 16, (uint32_t)c1 * unit_s(F) + soff_lane);
+    }
+    bf16x8 b[4];
+    decode_scaled<F>(wr, b);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = min(mb * 16 + m16, M - 1);  // rows past M repeat a valid row; never stored
+      const uint8_t* xr = xs + (g * M + row) * 64;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + 16 * j);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[mb], 0, 0, 0);
+      }
+    }
+    if (c1 < nchunk) wr = nx;
+  }
+
+  float* mine = red + ((size_t)wave * MB * 64 + lane) * 4;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(mine + (size_t)mb * 256) = acc[mb];
+  __syncthreads();
+  const int total = MB * 256;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int mb = e / 256, l = (e >> 2) & 63, r = e & 3;
+    const int mrow = mb * 16 + 4 * (l >> 4) + r;
+    const int col = tile * TILE_N + (l & 15);
+    if (mrow < M && col < N) {
+      float sum = 0.f;
+      for (int w = 0; w < W; ++w) sum += red[(size_t)w * total + e];
+      y[(int64_t)mrow * N + col] = sum * gscale;
+    }
+  }
+}
+
 constexpr int GEMV_LDS_MAX = 160 * 1024;
 
 template <int F, int T, int RU, int U, int MX, int MAXI>
@@ -402,6 +517,37 @@ static int check_item(int fmt, int64_t M, int64_t N, int64_t K, const void* q, c
   return 0;
 }
 
+template <int F, int MB>
+static void launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                        int M, int N, int K, float g) {
+  const int ntiles = (N + TILE_N - 1) / TILE_N, nchunk = (K + CHUNK_K - 1) / CHUNK_K;
+  const size_t lds = (size_t)W * 4 * M * 64 + (size_t)W * MB * 64 * 4 * sizeof(float);
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&midm_kernel<F, MB>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
+  (void)attr;
+  hipLaunchKernelGGL((midm_kernel<F, MB>), dim3(ntiles), dim3(64 * W), lds, st, q, s, x, y, M, N, K, ntiles, nchunk,
+                     g);
+}
+
+template <int F>
+static void dispatch_midm(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                          int N, int K, float g) {
+  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K, ntiles = (N + TILE_N - 1) / TILE_N;
+  // Waves per workgroup: the most (up to 8; the staged x of 8 waves at M = 64 fills 128 KiB of LDS)
+  // that give every wave at least two chunks and keep the grid resident at once (16 waves per CU
+  // with two 16-row blocks of x, 8 with more, at this kernel's register use).
+  const int resident = (M <= 32 ? 16 : 8) * 256;
+  int W = 8;
+  while (W > 1 && (nchunk < 2 * W || ntiles * W > resident)) W >>= 1;
+  if (const char* e = getenv("FP4_MIDM_WAVES")) {  // tuning override, read at each call
+    if (atoi(e) > 0 && atoi(e) <= 8) W = atoi(e);
+  }
+  const int mb = (M + 15) / 16;
+  if (mb <= 2)      launch_midm<F, 2>(W, st, q, s, x, y, M, N, K, g);
+  else if (mb == 3) launch_midm<F, 3>(W, st, q, s, x, y, M, N, K, g);
+  else              launch_midm<F, 4>(W, st, q, s, x, y, M, N, K, g);
+}
+
 extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                           float global_scale, const void* x_bf16, float* y, void* stream) {
   if (!fp4_valid_format(fmt)) return -1;
@@ -443,5 +589,29 @@ extern "C" int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_
   }
   for (int i = count; i < FP4_GEMV_MAX_ITEMS; ++i) b.it[i] = GemvItem{};
   dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
+  return fp4_launch_status();
+}
+
+// Mid-M entry point (17 <= M <= 64 through w4a16_matmul; any 1 <= M <= 64 accepted).
+extern "C" int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                          float global_scale, const void* x_bf16, float* y, void* stream) {
+  if (!fp4_valid_format(fmt)) return -1;
+  if (M < 0) return -2;
+  if (M > 64) return -4;
+  int rc = fp4_check_nk(fmt, N, K);
+  if (rc) return rc;
+  if (K > (1 << 24)) return -4;
+  if (M == 0) return 0;
+  rc = check_item(fmt, M, N, K, q, s, x_bf16, y);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const uint8_t* qq = (const uint8_t*)q;
+  const uint8_t* ss = (const uint8_t*)s;
+  const uint16_t* xx = (const uint16_t*)x_bf16;
+  switch (fmt) {
+    case NVFP4: dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+    case DUAL:  dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+    default:    dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+  }
   return fp4_launch_status();
 }

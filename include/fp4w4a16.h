@@ -127,7 +127,18 @@ int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items
 int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);
 
-/* Dispatch on M (row a11): M <= 16 -> w4a16_gemv, otherwise w4a16_gemm. */
+/*
+ * Mid-sized M, 1 <= M <= 64 (next-step row f4; the band between the decode and prefill shapes,
+ * e.g. speculative-decoding verification of many drafts or small batches, Nanbeige4.2-3B-NVFP4A16
+ * card, serving notes): the GEMV's layout and in-workgroup K split, with each weight decoded once
+ * into exact bf16 level*scale and reused by up to four 16-row blocks of x on the matrix cores.
+ * Deterministic. Arguments and errors as w4a16_gemv; M > 64 gives FP4_ERR_UNSUPPORTED.
+ */
+int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+               float global_scale, const void* x_bf16, float* y, void* stream);
+
+/* Dispatch on M (row a11): M <= 16 -> w4a16_gemv, 17 <= M <= 64 -> w4a16_midm, otherwise
+ * w4a16_gemm. */
 int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                  float global_scale, const void* x_bf16, float* y, void* stream);
 

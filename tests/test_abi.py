@@ -61,7 +61,7 @@ def _raw():
     return fp4.lib()
 
 
-@pytest.mark.parametrize("fn", ["w4a16_gemv", "w4a16_gemm", "w4a16_matmul"])
+@pytest.mark.parametrize("fn", ["w4a16_gemv", "w4a16_midm", "w4a16_gemm", "w4a16_matmul"])
 def test_product_argument_errors(fn):
     f = getattr(_raw(), fn)
     good = dict(fmt=NVFP4, M=1, N=16, K=64, q=FAKE, s=FAKE, g=1.0, x=FAKE, y=FAKE, st=None)
@@ -88,6 +88,8 @@ def test_product_argument_errors(fn):
     assert call(N=1 << 31) == UNSUP
     if fn == "w4a16_gemv":
         assert call(M=17) == UNSUP
+    if fn == "w4a16_midm":
+        assert call(M=65) == UNSUP
 
 
 def test_pack_layout_argument_errors():

@@ -182,6 +182,53 @@ def test_gemv_batched_many_items_and_repeatability():
         assert torch.equal(f, y)
 
 
+# ------------------------------------------------------------------ mid-M
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("m", [1, 8, 17, 31, 32, 33, 48, 63, 64])
+def test_midm_shapes(fmt, m):
+    for (n, k) in [(48, 256), (37, 160), (256, 1536)]:
+        _announce("midm", fmt, m, n, k)
+        w, packed = gc.make_case(fmt, n, k, cfg=60, mat=n)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=60, mat=k)
+        buf = torch.full((m * n + 64,), 12345.0, device="cuda")
+        y = buf[32:32 + m * n]
+        fp4.w4a16_midm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+        torch.cuda.synchronize()
+        gc.check_product(fmt, packed, x_bits, y.view(m, n), label=f"midm {fmt} M={m} {n}x{k}")
+        assert torch.all(buf[:32] == 12345.0) and torch.all(buf[32 + m * n:] == 12345.0)
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
+def test_midm_one_hot_returns_weight_columns_exactly(fmt):
+    n, k = 80, 384
+    _announce("midm-one-hot", fmt)
+    w, packed = gc.make_case(fmt, n, k, cfg=61)
+    pw = gc.upload(fmt, n, k, packed)
+    ks = np.arange(0, k, 7)[:50]
+    x_bits = np.zeros((len(ks), k), np.uint16)
+    x_bits[np.arange(len(ks)), ks] = 0x3F80
+    y = torch.empty((len(ks), n), device="cuda")
+    fp4.w4a16_midm(fmt, len(ks), n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), ref.dequant_f32(fmt, packed)[:, ks].T)
+
+
+def test_midm_repeatable():
+    fmt, m, n, k = "rocmfp4_dual", 40, 96, 1024
+    _announce("midm-repeat", fmt)
+    w, packed = gc.make_case(fmt, n, k, cfg=62)
+    pw = gc.upload(fmt, n, k, packed)
+    x = gc.x_tensor(synth.activations(m, k, cfg=62))
+    y1 = torch.empty((m, n), device="cuda")
+    y2 = torch.empty((m, n), device="cuda")
+    fp4.w4a16_midm(fmt, m, n, k, pw.q, pw.s, 1.0, x, y1)
+    fp4.w4a16_midm(fmt, m, n, k, pw.q, pw.s, 1.0, x, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 # ------------------------------------------------------------------ GEMM
 
 @pytest.mark.parametrize("fmt", gc.FMTS)
@@ -213,7 +260,7 @@ def test_gemm_identity_returns_weights_exactly(fmt):
     assert np.array_equal(y.cpu().numpy(), ref.dequant_f32(fmt, packed).T)
 
 
-@pytest.mark.parametrize("m", [1, 16, 17, 64])
+@pytest.mark.parametrize("m", [1, 16, 17, 40, 64, 65])
 def test_matmul_dispatch(m):
     fmt, n, k = "nvfp4", 64, 256
     _announce("matmul", m)

@@ -50,7 +50,7 @@ def test_decode_sweep_one_layer():
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "rocmfp4_dual", "rocmfp4_fast"])
-@pytest.mark.parametrize("m", [1, 9, 16])
+@pytest.mark.parametrize("m", [1, 9, 16, 33, 64])
 def test_spec_verify(fmt, m):
     for mat in range(2):
         _run(fmt, 3, mat, m)
