@@ -9,12 +9,16 @@ Sources:
   format comparison table: the Codebook10 grid 0, +-1, +-2, +-3, +-4, +-6, +-8,
   +-10, E2M1-derived with the outer magnitude retuned from 12 to 10; scales
   are unsigned E4M3 (UE4M3) and the search scores the finite candidates.
+* Same page, comparison table, stock Q4_0 column: a uniform integer grid, one
+  FP16 scale per 32 weights.
 
 Readings (the pages leave these open):
 * Codebook10 code order: codes 0..6 are twice the E2M1 magnitude of the same
   code, code 7 is 10 (the retuned 12); bit 3 is the sign. Code 8 is level 0.
 * UE4M3: the byte's bit 7 is ignored (masked); 0x7F is NaN and never emitted,
   so the finite candidates are the 127 codes 0x00..0x7E, zero included.
+* Q4_0: the 16 codes are the consecutive integers -8..7 (code q is level q - 8),
+  the usual stock Q4_0 grid that "uniform integer steps" in 4 bits describes.
 """
 from __future__ import annotations
 
@@ -38,6 +42,21 @@ def codebook10_value(code) -> np.ndarray:
     c = np.asarray(code, dtype=np.int64)
     mag = CODEBOOK10_MAGNITUDE[c & 7]
     return np.where(((c & 8) != 0) & (mag != 0.0), -mag, mag)
+
+
+def q4_0_value(code) -> np.ndarray:
+    """Q4_0 nibble -> integer level q - 8 in -8..7."""
+    return np.asarray(code, dtype=np.int64).astype(np.float64) - 8.0
+
+
+def fp16_value(bits) -> np.ndarray:
+    """IEEE binary16 bit pattern (uint16) -> exact FP64 value."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def fp16_encode_rne(v) -> np.ndarray:
+    """FP64 value -> IEEE binary16 bit pattern, round to nearest even (numpy's conversion)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
 
 
 def e4m3_value(byte) -> np.ndarray:

@@ -16,8 +16,20 @@ E4M3 scale per 16, FP32 global scale per matrix):
 ROCmFP4 - exhaustive finite-UE4M3 MSE search per scale group (ROCmFP4 design page,
 section 03); see csrc/rocmfp4_search.c for the steps and readings. g = 1.
 
+Q4_0 - signed abs-max scale (ROCmFP4 design page, comparison table: the stock Q4_0
+reference scale is derived from the signed abs-max; no imatrix):
+  1. per 32-weight block, m = the weight of largest magnitude, keeping its sign (the
+     first one in index order on a tie of magnitudes); d = m / -8 (exact in FP64), so
+     that m lands on the grid's -8 end;
+  2. the stored scale is d rounded to FP16 (RNE);
+  3. each code is the grid point nearest w / d rounding halves up, q = floor(w / d + 8.5)
+     clipped to 0..15, decided in FP64 with the unrounded d (exact: w / d is a ratio of
+     FP32 values scaled by 8); d = 0 (an all-zero block) gives code 8 (level 0).
+  Readings: which d decides the codes and the tie rule are not on the pages; the
+  stored scale is what dequantisation uses. g = 1.
+
 Return shapes: NVFP4 -> (wq u8[N, K/2], ws u8[N, K/16], g float32);
-ROCmFP4 -> (blocks u8[N, K/32, 18 | 17], g = float32(1)).
+ROCmFP4 and Q4_0 -> (blocks u8[N, K/32, 18 | 17], g = float32(1)).
 """
 from __future__ import annotations
 
@@ -134,9 +146,25 @@ def pack_rocmfp4(fmt: str, w: np.ndarray, importance: np.ndarray | None = None):
     return (blocks, np.float32(1.0))
 
 
+def pack_q4_0(w: np.ndarray):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    if k % layouts.ROCM_BLOCK:
+        raise ValueError("K must be a multiple of 32 for Q4_0")
+    b = w.astype(np.float64).reshape(n * (k // 32), 32)
+    first = np.argmax(np.abs(b), axis=1)                  # first index of the largest magnitude
+    m = b[np.arange(b.shape[0]), first]
+    d = m / -8.0 + 0.0                                    # + 0.0: an all-zero block stores +0
+    d_bits = formats.fp16_encode_rne(d)
+    safe = np.where(d != 0.0, d, 1.0)
+    q = np.floor(b / safe[:, None] + 8.5)
+    q = np.where((d != 0.0)[:, None], np.clip(q, 0, 15), 8).astype(np.uint8)
+    return (layouts.q4_0_join(q.reshape(n, k), d_bits.reshape(n, k // 32)), np.float32(1.0))
+
+
 def pack(fmt: str, w: np.ndarray, importance: np.ndarray | None = None):
-    if fmt == "nvfp4":
+    if fmt in ("nvfp4", "q4_0"):
         if importance is not None:
-            raise ValueError("the NVFP4 packer is data-free RTN; it takes no importance")
-        return pack_nvfp4(w)
+            raise ValueError(f"the {fmt} packer takes no importance")
+        return pack_nvfp4(w) if fmt == "nvfp4" else pack_q4_0(w)
     return pack_rocmfp4(fmt, w, importance)

@@ -6,6 +6,7 @@ page, sections 01-02 and the comparison table):
     NVFP4:         W[n, k] = e2m1(q[n, k]) * e4m3(ws[n, k // 16]) * g
     ROCmFP4 Dual:  W[n, 32b + j] = codebook10(q) * ue4m3(s[b][j >= 16])
     ROCmFP4 FAST:  W[n, 32b + j] = codebook10(q) * ue4m3(s[b])
+    Q4_0:          W[n, 32b + j] = (q - 8) * fp16(d[b])          (comparison table, stock Q4_0)
     y[m, n] = sum_k x[m, k] * W[n, k]          (x is bf16, y is reported in fp32)
 
 Readings:
@@ -13,8 +14,8 @@ Readings:
   every product above is exact (at most 3 + 4 + 24 significant bits), so the
   oracle's W is the exact product. The bit-exact FP32 dequant target is one
   round-to-nearest-even of that exact value.
-* The pages list no tensor-level scale for ROCmFP4 (the block metadata is the
-  scale bytes only), so g = 1 there; the interface still takes g.
+* The pages list no tensor-level scale for ROCmFP4 or Q4_0 (the block metadata is
+  the scale bytes only), so g = 1 there; the interface still takes g.
 
 Acceptance (the tolerance of the GPU path): |y_gpu - y_ref| <= 2e-3 * B + 1e-6 with
 B[m, n] = sum_k |x[m, k] * W[n, k]|.
@@ -51,12 +52,21 @@ def dequant_rocmfp4(fmt: str, blocks: np.ndarray, g: float = 1.0) -> np.ndarray:
     return level * scale * np.float64(np.float32(g))
 
 
+def dequant_q4_0(blocks: np.ndarray, g: float = 1.0) -> np.ndarray:
+    codes, d_bits = layouts.q4_0_split(blocks)
+    level = formats.q4_0_value(codes)
+    scale = np.repeat(formats.fp16_value(d_bits), layouts.ROCM_BLOCK, axis=1)
+    return level * scale * np.float64(np.float32(g))
+
+
 def dequant(fmt: str, packed) -> np.ndarray:
     """Exact FP64 W[N, K] from a packed matrix (see pack.py for the tuple shapes)."""
     if fmt == "nvfp4":
         wq, ws, g = packed
         return dequant_nvfp4(wq, ws, g)
     blocks, g = packed
+    if fmt == "q4_0":
+        return dequant_q4_0(blocks, g)
     return dequant_rocmfp4(fmt, blocks, g)
 
 

@@ -98,7 +98,7 @@ def test_e4m3_encode_rne_bruteforce():
 
 def test_block_densities_match_page():
     g = golden_io.read("block_density.txt")
-    for fmt in ("rocmfp4_dual", "rocmfp4_fast", "nvfp4"):
+    for fmt in ("rocmfp4_dual", "rocmfp4_fast", "nvfp4", "q4_0"):
         wpb, bb, bpw, group, nscale = g[fmt]
         assert layouts.canonical_bytes(fmt, 1, 32) * int(wpb) == int(bb) * 32
         assert layouts.bits_per_weight(fmt) == pytest.approx(float(bpw), abs=1e-12)
@@ -116,3 +116,53 @@ def test_layout_roundtrip():
         assert np.array_equal(layouts.rocm_join(fmt, codes, sc), blocks)
     wq = rng.integers(0, 256, size=(5, 8), dtype=np.uint8)
     assert np.array_equal(layouts.nvfp4_join(layouts.nvfp4_split(wq)), wq)
+    blocks = rng.integers(0, 256, size=(3, 4, 18), dtype=np.uint8)
+    codes, d = layouts.q4_0_split(blocks)
+    assert codes.shape == (3, 128) and d.shape == (3, 4)
+    assert np.array_equal(layouts.q4_0_join(codes, d), blocks)
+
+
+def test_q4_0_grid_is_uniform_integer_steps():
+    # comparison table, stock Q4_0: uniform integer steps; 16 codes -> the 16 consecutive integers -8..7
+    lv = formats.q4_0_value(np.arange(16))
+    assert lv.tolist() == list(range(-8, 8))
+    assert np.all(np.diff(lv) == 1.0)
+
+
+def _fp16_closed_form(b: int) -> float:
+    s, e, m = b >> 15, (b >> 10) & 31, b & 1023
+    if e == 31:
+        return float("nan") if m else (-1) ** s * float("inf")
+    mag = m * 2.0 ** -24 if e == 0 else (1024 + m) * 2.0 ** (e - 25)
+    return -mag if s else mag
+
+
+def test_fp16_codec_all_patterns():
+    # decode: every pattern against the IEEE binary16 closed form and against torch's decoder
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = formats.fp16_value(bits)
+    want = np.array([_fp16_closed_form(int(b)) for b in bits])
+    assert np.array_equal(v, want, equal_nan=True)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(v, t, equal_nan=True)
+    # encode: nearest finite value, ties to the even pattern, on values between and at the grid points
+    pos = np.sort(want[np.isfinite(want) & (want >= 0)])
+    pos = np.unique(pos)
+    rng = np.random.default_rng(4)
+    i = rng.integers(0, len(pos) - 1, 3000)
+    lo, hi = pos[i], pos[i + 1]
+    probes = np.concatenate([lo, (lo + hi) / 2, lo + (hi - lo) * rng.random(3000)])
+    got = formats.fp16_value(formats.fp16_encode_rne(probes))
+    for p, gv in zip(probes, got):
+        j = np.searchsorted(pos, p)
+        cands = [c for c in (pos[max(j - 1, 0)], pos[min(j, len(pos) - 1)])]
+        best = min(cands, key=lambda c: (abs(c - p), int(formats.fp16_encode_rne(c)) & 1))
+        assert gv == best, (p, gv, best)
+
+
+def test_widget_q4_0_shared_scale_displays_as_page():
+    # section 02's lab shows a Q4_0 shared scale of 1.025 beside ROCmFP4 half scales 0.813 / 0.094;
+    # under the signed abs-max rule that is an outlier of magnitude 8.2 (8.2 / 8 = 1.025), and its
+    # FP16 scale prints as 1.025 to three decimals
+    d16 = formats.fp16_value(formats.fp16_encode_rne(8.2 / 8.0))
+    assert f"{abs(float(d16)):.3f}" == "1.025"

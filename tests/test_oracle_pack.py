@@ -211,3 +211,60 @@ def test_level_ties_go_to_even_code():
     wq, ws, g = pack.pack_nvfp4(w)
     assert g == 1.0 and ws[0, 1] == 0x38
     assert layouts.nvfp4_split(wq)[0, 17:24].tolist() == [0, 2, 2, 4, 4, 6, 6]
+
+
+# ---------------------------------------------------------------- Q4_0 (signed abs-max)
+
+def test_q4_0_worked_case():
+    g = golden_io.read("hand_packed.txt")
+    w = np.zeros((1, 32), np.float32)
+    w[0, :8] = golden_io.floats(g["q4_0_pack_weights"])
+    blocks, gs = pack.pack_q4_0(w)
+    assert gs == 1.0
+    assert blocks[0, 0, :2].tolist() == golden_io.hex_bytes(g["q4_0_pack_scale_bytes"])
+    codes, _ = layouts.q4_0_split(blocks)
+    assert codes[0].tolist() == golden_io.hex_bytes(g["q4_0_pack_codes"])
+
+
+def test_q4_0_signed_absmax_maps_extreme_to_grid_end():
+    # the largest-magnitude weight (sign kept) always gets code 0, i.e. level -8; when m / -8 is an
+    # FP16 value it is reconstructed exactly
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((40, 64)) * 0.02).astype(np.float32)
+    w[3, 5] = 0.25                      # positive extreme: d = -0.03125, exact in FP16
+    w[7, 40] = -0.5                     # negative extreme: d = 0.0625
+    blocks, _ = pack.pack_q4_0(w)
+    codes, d = layouts.q4_0_split(blocks)
+    b = w.reshape(-1, 32).astype(np.float64)
+    first = np.argmax(np.abs(b), axis=1)
+    assert np.all(codes.reshape(-1, 32)[np.arange(b.shape[0]), first] == 0)
+    w64 = ref.dequant("q4_0", (blocks, np.float32(1)))
+    assert w64[3, 5] == 0.25 and w64[7, 40] == -0.5
+
+
+def test_q4_0_codes_are_nearest_level_bruteforce():
+    # every code is the level nearest w / d (exact rationals), a tie taking the larger level
+    rng = np.random.default_rng(22)
+    w = (rng.standard_t(4, (6, 64)) * 0.05).astype(np.float32)
+    w[0, 1] = w[0, 0] * np.float32(-0.0625)   # exactly half a step: w / d = 0.5
+    blocks, _ = pack.pack_q4_0(w)
+    codes, _ = layouts.q4_0_split(blocks)
+    bw = w.reshape(-1, 32)
+    bc = codes.reshape(-1, 32)
+    for r in range(bw.shape[0]):
+        a = [Fraction(float(v)) for v in bw[r]]
+        m = max(a, key=abs)
+        m = next(v for v in a if abs(v) == abs(m))          # first of the largest magnitude
+        d = m / -8
+        for v, c in zip(a, bc[r]):
+            if d == 0:
+                assert c == 8
+                continue
+            best = min(range(16), key=lambda q: (abs(v - (q - 8) * d), -q))
+            assert c == best, (r, v, c, best)
+
+
+def test_q4_0_zero_block():
+    blocks, _ = pack.pack_q4_0(np.zeros((2, 32), np.float32))
+    codes, d = layouts.q4_0_split(blocks)
+    assert np.all(codes == 8) and np.all(d == 0)

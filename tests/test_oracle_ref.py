@@ -38,6 +38,14 @@ def test_dequant_nvfp4_hand_packed():
     assert np.array_equal(np.signbit(w[0]), np.signbit(np.array(want)))
 
 
+def test_dequant_q4_0_hand_packed():
+    g = _hand()
+    qs = golden_io.hex_bytes(g["qs"])
+    block = np.array(golden_io.hex_bytes(g["q4_0_scale_bytes"]) + qs, dtype=np.uint8).reshape(1, 1, 18)
+    w = ref.dequant("q4_0", (block, np.float32(1)))
+    assert w.tolist() == [golden_io.floats(g["q4_0_values"])]
+
+
 def test_dequant_f32_is_single_rounding_of_exact_product():
     # e2m1 * e4m3 has <= 6 significant bits, so fl32(fl32(level*scale)*g) is the RN of the exact value,
     # while fl32(level*fl32(scale*g)) is not in general. The oracle rounds the exact product once.
