@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 COLD_BYTES = 1 << 30            # 4x the 256 MB last-level cache
-BLOCK_BYTES = {"rocmfp4_dual": 18, "rocmfp4_fast": 17}
+BLOCK_BYTES = {"rocmfp4_dual": 18, "rocmfp4_fast": 17, "q4_0": 18}
 
 WORKLOADS = {
     # name: (synth cfg, matrix index, fmt, M)
@@ -45,8 +45,11 @@ WORKLOADS = {
     "rocmfp4_dual_down_2560x9728_m1": (3, 1, "rocmfp4_dual", 1),
     "rocmfp4_fast_down_2560x9728_m1": (3, 1, "rocmfp4_fast", 1),
 }
+WORKLOADS["q4_0_4096x4096_m1"] = (1, 0, "q4_0", 1)          # the Dual matrix in stock Q4_0 (same bytes)
+WORKLOADS["q4_0_gate_9728x2560_m1"] = (3, 0, "q4_0", 1)
+WORKLOADS["q4_0_down_2560x9728_m1"] = (3, 1, "q4_0", 1)
 for _m in (9, 16):
-    for _f in ("nvfp4", "rocmfp4_dual", "rocmfp4_fast"):
+    for _f in ("nvfp4", "rocmfp4_dual", "rocmfp4_fast", "q4_0"):
         WORKLOADS[f"{_f}_gate_9728x2560_m{_m}"] = (3, 0, _f, _m)
         WORKLOADS[f"{_f}_down_2560x9728_m{_m}"] = (3, 1, _f, _m)
 

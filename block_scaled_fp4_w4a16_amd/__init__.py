@@ -17,8 +17,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4w4a16.so")
 
-FORMATS = {"nvfp4": 1, "rocmfp4_dual": 2, "rocmfp4_fast": 3}
-BLOCK_BYTES = {"rocmfp4_dual": 18, "rocmfp4_fast": 17}
+FORMATS = {"nvfp4": 1, "rocmfp4_dual": 2, "rocmfp4_fast": 3, "q4_0": 4}
+BLOCK_BYTES = {"rocmfp4_dual": 18, "rocmfp4_fast": 17, "q4_0": 18}
 GEMV_MAX_M = 16
 
 _c = ctypes.c_int
@@ -49,6 +49,7 @@ _SIGS = {
     "fp4_dequant_f32": (_c, [_c, _i64, _i64, _p, _p, _f, _p, _p]),
     "fp4_quantize_nvfp4": (_c, [_i64, _i64, _p, _p, _p, _p, _p]),
     "fp4_quantize_rocmfp4": (_c, [_c, _i64, _i64, _p, _p, _p, _p]),
+    "fp4_quantize_q4_0": (_c, [_i64, _i64, _p, _p, _p]),
 }
 
 _lib = None
@@ -190,6 +191,14 @@ def fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream=None):
            "fp4_quantize_rocmfp4")
 
 
+def fp4_quantize_q4_0(N, K, w, blocks, stream=None):
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
+    if w.numel() < N * K or blocks.numel() < N * (K // 32) * 18:
+        raise ValueError("buffer too small")
+    _check(lib().fp4_quantize_q4_0(N, K, _ptr(w), _ptr(blocks), _stream(stream)), "fp4_quantize_q4_0")
+
+
 # ----------------------------------------------------------------------------------------------
 # Convenience: a packed weight in kernel layout (allocation through torch, compute in the library)
 # ----------------------------------------------------------------------------------------------
@@ -229,7 +238,12 @@ class PackedWeight:
             gs = float(g.item())
             return PackedWeight.from_canonical(fmt, N, K, wq, ws, gs, stream)
         blocks = torch.empty(N * (K // 32) * BLOCK_BYTES[fmt], dtype=torch.uint8, device=w.device)
-        fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream)
+        if fmt == "q4_0":
+            if importance is not None:
+                raise ValueError("the Q4_0 packer takes no importance")
+            fp4_quantize_q4_0(N, K, w, blocks, stream)
+        else:
+            fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream)
         return PackedWeight.from_canonical(fmt, N, K, blocks, None, 1.0, stream)
 
     def matmul(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

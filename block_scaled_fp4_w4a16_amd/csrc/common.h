@@ -5,30 +5,36 @@
 
 namespace fp4 {
 
-enum Fmt { NVFP4 = 1, DUAL = 2, FAST = 3 };
+enum Fmt { NVFP4 = 1, DUAL = 2, FAST = 3, Q4_0 = 4 };
 
 // Kernel layout. A "unit" is one 16-row tile x one 128-wide K chunk.
 //   nibble plane: [tile][chunk][g = 0..3][n = 0..15][16 bytes]  -> 1024 B per unit
 //   scale plane:  [tile][chunk][n = 0..15][spr bytes]           -> 16*spr B per unit
+//                 (spr = 8 scale bytes for NVFP4 / Dual, 4 for FAST, 4 little-endian FP16 for Q4_0)
 // Lane l = 16 g + n of a wave reads 16 bytes at offset 16 l of a unit: row n, the 32
 // positions k' = 32 g + i (i = 0..31) of the chunk, permuted so that one MFMA covers
 // exactly one scale group per row:
 //   16-weight groups (NVFP4, Dual), MFMA 16x16x16: i = 4 j + t  <->  k = 16 j + 4 g + t
-//   32-weight blocks (FAST),        MFMA 16x16x32: i = 8 j + t  <->  k = 32 j + 8 g + t
+//   32-weight blocks (FAST, Q4_0),  MFMA 16x16x32: i = 8 j + t  <->  k = 32 j + 8 g + t
 // Within the 16 bytes the nibble of position i sits where the decoder wants it:
 //   NVFP4 (hardware E2M1 pair convert): byte i/2, low nibble when i is even;
-//   Codebook10 (byte LUT + FP8 pair convert): dword i/8, byte (i%8)%4, high nibble iff i%8 >= 4.
+//   Codebook10 (byte LUT + FP8 pair convert) and Q4_0 (byte permute into bf16 mantissas):
+//   dword i/8, byte (i%8)%4, high nibble iff i%8 >= 4.
 constexpr int TILE_N = 16;
 constexpr int CHUNK_K = 128;
 constexpr int UNIT_Q = 1024;
 
-__host__ __device__ constexpr int group_size(int f) { return f == FAST ? 32 : 16; }
+// 32-weight blocks (FAST, Q4_0) or 16-weight groups (NVFP4, Dual) share one scale
+__host__ __device__ constexpr bool block32(int f) { return f == FAST || f == Q4_0; }
+__host__ __device__ constexpr int group_size(int f) { return block32(f) ? 32 : 16; }
 __host__ __device__ constexpr int scales_per_row_chunk(int f) { return CHUNK_K / group_size(f); }
-__host__ __device__ constexpr int unit_s(int f) { return TILE_N * scales_per_row_chunk(f); }
+// scale bytes per row and chunk: one byte per scale, two for Q4_0's FP16 scales
+__host__ __device__ constexpr int scale_bytes_row_chunk(int f) { return scales_per_row_chunk(f) * (f == Q4_0 ? 2 : 1); }
+__host__ __device__ constexpr int unit_s(int f) { return TILE_N * scale_bytes_row_chunk(f); }
 
 // chunk-relative k of lane-group g, lane position i
 __host__ __device__ constexpr int kmap(int f, int g, int i) {
-  return f == FAST ? 32 * (i >> 3) + 8 * g + (i & 7) : 16 * (i >> 2) + 4 * g + (i & 3);
+  return block32(f) ? 32 * (i >> 3) + 8 * g + (i & 7) : 16 * (i >> 2) + 4 * g + (i & 3);
 }
 // (byte, high-nibble?) of lane position i inside the 16-byte lane piece
 __host__ __device__ constexpr int nib_byte(int f, int i) { return f == NVFP4 ? (i >> 1) : 4 * (i >> 3) + (i & 3); }

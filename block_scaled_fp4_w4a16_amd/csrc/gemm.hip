@@ -324,6 +324,7 @@ extern "C" int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
                           float global_scale, const void* x_bf16, float* y, void* stream) {
   if (!fp4_valid_format(fmt)) return -1;
   if (M < 0) return -2;
+  if (fmt == Q4_0) return -4;  // its FP16-scaled weights are not exact in bf16; Q4_0 runs through the GEMV
   int rc = fp4_check_nk(fmt, N, K);
   if (rc) return rc;
   if (M == 0) return 0;

@@ -86,7 +86,7 @@ __device__ __forceinline__ void unit_mac(f32x4& acc, const WeightRegs<F>& w, con
       fold<RU>(acc, p0, sc0);
       fold<RU>(acc, p1, sc1);
     }
-  } else {
+  } else if constexpr (F == FAST) {
     const bf16x8* xf = reinterpret_cast<const bf16x8*>(xa);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -103,6 +103,31 @@ __device__ __forceinline__ void unit_mac(f32x4& acc, const WeightRegs<F>& w, con
         default: sc = e4m3_to_f32<3>(w.s[0]); break;
       }
       fold<RU>(acc, p, sc);
+    }
+  } else {
+    // Q4_0, level q - 8: B holds the bf16 numbers 128 + q, built by placing each nibble in the low
+    // mantissa bits of bf16 128 (exact), and the MFMA starts from C = -136 * (x . 1) of the block
+    // (one more MFMA against a constant -136), so that it returns sum (q - 8) x in FP32.
+    const bf16x8* xf = reinterpret_cast<const bf16x8*>(xa);
+    const u32x4 m136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+    const bf16x8 neg136 = __builtin_bit_cast(bf16x8, m136);
+    // bf16 128 in both halves, kept in a VGPR so that mask-and-insert is one v_and_or_b32 (a VOP3
+    // instruction can take one scalar operand, here the mask, but no literal)
+    uint32_t magic = 0x43004300u;
+    asm volatile("" : "+v"(magic));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[d], neg136, zero, 0, 0, 0);
+      const uint32_t wq = w.q[d];
+      // positions 8d..8d+3 are the low nibbles of bytes 0..3, 8d+4..8d+7 the high nibbles
+      const uint32_t p01 = __builtin_amdgcn_perm(0u, wq, 0x0C010C00u);  // bytes 0, 1 -> halves 0, 1
+      const uint32_t p23 = __builtin_amdgcn_perm(0u, wq, 0x0C030C02u);  // bytes 2, 3 -> halves 0, 1
+      const u32x4 bw = {(p01 & 0x000F000Fu) | magic, (p23 & 0x000F000Fu) | magic,
+                        ((p01 >> 4) & 0x000F000Fu) | magic, ((p23 >> 4) & 0x000F000Fu) | magic};
+      const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[d], __builtin_bit_cast(bf16x8, bw), c0, 0, 0, 0);
+      // the block's FP16 scale: half-word d % 2 of scale dword d / 2
+      const uint16_t hb = (uint16_t)(w.s[d >> 1] >> (16 * (d & 1)));
+      fold<RU>(acc, p, (float)__builtin_bit_cast(_Float16, hb));
     }
   }
 }
@@ -148,9 +173,9 @@ __device__ __forceinline__ void stage_x_commit(uint8_t* xs, const XStage<U, MX>&
     const int p = 64 * i + lane;
     if (p < pieces) {
       const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
-      const int dst = (u * 4 * M + m) * 64 + ((F == FAST) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
+      const int dst = (u * 4 * M + m) * 64 + (block32(F) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
                                                            : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
-      if constexpr (F == FAST) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
+      if constexpr (block32(F)) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
         *reinterpret_cast<u32x4*>(xs + dst) = st.v[i];
       } else {                          // k = 16 j + 4 g + t: halves go to lane groups 2 (qq & 1) and +1
         *reinterpret_cast<u32x2*>(xs + dst) = u32x2{st.v[i][0], st.v[i][1]};
@@ -178,9 +203,9 @@ __device__ __forceinline__ void stage_x_now(uint8_t* xs, const Srcs& src, int M,
       const int p = p0 + 64 * i + lane;
       if (p >= pieces) continue;
       const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
-      const int dst = (u * 4 * M + m) * 64 + ((F == FAST) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
+      const int dst = (u * 4 * M + m) * 64 + (block32(F) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
                                                            : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
-      if constexpr (F == FAST) {
+      if constexpr (block32(F)) {
         *reinterpret_cast<u32x4*>(xs + dst) = v[i];
       } else {
         *reinterpret_cast<u32x2*>(xs + dst) = u32x2{v[i][0], v[i][1]};
@@ -497,7 +522,8 @@ static void dispatch_fmt(int fmt, GemvBatch<MAXI>& b, int M, hipStream_t st) {
   switch (fmt) {
     case NVFP4: dispatch_gemv<NVFP4>(b, M, st); break;
     case DUAL:  dispatch_gemv<DUAL>(b, M, st); break;
-    default:    dispatch_gemv<FAST>(b, M, st); break;
+    case FAST:  dispatch_gemv<FAST>(b, M, st); break;
+    default:    dispatch_gemv<Q4_0>(b, M, st); break;
   }
 }
 
@@ -598,6 +624,7 @@ extern "C" int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   if (!fp4_valid_format(fmt)) return -1;
   if (M < 0) return -2;
   if (M > 64) return -4;
+  if (fmt == Q4_0) return -4;  // its FP16-scaled weights are not exact in bf16; Q4_0 runs through the GEMV
   int rc = fp4_check_nk(fmt, N, K);
   if (rc) return rc;
   if (K > (1 << 24)) return -4;
@@ -611,7 +638,7 @@ extern "C" int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   switch (fmt) {
     case NVFP4: dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
     case DUAL:  dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
-    default:    dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+    default:    dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;  // FAST
   }
   return fp4_launch_status();
 }

@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-static inline bool fp4_valid_format(int f) { return f == 1 || f == 2 || f == 3; }
+static inline bool fp4_valid_format(int f) { return f >= 1 && f <= 4; }
 
 static inline bool fp4_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 

@@ -32,7 +32,8 @@ __global__ void pack_layout_kernel(int N, int K, int nchunk, int64_t npieces,
         uint8_t b = src_q[row * (K / 2) + k / 2];
         code = (k & 1) ? (b >> 4) : (b & 15);
       } else {
-        const int bb = (F == DUAL) ? 18 : 17, ns = (F == DUAL) ? 2 : 1;
+        // the nibble bytes follow the block's scale field: 2 bytes (Dual, Q4_0) or 1 (FAST)
+        const int bb = (F == FAST) ? 17 : 18, ns = (F == FAST) ? 1 : 2;
         const int blk = k >> 5, j = k & 31;
         uint8_t b = src_q[(row * (K / 32) + blk) * bb + ns + (j & 15)];
         code = (j >= 16) ? (b >> 4) : (b & 15);
@@ -46,29 +47,33 @@ __global__ void pack_layout_kernel(int N, int K, int nchunk, int64_t npieces,
 
   // lane group 0 writes this row's scale bytes for the chunk
   if (g == 0) {
-    constexpr int spr = scales_per_row_chunk(F);
+    constexpr int sbytes = scale_bytes_row_chunk(F);
     uint8_t sb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < spr; ++j) {
+    for (int j = 0; j < scales_per_row_chunk(F); ++j) {
       const int k0 = chunk * CHUNK_K + j * group_size(F);
       if (row_ok && k0 < K) {
         if (F == NVFP4) {
           sb[j] = src_s[row * (K / 16) + k0 / 16];
         } else if (F == DUAL) {
           sb[j] = src_q[(row * (K / 32) + (k0 >> 5)) * 18 + ((k0 >> 4) & 1)] & 0x7F;
-        } else {
+        } else if (F == FAST) {
           sb[j] = src_q[(row * (K / 32) + (k0 >> 5)) * 17] & 0x7F;
+        } else {  // Q4_0: the FP16 scale, little-endian
+          sb[2 * j] = src_q[(row * (K / 32) + (k0 >> 5)) * 18];
+          sb[2 * j + 1] = src_q[(row * (K / 32) + (k0 >> 5)) * 18 + 1];
         }
       }
     }
-    uint8_t* d = dst_s + unit * unit_s(F) + n * spr;
+    uint8_t* d = dst_s + unit * unit_s(F) + n * sbytes;
 #pragma unroll
-    for (int j = 0; j < spr; ++j) d[j] = sb[j];
+    for (int j = 0; j < sbytes; ++j) d[j] = sb[j];
   }
 }
 
 template <int F>
 __device__ __forceinline__ float level_of(uint32_t code) {
+  if (F == Q4_0) return (float)((int)code - 8);
   const uint32_t m = code & 7;
   float mag;
   if (F == NVFP4)  // E2M1: 0, .5, 1, 1.5, then 2, 3, 4, 6 = 2^((m>>1)-1) * (1 or 1.5)
@@ -94,8 +99,7 @@ __global__ void dequant_kernel(int N, int K, int nchunk, int64_t npieces, const 
   const u32x4 qv = *reinterpret_cast<const u32x4*>(q + p * 16);
   uint8_t qb[16];
   __builtin_memcpy(qb, &qv, 16);
-  constexpr int spr = scales_per_row_chunk(F);
-  const uint8_t* srow = s + unit * unit_s(F) + n * spr;
+  const uint8_t* srow = s + unit * unit_s(F) + n * scale_bytes_row_chunk(F);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int kk = kmap(F, g, i);
@@ -103,9 +107,15 @@ __global__ void dequant_kernel(int N, int K, int nchunk, int64_t npieces, const 
     if (k >= K) continue;
     const uint32_t code = (qb[nib_byte(F, i)] >> (4 * nib_high(F, i))) & 15u;
     const float level = level_of<F>(code);
-    const uint32_t sbyte = srow[kk / group_size(F)];
-    const float sc = __builtin_amdgcn_cvt_f32_fp8(sbyte, 0);
-    const float prod = level * sc;  // exact: at most 3 + 4 significant bits
+    const int j = kk / group_size(F);
+    float sc;
+    if (F == Q4_0) {
+      const uint16_t hb = (uint16_t)(srow[2 * j] | (srow[2 * j + 1] << 8));
+      sc = (float)__builtin_bit_cast(_Float16, hb);
+    } else {
+      sc = __builtin_amdgcn_cvt_f32_fp8(srow[j], 0);
+    }
+    const float prod = level * sc;  // exact: at most 3 + 4 (or, for Q4_0, 4 + 11) significant bits
     w[row * (int64_t)K + k] = prod * gscale;
   }
 }
@@ -146,7 +156,8 @@ extern "C" int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q,
   switch (fmt) {
     case NVFP4: hipLaunchKernelGGL(pack_layout_kernel<NVFP4>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
     case DUAL:  hipLaunchKernelGGL(pack_layout_kernel<DUAL>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
-    default:    hipLaunchKernelGGL(pack_layout_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
+    case FAST:  hipLaunchKernelGGL(pack_layout_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
+    default:    hipLaunchKernelGGL(pack_layout_kernel<Q4_0>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
   }
   return fp4_launch_status();
 }
@@ -169,7 +180,8 @@ extern "C" int fp4_dequant_f32(int fmt, int64_t N, int64_t K, const void* q, con
   switch (fmt) {
     case NVFP4: hipLaunchKernelGGL(dequant_kernel<NVFP4>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
     case DUAL:  hipLaunchKernelGGL(dequant_kernel<DUAL>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
-    default:    hipLaunchKernelGGL(dequant_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
+    case FAST:  hipLaunchKernelGGL(dequant_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
+    default:    hipLaunchKernelGGL(dequant_kernel<Q4_0>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
   }
   return fp4_launch_status();
 }

@@ -10,6 +10,10 @@
 // index order, then a wave reduction keeps the smallest error, breaking ties by distance to the
 // start code (E4M3 RNE of max|w| / 10) and then by the lower code.
 //
+// Q4_0, signed abs-max (ROCmFP4 design page, comparison table, stock Q4_0 reference scale): one thread
+// per 32-weight block; m = the first weight of largest magnitude, d = m / -8 (exact), stored as FP16
+// (RNE); each code is floor(w / d + 8.5) clipped to 0..15, computed in FP64 with the unrounded d.
+//
 // Every FP64 operation here is a separately rounded IEEE operation: contraction into fused
 // multiply-adds is switched off for this file, so the chosen codes do not depend on it.
 #include "common.h"
@@ -208,6 +212,36 @@ __global__ __launch_bounds__(256) void rocm_pack_kernel(const float* __restrict_
   }
 }
 
+__global__ void q4_0_pack_kernel(const float* __restrict__ w, int64_t nblocks, uint8_t* __restrict__ out) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const float* wb = w + b * 32;
+  float m = 0.f, am = 0.f;
+  for (int i = 0; i < 32; ++i) {       // first weight of the largest magnitude, sign kept
+    const float a = fabsf(wb[i]);
+    if (a > am) {
+      am = a;
+      m = wb[i];
+    }
+  }
+  const float d = m * -0.125f + 0.0f;  // m / -8, exact; an all-zero block gives +0
+  const _Float16 d16 = (_Float16)d;    // round to nearest even
+  const uint16_t hb = __builtin_bit_cast(uint16_t, d16);
+  uint8_t* ob = out + b * 18;
+  ob[0] = (uint8_t)(hb & 0xFF);
+  ob[1] = (uint8_t)(hb >> 8);
+  uint8_t q[32];
+  for (int i = 0; i < 32; ++i) {
+    int c = 8;
+    if (d != 0.f) {
+      const double t = floor((double)wb[i] / (double)d + 8.5);
+      c = t < 0.0 ? 0 : t > 15.0 ? 15 : (int)t;
+    }
+    q[i] = (uint8_t)c;
+  }
+  for (int j = 0; j < 16; ++j) ob[2 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
+}
+
 }  // namespace fp4
 
 using namespace fp4;
@@ -246,5 +280,18 @@ extern "C" int fp4_quantize_rocmfp4(int fmt, int64_t N, int64_t K, const float* 
   else
     hipLaunchKernelGGL(rocm_pack_kernel<FAST>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
                        (uint8_t*)blocks);
+  return fp4_launch_status();
+}
+
+extern "C" int fp4_quantize_q4_0(int64_t N, int64_t K, const float* w, void* blocks, void* stream) {
+  if (!w || !blocks) return -1;
+  int rc = fp4_check_nk(Q4_0, N, K);
+  if (rc) return rc;
+  if (!fp4_aligned(w, 16)) return -3;
+  const int64_t nblocks = N * K / 32;
+  const int64_t grid = (nblocks + 255) / 256;
+  if (grid > 0x7fffffffLL) return -4;
+  hipLaunchKernelGGL(q4_0_pack_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w, nblocks,
+                     (uint8_t*)blocks);
   return fp4_launch_status();
 }

@@ -10,9 +10,10 @@
  *   NVFP4:          W[n][k] = e2m1(q) * e4m3(s[n][k/16]) * g
  *   ROCmFP4 Dual:   W[n][k] = codebook10(q) * ue4m3(s_half) * g   (one scale per 16)
  *   ROCmFP4 FAST:   W[n][k] = codebook10(q) * ue4m3(s_block) * g  (one scale per 32)
+ *   Q4_0:           W[n][k] = (q - 8) * fp16(d_block) * g            (one scale per 32)
  *
  * with e2m1 in {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}, codebook10 in {0, +-1, +-2,
- * +-3, +-4, +-6, +-8, +-10}, g the per-matrix FP32 global scale (1.0 for ROCmFP4).
+ * +-3, +-4, +-6, +-8, +-10}, g the per-matrix FP32 global scale (1.0 for ROCmFP4 and Q4_0).
  * The library computes level*scale exactly, applies g last (fl32(fl32(level*scale)*g)),
  * and accumulates in FP32.
  *
@@ -45,7 +46,8 @@ extern "C" {
 enum {
   FP4_NVFP4 = 1,        /* E2M1 nibbles, E4M3 scale per 16, FP32 global scale      */
   FP4_ROCMFP4_DUAL = 2, /* Codebook10 nibbles, two UE4M3 half-block scales, 18 B/32 */
-  FP4_ROCMFP4_FAST = 3  /* Codebook10 nibbles, one UE4M3 block scale, 17 B/32        */
+  FP4_ROCMFP4_FAST = 3, /* Codebook10 nibbles, one UE4M3 block scale, 17 B/32        */
+  FP4_Q4_0 = 4          /* stock Q4_0: levels q - 8, one FP16 block scale, 18 B/32   */
 };
 
 /* Status codes. */
@@ -73,13 +75,15 @@ const char* fp4_status_string(int status);
 int fp4_layout_bytes(int fmt, int64_t N, int64_t K, size_t* q_bytes, size_t* s_bytes);
 
 /*
- * Repack canonical packed weights into the kernel layout (load time; row a1 of the path).
+ * Repack canonical packed weights into the kernel layout (load time, once per matrix).
  * Canonical input (device memory):
  *   NVFP4:    src_q = wq uint8[N][K/2], byte j holds element 2j (bits 0-3) and 2j+1
  *             (bits 4-7); src_s = ws uint8[N][K/16] E4M3 scales.
  *   ROCmFP4:  src_q = blocks uint8[N][K/32][B] with B = 18 (Dual: s_lo, s_hi, qs[16]) or
  *             17 (FAST: s, qs[16]); qs[j] holds weight j (bits 0-3) and j+16 (bits 4-7);
  *             src_s must be NULL. UE4M3 bit 7 is ignored.
+ *   Q4_0:     src_q = blocks uint8[N][K/32][18] = [FP16 d, little-endian; qs[16]] with the
+ *             same qs order; src_s must be NULL.
  * Output: dst_q / dst_s of the sizes fp4_layout_bytes reports (16-byte aligned). The
  * layout's internal order is private to this library and may change with the ABI version.
  */
@@ -87,7 +91,7 @@ int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q, const void
                     void* dst_q, void* dst_s, void* stream);
 
 /*
- * Decode-shaped product, 1 <= M <= 16 (rows a2-a6): streams each nibble and scale byte
+ * Decode-shaped product, 1 <= M <= 16: streams each nibble and scale byte
  * once, decodes to exact bf16 levels, contracts against x on the matrix cores, applies
  * the group scales to the FP32 partial sums, reduces the K split inside the workgroup and
  * multiplies by g. q/s are fp4_pack_layout output. Deterministic (no atomics).
@@ -96,8 +100,8 @@ int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const vo
                float global_scale, const void* x_bf16, float* y, void* stream);
 
 /*
- * Several decode-shaped products in one launch (next-step row f1: the per-launch cost dominates
- * decode matrices of a few MB, Nanbeige4.2-3B-NVFP4A16 card, speed notes). Each item is one
+ * Several decode-shaped products in one launch (the per-launch cost dominates decode matrices
+ * of a few MB, whose weight bytes set the decode speed: Nanbeige4.2-3B-NVFP4A16 card, speed notes). Each item is one
  * matrix with its own planes, x, y, N, K and global scale; all share fmt and M (1 <= M <= 16).
  * Typical use: the q|k|v or gate|up projections of one token, which read the same x, or any
  * list of independent products. Each y equals what w4a16_gemv would produce to within the
@@ -120,7 +124,7 @@ typedef struct fp4_gemv_item {
 int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items, void* stream);
 
 /*
- * Prefill-shaped product, any M >= 1, intended for M >= 64 (rows a7-a10): stages x tiles
+ * Prefill-shaped product, any M >= 1, intended for M >= 64: stages x tiles
  * and packed weight tiles, dequantizes each weight tile once into LDS as exact bf16
  * level*scale, contracts with bf16 MFMA in FP32 and multiplies by g in the epilogue.
  */
@@ -128,7 +132,7 @@ int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const vo
                float global_scale, const void* x_bf16, float* y, void* stream);
 
 /*
- * Mid-sized M, 1 <= M <= 64 (next-step row f4; the band between the decode and prefill shapes,
+ * Mid-sized M, 1 <= M <= 64 (the band between the decode and prefill shapes,
  * e.g. speculative-decoding verification of many drafts or small batches, Nanbeige4.2-3B-NVFP4A16
  * card, serving notes): the GEMV's layout and in-workgroup K split, with each weight decoded once
  * into exact bf16 level*scale and reused by up to four 16-row blocks of x on the matrix cores.
@@ -137,7 +141,7 @@ int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const vo
 int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);
 
-/* Dispatch on M (row a11): M <= 16 -> w4a16_gemv, 17 <= M <= 64 -> w4a16_midm, otherwise
+/* Dispatch on M: M <= 16 -> w4a16_gemv, 17 <= M <= 64 -> w4a16_midm, otherwise
  * w4a16_gemm. */
 int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                  float global_scale, const void* x_bf16, float* y, void* stream);
@@ -171,6 +175,18 @@ int fp4_quantize_nvfp4(int64_t N, int64_t K, const float* w, void* wq, void* ws,
  */
 int fp4_quantize_rocmfp4(int fmt, int64_t N, int64_t K, const float* w, const float* importance,
                          void* blocks, void* stream);
+
+/*
+ * Device packer, stock Q4_0 with the signed abs-max scale (ROCmFP4 design page, format
+ * comparison table, stock Q4_0 column): w fp32[N][K] -> canonical Q4_0 blocks
+ * uint8[N][K/32][18] = [FP16 d (little-endian), qs[16]], qs[j] = code j | code j+16 << 4.
+ * Per block m = the first weight of largest magnitude, d = m / -8, stored as FP16 (RNE);
+ * code = floor(w / d + 8.5) clipped to 0..15 in FP64 with the unrounded d; d = 0 gives
+ * code 8. Q4_0 runs through w4a16_gemv, w4a16_gemv_batched and fp4_dequant_f32; the
+ * matrix-core paths (w4a16_midm, w4a16_gemm) return FP4_ERR_UNSUPPORTED for it because its
+ * level*scale products are not exact in bf16.
+ */
+int fp4_quantize_q4_0(int64_t N, int64_t K, const float* w, void* blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,8 @@ import torch
 import synth
 from oracle import pack, ref
 
-FMTS = ("nvfp4", "rocmfp4_dual", "rocmfp4_fast")
+FMTS = ("nvfp4", "rocmfp4_dual", "rocmfp4_fast")   # every path, matrix-core GEMM and mid-M included
+FMTS_ALL = FMTS + ("q4_0",)                          # the GEMV family and the dequantizer
 
 
 def canonical_tensors(fmt, packed, device="cuda"):

@@ -13,7 +13,7 @@ fp4 = pytest.importorskip("block_scaled_fp4_w4a16_amd")
 
 OK, ARG, SHAPE, ALIGN, UNSUP = 0, -1, -2, -3, -4
 FAKE = 1 << 20   # a 16-byte-aligned non-null address; never dereferenced by these calls
-NVFP4, DUAL, FAST = 1, 2, 3
+NVFP4, DUAL, FAST, Q4_0 = 1, 2, 3, 4
 
 
 def declared_functions():
@@ -41,6 +41,7 @@ def test_layout_bytes():
     assert fp4.fp4_layout_bytes("nvfp4", 2048, 2048) == (2048 * 2048 // 2, 2048 * 2048 // 16)
     assert fp4.fp4_layout_bytes("rocmfp4_dual", 4096, 4096) == (4096 * 4096 // 2, 4096 * 4096 // 16)
     assert fp4.fp4_layout_bytes("rocmfp4_fast", 14336, 4096) == (14336 * 4096 // 2, 14336 * 4096 // 32)
+    assert fp4.fp4_layout_bytes("q4_0", 4096, 4096) == (4096 * 4096 // 2, 4096 * 4096 // 16)  # FP16 per 32
     # ragged: N = 17 -> 2 tiles, K = 160 -> 2 chunks
     assert fp4.fp4_layout_bytes("rocmfp4_dual", 17, 160) == (2 * 2 * 1024, 2 * 2 * 128)
     with pytest.raises(RuntimeError):
@@ -52,7 +53,7 @@ def test_layout_bytes():
 def test_layout_bytes_matches_weight_bytes_for_aligned_shapes():
     # the kernel layout stores exactly the canonical weight + scale bytes when N % 16 == K % 128 == 0
     from oracle import layouts
-    for fmt in ("nvfp4", "rocmfp4_dual", "rocmfp4_fast"):
+    for fmt in ("nvfp4", "rocmfp4_dual", "rocmfp4_fast", "q4_0"):
         q, s = fp4.fp4_layout_bytes(fmt, 256, 1024)
         assert q + s == layouts.canonical_bytes(fmt, 256, 1024)
 
@@ -72,6 +73,11 @@ def test_product_argument_errors(fn):
 
     assert call(fmt=7) == ARG
     assert call(fmt=0) == ARG
+    assert call(fmt=5) == ARG
+    if fn in ("w4a16_midm", "w4a16_gemm"):
+        assert call(fmt=Q4_0) == UNSUP          # Q4_0 runs through the GEMV only
+    else:
+        assert call(fmt=Q4_0, K=48) == SHAPE   # Q4_0 needs K % 32 == 0
     assert call(q=None) == ARG
     assert call(s=None) == ARG
     assert call(x=None) == ARG
@@ -94,6 +100,7 @@ def test_product_argument_errors(fn):
 
 def test_pack_layout_argument_errors():
     f = _raw().fp4_pack_layout
+    assert f(Q4_0, 16, 64, FAKE, FAKE, FAKE, FAKE, None) == ARG       # Q4_0 carries scales in blocks
     assert f(NVFP4, 16, 64, FAKE, None, FAKE, FAKE, None) == ARG      # NVFP4 needs the scale plane
     assert f(DUAL, 16, 64, FAKE, FAKE, FAKE, FAKE, None) == ARG       # ROCmFP4 carries scales in blocks
     assert f(FAST, 16, 48, FAKE, None, FAKE, FAKE, None) == SHAPE
@@ -110,6 +117,11 @@ def test_dequant_and_quantize_argument_errors():
     assert r.fp4_quantize_rocmfp4(NVFP4, 16, 64, FAKE, None, FAKE, None) == ARG
     assert r.fp4_quantize_rocmfp4(DUAL, 16, 48, FAKE, None, FAKE, None) == SHAPE
     assert r.fp4_quantize_rocmfp4(FAST, 16, 64, FAKE + 4, None, FAKE, None) == ALIGN
+    assert r.fp4_quantize_rocmfp4(Q4_0, 16, 64, FAKE, None, FAKE, None) == ARG
+    assert r.fp4_quantize_q4_0(16, 48, FAKE, FAKE, None) == SHAPE
+    assert r.fp4_quantize_q4_0(16, 64, None, FAKE, None) == ARG
+    assert r.fp4_quantize_q4_0(16, 64, FAKE + 4, FAKE, None) == ALIGN
+    assert r.fp4_dequant_f32(Q4_0, 16, 48, FAKE, FAKE, 1.0, FAKE, None) == SHAPE
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -28,7 +28,7 @@ def _announce(*a):
 
 # ------------------------------------------------------------------ dequant (bit-exact)
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 @pytest.mark.parametrize("n,k", [(16, 128), (37, 160), (64, 1024), (5, 32 * 7)])
 def test_dequant_bit_exact(fmt, n, k):
     if fmt == "nvfp4" and k % 16:
@@ -42,7 +42,7 @@ def test_dequant_bit_exact(fmt, n, k):
     assert np.array_equal(got, want)  # == treats +0 and -0 as equal
 
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 def test_dequant_all_codes_and_scales(fmt):
     # every nibble code against every finite scale byte (and NaN scales for NVFP4)
     _announce("dequant-all-codes", fmt)
@@ -52,6 +52,14 @@ def test_dequant_all_codes_and_scales(fmt):
         wq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
         ws = (np.arange(n * k // 16) % 256).astype(np.uint8).reshape(n, k // 16)
         packed = (wq, ws, np.float32(0.37))
+    elif fmt == "q4_0":
+        blocks = rng.integers(0, 256, size=(n, k // 32, 18), dtype=np.uint8)
+        d = np.arange(n * (k // 32), dtype=np.uint32) * 7 % (1 << 16)
+        d = d[((d >> 10) & 31) != 31][: n * (k // 32)]         # finite FP16 scales of both signs
+        d = np.resize(d, n * (k // 32)).astype(np.uint16).reshape(n, k // 32)
+        blocks[:, :, 0] = d & 0xFF
+        blocks[:, :, 1] = d >> 8
+        packed = (blocks, np.float32(1.0))
     else:
         bb = layouts.BLOCK_BYTES[fmt]
         blocks = rng.integers(0, 256, size=(n, k // 32, bb), dtype=np.uint8)
@@ -68,7 +76,7 @@ def test_dequant_all_codes_and_scales(fmt):
 
 # ------------------------------------------------------------------ GEMV (M <= 16)
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16])
 def test_gemv_small_shapes(fmt, m):
     for (n, k) in [(48, 256), (37, 160), (256, 1536)]:
@@ -82,7 +90,7 @@ def test_gemv_small_shapes(fmt, m):
         gc.check_product(fmt, packed, x_bits, y, label=f"gemv {fmt} M={m} {n}x{k}")
 
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 def test_gemv_one_hot_returns_weight_columns_exactly(fmt):
     # x = e_k gives y[:, n] = W32[n, k] exactly (a single product, times g)
     n, k = 64, 256
@@ -127,7 +135,7 @@ def test_gemv_m0_is_noop():
 
 # ------------------------------------------------------------------ batched GEMV
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 @pytest.mark.parametrize("m", [1, 3, 9, 16])
 def test_gemv_batched_matches_oracle(fmt, m):
     # matrices of different N and K (ragged tiles and chunks), two of them sharing one x, with
@@ -274,7 +282,7 @@ def test_matmul_dispatch(m):
 
 # ------------------------------------------------------------------ device packers (byte-exact)
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 @pytest.mark.parametrize("dist,outl", [("t", 0.0), ("t", 0.001), ("normal", 0.0)])
 def test_device_packer_matches_oracle(fmt, dist, outl):
     n, k = 64, 512
@@ -294,7 +302,10 @@ def test_device_packer_matches_oracle(fmt, dist, outl):
     else:
         bb = layouts.BLOCK_BYTES[fmt]
         blocks = torch.empty(n * (k // 32) * bb, dtype=torch.uint8, device="cuda")
-        fp4.fp4_quantize_rocmfp4(fmt, n, k, wt, None, blocks)
+        if fmt == "q4_0":
+            fp4.fp4_quantize_q4_0(n, k, wt, blocks)
+        else:
+            fp4.fp4_quantize_rocmfp4(fmt, n, k, wt, None, blocks)
         torch.cuda.synchronize()
         assert np.array_equal(blocks.cpu().numpy().reshape(n, k // 32, bb), want[0])
 
@@ -321,7 +332,10 @@ def test_device_packer_edge_values():
     w[2, :32] = np.array([0.5, 1.5, 2.5, 3.5, 5, 7, 9] * 4 + [10, 11, 12, 13], np.float32)
     w[3, :32] = 1e-6
     w[4, 16:48] = -3e-3
-    for fmt in gc.FMTS:
+    w[5, :32] = np.array([-2.0, 1.0, 0.125, 0.25, 0.375, 1.75, -1.75] + [0.0] * 25, np.float32)  # Q4_0 halves
+    w[6, :32] = 7.0
+    w[6, 5] = -7.0                                   # equal magnitudes: the first (+7) decides the sign
+    for fmt in gc.FMTS_ALL:
         _announce("quantize-edges", fmt)
         want = pack.pack(fmt, w)
         wt = torch.from_numpy(w).cuda()
@@ -337,7 +351,10 @@ def test_device_packer_edge_values():
         else:
             bb = layouts.BLOCK_BYTES[fmt]
             blocks = torch.empty(n * (k // 32) * bb, dtype=torch.uint8, device="cuda")
-            fp4.fp4_quantize_rocmfp4(fmt, n, k, wt, None, blocks)
+            if fmt == "q4_0":
+                fp4.fp4_quantize_q4_0(n, k, wt, blocks)
+            else:
+                fp4.fp4_quantize_rocmfp4(fmt, n, k, wt, None, blocks)
             torch.cuda.synchronize()
             assert np.array_equal(blocks.cpu().numpy().reshape(n, k // 32, bb), want[0])
     # all-zero matrix: g = 1 and zero codes

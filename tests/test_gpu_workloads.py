@@ -49,9 +49,11 @@ def test_decode_sweep_one_layer():
         _run("nvfp4", 2, mat, 1)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "rocmfp4_dual", "rocmfp4_fast"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "rocmfp4_dual", "rocmfp4_fast", "q4_0"])
 @pytest.mark.parametrize("m", [1, 9, 16, 33, 64])
 def test_spec_verify(fmt, m):
+    if fmt == "q4_0" and m > 16:
+        pytest.skip("Q4_0 runs through the GEMV only (M <= 16)")
     for mat in range(2):
         _run(fmt, 3, mat, m)
 
