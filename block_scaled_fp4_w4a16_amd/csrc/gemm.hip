@@ -36,36 +36,6 @@ __host__ __device__ constexpr int gm_loads_per_stage(int f) { return GM_X_SLOTS 
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// B operand of k-step s for this lane: 8 consecutive positions of the stage's k subset (see the kernel),
-// dequantized to bf16 level * scale. w0 / w1 are this lane's two dwords of lane piece 2hh / 2hh + 1.
-template <int F, int S>
-__device__ __forceinline__ bf16x8 b_operand(const u32x2& w0, const u32x2& w1, float sc) {
-  if constexpr (F == FAST) {
-    // 8 positions = one dword: dword S / 2 of piece S % 2, positions in lane-piece order
-    const uint32_t w = (S & 1) ? w1[S >> 1] : w0[S >> 1];
-    const uint32_t lo = cb10_quad<false>(w), hi = cb10_quad<true>(w);
-    return to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true), sc);
-  } else if constexpr (F == DUAL) {
-    // 4 positions from piece 2hh (k 0..3 of the run) and 4 from piece 2hh + 1 (k 4..7): the low or high
-    // nibbles of dword S / 2 of each piece
-    const uint32_t a = cb10_quad<(S & 1) != 0>(w0[S >> 1]), b = cb10_quad<(S & 1) != 0>(w1[S >> 1]);
-    return to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(a, 1.0f, false),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(a, 1.0f, true),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b, 1.0f, false),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b, 1.0f, true), sc);
-  } else {
-    // NVFP4: 16-bit half S % 2 of dword S / 2 of each piece (4 nibbles each), joined into one dword
-    const uint32_t w = __builtin_amdgcn_perm(w1[S >> 1], w0[S >> 1], (S & 1) ? 0x07060302u : 0x05040100u);
-    return to_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
-                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), sc);
-  }
-}
-
 // This lane's weight bytes for one stage, read back from LDS: for each of the wave's two 32-row column
 // tiles, dwords 2 kh and 2 kh + 1 of the row's two lane pieces, and the row's scale bytes of the chunk.
 struct WRegs {
@@ -132,6 +102,74 @@ __device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h
   }
 }
 
+// Per-lane parts of the direct-load offsets, computed once per tile. Rows and tiles stay in the
+// per-lane (range-checked) offset: x slot i of a lane is 8 rows below slot 0, the second weight and
+// scale parts two tiles further, each one add per load. Only the stage term (chunk, half-chunk), which
+// stays inside a row of x and a tile's row of units, goes into the scalar offset.
+struct LoadOffs {
+  uint32_t x, w, s;
+};
+
+template <int F>
+__device__ __forceinline__ void load_offsets(LoadOffs& o, int K, int nchunk, int wave, int lane) {
+  const int row = wave * 64 + (lane >> 3);              // slot 0 of the lane: row of x in the tile
+  const int sigma = (lane & 7) ^ (row & 7);
+  const int kk = (F == FAST) ? 32 * (sigma >> 1) + 8 * (sigma & 1) : 16 * sigma;   // stage_k without c, hh
+  o.x = (uint32_t)(row * K + kk) * 2u;
+  o.w = (uint32_t)((lane >> 5) * nchunk) * UNIT_Q + (lane & 31) * 16;
+  constexpr int us = unit_s(F), lanes_per_tile = us / 4;
+  o.s = (uint32_t)((lane / lanes_per_tile) * nchunk) * us + (lane % lanes_per_tile) * 4;
+}
+
+// Part P (0, 1, 2) of stage h's direct loads (K a multiple of 128): x slots 3P .. 3P + 2 (the last part
+// has two), then in part 1 the weight pieces and in part 2 the scale bytes. Spreading a stage's loads over
+// three k-steps keeps each burst of vector-memory issue short.
+template <int F, int P>
+__device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
+                                                 int nchunk, int wave) {
+  const int c = h >> 1, hh = h & 1;
+  uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
+  const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
+  const uint32_t xrow8 = (uint32_t)K * 16u;                 // 8 rows of bf16
+#pragma unroll
+  for (int i = 3 * P; i < 3 * P + 3 && i < GM_X_SLOTS; ++i) {
+    const int first = (wave * GM_X_SLOTS + i) * 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(stage + first * 16), 16,
+                                             o.x + i * xrow8, xs, 0, 0);
+  }
+  if constexpr (P == 1) {
+    const int ws = c * UNIT_Q + 512 * hh;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16,
+          o.w + (uint32_t)(part * 2 * nchunk * UNIT_Q), ws, 0, 0);
+  }
+  if constexpr (P == 2) {
+    constexpr int us = unit_s(F), parts = 4 * (us / 4) / 64;
+    const int ss = c * us;
+#pragma unroll
+    for (int part = 0; part < parts; ++part)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256),
+          4, o.s + (uint32_t)(part * 2 * nchunk * us), ss, 0, 0);
+  }
+}
+
+// All of stage h's loads: the three parts, or the per-slot path when K is ragged.
+template <int F, bool RAGGED>
+__device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
+                                            int nchunk, int wave, int lane) {
+  if constexpr (RAGGED) {
+    issue_x<F, RAGGED>(src, ring, h, K, wave, lane);
+    issue_w<F>(src, ring, h, nchunk, wave, lane);
+  } else {
+    issue_stage_part<F, 0>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, 1>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, 2>(src, o, ring, h, K, nchunk, wave);
+  }
+}
+
 __device__ __forceinline__ void read_w(WRegs& r, const uint8_t* stage, int F_spr, int F_us, int wave, int lane) {
   const int kh = lane >> 5;
 #pragma unroll
@@ -157,82 +195,131 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// B operands of k-step S for the wave's two column tiles.
-template <int F, int S>
-__device__ __forceinline__ void b_pair(bf16x8 (&b)[2], const WRegs& r, int kh) {
-  const int sigma = 4 * kh + S;
-  const int gi = (F == FAST) ? (sigma >> 1) : sigma;     // scale byte of this k-step
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
+// Dequantization of one B operand (k-step S, column tile j) in four slices, so that the work can be
+// spread between the MFMAs of the previous k-step: scale and byte lookup, pair converts to FP32, then
+// the two halves of "times scale, round to bf16" (exact). The operand is 8 consecutive positions of the
+// stage's k subset for weight row 32 j + lane % 32, taken from this lane's two dwords of lane pieces
+// 2 hh and 2 hh + 1 (w0, w1):
+//   FAST:  dword S / 2 of piece S % 2, positions in lane-piece order;
+//   Dual:  the low (S even) or high nibbles of dword S / 2 of each piece: 4 positions from each;
+//   NVFP4: 16-bit half S % 2 of dword S / 2 of each piece (4 nibbles each), joined into one dword.
+struct BDec {
+  uint32_t q0, q1;
+  f32x2 p[4];
+  float sc;
+};
+
+template <int F, int S, int SL>
+__device__ __forceinline__ void b_slice(BDec& d, u32x4& out, const WRegs& r, int j, int kh) {
+  if constexpr (SL == 0) {
+    const int sigma = 4 * kh + S;
+    const int gi = (F == FAST) ? (sigma >> 1) : sigma;     // scale byte of this k-step
     const uint32_t sw = (gi & 4) ? r.sc[j][1] : r.sc[j][0];
-    const float sc = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * (gi & 3)), 0);
-    b[j] = b_operand<F, S>(r.w[j][0], r.w[j][1], sc);
+    d.sc = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * (gi & 3)), 0);
+    const u32x2 w0 = r.w[j][0], w1 = r.w[j][1];
+    if constexpr (F == FAST) {
+      const uint32_t w = (S & 1) ? w1[S >> 1] : w0[S >> 1];
+      d.q0 = cb10_quad<false>(w);
+      d.q1 = cb10_quad<true>(w);
+    } else if constexpr (F == DUAL) {
+      d.q0 = cb10_quad<(S & 1) != 0>(w0[S >> 1]);
+      d.q1 = cb10_quad<(S & 1) != 0>(w1[S >> 1]);
+    } else {
+      d.q0 = __builtin_amdgcn_perm(w1[S >> 1], w0[S >> 1], (S & 1) ? 0x07060302u : 0x05040100u);
+    }
+  } else if constexpr (SL == 1) {
+    if constexpr (F == NVFP4) {
+      d.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 0);
+      d.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 1);
+      d.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 2);
+      d.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 3);
+    } else {
+      d.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q0, 1.0f, false);
+      d.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q0, 1.0f, true);
+      d.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q1, 1.0f, false);
+      d.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q1, 1.0f, true);
+    }
+  } else if constexpr (SL == 2) {
+    out[0] = pack_bf16x2(d.p[0][0] * d.sc, d.p[0][1] * d.sc);
+    out[1] = pack_bf16x2(d.p[1][0] * d.sc, d.p[1][1] * d.sc);
+  } else {
+    out[2] = pack_bf16x2(d.p[2][0] * d.sc, d.p[2][1] * d.sc);
+    out[3] = pack_bf16x2(d.p[3][0] * d.sc, d.p[3][1] * d.sc);
   }
 }
 
+// x fragment i (rows 32 i .. 32 i + 31) of k-step S: segment sigma = 4 kh + S of the lane's row.
 template <int S>
-__device__ __forceinline__ void a_frags(bf16x8 (&a)[8], const uint8_t* stage, int lane) {
+__device__ __forceinline__ bf16x8 a_frag(const uint8_t* stage, int lane, int i) {
   const int sigma = 4 * (lane >> 5) + S;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * i + (lane & 31);
-    a[i] = *reinterpret_cast<const bf16x8*>(stage + row * GM_ROW_BYTES + 16 * (sigma ^ (row & 7)));
-  }
+  const int row = 32 * i + (lane & 31);
+  return *reinterpret_cast<const bf16x8*>(stage + row * GM_ROW_BYTES + 16 * (sigma ^ (row & 7)));
 }
 
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[8][2], const bf16x8 (&a)[8], const bf16x8 (&b)[2]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-}
+// Operands of one k-step, double-buffered across k-steps.
+struct KOps {
+  bf16x8 a[8];
+  u32x4 b[2];
+};
 
-// MFMAs of one stage for the wave's 256 x 64 tile. k-step s, lane half kh = lane / 32 use segment
-// sigma = 4 kh + s: the x fragment is that segment of the lane's row, and the B operand is built from
-// dwords 2 kh + s / 2 of the two lane pieces (see b_operand), whose scale group is sigma (16-weight
-// groups) or block sigma / 2 (FAST). Software-pipelined: operands of k-step s + 1 are fetched and
-// dequantized before the MFMAs of k-step s are issued.
-// Scheduling of one k-step region: its 16 MFMAs (operands prepared in the previous region) interleaved with
-// the next k-step's 8 LDS reads (early, so their latency is covered) and its dequantization (VALU). With one
-// wave per SIMD and in-order issue, the instructions between two MFMAs run while the matrix core is busy.
-__device__ __forceinline__ void kstep_schedule() {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
-  }
-}
-
-template <int F>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[8][2], const uint8_t* stage, int wave, int lane) {
-  WRegs r;
-  read_w(r, stage, scales_per_row_chunk(F), unit_s(F), wave, lane);
+// The next k-step's operands, prepared in eight slices; slice g runs between MFMA groups g and g + 1.
+template <int F, int S, int G>
+__device__ __forceinline__ void prep_slice(KOps& nx, BDec (&d)[2], const WRegs& r, const uint8_t* stage, int lane) {
   const int kh = lane >> 5;
-  bf16x8 a0[8], a1[8], b0[2], b1[2];
-  a_frags<0>(a0, stage, lane);
-  b_pair<F, 0>(b0, r, kh);
+  nx.a[G] = a_frag<S>(stage, lane, G);
+  b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2, kh);
+}
+
+template <int G>
+__device__ __forceinline__ void mfma_group(f32x16 (&acc)[8][2], const KOps& k) {
+  const bf16x8 b0 = __builtin_bit_cast(bf16x8, k.b[0]), b1 = __builtin_bit_cast(bf16x8, k.b[1]);
+  acc[G][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], b0, acc[G][0], 0, 0, 0);
+  acc[G][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], b1, acc[G][1], 0, 0, 0);
+}
+
+// Direct loads to issue during a k-step: part P of stage h (nothing when h is past the last stage).
+struct StageLoads {
+  const GemmSrc* src;
+  const LoadOffs* o;
+  uint8_t* ring;
+  int h, K, nchunk, wave, lane;
+};
+
+template <int F, bool RAGGED, int P>
+__device__ __forceinline__ void issue_part(const StageLoads& L) {
+  if constexpr (RAGGED) {
+    if constexpr (P == 0) issue_stage<F, true>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
+  } else {
+    issue_stage_part<F, P>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave);
+  }
+}
+
+// One k-step of the wave's 256 x 64 tile: 8 groups of 2 MFMAs (x fragment G against both column tiles),
+// each followed by one slice of the next k-step's operands (k-step S + 1 of this stage); after group 1
+// the wave issues part S of the loads of two stages ahead. Scheduling fences keep that order, so the
+// slices' LDS reads and VALU work and the loads run while the matrix core is busy.
+template <int F, bool RAGGED, int S>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[8][2], const KOps& cur, KOps& nx, const WRegs& r,
+                                      const uint8_t* stage, int lane, const StageLoads& L, bool load) {
+  BDec d[2];
+#define FP4_GROUP(G)                                   \
+  mfma_group<G>(acc, cur);                             \
+  prep_slice<F, S + 1, G>(nx, d, r, stage, lane);      \
+  if (G == 1 && load) issue_part<F, RAGGED, S>(L);     \
   __builtin_amdgcn_sched_barrier(0);
-  mfma_step(acc, a0, b0);
-  a_frags<1>(a1, stage, lane);
-  b_pair<F, 1>(b1, r, kh);
-  kstep_schedule();
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step(acc, a1, b1);
-  a_frags<2>(a0, stage, lane);
-  b_pair<F, 2>(b0, r, kh);
-  kstep_schedule();
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step(acc, a0, b0);
-  a_frags<3>(a1, stage, lane);
-  b_pair<F, 3>(b1, r, kh);
-  kstep_schedule();
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step(acc, a1, b1);
+  FP4_GROUP(0) FP4_GROUP(1) FP4_GROUP(2) FP4_GROUP(3) FP4_GROUP(4) FP4_GROUP(5) FP4_GROUP(6) FP4_GROUP(7)
+#undef FP4_GROUP
+}
+
+// Operands of k-step 0 of a stage, all at once (the first stage only; later stages prepare them inside
+// the previous stage's last k-step).
+template <int F>
+__device__ __forceinline__ void prep_all0(KOps& k, const WRegs& r, const uint8_t* stage, int lane) {
+  BDec d[2];
+  prep_slice<F, 0, 0>(k, d, r, stage, lane); prep_slice<F, 0, 1>(k, d, r, stage, lane);
+  prep_slice<F, 0, 2>(k, d, r, stage, lane); prep_slice<F, 0, 3>(k, d, r, stage, lane);
+  prep_slice<F, 0, 4>(k, d, r, stage, lane); prep_slice<F, 0, 5>(k, d, r, stage, lane);
+  prep_slice<F, 0, 6>(k, d, r, stage, lane); prep_slice<F, 0, 7>(k, d, r, stage, lane);
 }
 
 template <int F, bool RAGGED>
@@ -256,6 +343,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
   const int tiles_here = max(0, min(ntiles - wrow0 / TILE_N, 4));
   src.q = make_rsrc(qp + (int64_t)(wrow0 / TILE_N) * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
   src.s = make_rsrc(sp + (int64_t)(wrow0 / TILE_N) * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
+  LoadOffs lo;
+  load_offsets<F>(lo, K, nchunk, wave, lane);
 
   f32x16 acc[8][2];
 #pragma unroll
@@ -263,24 +352,53 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
+  // Pipeline over stages of 64 positions (4 k-steps each), 3 ring slots. Stage h + 1 is in LDS or on its
+  // way while stage h is computed, and stage h + 2's loads are issued during k-steps 0-2 of stage h, into
+  // the slot stage h - 1 freed at the last barrier. K-steps 0-2 prepare the next k-step's operands
+  // between their MFMAs. In k-step 3 the wave waits for its share of stage h + 1, meets the other waves
+  // at a barrier (every wave's share of stage h + 1 is then in LDS, and every wave is done reading stage
+  // h), reads stage h + 1's packed weights and prepares its k-step 0 -- still between MFMAs.
   const int H = 2 * nchunk;
-  issue_x<F, RAGGED>(src, ring, 0, K, wave, lane);
-  issue_w<F>(src, ring, 0, nchunk, wave, lane);
-  if (1 < H) {
-    issue_x<F, RAGGED>(src, ring, 1, K, wave, lane);
-    issue_w<F>(src, ring, 1, nchunk, wave, lane);
-  }
+  constexpr int LPS = gm_loads_per_stage(F);
+  issue_stage<F, RAGGED>(src, lo, ring, 0, K, nchunk, wave, lane);
+  if (1 < H) issue_stage<F, RAGGED>(src, lo, ring, 1, K, nchunk, wave, lane);
+  if (1 < H) wait_vmcnt<LPS>();
+  else wait_vmcnt<0>();
+  workgroup_barrier();
+  WRegs r;
+  KOps ka, kb;
+  read_w(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
+  prep_all0<F>(ka, r, ring, lane);
+
   for (int h = 0; h < H; ++h) {
-    // wait for this wave's loads of stage h (stage h + 1's may stay in flight), then a barrier: every
-    // wave's share of stage h is in LDS and stage h - 1, whose ring slot is refilled next, is finished
-    if (h + 1 < H) wait_vmcnt<gm_loads_per_stage(F)>();
-    else wait_vmcnt<0>();
-    workgroup_barrier();
-    if (h + 2 < H) {
-      issue_x<F, RAGGED>(src, ring, h + 2, K, wave, lane);
-      issue_w<F>(src, ring, h + 2, nchunk, wave, lane);
+    const uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
+    const StageLoads L{&src, &lo, ring, h + 2, K, nchunk, wave, lane};
+    const bool load = h + 2 < H;
+    kstep<F, RAGGED, 0>(acc, ka, kb, r, stage, lane, L, load);
+    kstep<F, RAGGED, 1>(acc, kb, ka, r, stage, lane, L, load);
+    kstep<F, RAGGED, 2>(acc, ka, kb, r, stage, lane, L, load);
+    // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
+    mfma_group<0>(acc, kb);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = h + 1 < H;
+    const uint8_t* next = ring + ((h + 1) % GM_RING) * GM_STAGE_BYTES;
+    if (more) {
+      // outstanding direct loads, oldest first: stage h + 1, then stage h + 2 if issued
+      if (load) wait_vmcnt<LPS>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads of stage h are done
+      workgroup_barrier();
+      read_w(r, next, scales_per_row_chunk(F), unit_s(F), wave, lane);
     }
-    compute_stage<F>(acc, ring + (h % GM_RING) * GM_STAGE_BYTES, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    BDec d[2];
+#define FP4_LAST(G)                                              \
+    mfma_group<G>(acc, kb);                                      \
+    if (more) prep_slice<F, 0, G - 1>(ka, d, r, next, lane);     \
+    __builtin_amdgcn_sched_barrier(0);
+    FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
+#undef FP4_LAST
+    if (more) prep_slice<F, 0, 7>(ka, d, r, next, lane);
   }
 
   // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]
