@@ -56,8 +56,13 @@ __device__ __forceinline__ int stage_k(int c, int hh, int sigma) {
   return c * CHUNK_K + (F == FAST ? 32 * (sigma >> 1) + 16 * hh + 8 * (sigma & 1) : 16 * sigma + 8 * hh);
 }
 
+// Segment swizzle of x row `row` in a stage: any 8 consecutive rows (aligned) use 8 different 16-byte
+// segments, and within any 16 aligned rows the even rows and the odd rows each use 8 different ones, so
+// the MFMA operand reads (8 or 16 lanes per LDS access, consecutive rows) have no bank conflicts.
+__device__ __forceinline__ int x_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 // x of stage h: global -> LDS ring slot, one 16-byte direct load per slot. Slot S of the stage holds row
-// S / 8, physical segment S % 8 = sigma ^ (row % 8).
+// S / 8, physical segment S % 8 = sigma ^ x_swizzle(row).
 template <int F, bool RAGGED>
 __device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h, int K, int wave, int lane) {
   const int c = h >> 1, hh = h & 1;
@@ -66,7 +71,7 @@ __device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h
   for (int i = 0; i < GM_X_SLOTS; ++i) {
     const int first = (wave * GM_X_SLOTS + i) * 64;          // first slot of this instruction (uniform)
     const int slot = first + lane;
-    const int row = slot >> 3, sigma = (slot & 7) ^ (row & 7);
+    const int row = slot >> 3, sigma = (slot & 7) ^ x_swizzle(row);
     const int k = stage_k<F>(c, hh, sigma);
     const uint32_t off = (!RAGGED || k < K) ? (uint32_t)(row * K + k) * 2u : 0xFFFFFFF0u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(base + first * 16),
@@ -103,19 +108,25 @@ __device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h
 }
 
 // Per-lane parts of the direct-load offsets, computed once per tile. Rows and tiles stay in the
-// per-lane (range-checked) offset: x slot i of a lane is 8 rows below slot 0, the second weight and
-// scale parts two tiles further, each one add per load. Only the stage term (chunk, half-chunk), which
-// stays inside a row of x and a tile's row of units, goes into the scalar offset.
+// per-lane (range-checked) offset: x slot i of a lane is 8 rows below slot 0 (its segment differs in the
+// swizzle's parity bit for odd i, hence two x offsets), the second weight and scale parts two tiles
+// further, each one add per load. Only the stage term (chunk, half-chunk), which stays inside a row of x
+// and a tile's row of units, goes into the scalar offset.
 struct LoadOffs {
-  uint32_t x, w, s;
+  uint32_t x[2], w, s;
 };
+
+template <int F>
+__host__ __device__ constexpr int seg_k(int sigma) {   // stage_k without the chunk and half-chunk terms
+  return (F == FAST) ? 32 * (sigma >> 1) + 8 * (sigma & 1) : 16 * sigma;
+}
 
 template <int F>
 __device__ __forceinline__ void load_offsets(LoadOffs& o, int K, int nchunk, int wave, int lane) {
   const int row = wave * 64 + (lane >> 3);              // slot 0 of the lane: row of x in the tile
-  const int sigma = (lane & 7) ^ (row & 7);
-  const int kk = (F == FAST) ? 32 * (sigma >> 1) + 8 * (sigma & 1) : 16 * sigma;   // stage_k without c, hh
-  o.x = (uint32_t)(row * K + kk) * 2u;
+  const int sigma = (lane & 7) ^ x_swizzle(row);
+  o.x[0] = (uint32_t)(row * K + seg_k<F>(sigma)) * 2u;
+  o.x[1] = (uint32_t)(row * K + seg_k<F>(sigma ^ 1)) * 2u;
   o.w = (uint32_t)((lane >> 5) * nchunk) * UNIT_Q + (lane & 31) * 16;
   constexpr int us = unit_s(F), lanes_per_tile = us / 4;
   o.s = (uint32_t)((lane / lanes_per_tile) * nchunk) * us + (lane % lanes_per_tile) * 4;
@@ -135,7 +146,7 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
   for (int i = 3 * P; i < 3 * P + 3 && i < GM_X_SLOTS; ++i) {
     const int first = (wave * GM_X_SLOTS + i) * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(stage + first * 16), 16,
-                                             o.x + i * xrow8, xs, 0, 0);
+                                             o.x[i & 1] + i * xrow8, xs, 0, 0);
   }
   if constexpr (P == 1) {
     const int ws = c * UNIT_Q + 512 * hh;
@@ -253,7 +264,7 @@ template <int S>
 __device__ __forceinline__ bf16x8 a_frag(const uint8_t* stage, int lane, int i) {
   const int sigma = 4 * (lane >> 5) + S;
   const int row = 32 * i + (lane & 31);
-  return *reinterpret_cast<const bf16x8*>(stage + row * GM_ROW_BYTES + 16 * (sigma ^ (row & 7)));
+  return *reinterpret_cast<const bf16x8*>(stage + row * GM_ROW_BYTES + 16 * (sigma ^ x_swizzle(row)));
 }
 
 // Operands of one k-step, double-buffered across k-steps.
