@@ -195,8 +195,11 @@ __device__ __forceinline__ void stage_x_now(uint8_t* xs, const Srcs& src, int M,
     u32x4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = x_piece_off<U>(p0 + 64 * i + lane, M, K, c0, W, nchunk);
-      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, off, 0, 0));
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (p0 + 64 * i < pieces) {      // wave-uniform: no load instruction for a wholly empty group
+        const uint32_t off = x_piece_off<U>(p0 + 64 * i + lane, M, K, c0, W, nchunk);
+        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, off, 0, 0));
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -404,9 +407,9 @@ __device__ __forceinline__ void decode_scaled(const WeightRegs<F>& w, bf16x8 (&b
   }
 }
 
-// Dynamic LDS: [W waves][4 lane groups][M rows][64 B] of staged x (one chunk per wave), then the
-// cross-wave reduction buffer [W][MB][64 lanes][4] floats.
-template <int F, int MB>
+// Dynamic LDS: [W waves][4 lane groups][M rows][64 B] of staged x (one chunk per wave); after the K loop
+// the same space holds the cross-wave reduction buffer [W][T][MB][64 lanes][4] floats.
+template <int F, int MB, int T>
 __global__ __launch_bounds__(512) void midm_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                                    const uint16_t* __restrict__ x, float* __restrict__ y, int M,
                                                    int N, int K, int ntiles, int nchunk, float gscale) {
@@ -414,60 +417,79 @@ __global__ __launch_bounds__(512) void midm_kernel(const uint8_t* __restrict__ q
   const int lane = threadIdx.x & 63, W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4, m16 = lane & 15;
-  const int tile = blockIdx.x;
+  const int tile0 = blockIdx.x * T;
+  const int tiles_here = min(T, ntiles - tile0);
   Srcs src;
-  src.q = make_rsrc(qp + (int64_t)tile * nchunk * UNIT_Q, (uint32_t)(nchunk * UNIT_Q));
-  src.s = make_rsrc(sp + (int64_t)tile * nchunk * unit_s(F), (uint32_t)(nchunk * unit_s(F)));
+  src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
+  src.s = make_rsrc(sp + (int64_t)tile0 * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
   src.x = make_rsrc(x, (uint32_t)(M * K) * 2u);
   const size_t xw_bytes = (size_t)4 * M * 64;
   uint8_t* xs = smem + wave * xw_bytes;
-  float* red = reinterpret_cast<float*>(smem + W * xw_bytes);
   const uint32_t soff_lane = n * (unit_s(F) / TILE_N);
 
-  f32x4 acc[MB];
+  f32x4 acc[T][MB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // x of the wave's next chunk is loaded into registers (all of it at once) together with the next
   // weights while the current chunk is computed, then committed to LDS at the top of the next chunk.
+  // The T tiles of the workgroup share that x.
   XStage<1, 16 * MB> xst;
-  WeightRegs<F> wr;
+  WeightRegs<F> wr[T];
   if (wave < nchunk) {
     stage_x_issue<F, 1, 16 * MB>(xst, src, M, K, wave, W, nchunk, lane);
-    load_unit<F>(wr, src, (uint32_t)wave * UNIT_Q + lane * 16, (uint32_t)wave * unit_s(F) + soff_lane);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      load_unit<F>(wr[t], src, (uint32_t)(t * nchunk + wave) * UNIT_Q + lane * 16,
+                   (uint32_t)(t * nchunk + wave) * unit_s(F) + soff_lane);
   }
   for (int c = wave; c < nchunk; c += W) {
     stage_x_commit<F, 1, 16 * MB>(xs, xst, M, lane);
-    WeightRegs<F> nx;                  // next unit of this wave, in flight during this one
+    WeightRegs<F> nx[T];               // next units of this wave, in flight during these
     const int c1 = c + W;
     if (c1 < nchunk) {
       stage_x_issue<F, 1, 16 * MB>(xst, src, M, K, c1, W, nchunk, lane);
-      load_unit<F>(nx, src, (uint32_t)c1 * UNIT_Q + lane * 16, (uint32_t)c1 * unit_s(F) + soff_lane);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        load_unit<F>(nx[t], src, (uint32_t)(t * nchunk + c1) * UNIT_Q + lane * 16,
+                     (uint32_t)(t * nchunk + c1) * unit_s(F) + soff_lane);
     }
-    bf16x8 b[4];
-    decode_scaled<F>(wr, b);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = min(mb * 16 + m16, M - 1);  // rows past M repeat a valid row; never stored
-      const uint8_t* xr = xs + (g * M + row) * 64;
+    for (int t = 0; t < T; ++t) {
+      bf16x8 b[4];
+      decode_scaled<F>(wr[t], b);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + 16 * j);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = min(mb * 16 + m16, M - 1);  // rows past M repeat a valid row; never stored
+        const uint8_t* xr = xs + (g * M + row) * 64;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + 16 * j);
+          acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[t][mb], 0, 0, 0);
+        }
       }
     }
-    if (c1 < nchunk) wr = nx;
+    if (c1 < nchunk) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) wr[t] = nx[t];
+    }
   }
 
-  float* mine = red + ((size_t)wave * MB * 64 + lane) * 4;
+  __syncthreads();                     // every wave is done with its staged x: reuse the space
+  float* red = reinterpret_cast<float*>(smem);
+  const int total = T * MB * 256;
+  float* mine = red + (size_t)wave * total + lane * 4;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(mine + (size_t)mb * 256) = acc[mb];
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(mine + (size_t)(t * MB + mb) * 256) = acc[t][mb];
   __syncthreads();
-  const int total = MB * 256;
   for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int mb = e / 256, l = (e >> 2) & 63, r = e & 3;
+    const int t = e / (MB * 256), mb = (e / 256) % MB, l = (e >> 2) & 63, r = e & 3;
     const int mrow = mb * 16 + 4 * (l >> 4) + r;
-    const int col = tile * TILE_N + (l & 15);
+    const int col = (tile0 + t) * TILE_N + (l & 15);
     if (mrow < M && col < N) {
       float sum = 0.f;
       for (int w = 0; w < W; ++w) sum += red[(size_t)w * total + e];
@@ -491,7 +513,11 @@ static void launch_gemv(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStre
 // Fills in the workgroup ranges, picks the wave count and launches. Every item has N, K >= 1.
 template <int F, int MAXI>
 static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
-  const int T = (M > 4) ? 2 : 1;
+  // With more than 4 x rows a workgroup takes two tiles (they share the staged x) when there are enough
+  // tiles for one such workgroup per CU; otherwise one.
+  int total_tiles = 0;
+  for (int i = 0; i < b.count; ++i) total_tiles += (b.it[i].N + TILE_N - 1) / TILE_N;
+  const int T = (M > 4 && total_tiles >= 2 * 256) ? 2 : 1;
   int nwg = 0, min_chunks = 1 << 30;
   for (int i = 0; i < b.count; ++i) {
     GemvItem& it = b.it[i];
@@ -514,7 +540,8 @@ static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   if (M == 1)      launch_gemv<F, 1, 1, 4, 1, MAXI>(b, nwg, W, M, st);
   else if (M == 2) launch_gemv<F, 1, 2, 4, 2, MAXI>(b, nwg, W, M, st);
   else if (M <= 4) launch_gemv<F, 1, 4, 4, 4, MAXI>(b, nwg, W, M, st);
-  else             launch_gemv<F, 2, 4, 2, 16, MAXI>(b, nwg, W, M, st);
+  else if (T == 2) launch_gemv<F, 2, 4, 2, 16, MAXI>(b, nwg, W, M, st);
+  else             launch_gemv<F, 1, 4, 2, 16, MAXI>(b, nwg, W, M, st);
 }
 
 template <int MAXI>
@@ -543,36 +570,55 @@ static int check_item(int fmt, int64_t M, int64_t N, int64_t K, const void* q, c
   return 0;
 }
 
-template <int F, int MB>
+template <int F, int MB, int T>
 static void launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                         int M, int N, int K, float g) {
   const int ntiles = (N + TILE_N - 1) / TILE_N, nchunk = (K + CHUNK_K - 1) / CHUNK_K;
-  const size_t lds = (size_t)W * 4 * M * 64 + (size_t)W * MB * 64 * 4 * sizeof(float);
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&midm_kernel<F, MB>),
+  const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
+  const size_t lds = stage > red ? stage : red;
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&midm_kernel<F, MB, T>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((midm_kernel<F, MB>), dim3(ntiles), dim3(64 * W), lds, st, q, s, x, y, M, N, K, ntiles, nchunk,
-                     g);
+  hipLaunchKernelGGL((midm_kernel<F, MB, T>), dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, M, N, K,
+                     ntiles, nchunk, g);
+}
+
+template <int F, int MB>
+static void dispatch_midm_mb(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                             int N, int K, float g) {
+  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K, ntiles = (N + TILE_N - 1) / TILE_N;
+  // Two tiles per workgroup share the staged x (half the x traffic) when that still leaves two
+  // workgroups per CU; not with four 16-row blocks of x, where the registers would not suffice.
+  const int T = (MB <= 3 && ntiles >= 2 * 2 * 256) ? 2 : 1;
+  const int nwg = (ntiles + T - 1) / T;
+  // Waves per workgroup: the most (up to 8; the staged x of 8 waves at M = 64 fills 128 KiB of LDS)
+  // that give every wave at least two chunks and keep the grid resident at once (16 waves per CU
+  // with two 16-row blocks of x and one tile, 8 otherwise, at this kernel's register use).
+  const int resident = (MB <= 2 && T == 1 ? 16 : 8) * 256;
+  int W = 8;
+  while (W > 1 && (nchunk < 2 * W || nwg * W > resident)) W >>= 1;
+  if (const char* e = getenv("FP4_MIDM_WAVES")) {  // tuning override, read at each call
+    if (atoi(e) > 0 && atoi(e) <= 8) W = atoi(e);
+  }
+  if constexpr (MB <= 3) {
+    if (T == 2) {
+      launch_midm<F, MB, 2>(W, st, q, s, x, y, M, N, K, g);
+      return;
+    }
+  }
+  launch_midm<F, MB, 1>(W, st, q, s, x, y, M, N, K, g);
 }
 
 template <int F>
 static void dispatch_midm(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                           int N, int K, float g) {
-  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K, ntiles = (N + TILE_N - 1) / TILE_N;
-  // Waves per workgroup: the most (up to 8; the staged x of 8 waves at M = 64 fills 128 KiB of LDS)
-  // that give every wave at least two chunks and keep the grid resident at once (16 waves per CU
-  // with two 16-row blocks of x, 8 with more, at this kernel's register use).
-  const int resident = (M <= 32 ? 16 : 8) * 256;
-  int W = 8;
-  while (W > 1 && (nchunk < 2 * W || ntiles * W > resident)) W >>= 1;
-  if (const char* e = getenv("FP4_MIDM_WAVES")) {  // tuning override, read at each call
-    if (atoi(e) > 0 && atoi(e) <= 8) W = atoi(e);
-  }
   const int mb = (M + 15) / 16;
-  if (mb <= 2)      launch_midm<F, 2>(W, st, q, s, x, y, M, N, K, g);
-  else if (mb == 3) launch_midm<F, 3>(W, st, q, s, x, y, M, N, K, g);
-  else              launch_midm<F, 4>(W, st, q, s, x, y, M, N, K, g);
+  if (mb == 1)      dispatch_midm_mb<F, 1>(M, st, q, s, x, y, N, K, g);
+  else if (mb == 2) dispatch_midm_mb<F, 2>(M, st, q, s, x, y, N, K, g);
+  else if (mb == 3) dispatch_midm_mb<F, 3>(M, st, q, s, x, y, N, K, g);
+  else              dispatch_midm_mb<F, 4>(M, st, q, s, x, y, N, K, g);
 }
+
 
 extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                           float global_scale, const void* x_bf16, float* y, void* stream) {
@@ -585,6 +631,20 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   if (M == 0) return 0;
   rc = check_item(fmt, M, N, K, q, s, x_bf16, y);
   if (rc) return rc;
+  if (M >= 5 && fmt != Q4_0) {
+    // from 5 rows of x on, decoding each weight once into scaled bf16 operands (the mid-M kernel) is
+    // faster than folding the scales per group and per x row
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* qq = (const uint8_t*)q;
+    const uint8_t* ss = (const uint8_t*)s;
+    const uint16_t* xx = (const uint16_t*)x_bf16;
+    switch (fmt) {
+      case NVFP4: dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+      case DUAL:  dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+      default:    dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+    }
+    return fp4_launch_status();
+  }
   GemvBatch<1> b;
   b.count = 1;
   b.it[0] = GemvItem{(const uint8_t*)q, (const uint8_t*)s, (const uint16_t*)x_bf16, y, (int)N, (int)K, 0, 0,

@@ -94,7 +94,9 @@ int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q, const void
  * Decode-shaped product, 1 <= M <= 16: streams each nibble and scale byte
  * once, decodes to exact bf16 levels, contracts against x on the matrix cores, applies
  * the group scales to the FP32 partial sums, reduces the K split inside the workgroup and
- * multiplies by g. q/s are fp4_pack_layout output. Deterministic (no atomics).
+ * multiplies by g. From M = 5 on (NVFP4, Dual, FAST) it runs the w4a16_midm kernel instead,
+ * which decodes each weight once into exact bf16 level*scale shared by all rows of x.
+ * q/s are fp4_pack_layout output. Deterministic (no atomics).
  */
 int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);
