@@ -11,6 +11,7 @@
 #include "launch.h"
 #include "fp4w4a16.h"
 #include <stdlib.h>
+#include <atomic>
 
 namespace fp4 {
 
@@ -145,33 +146,37 @@ struct XStage {
   u32x4 v[NX];
 };
 
-// byte offset of x piece p (16 bytes: 8 consecutive k of one row) of the batch starting at chunk c0
-template <int U>
+// byte offset of x piece p (16 bytes: 8 consecutive k of one row) of the batch starting at chunk c0.
+// WRAP (M known at compile time): lanes past the last piece take piece p % pieces, so that they load and
+// stage the same bytes as another lane and the staging store needs no branch (a branch there lets the
+// compiler sink the x load below the weight loads, and staging x would then wait for all of them).
+template <int U, bool WRAP = false>
 __device__ __forceinline__ uint32_t x_piece_off(int p, int M, int K, int c0, int W, int nchunk) {
   const int pieces = U * M * 16;
+  if constexpr (WRAP) p = p % pieces;
   const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
   const int c = c0 + u * W;
   const int k = c * CHUNK_K + 8 * qq;
   return (p < pieces && c < nchunk && k < K) ? (uint32_t)(m * K + k) * 2u : OOB;
 }
 
-template <int F, int U, int MX>
+template <int F, int U, int MX, bool WRAP = false>
 __device__ __forceinline__ void stage_x_issue(XStage<U, MX>& st, const Srcs& src, int M, int K, int c0, int W,
                                               int nchunk, int lane) {
 #pragma unroll
   for (int i = 0; i < XStage<U, MX>::NX; ++i) {
-    const uint32_t off = x_piece_off<U>(64 * i + lane, M, K, c0, W, nchunk);
+    const uint32_t off = x_piece_off<U, WRAP>(64 * i + lane, M, K, c0, W, nchunk);
     st.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, off, 0, 0));
   }
 }
 
-template <int F, int U, int MX>
+template <int F, int U, int MX, bool WRAP = false>
 __device__ __forceinline__ void stage_x_commit(uint8_t* xs, const XStage<U, MX>& st, int M, int lane) {
   const int pieces = U * M * 16;
 #pragma unroll
   for (int i = 0; i < XStage<U, MX>::NX; ++i) {
-    const int p = 64 * i + lane;
-    if (p < pieces) {
+    const int p = WRAP ? (64 * i + lane) % pieces : 64 * i + lane;
+    if (WRAP || p < pieces) {
       const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
       const int dst = (u * 4 * M + m) * 64 + (block32(F) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
                                                            : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
@@ -232,6 +237,7 @@ __device__ __forceinline__ void load_batch(WeightRegs<F> (&wr)[U][T], const Srcs
       const bool ok = c < nchunk;
       load_unit<F>(wr[u][t], src, ok ? unit * UNIT_Q + lane * 16 : OOB,
                    ok ? unit * unit_s(F) + n * (unit_s(F) / TILE_N) : OOB);
+      __builtin_amdgcn_sched_barrier(0);  // units in order: each unit's nibbles and scales together
     }
   }
 }
@@ -256,9 +262,13 @@ struct GemvBatch {
 
 // Dynamic LDS: [W waves][U chunks][4 lane groups][M rows][64 B] of staged x, then the
 // cross-wave reduction buffer [W][T][64 lanes][4] floats.
-template <int F, int T, int RU, int U, int MX, int MAXI>
-__global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch, int M) {
+// MC > 0 fixes M = MC at compile time (the x address arithmetic then reduces to shifts and masks);
+// MC = 0 takes M from the argument (at most MX). ONE: every wave's chunks fit in one batch
+// (nchunk <= U * W for every matrix of the launch), so there is no next batch to prefetch.
+template <int F, int T, int RU, int U, int MX, int MAXI, int MC, bool ONE>
+__global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch, int m_arg) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int M = MC > 0 ? MC : m_arg;
   // this workgroup's matrix (a uniform search over at most MAXI starts)
   int item = 0;
 #pragma unroll
@@ -301,24 +311,28 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch,
   XStage<U, XPF ? MX : 1> xst;
   if constexpr (XPF) {
     if (wave < nchunk) {
-      stage_x_issue<F, U, MX>(xst, src, M, K, wave, W, nchunk, lane);
+      // x first, then every weight load, in that order (the scheduler may not interleave them with
+      // the staging below: staging waits for x only because loads complete in order)
+      stage_x_issue<F, U, MX, (MC > 0)>(xst, src, M, K, wave, W, nchunk, lane);
+      __builtin_amdgcn_sched_barrier(0);
       load_batch<F, T, U>(wr, src, wave, W, nchunk, lane, n);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   bool have = XPF;  // wr already holds this batch's weights
-  for (int c0 = wave; c0 < nchunk; c0 += W * U) {
+  for (int c0 = wave; c0 < nchunk; c0 += ONE ? nchunk : W * U) {
     if constexpr (XPF) {
-      stage_x_commit<F, U, MX>(xs, xst, M, lane);
+      stage_x_commit<F, U, MX, (MC > 0)>(xs, xst, M, lane);
     } else {
       stage_x_now<F, U>(xs, src, M, K, c0, W, nchunk, lane);
       if (!have) load_batch<F, T, U>(wr, src, c0, W, nchunk, lane, n);
     }
     // the next batch (x first, then weights) goes out before this batch is computed
     WeightRegs<F> nx[U][T];
-    const int c1 = c0 + W * U;
-    have = c1 < nchunk;
+    const int c1 = ONE ? nchunk : c0 + W * U;
+    have = !ONE && c1 < nchunk;
     if (have) {
-      if constexpr (XPF) stage_x_issue<F, U, MX>(xst, src, M, K, c1, W, nchunk, lane);
+      if constexpr (XPF) stage_x_issue<F, U, MX, (MC > 0)>(xst, src, M, K, c1, W, nchunk, lane);
       load_batch<F, T, U>(nx, src, c1, W, nchunk, lane, n);
     }
 #pragma unroll
@@ -500,17 +514,70 @@ __global__ __launch_bounds__(512) void midm_kernel(const uint8_t* __restrict__ q
 
 constexpr int GEMV_LDS_MAX = 160 * 1024;
 
-template <int F, int T, int RU, int U, int MX, int MAXI>
-static void launch_gemv(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
-  const size_t lds = (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float);
-  // allow more than 64 KiB of dynamic LDS for this instantiation (once; thread-safe static init)
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX, MAXI>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
-  (void)attr;
-  hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX, MAXI>), dim3(nwg), dim3(64 * W), lds, st, b, M);
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
 }
 
-// Fills in the workgroup ranges, picks the wave count and launches. Every item has N, K >= 1.
+// Workgroups of W waves of kernel `k` that one compute unit holds at once, with `lds` bytes of dynamic
+// LDS each (from the occupancy calculator; remembered per wave count and LDS size class).
+static int resident_per_cu(const void* k, int W, size_t lds) {
+  int b = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, 64 * W, lds) != hipSuccess || b < 1) b = 1;
+  return b;
+}
+
+template <int F, int T, int RU, int U, int MX, int MAXI, int MC, bool ONE = false>
+struct GemvLaunch {
+  static const void* fn() { return reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX, MAXI, MC, ONE>); }
+  static size_t lds(int W, int M) { return (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float); }
+  // workgroups resident per CU for W = 1, 2, 4, 8, 16 at this M (computed once per M class)
+  static int resident(int W, int M) {
+    static std::atomic<int> cache[5][17];
+    int wi = 0;
+    while ((1 << wi) < W) ++wi;
+    const int mi = M > 16 ? 16 : M;
+    int r = cache[wi][mi].load(std::memory_order_relaxed);
+    if (r <= 0) {
+      attr();
+      r = resident_per_cu(fn(), W, lds(W, M));
+      cache[wi][mi].store(r, std::memory_order_relaxed);
+    }
+    return r;
+  }
+  // allow more than 64 KiB of dynamic LDS for this instantiation (once; thread-safe static init)
+  static void attr() {
+    static const bool ok = hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
+    (void)ok;
+  }
+  static void launch(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
+    attr();
+    hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX, MAXI, MC, ONE>), dim3(nwg), dim3(64 * W), lds(W, M), st, b, M);
+  }
+};
+
+// Picks the wave count of a launch: the most (up to 16, and up to wmax) that give every wave at least
+// two K chunks and keep the whole grid resident at once (one round of workgroups).
+template <class L>
+static int pick_waves(int nwg, int min_chunks, int M, int wmax) {
+  const int cus = device_cus();
+  int W = 16;
+  while (W > 1 && (W > wmax || min_chunks < 2 * W || (int64_t)nwg > (int64_t)L::resident(W, M) * cus)) W >>= 1;
+  if (const char* e = getenv("FP4_GEMV_WAVES")) {  // tuning override, read at each call
+    if (atoi(e) > 0 && atoi(e) <= 16) W = atoi(e);
+  }
+  return W;
+}
+
+// Fills in the workgroup ranges, picks the variant and wave count, and launches. Every item has N, K >= 1.
 template <int F, int MAXI>
 static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   // With more than 4 x rows a workgroup takes two tiles (they share the staged x) when there are enough
@@ -518,7 +585,7 @@ static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   int total_tiles = 0;
   for (int i = 0; i < b.count; ++i) total_tiles += (b.it[i].N + TILE_N - 1) / TILE_N;
   const int T = (M > 4 && total_tiles >= 2 * 256) ? 2 : 1;
-  int nwg = 0, min_chunks = 1 << 30;
+  int nwg = 0, min_chunks = 1 << 30, max_chunks = 0;
   for (int i = 0; i < b.count; ++i) {
     GemvItem& it = b.it[i];
     it.nchunk = (it.K + CHUNK_K - 1) / CHUNK_K;
@@ -526,22 +593,47 @@ static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     const int ntiles = (it.N + TILE_N - 1) / TILE_N;
     nwg += (ntiles + T - 1) / T;
     min_chunks = min_chunks < it.nchunk ? min_chunks : it.nchunk;
+    max_chunks = max_chunks > it.nchunk ? max_chunks : it.nchunk;
   }
-  // Waves per workgroup: the most (up to 16) that still give every wave at least two K chunks and
-  // keep the whole grid resident at once (about 20 waves per CU at this kernel's register use).
-  int W = 16;
-  while (W > 1 && (min_chunks < 2 * W || nwg * W > 5120)) W >>= 1;
-  if (const char* e = getenv("FP4_GEMV_WAVES")) {  // tuning override, read at each call
-    if (atoi(e) > 0) W = atoi(e);
-  }
+  // Batches of two chunk slots when the wave count that would be picked leaves at most two chunks per
+  // wave (no load slots that read nothing), else four.
   const int wmax = (M > 4) ? 8 : 16;  // keep the staged x (W * U * M * 256 B) inside the LDS
-  if (W > wmax) W = wmax;
-  if (W < 1) W = 1;
-  if (M == 1)      launch_gemv<F, 1, 1, 4, 1, MAXI>(b, nwg, W, M, st);
-  else if (M == 2) launch_gemv<F, 1, 2, 4, 2, MAXI>(b, nwg, W, M, st);
-  else if (M <= 4) launch_gemv<F, 1, 4, 4, 4, MAXI>(b, nwg, W, M, st);
-  else if (T == 2) launch_gemv<F, 2, 4, 2, 16, MAXI>(b, nwg, W, M, st);
-  else             launch_gemv<F, 1, 4, 2, 16, MAXI>(b, nwg, W, M, st);
+  if (M == 1) {
+    // One batch of U chunk slots per wave when W * U covers the longest K (no prefetch registers);
+    // U is the fewest slots that do at the picked wave count.
+    using L4 = GemvLaunch<F, 1, 1, 4, 1, MAXI, 1>;
+    using O2 = GemvLaunch<F, 1, 1, 2, 1, MAXI, 1, true>;
+    using O3 = GemvLaunch<F, 1, 1, 3, 1, MAXI, 1, true>;
+    using O4 = GemvLaunch<F, 1, 1, 4, 1, MAXI, 1, true>;
+    int W = pick_waves<O4>(nwg, min_chunks, M, wmax);
+    int U = (max_chunks + W - 1) / W;
+    if (const char* e = getenv("FP4_GEMV_U")) {  // tuning override, read at each call
+      if (atoi(e) >= 2 && atoi(e) <= 4 && atoi(e) * W >= max_chunks) U = atoi(e);
+    }
+    using L2 = GemvLaunch<F, 1, 1, 2, 1, MAXI, 1>;
+    const char* one = getenv("FP4_GEMV_ONE");  // tuning override: 0 = batch loop with prefetch
+    if (one && atoi(one) == 0 && U <= 2) L2::launch(b, nwg, W, M, st);
+    else if (one && atoi(one) == 0 && U <= 4) L4::launch(b, nwg, W, M, st);
+    else if (U <= 2) O2::launch(b, nwg, W, M, st);
+    else if (U == 3) O3::launch(b, nwg, W, M, st);
+    else if (U == 4) O4::launch(b, nwg, W, M, st);
+    else L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+  } else if (M == 2) {
+    using L4 = GemvLaunch<F, 1, 2, 4, 2, MAXI, 2>;
+    L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+  } else if (M == 3) {
+    using L4 = GemvLaunch<F, 1, 4, 4, 3, MAXI, 3>;
+    L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+  } else if (M == 4) {
+    using L4 = GemvLaunch<F, 1, 4, 4, 4, MAXI, 4>;
+    L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+  } else if (T == 2) {
+    using L = GemvLaunch<F, 2, 4, 2, 16, MAXI, 0>;
+    L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
+  } else {
+    using L = GemvLaunch<F, 1, 4, 2, 16, MAXI, 0>;
+    L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
+  }
 }
 
 template <int MAXI>
