@@ -97,12 +97,10 @@ __device__ __forceinline__ bf16x8 cat(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// bf16 of two f32 values (exact for level*scale, which has at most 7 significant bits)
+// bf16 pair of two f32 values that bf16 holds exactly (level * scale has at most 8 significant bits, so
+// the low 16 bits of its f32 encoding are zero): the high halves of both, joined with one byte permute.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2 v = {(__bf16)a, (__bf16)b};
-  uint32_t u;
-  __builtin_memcpy(&u, &v, 4);
-  return u;
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07060302u);
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x2& a, const f32x2& b, const f32x2& c, const f32x2& e, float sc) {

@@ -167,6 +167,35 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
   }
 }
 
+// Load I (0 .. 11) of stage h's direct loads (K a multiple of 128): x slots 0-7, the two weight pieces, then
+// the scale loads (two for 16-weight groups, one for FAST; I = 11 issues nothing for FAST). Issued one at a
+// time between MFMAs so that no burst of vector-memory instructions holds up the wave.
+template <int F, int I>
+__device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
+                                                int nchunk, int wave) {
+  const int c = h >> 1, hh = h & 1;
+  uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
+  if constexpr (I < GM_X_SLOTS) {
+    const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
+    const uint32_t xrow8 = (uint32_t)K * 16u;               // 8 rows of bf16
+    const int first = (wave * GM_X_SLOTS + I) * 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(stage + first * 16), 16,
+                                             o.x[I & 1] + I * xrow8, xs, 0, 0);
+  } else if constexpr (I < GM_X_SLOTS + 2) {
+    constexpr int part = I - GM_X_SLOTS;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16,
+        o.w + (uint32_t)(part * 2 * nchunk * UNIT_Q), c * UNIT_Q + 512 * hh, 0, 0);
+  } else {
+    constexpr int us = unit_s(F), parts = 4 * (us / 4) / 64;
+    constexpr int part = I - GM_X_SLOTS - 2;
+    if constexpr (part < parts)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256),
+          4, o.s + (uint32_t)(part * 2 * nchunk * us), c * us, 0, 0);
+  }
+}
+
 // All of stage h's loads: the three parts, or the per-slot path when K is ragged.
 template <int F, bool RAGGED>
 __device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
@@ -296,12 +325,14 @@ struct StageLoads {
   int h, K, nchunk, wave, lane;
 };
 
-template <int F, bool RAGGED, int P>
+// Loads issued after MFMA group G of k-step S: with K ragged, all of the stage at once (k-step 0, group 1);
+// otherwise load 4 S + G / 2 of the stage after each odd group of k-steps 0-2.
+template <int F, bool RAGGED, int S, int G>
 __device__ __forceinline__ void issue_part(const StageLoads& L) {
   if constexpr (RAGGED) {
-    if constexpr (P == 0) issue_stage<F, true>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
+    if constexpr (S == 0 && G == 1) issue_stage<F, true>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
   } else {
-    issue_stage_part<F, P>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave);
+    if constexpr (S < 3 && (G & 1)) issue_stage_one<F, 4 * S + (G >> 1)>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave);
   }
 }
 
@@ -309,14 +340,14 @@ __device__ __forceinline__ void issue_part(const StageLoads& L) {
 // each followed by one slice of the next k-step's operands (k-step S + 1 of this stage); after group 1
 // the wave issues part S of the loads of two stages ahead. Scheduling fences keep that order, so the
 // slices' LDS reads and VALU work and the loads run while the matrix core is busy.
-template <int F, bool RAGGED, int S>
+template <int F, bool RAGGED, int S, bool LOAD>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[8][2], const KOps& cur, KOps& nx, const WRegs& r,
-                                      const uint8_t* stage, int lane, const StageLoads& L, bool load) {
+                                      const uint8_t* stage, int lane, const StageLoads& L) {
   BDec d[2];
 #define FP4_GROUP(G)                                   \
   mfma_group<G>(acc, cur);                             \
   prep_slice<F, S + 1, G>(nx, d, r, stage, lane);      \
-  if (G == 1 && load) issue_part<F, RAGGED, S>(L);     \
+  if constexpr (LOAD) issue_part<F, RAGGED, S, G>(L);  \
   __builtin_amdgcn_sched_barrier(0);
   FP4_GROUP(0) FP4_GROUP(1) FP4_GROUP(2) FP4_GROUP(3) FP4_GROUP(4) FP4_GROUP(5) FP4_GROUP(6) FP4_GROUP(7)
 #undef FP4_GROUP
@@ -331,6 +362,41 @@ __device__ __forceinline__ void prep_all0(KOps& k, const WRegs& r, const uint8_t
   prep_slice<F, 0, 2>(k, d, r, stage, lane); prep_slice<F, 0, 3>(k, d, r, stage, lane);
   prep_slice<F, 0, 4>(k, d, r, stage, lane); prep_slice<F, 0, 5>(k, d, r, stage, lane);
   prep_slice<F, 0, 6>(k, d, r, stage, lane); prep_slice<F, 0, 7>(k, d, r, stage, lane);
+}
+
+// Stage h of the K loop (see the kernel). LOAD: the stage issues stage h + 2's loads; MORE: there is a
+// stage h + 1, whose k-step 0 operands this stage prepares into ka.
+template <int F, bool RAGGED, bool LOAD, bool MORE>
+__device__ __forceinline__ void stage_body(f32x16 (&acc)[8][2], KOps& ka, KOps& kb, WRegs& r, const GemmSrc& src,
+                                           const LoadOffs& lo, uint8_t* ring, int h, int K, int nchunk, int wave,
+                                           int lane) {
+  constexpr int LPS = gm_loads_per_stage(F);
+  const uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
+  const StageLoads L{&src, &lo, ring, h + 2, K, nchunk, wave, lane};
+  kstep<F, RAGGED, 0, LOAD>(acc, ka, kb, r, stage, lane, L);
+  kstep<F, RAGGED, 1, LOAD>(acc, kb, ka, r, stage, lane, L);
+  kstep<F, RAGGED, 2, LOAD>(acc, ka, kb, r, stage, lane, L);
+  // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
+  mfma_group<0>(acc, kb);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t* next = ring + ((h + 1) % GM_RING) * GM_STAGE_BYTES;
+  if constexpr (MORE) {
+    // outstanding direct loads, oldest first: stage h + 1, then stage h + 2 if issued
+    if constexpr (LOAD) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads of stage h are done
+    workgroup_barrier();
+    read_w(r, next, scales_per_row_chunk(F), unit_s(F), wave, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  BDec d[2];
+#define FP4_LAST(G)                                                \
+  mfma_group<G>(acc, kb);                                          \
+  if constexpr (MORE) prep_slice<F, 0, G - 1>(ka, d, r, next, lane); \
+  __builtin_amdgcn_sched_barrier(0);
+  FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
+#undef FP4_LAST
+  if constexpr (MORE) prep_slice<F, 0, 7>(ka, d, r, next, lane);
 }
 
 template <int F, bool RAGGED>
@@ -381,36 +447,12 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
   read_w(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
   prep_all0<F>(ka, r, ring, lane);
 
-  for (int h = 0; h < H; ++h) {
-    const uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
-    const StageLoads L{&src, &lo, ring, h + 2, K, nchunk, wave, lane};
-    const bool load = h + 2 < H;
-    kstep<F, RAGGED, 0>(acc, ka, kb, r, stage, lane, L, load);
-    kstep<F, RAGGED, 1>(acc, kb, ka, r, stage, lane, L, load);
-    kstep<F, RAGGED, 2>(acc, ka, kb, r, stage, lane, L, load);
-    // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
-    mfma_group<0>(acc, kb);
-    __builtin_amdgcn_sched_barrier(0);
-    const bool more = h + 1 < H;
-    const uint8_t* next = ring + ((h + 1) % GM_RING) * GM_STAGE_BYTES;
-    if (more) {
-      // outstanding direct loads, oldest first: stage h + 1, then stage h + 2 if issued
-      if (load) wait_vmcnt<LPS>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads of stage h are done
-      workgroup_barrier();
-      read_w(r, next, scales_per_row_chunk(F), unit_s(F), wave, lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    BDec d[2];
-#define FP4_LAST(G)                                              \
-    mfma_group<G>(acc, kb);                                      \
-    if (more) prep_slice<F, 0, G - 1>(ka, d, r, next, lane);     \
-    __builtin_amdgcn_sched_barrier(0);
-    FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
-#undef FP4_LAST
-    if (more) prep_slice<F, 0, 7>(ka, d, r, next, lane);
-  }
+  // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
+  // body is compiled for each case, so the loop has no per-group branches.
+  int h = 0;
+  for (; h + 2 < H; ++h) stage_body<F, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
+  if (h + 1 < H) stage_body<F, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, h++, K, nchunk, wave, lane);
+  stage_body<F, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
 
   // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]
 #pragma unroll
