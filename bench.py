@@ -293,10 +293,14 @@ def main():
     ap.add_argument("--steps", type=int, default=11400)
     ap.add_argument("--warmup", type=int, default=1140)
     ap.add_argument("--workload", default="rocmfp4_dual_4096x4096_m1", choices=sorted(WORKLOADS))
-    ap.add_argument("--gemm-steps", type=int, default=30)
+    # The GEMM's clocks take tens of milliseconds of matrix-core load to settle (from ~245 to ~207 us per
+    # launch on MI355X); the default warmup covers that, so the timed launches measure steady state.
+    ap.add_argument("--gemm-steps", type=int, default=200)
+    ap.add_argument("--gemm-warmup", type=int, default=200)
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=50)
+    ap.add_argument("--sweep-warmup", type=int, default=20)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (scale factor for HBM byte counters)")
@@ -324,14 +328,14 @@ def main():
     gm = None
     if not args.no_gemm:
         t1 = time.time()
-        gm = bench_gemm(fp4, torch, synth, "rocmfp4_fast", args.gemm_steps, 3)
+        gm = bench_gemm(fp4, torch, synth, "rocmfp4_fast", args.gemm_steps, args.gemm_warmup)
         print(f"# gemm FAST M=2048: {gm['per_launch_s'] * 1e6:.1f} us/launch, {gm['tflops']:.1f} TFLOP/s "
               f"({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
 
     sw = None
     if not args.no_sweep:
         t2 = time.time()
-        sw = bench_decode_sweep(fp4, torch, synth, args.sweep_steps, 3)
+        sw = bench_decode_sweep(fp4, torch, synth, args.sweep_steps, args.sweep_warmup)
         print(f"# decode sweep NVFP4 M=1 (252 matrices, {sw['bytes'] / 1e9:.3f} GB): grouped "
               f"{sw['grouped'] * 1e6:.1f} us ({sw['bytes'] / sw['grouped'] / 1e9:.1f} GB/s), one launch per matrix "
               f"{sw['single'] * 1e6:.1f} us ({sw['bytes'] / sw['single'] / 1e9:.1f} GB/s) ({time.time() - t2:.1f}s)",
@@ -368,6 +372,7 @@ def main():
     if gm:
         line["gemm"] = {"workload": "rocmfp4_fast_prefill_m2048_k4096_n14336", "value": round(gm["tflops"], 2),
                         "unit": "TFLOP/s", "us_per_launch": round(gm["per_launch_s"] * 1e6, 2),
+                        "steps": args.gemm_steps, "warmup": args.gemm_warmup,
                         "roofline": {"bound": "mfma", "achieved": round(gm["tflops"], 2),
                                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                      "frac": round(gm["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),

@@ -171,10 +171,9 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
 // the scale loads (two for 16-weight groups, one for FAST; I = 11 issues nothing for FAST). Issued one at a
 // time between MFMAs so that no burst of vector-memory instructions holds up the wave.
 template <int F, int I>
-__device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
+__device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOffs& o, uint8_t* stage, int h, int K,
                                                 int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
-  uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
   if constexpr (I < GM_X_SLOTS) {
     const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
     const uint32_t xrow8 = (uint32_t)K * 16u;               // 8 rows of bf16
@@ -288,6 +287,45 @@ __device__ __forceinline__ void b_slice(BDec& d, u32x4& out, const WRegs& r, int
   }
 }
 
+// The same dequantization in eight smaller pieces (one per MFMA of a group of four), so that each runs
+// in the shadow of a single MFMA: scale and low lookup, high lookup, two pair converts each, then the
+// four "times scale, pack" steps.
+template <int F, int S, int SUB>
+__device__ __forceinline__ void b_sub(BDec& d, u32x4& out, const WRegs& r, int j, int kh) {
+  const u32x2 w0 = r.w[j][0], w1 = r.w[j][1];
+  if constexpr (SUB == 0) {
+    const int sigma = 4 * kh + S;
+    const int gi = (F == FAST) ? (sigma >> 1) : sigma;
+    const uint32_t sw = (gi & 4) ? r.sc[j][1] : r.sc[j][0];
+    d.sc = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * (gi & 3)), 0);
+    if constexpr (F == FAST) d.q0 = cb10_quad<false>((S & 1) ? w1[S >> 1] : w0[S >> 1]);
+    else if constexpr (F == DUAL) d.q0 = cb10_quad<(S & 1) != 0>(w0[S >> 1]);
+    else d.q0 = __builtin_amdgcn_perm(w1[S >> 1], w0[S >> 1], (S & 1) ? 0x07060302u : 0x05040100u);
+  } else if constexpr (SUB == 1) {
+    if constexpr (F == FAST) d.q1 = cb10_quad<true>((S & 1) ? w1[S >> 1] : w0[S >> 1]);
+    else if constexpr (F == DUAL) d.q1 = cb10_quad<(S & 1) != 0>(w1[S >> 1]);
+  } else if constexpr (SUB == 2) {
+    if constexpr (F == NVFP4) {
+      d.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 0);
+      d.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 1);
+    } else {
+      d.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q0, 1.0f, false);
+      d.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q0, 1.0f, true);
+    }
+  } else if constexpr (SUB == 3) {
+    if constexpr (F == NVFP4) {
+      d.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 2);
+      d.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 3);
+    } else {
+      d.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q1, 1.0f, false);
+      d.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q1, 1.0f, true);
+    }
+  } else {
+    constexpr int e = SUB - 4;
+    out[e] = pack_bf16x2(d.p[e][0] * d.sc, d.p[e][1] * d.sc);
+  }
+}
+
 // x fragment i (rows 32 i .. 32 i + 31) of k-step S: segment sigma = 4 kh + S of the lane's row.
 template <int S>
 __device__ __forceinline__ bf16x8 a_frag(const uint8_t* stage, int lane, int i) {
@@ -310,6 +348,11 @@ __device__ __forceinline__ void prep_slice(KOps& nx, BDec (&d)[2], const WRegs& 
   b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2, kh);
 }
 
+template <int G, int J>
+__device__ __forceinline__ void mfma_one(f32x16 (&acc)[8][2], const KOps& k) {
+  acc[G][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], __builtin_bit_cast(bf16x8, k.b[J]), acc[G][J], 0, 0, 0);
+}
+
 template <int G>
 __device__ __forceinline__ void mfma_group(f32x16 (&acc)[8][2], const KOps& k) {
   const bf16x8 b0 = __builtin_bit_cast(bf16x8, k.b[0]), b1 = __builtin_bit_cast(bf16x8, k.b[1]);
@@ -322,6 +365,7 @@ struct StageLoads {
   const GemmSrc* src;
   const LoadOffs* o;
   uint8_t* ring;
+  uint8_t* dst;  // ring slot of stage h
   int h, K, nchunk, wave, lane;
 };
 
@@ -332,7 +376,7 @@ __device__ __forceinline__ void issue_part(const StageLoads& L) {
   if constexpr (RAGGED) {
     if constexpr (S == 0 && G == 1) issue_stage<F, true>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
   } else {
-    if constexpr (S < 3 && (G & 1)) issue_stage_one<F, 4 * S + (G >> 1)>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave);
+    if constexpr (S < 3 && (G & 1)) issue_stage_one<F, 4 * S + (G >> 1)>(*L.src, *L.o, L.dst, L.h, L.K, L.nchunk, L.wave);
   }
 }
 
@@ -344,10 +388,15 @@ template <int F, bool RAGGED, int S, bool LOAD>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[8][2], const KOps& cur, KOps& nx, const WRegs& r,
                                       const uint8_t* stage, int lane, const StageLoads& L) {
   BDec d[2];
-#define FP4_GROUP(G)                                   \
-  mfma_group<G>(acc, cur);                             \
-  prep_slice<F, S + 1, G>(nx, d, r, stage, lane);      \
-  if constexpr (LOAD) issue_part<F, RAGGED, S, G>(L);  \
+  const int kh = lane >> 5;
+#define FP4_GROUP(G)                                                      \
+  mfma_one<G, 0>(acc, cur);                                               \
+  nx.a[G] = a_frag<S + 1>(stage, lane, G);                                \
+  b_sub<F, S + 1, (2 * (G)) & 7>(d[(G) >> 2], nx.b[(G) >> 2], r, (G) >> 2, kh); \
+  __builtin_amdgcn_sched_barrier(0);                                      \
+  mfma_one<G, 1>(acc, cur);                                               \
+  b_sub<F, S + 1, (2 * (G) + 1) & 7>(d[(G) >> 2], nx.b[(G) >> 2], r, (G) >> 2, kh); \
+  if constexpr (LOAD) issue_part<F, RAGGED, S, G>(L);                     \
   __builtin_amdgcn_sched_barrier(0);
   FP4_GROUP(0) FP4_GROUP(1) FP4_GROUP(2) FP4_GROUP(3) FP4_GROUP(4) FP4_GROUP(5) FP4_GROUP(6) FP4_GROUP(7)
 #undef FP4_GROUP
@@ -365,21 +414,25 @@ __device__ __forceinline__ void prep_all0(KOps& k, const WRegs& r, const uint8_t
 }
 
 // Stage h of the K loop (see the kernel). LOAD: the stage issues stage h + 2's loads; MORE: there is a
-// stage h + 1, whose k-step 0 operands this stage prepares into ka.
-template <int F, bool RAGGED, bool LOAD, bool MORE>
+// stage h + 1, whose k-step 0 operands this stage prepares into ka. SLOT = h % 3 when known at compile
+// time (the ring offsets are then constants), else -1.
+template <int F, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1>
 __device__ __forceinline__ void stage_body(f32x16 (&acc)[8][2], KOps& ka, KOps& kb, WRegs& r, const GemmSrc& src,
                                            const LoadOffs& lo, uint8_t* ring, int h, int K, int nchunk, int wave,
                                            int lane) {
   constexpr int LPS = gm_loads_per_stage(F);
-  const uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
-  const StageLoads L{&src, &lo, ring, h + 2, K, nchunk, wave, lane};
+  const int s0 = SLOT >= 0 ? SLOT : h % GM_RING;
+  const int s1 = SLOT >= 0 ? (SLOT + 1) % GM_RING : (s0 == GM_RING - 1 ? 0 : s0 + 1);
+  const int s2 = SLOT >= 0 ? (SLOT + 2) % GM_RING : (s1 == GM_RING - 1 ? 0 : s1 + 1);
+  const uint8_t* stage = ring + s0 * GM_STAGE_BYTES;
+  const StageLoads L{&src, &lo, ring, ring + s2 * GM_STAGE_BYTES, h + 2, K, nchunk, wave, lane};
   kstep<F, RAGGED, 0, LOAD>(acc, ka, kb, r, stage, lane, L);
   kstep<F, RAGGED, 1, LOAD>(acc, kb, ka, r, stage, lane, L);
   kstep<F, RAGGED, 2, LOAD>(acc, ka, kb, r, stage, lane, L);
   // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
   mfma_group<0>(acc, kb);
   __builtin_amdgcn_sched_barrier(0);
-  const uint8_t* next = ring + ((h + 1) % GM_RING) * GM_STAGE_BYTES;
+  const uint8_t* next = ring + s1 * GM_STAGE_BYTES;
   if constexpr (MORE) {
     // outstanding direct loads, oldest first: stage h + 1, then stage h + 2 if issued
     if constexpr (LOAD) wait_vmcnt<LPS>();
@@ -390,13 +443,26 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[8][2], KOps& ka, KOps& 
   }
   __builtin_amdgcn_sched_barrier(0);
   BDec d[2];
-#define FP4_LAST(G)                                                \
-  mfma_group<G>(acc, kb);                                          \
-  if constexpr (MORE) prep_slice<F, 0, G - 1>(ka, d, r, next, lane); \
+  const int kh = lane >> 5;
+  // MFMA groups 1-7 of k-step 3 carry the preparation of stage h + 1's k-step 0 (its pieces 0-6 here,
+  // piece 7 after the loop body)
+#define FP4_LAST(G)                                                                                   \
+  mfma_one<G, 0>(acc, kb);                                                                            \
+  if constexpr (MORE) {                                                                               \
+    ka.a[G - 1] = a_frag<0>(next, lane, G - 1);                                                       \
+    b_sub<F, 0, (2 * (G - 1)) & 7>(d[(G - 1) >> 2], ka.b[(G - 1) >> 2], r, (G - 1) >> 2, kh);         \
+  }                                                                                                   \
+  __builtin_amdgcn_sched_barrier(0);                                                                  \
+  mfma_one<G, 1>(acc, kb);                                                                            \
+  if constexpr (MORE) b_sub<F, 0, (2 * (G - 1) + 1) & 7>(d[(G - 1) >> 2], ka.b[(G - 1) >> 2], r, (G - 1) >> 2, kh); \
   __builtin_amdgcn_sched_barrier(0);
   FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
 #undef FP4_LAST
-  if constexpr (MORE) prep_slice<F, 0, 7>(ka, d, r, next, lane);
+  if constexpr (MORE) {
+    ka.a[7] = a_frag<0>(next, lane, 7);
+    b_sub<F, 0, 6>(d[1], ka.b[1], r, 1, kh);
+    b_sub<F, 0, 7>(d[1], ka.b[1], r, 1, kh);
+  }
 }
 
 template <int F, bool RAGGED>
@@ -450,6 +516,12 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
   // body is compiled for each case, so the loop has no per-group branches.
   int h = 0;
+  // three stages per iteration (the ring period), so that every ring offset is a constant
+  for (; h + 4 < H; h += 3) {
+    stage_body<F, RAGGED, true, true, 0>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
+    stage_body<F, RAGGED, true, true, 1>(acc, ka, kb, r, src, lo, ring, h + 1, K, nchunk, wave, lane);
+    stage_body<F, RAGGED, true, true, 2>(acc, ka, kb, r, src, lo, ring, h + 2, K, nchunk, wave, lane);
+  }
   for (; h + 2 < H; ++h) stage_body<F, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
   if (h + 1 < H) stage_body<F, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, h++, K, nchunk, wave, lane);
   stage_body<F, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
