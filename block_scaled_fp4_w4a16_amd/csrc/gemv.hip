@@ -254,9 +254,12 @@ struct GemvItem {
   int pad;
 };
 
+// start[i] is item i's first workgroup (INT_MAX for unused entries); the starts sit together ahead of the
+// items so that a workgroup finds its matrix from two wide scalar loads.
 template <int MAXI>
 struct GemvBatch {
   int count;
+  int start[MAXI];
   GemvItem it[MAXI];
 };
 
@@ -272,8 +275,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch,
   // this workgroup's matrix (a uniform search over at most MAXI starts)
   int item = 0;
 #pragma unroll
-  for (int i = 1; i < MAXI; ++i)
-    if (i < batch.count && (int)blockIdx.x >= batch.it[i].wg0) item = i;
+  for (int i = 1; i < MAXI; ++i) item += (int)blockIdx.x >= batch.start[i] ? 1 : 0;  // starts ascend
   const GemvItem& it = batch.it[item];
   const uint8_t* __restrict__ qp = it.q;
   const uint8_t* __restrict__ sp = it.s;
@@ -565,12 +567,16 @@ struct GemvLaunch {
 };
 
 // Picks the wave count of a launch: the most (up to 16, and up to wmax) that give every wave at least
-// two K chunks and keep the whole grid resident at once (one round of workgroups).
+// two K chunks and, for M > 1, keep the whole grid resident at once (one round of workgroups).
 template <class L>
 static int pick_waves(int nwg, int min_chunks, int M, int wmax) {
   const int cus = device_cus();
   int W = 16;
-  while (W > 1 && (W > wmax || min_chunks < 2 * W || (int64_t)nwg > (int64_t)L::resident(W, M) * cus)) W >>= 1;
+  // M = 1 (single-batch kernels, high occupancy): the most waves that keep two chunks per wave, even when
+  // the grid then takes a second round (a wave working through more chunks costs more than the round).
+  const bool fit = M > 1;
+  while (W > 1 && (W > wmax || min_chunks < 2 * W || (fit && (int64_t)nwg > (int64_t)L::resident(W, M) * cus)))
+    W >>= 1;
   if (const char* e = getenv("FP4_GEMV_WAVES")) {  // tuning override, read at each call
     if (atoi(e) > 0 && atoi(e) <= 16) W = atoi(e);
   }
@@ -590,11 +596,13 @@ static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     GemvItem& it = b.it[i];
     it.nchunk = (it.K + CHUNK_K - 1) / CHUNK_K;
     it.wg0 = nwg;
+    b.start[i] = nwg;
     const int ntiles = (it.N + TILE_N - 1) / TILE_N;
     nwg += (ntiles + T - 1) / T;
     min_chunks = min_chunks < it.nchunk ? min_chunks : it.nchunk;
     max_chunks = max_chunks > it.nchunk ? max_chunks : it.nchunk;
   }
+  for (int i = b.count; i < MAXI; ++i) b.start[i] = 0x7fffffff;
   // Batches of two chunk slots when the wave count that would be picked leaves at most two chunks per
   // wave (no load slots that read nothing), else four.
   const int wmax = (M > 4) ? 8 : 16;  // keep the staged x (W * U * M * 256 B) inside the LDS
@@ -745,6 +753,17 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   return fp4_launch_status();
 }
 
+template <int MAXI>
+static void fill_batch(GemvBatch<MAXI>& b, int count, const fp4_gemv_item* items) {
+  b.count = count;
+  for (int i = 0; i < count; ++i) {
+    const fp4_gemv_item& it = items[i];
+    b.it[i] = GemvItem{(const uint8_t*)it.q, (const uint8_t*)it.s, (const uint16_t*)it.x_bf16, it.y, (int)it.N,
+                       (int)it.K, 0, 0, it.global_scale, 0};
+  }
+  for (int i = count; i < MAXI; ++i) b.it[i] = GemvItem{};
+}
+
 extern "C" int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items, void* stream) {
   if (!fp4_valid_format(fmt)) return -1;
   if (M < 0) return -2;
@@ -758,15 +777,16 @@ extern "C" int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_
     const int rc = check_item(fmt, M, it.N, it.K, it.q, it.s, it.x_bf16, it.y);
     if (rc) return rc;
   }
-  GemvBatch<FP4_GEMV_MAX_ITEMS> b;
-  b.count = count;
-  for (int i = 0; i < count; ++i) {
-    const fp4_gemv_item& it = items[i];
-    b.it[i] = GemvItem{(const uint8_t*)it.q, (const uint8_t*)it.s, (const uint16_t*)it.x_bf16, it.y, (int)it.N,
-                       (int)it.K, 0, 0, it.global_scale, 0};
+  // a launch of up to 4 matrices passes a 4-entry table (a smaller kernel-argument block), else 32
+  if (count <= 4) {
+    GemvBatch<4> b;
+    fill_batch(b, count, items);
+    dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
+  } else {
+    GemvBatch<FP4_GEMV_MAX_ITEMS> b;
+    fill_batch(b, count, items);
+    dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
   }
-  for (int i = count; i < FP4_GEMV_MAX_ITEMS; ++i) b.it[i] = GemvItem{};
-  dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
   return fp4_launch_status();
 }
 

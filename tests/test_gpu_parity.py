@@ -166,6 +166,34 @@ def test_gemv_batched_matches_oracle(fmt, m):
         assert torch.all(buf[:32] == 12345.0) and torch.all(buf[32 + m * n:] == 12345.0)
 
 
+@pytest.mark.parametrize("count", [1, 2, 3, 4])
+def test_gemv_batched_small_counts(count):
+    # launches of up to four matrices pass a smaller item table; each output against the oracle, and a
+    # single item bitwise equal to the single-matrix entry point (same kernel and wave count)
+    fmt, m = "rocmfp4_dual", 1
+    shapes = [(80, 384), (37, 160), (256, 4096), (16, 32)][:count]
+    _announce("gemv-batched-small", fmt, m, shapes)
+    items, cases = [], []
+    for i, (n, k) in enumerate(shapes):
+        w, packed = gc.make_case(fmt, n, k, cfg=61, mat=i)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=61, mat=i)
+        x = gc.x_tensor(x_bits)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        items.append((pw.q, pw.s, pw.global_scale, x, y, n, k))
+        cases.append((packed, pw, x, x_bits, y, n, k))
+    fp4.w4a16_gemv_batched(fmt, m, items)
+    torch.cuda.synchronize()
+    for packed, pw, x, x_bits, y, n, k in cases:
+        gc.check_product(fmt, packed, x_bits, y, label=f"batched-small {count} {n}x{k}")
+    if count == 1:
+        packed, pw, x, x_bits, y, n, k = cases[0]
+        y1 = torch.empty_like(y)
+        fp4.w4a16_gemv(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y1)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y)
+
+
 def test_gemv_batched_many_items_and_repeatability():
     # the full item count; every item a different matrix; outputs bitwise repeatable
     fmt, m = "nvfp4", 2
