@@ -154,7 +154,8 @@ template <int U, bool WRAP = false>
 __device__ __forceinline__ uint32_t x_piece_off(int p, int M, int K, int c0, int W, int nchunk) {
   const int pieces = U * M * 16;
   if constexpr (WRAP) p = p % pieces;
-  const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
+  // (with one chunk slot every valid piece is in slot 0: no division)
+  const int u = U == 1 ? 0 : p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
   const int c = c0 + u * W;
   const int k = c * CHUNK_K + 8 * qq;
   return (p < pieces && c < nchunk && k < K) ? (uint32_t)(m * K + k) * 2u : OOB;
@@ -177,7 +178,7 @@ __device__ __forceinline__ void stage_x_commit(uint8_t* xs, const XStage<U, MX>&
   for (int i = 0; i < XStage<U, MX>::NX; ++i) {
     const int p = WRAP ? (64 * i + lane) % pieces : 64 * i + lane;
     if (WRAP || p < pieces) {
-      const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
+      const int u = U == 1 ? 0 : p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
       const int dst = (u * 4 * M + m) * 64 + (block32(F) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
                                                            : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
       if constexpr (block32(F)) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
