@@ -426,8 +426,8 @@ __device__ __forceinline__ void decode_scaled(const WeightRegs<F>& w, bf16x8 (&b
 
 // Dynamic LDS: [W waves][4 lane groups][M rows][64 B] of staged x (one chunk per wave); after the K loop
 // the same space holds the cross-wave reduction buffer [W][T][MB][64 lanes][4] floats.
-template <int F, int MB, int T>
-__global__ __launch_bounds__(512) void midm_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
+template <int F, int MB, int T, int WMAX = 8>
+__global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                                    const uint16_t* __restrict__ x, float* __restrict__ y, int M,
                                                    int N, int K, int ntiles, int nchunk, float gscale) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -671,17 +671,17 @@ static int check_item(int fmt, int64_t M, int64_t N, int64_t K, const void* q, c
   return 0;
 }
 
-template <int F, int MB, int T>
+template <int F, int MB, int T, int WMAX = 8>
 static void launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                         int M, int N, int K, float g) {
   const int ntiles = (N + TILE_N - 1) / TILE_N, nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
   const size_t lds = stage > red ? stage : red;
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&midm_kernel<F, MB, T>),
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&midm_kernel<F, MB, T, WMAX>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((midm_kernel<F, MB, T>), dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, M, N, K,
-                     ntiles, nchunk, g);
+  hipLaunchKernelGGL((midm_kernel<F, MB, T, WMAX>), dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, M, N,
+                     K, ntiles, nchunk, g);
 }
 
 template <int F, int MB>
@@ -692,14 +692,22 @@ static void dispatch_midm_mb(int M, hipStream_t st, const uint8_t* q, const uint
   // workgroups per CU; not with four 16-row blocks of x, where the registers would not suffice.
   const int T = (MB <= 3 && ntiles >= 2 * 2 * 256) ? 2 : 1;
   const int nwg = (ntiles + T - 1) / T;
-  // Waves per workgroup: the most (up to 8; the staged x of 8 waves at M = 64 fills 128 KiB of LDS)
-  // that give every wave at least two chunks and keep the grid resident at once (16 waves per CU
-  // with two 16-row blocks of x and one tile, 8 otherwise, at this kernel's register use).
+  // Waves per workgroup: the most that give every wave at least two chunks and keep the grid resident at
+  // once (16 waves per CU with two 16-row blocks of x and one tile, 8 otherwise, at this kernel's register
+  // use). Up to 16 with one block of x and one tile (the kernel then fits 128 VGPRs; the staged x of 16 waves
+  // is at most 64 KiB), else up to 8 (the staged x of 8 waves at M = 64 fills 128 KiB of LDS).
   const int resident = (MB <= 2 && T == 1 ? 16 : 8) * 256;
-  int W = 8;
+  const int wmax = (MB == 1 && T == 1) ? 16 : 8;
+  int W = wmax;
   while (W > 1 && (nchunk < 2 * W || nwg * W > resident)) W >>= 1;
   if (const char* e = getenv("FP4_MIDM_WAVES")) {  // tuning override, read at each call
-    if (atoi(e) > 0 && atoi(e) <= 8) W = atoi(e);
+    if (atoi(e) > 0 && atoi(e) <= wmax) W = atoi(e);
+  }
+  if constexpr (MB == 1) {
+    if (T == 1 && W > 8) {
+      launch_midm<F, 1, 1, 16>(W, st, q, s, x, y, M, N, K, g);
+      return;
+    }
   }
   if constexpr (MB <= 3) {
     if (T == 2) {
