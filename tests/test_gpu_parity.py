@@ -282,6 +282,22 @@ def test_gemm_shapes(fmt, m):
 
 
 @pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("k", [512, 640, 1152])
+def test_gemm_multi_tile(fmt, k):
+    # 2 x 3 output tiles with ragged last ones; K = 512, 640, 1152 give 8, 10 and 18 stages, which take the
+    # stage loop's three-stage iterations, its single-stage remainder and the two peeled last stages
+    m, n = 300, 600
+    _announce("gemm-multi", fmt, m, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=57, mat=k)
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.activations(m, k, cfg=57, mat=k + 1)
+    y = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    gc.check_product(fmt, packed, x_bits, y, label=f"gemm-multi {fmt} M={m} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
 def test_gemm_identity_returns_weights_exactly(fmt):
     # x = I (M = K) gives y = W32^T exactly
     n, k = 96, 256
