@@ -18,6 +18,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
     # no packed FP32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the GEMV and mid-M kernels take their leading 8 arguments (at most 12 dwords) in preloaded
+    # scalar registers, so that a wave's first loads do not wait on the kernel-argument memory
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -267,29 +267,23 @@ struct GemvBatch {
 // Dynamic LDS: [W waves][U chunks][4 lane groups][M rows][64 B] of staged x, then the
 // cross-wave reduction buffer [W][T][64 lanes][4] floats.
 // MC > 0 fixes M = MC at compile time (the x address arithmetic then reduces to shifts and masks);
-// MC = 0 takes M from the argument (at most MX). ONE: every wave's chunks fit in one batch
-// (nchunk <= U * W for every matrix of the launch), so there is no next batch to prefetch.
-template <int F, int T, int RU, int U, int MX, int MAXI, int MC, bool ONE>
-__global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch, int m_arg) {
+// MC = 0 takes M from mw (at most MX). mw = M | W << 8, W = waves per workgroup. ONE: every wave's
+// chunks fit in one batch (nchunk <= U * W for every matrix of the launch), so there is no next batch
+// to prefetch. wg0 is the matrix's first workgroup.
+template <int F, int T, int RU, int U, int MX, int MC, bool ONE>
+__device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
+                                          const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K,
+                                          float gscale, int wg0, int mw) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int M = MC > 0 ? MC : m_arg;
-  // this workgroup's matrix (a uniform search over at most MAXI starts)
-  int item = 0;
-#pragma unroll
-  for (int i = 1; i < MAXI; ++i) item += (int)blockIdx.x >= batch.start[i] ? 1 : 0;  // starts ascend
-  const GemvItem& it = batch.it[item];
-  const uint8_t* __restrict__ qp = it.q;
-  const uint8_t* __restrict__ sp = it.s;
-  const uint16_t* __restrict__ x = it.x;
-  float* __restrict__ y = it.y;
-  const int N = it.N, K = it.K, nchunk = it.nchunk;
-  const float gscale = it.g;
+  const int M = MC > 0 ? MC : (mw & 0xff);
+  const int W = mw >> 8;
+  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const int ntiles = (N + TILE_N - 1) / TILE_N;
 
-  const int lane = threadIdx.x & 63, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar branches
   const int n = lane & 15, g = lane >> 4, m = lane & 15;
-  const int tile0 = ((int)blockIdx.x - it.wg0) * T;
+  const int tile0 = ((int)blockIdx.x - wg0) * T;
   const int tiles_here = min(T, ntiles - tile0);
   Srcs src;
   src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
@@ -369,7 +363,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch,
   }
   __syncthreads();
   const int total = T * 64 * 4;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+  for (int e = threadIdx.x; e < total; e += W * 64) {
     const int t = e / 256, l = (e >> 2) & 63, r = e & 3;
     const int mrow = 4 * (l >> 4) + r;
     const int col = (tile0 + t) * TILE_N + (l & 15);
@@ -379,6 +373,33 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvBatch<MAXI> batch,
       y[(int64_t)mrow * N + col] = sum * gscale;
     }
   }
+}
+
+// Entry points. Both take their leading arguments in scalar registers that the library is built to
+// preload at wave start, so a wave does not first wait on the kernel-argument memory; W comes in mw, so
+// no dispatch-packet field is read either.
+// One matrix: everything the body needs is preloaded.
+template <int F, int T, int RU, int U, int MX, int MC, bool ONE>
+__global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                                                    int N, int K, float g, int mw) {
+  gemv_body<F, T, RU, U, MX, MC, ONE>(q, s, x, y, N, K, g, 0, mw);
+}
+
+// Several matrices: with at most 4 the starts of matrices 1..3 are preloaded (INT_MAX where unused), so
+// the workgroup's matrix is known at once and its fields take one read of the argument memory; with
+// more the starts are searched in the GemvBatch.
+template <int F, int T, int RU, int U, int MX, int MAXI, int MC, bool ONE>
+__global__ __launch_bounds__(1024) void gemv_group_kernel(int st1, int st2, int st3, int mw, const GemvBatch<MAXI> batch) {
+  const int b = (int)blockIdx.x;
+  int item = 0;
+  if constexpr (MAXI <= 4) {
+    item = (b >= st1 ? 1 : 0) + (b >= st2 ? 1 : 0) + (b >= st3 ? 1 : 0);
+  } else {
+#pragma unroll
+    for (int i = 1; i < MAXI; ++i) item += b >= batch.start[i] ? 1 : 0;  // starts ascend
+  }
+  const GemvItem& it = batch.it[item];
+  gemv_body<F, T, RU, U, MX, MC, ONE>(it.q, it.s, it.x, it.y, it.N, it.K, it.g, it.wg0, mw);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -428,10 +449,12 @@ __device__ __forceinline__ void decode_scaled(const WeightRegs<F>& w, bf16x8 (&b
 // the same space holds the cross-wave reduction buffer [W][T][MB][64 lanes][4] floats.
 template <int F, int MB, int T, int WMAX = 8>
 __global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
-                                                   const uint16_t* __restrict__ x, float* __restrict__ y, int M,
-                                                   int N, int K, int ntiles, int nchunk, float gscale) {
+                                                   const uint16_t* __restrict__ x, float* __restrict__ y, int N,
+                                                   int K, float gscale, int mw) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int lane = threadIdx.x & 63, W = blockDim.x >> 6;
+  const int M = mw & 0xff, W = mw >> 8;
+  const int ntiles = (N + TILE_N - 1) / TILE_N, nchunk = (K + CHUNK_K - 1) / CHUNK_K;
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4, m16 = lane & 15;
   const int tile0 = blockIdx.x * T;
@@ -503,7 +526,7 @@ __global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restri
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(mine + (size_t)(t * MB + mb) * 256) = acc[t][mb];
   __syncthreads();
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+  for (int e = threadIdx.x; e < total; e += W * 64) {
     const int t = e / (MB * 256), mb = (e / 256) % MB, l = (e >> 2) & 63, r = e & 3;
     const int mrow = mb * 16 + 4 * (l >> 4) + r;
     const int col = (tile0 + t) * TILE_N + (l & 15);
@@ -540,7 +563,10 @@ static int resident_per_cu(const void* k, int W, size_t lds) {
 
 template <int F, int T, int RU, int U, int MX, int MAXI, int MC, bool ONE = false>
 struct GemvLaunch {
-  static const void* fn() { return reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX, MAXI, MC, ONE>); }
+  static const void* fn() {
+    if constexpr (MAXI == 1) return reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX, MC, ONE>);
+    else return reinterpret_cast<const void*>(&gemv_group_kernel<F, T, RU, U, MX, MAXI, MC, ONE>);
+  }
   static size_t lds(int W, int M) { return (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float); }
   // workgroups resident per CU for W = 1, 2, 4, 8, 16 at this M (computed once per M class)
   static int resident(int W, int M) {
@@ -563,7 +589,16 @@ struct GemvLaunch {
   }
   static void launch(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
     attr();
-    hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX, MAXI, MC, ONE>), dim3(nwg), dim3(64 * W), lds(W, M), st, b, M);
+    if constexpr (MAXI == 1) {
+      const GemvItem& i0 = b.it[0];
+      hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX, MC, ONE>), dim3(nwg), dim3(64 * W), lds(W, M), st, i0.q, i0.s,
+                         i0.x, i0.y, i0.N, i0.K, i0.g, M | (W << 8));
+    } else {
+      const int inf = 0x7fffffff;
+      hipLaunchKernelGGL((gemv_group_kernel<F, T, RU, U, MX, MAXI, MC, ONE>), dim3(nwg), dim3(64 * W), lds(W, M), st,
+                         MAXI > 1 ? b.start[1 % MAXI] : inf, MAXI > 2 ? b.start[2 % MAXI] : inf,
+                         MAXI > 3 ? b.start[3 % MAXI] : inf, M | (W << 8), b);
+    }
   }
 };
 
@@ -674,14 +709,14 @@ static int check_item(int fmt, int64_t M, int64_t N, int64_t K, const void* q, c
 template <int F, int MB, int T, int WMAX = 8>
 static void launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                         int M, int N, int K, float g) {
-  const int ntiles = (N + TILE_N - 1) / TILE_N, nchunk = (K + CHUNK_K - 1) / CHUNK_K;
+  const int ntiles = (N + TILE_N - 1) / TILE_N;
   const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
   const size_t lds = stage > red ? stage : red;
   static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&midm_kernel<F, MB, T, WMAX>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((midm_kernel<F, MB, T, WMAX>), dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, M, N,
-                     K, ntiles, nchunk, g);
+  hipLaunchKernelGGL((midm_kernel<F, MB, T, WMAX>), dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, N, K,
+                     g, M | (W << 8));
 }
 
 template <int F, int MB>
@@ -786,8 +821,13 @@ extern "C" int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_
     const int rc = check_item(fmt, M, it.N, it.K, it.q, it.s, it.x_bf16, it.y);
     if (rc) return rc;
   }
-  // a launch of up to 4 matrices passes a 4-entry table (a smaller kernel-argument block), else 32
-  if (count <= 4) {
+  // one matrix takes the one-matrix kernel (all of its arguments preloaded); up to 4 pass a 4-entry table
+  // (a smaller kernel-argument block, starts preloaded), else 32
+  if (count == 1) {
+    GemvBatch<1> b;
+    fill_batch(b, count, items);
+    dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
+  } else if (count <= 4) {
     GemvBatch<4> b;
     fill_batch(b, count, items);
     dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
