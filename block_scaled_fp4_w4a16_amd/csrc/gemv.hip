@@ -27,6 +27,9 @@ struct WeightRegs {
 // descriptor here covers less than 2^31 bytes).
 constexpr uint32_t OOB = 0x80000000u;
 
+// dynamic LDS a workgroup may ask for (all of a CU's LDS)
+constexpr int GEMV_LDS_MAX = 160 * 1024;
+
 struct Srcs {
   __amdgpu_buffer_rsrc_t q, s, x;
 };
@@ -375,6 +378,135 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
   }
 }
 
+// Long-K single-row product (M = 1, one tile per workgroup, more than 4 chunks per wave): each wave
+// keeps D chunks in flight in a ring of D weight-register slots, refilling a slot as soon as its chunk
+// has been multiplied, so a wave holds D units of registers (not two batches of them) and more waves fit
+// on a CU. The workgroup's whole x (nchunk * 256 B) is staged in LDS once, in fragment order, behind a
+// single barrier; the waves' first weight loads are issued before it.
+template <int F, int D>
+__device__ __forceinline__ void gemv_ring_body(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
+                                               const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K,
+                                               float gscale, int mw) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int XMAX = 4;  // x pieces per thread: 16 * nchunk <= XMAX * 64 * W (the host keeps nchunk <= 256, W = 16)
+  const int W = mw >> 8;
+  const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int tile = (int)blockIdx.x;
+  Srcs src;
+  src.q = make_rsrc(qp + (int64_t)tile * nchunk * UNIT_Q, (uint32_t)(nchunk * UNIT_Q));
+  src.s = make_rsrc(sp + (int64_t)tile * nchunk * unit_s(F), (uint32_t)(nchunk * unit_s(F)));
+  src.x = make_rsrc(x, (uint32_t)K * 2u);
+  uint8_t* xs = smem;                                               // [nchunk][4 lane groups][64 B]
+  float* red = reinterpret_cast<float*>(smem + (size_t)nchunk * 256);  // [W][64 lanes][4]
+  const int pieces = nchunk * 16;
+  const int nthr = W * 64;
+
+  // x pieces of the workgroup (16 B = 8 consecutive k each), first
+  u32x4 xv[XMAX];
+#pragma unroll
+  for (int i = 0; i < XMAX; ++i) {
+    const int p = (int)threadIdx.x + i * nthr;
+    const uint32_t off = (p < pieces && 8 * p < K) ? (uint32_t)p * 16u : OOB;
+    xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, off, 0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's chunks: wave + j W, j = 0 .. nper - 1; the first D go out now
+  const int nper = wave < nchunk ? (nchunk - wave + W - 1) / W : 0;
+  WeightRegs<F> wr[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    const int c = wave + s * W;
+    const bool ok = c < nchunk;
+    load_unit<F>(wr[s], src, ok ? (uint32_t)c * UNIT_Q + lane * 16 : OOB,
+                 ok ? (uint32_t)c * unit_s(F) + n * (unit_s(F) / TILE_N) : OOB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // x into LDS in fragment order (piece p: chunk p / 16, piece qq = p % 16 of it)
+#pragma unroll
+  for (int i = 0; i < XMAX; ++i) {
+    const int p = (int)threadIdx.x + i * nthr;
+    if (p < pieces) {
+      const int c = p >> 4, qq = p & 15;
+      const int dst = c * 256 + (block32(F) ? ((qq & 3) * 64 + 16 * (qq >> 2)) : (2 * (qq & 1) * 64 + 8 * (qq >> 1)));
+      if constexpr (block32(F)) {
+        *reinterpret_cast<u32x4*>(xs + dst) = xv[i];
+      } else {
+        *reinterpret_cast<u32x2*>(xs + dst) = u32x2{xv[i][0], xv[i][1]};
+        *reinterpret_cast<u32x2*>(xs + dst + 64) = u32x2{xv[i][2], xv[i][3]};
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's x stores are done
+  asm volatile("s_barrier" ::: "memory");
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < nper; base += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int j = base + s;
+      const int c = wave + j * W;
+      if (j < nper) {
+        uint32_t xa[16];
+        const u32x4* xsrc = reinterpret_cast<const u32x4*>(xs + c * 256 + g * 64);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 w4 = xsrc[v];
+          xa[4 * v] = w4[0]; xa[4 * v + 1] = w4[1]; xa[4 * v + 2] = w4[2]; xa[4 * v + 3] = w4[3];
+        }
+        unit_mac<F, 1>(acc, wr[s], xa);
+      }
+      // refill the slot, on every path (past this wave's last chunk the load reads nothing): every
+      // path then has the same loads in flight, so the waits stay counted instead of draining
+      const bool more = j + D < nper;
+      const uint32_t cn = (uint32_t)(c + D * W);
+      load_unit<F>(wr[s], src, more ? cn * UNIT_Q + lane * 16 : OOB,
+                   more ? cn * unit_s(F) + n * (unit_s(F) / TILE_N) : OOB);
+    }
+  }
+
+  // cross-wave reduction in a fixed order, then y = g * sum
+  *reinterpret_cast<f32x4*>(red + ((size_t)wave * 64 + lane) * 4) = acc;
+  __syncthreads();
+  const int total = 64 * 4;
+  for (int e = threadIdx.x; e < total; e += nthr) {
+    const int l = (e >> 2) & 63, r = e & 3;
+    const int mrow = 4 * (l >> 4) + r;
+    const int col = tile * TILE_N + (l & 15);
+    if (mrow < 1 && col < N) {
+      float sum = 0.f;
+      for (int w = 0; w < W; ++w) sum += red[(size_t)w * total + e];
+      y[col] = sum * gscale;
+    }
+  }
+}
+
+template <int F, int D>
+__global__ __launch_bounds__(1024) void gemv_ring_kernel(const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                                                         int N, int K, float g, int mw) {
+  gemv_ring_body<F, D>(q, s, x, y, N, K, g, mw);
+}
+
+// The ring kernel runs with 16 waves, so one thread stages at most 4 of the 16 * nchunk x pieces: up to
+// RING_MAX_CHUNKS = 256 chunks (K <= 32768), 64 KiB of staged x.
+constexpr int RING_WAVES = 16;
+constexpr int RING_MAX_CHUNKS = 256;
+
+template <int F, int D>
+struct RingLaunch {
+  static const void* fn() { return reinterpret_cast<const void*>(&gemv_ring_kernel<F, D>); }
+  static size_t lds(int W, int nchunk) { return (size_t)nchunk * 256 + (size_t)W * 64 * 4 * sizeof(float); }
+  static void launch(const GemvItem& it, int W, hipStream_t st) {
+    static const bool ok = hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
+    (void)ok;
+    const int nchunk = (it.K + CHUNK_K - 1) / CHUNK_K, ntiles = (it.N + TILE_N - 1) / TILE_N;
+    hipLaunchKernelGGL((gemv_ring_kernel<F, D>), dim3(ntiles), dim3(64 * W), lds(W, nchunk), st, it.q, it.s, it.x, it.y,
+                       it.N, it.K, it.g, 1 | (W << 8));
+  }
+};
+
 // Entry points. Both take their leading arguments in scalar registers that the library is built to
 // preload at wave start, so a wave does not first wait on the kernel-argument memory; W comes in mw, so
 // no dispatch-packet field is read either.
@@ -538,8 +670,6 @@ __global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restri
   }
 }
 
-constexpr int GEMV_LDS_MAX = 160 * 1024;
-
 // Compute units of the current device (queried once per device).
 static int device_cus() {
   static std::atomic<int> cus[64];
@@ -656,7 +786,13 @@ static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     }
     using L2 = GemvLaunch<F, 1, 1, 2, 1, MAXI, 1>;
     const char* one = getenv("FP4_GEMV_ONE");  // tuning override: 0 = batch loop with prefetch
-    if (one && atoi(one) == 0 && U <= 2) L2::launch(b, nwg, W, M, st);
+    // Long K on a grid of at least two workgroups per CU: the ring kernel (3 chunks in flight per wave,
+    // so two 16-wave workgroups fit on a CU where the batch loop fits one).
+    const char* rg = getenv("FP4_GEMV_RING");   // tuning override: 0 = never, 1 = whenever it applies
+    const bool ring_fits = MAXI == 1 && max_chunks <= RING_MAX_CHUNKS;
+    const bool ring = ring_fits && (rg ? atoi(rg) == 1 : (U > 4 && nwg >= 2 * device_cus()));
+    if (ring) RingLaunch<F, 3>::launch(b.it[0], RING_WAVES, st);
+    else if (one && atoi(one) == 0 && U <= 2) L2::launch(b, nwg, W, M, st);
     else if (one && atoi(one) == 0 && U <= 4) L4::launch(b, nwg, W, M, st);
     else if (U <= 2) O2::launch(b, nwg, W, M, st);
     else if (U == 3) O3::launch(b, nwg, W, M, st);

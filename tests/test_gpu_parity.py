@@ -91,6 +91,41 @@ def test_gemv_small_shapes(fmt, m):
 
 
 @pytest.mark.parametrize("fmt", gc.FMTS_ALL)
+def test_gemv_ring_forced(fmt, monkeypatch):
+    # The long-K ring kernel (M = 1), switched on for small grids: a ragged last tile, a partial last
+    # 128-wide chunk, chunk counts that are not a multiple of 16 waves x 3 slots, waves with no chunk at
+    # all (10 chunks for 16 waves), and the largest K it takes (256 chunks, 64 KiB of staged x).
+    monkeypatch.setenv("FP4_GEMV_RING", "1")
+    for n, k in [(200, 8288), (37, 1184), (16, 32768)]:
+        _announce("gemv-ring", fmt, n, k)
+        w, packed = gc.make_case(fmt, n, k, cfg=59, mat=n)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(1, k, cfg=59, mat=k)
+        y = torch.full((1, n), float("nan"), device="cuda")
+        fp4.w4a16_gemv(fmt, 1, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+        torch.cuda.synchronize()
+        gc.check_product(fmt, packed, x_bits, y, label=f"gemv-ring {fmt} {n}x{k}")
+
+
+def test_gemv_ring_full_grid():
+    # a grid of 512 tiles with 65 chunks per row: the shape rule itself picks the ring kernel on a
+    # 256-CU GPU; sampled rows are checked
+    fmt, n, k = "nvfp4", 8192, 8320
+    _announce("gemv-ring-grid", fmt, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=58)
+    del w
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.activations(1, k, cfg=58, mat=1)
+    y = torch.full((1, n), float("nan"), device="cuda")
+    fp4.w4a16_gemv(fmt, 1, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    rng = np.random.default_rng(58)
+    cols = np.unique(np.concatenate([[0, 15, 16, n - 17, n - 1], rng.choice(n, 91, replace=False)]))
+    gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"gemv-ring-grid {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 def test_gemv_one_hot_returns_weight_columns_exactly(fmt):
     # x = e_k gives y[:, n] = W32[n, k] exactly (a single product, times g)
     n, k = 64, 256
