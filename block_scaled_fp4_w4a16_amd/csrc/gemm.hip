@@ -18,6 +18,8 @@
 #include "common.h"
 #include "launch.h"
 #include "fp4w4a16.h"
+#include <atomic>
+#include <stdlib.h>
 
 namespace fp4 {
 
@@ -30,9 +32,12 @@ constexpr int GM_S_BYTES = GM_WAVES * 4 * 128;        // per wave: 4 tiles x sca
 constexpr int GM_STAGE_BYTES = GM_X_BYTES + GM_W_BYTES + GM_S_BYTES;  // 42 KiB
 constexpr int GM_RING = 3;
 constexpr int GM_LDS = GM_RING * GM_STAGE_BYTES;      // 126 KiB
-constexpr int GM_X_SLOTS = GM_BM * 8 / GM_THREADS;    // 16-byte x slots per thread per stage (8)
-// vector-memory instructions per thread per stage: x slots, 2 weight loads, scale loads (512 or 256 bytes)
-__host__ __device__ constexpr int gm_loads_per_stage(int f) { return GM_X_SLOTS + 2 + (f == FAST ? 1 : 2); }
+// A tile has 32 MI rows of x: MI = 8 (256 rows) or 6 (192 rows, the shorter tiles that even out the last
+// round of a grid). A thread then has MI 16-byte x slots per stage (each 8 rows below the previous).
+// Vector-memory instructions per thread per stage: x slots, 2 weight loads, scale loads (512 or 256 bytes).
+__host__ __device__ constexpr int gm_loads_per_stage(int f, int mi) { return mi + 2 + (f == FAST ? 1 : 2); }
+constexpr int GM_SHORT_ROWS = 192;   // rows of an MI = 6 tile
+constexpr int GM_SHORT_BANDS = 8;    // MI = 6 tiles cover rows 0 .. 8 * 192 - 1 of their columns
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -63,13 +68,13 @@ __device__ __forceinline__ int x_swizzle(int row) { return (row & 7) ^ ((row >> 
 
 // x of stage h: global -> LDS ring slot, one 16-byte direct load per slot. Slot S of the stage holds row
 // S / 8, physical segment S % 8 = sigma ^ x_swizzle(row).
-template <int F, bool RAGGED>
+template <int F, int MI, bool RAGGED>
 __device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h, int K, int wave, int lane) {
   const int c = h >> 1, hh = h & 1;
   uint8_t* base = ring + (h % GM_RING) * GM_STAGE_BYTES;
 #pragma unroll
-  for (int i = 0; i < GM_X_SLOTS; ++i) {
-    const int first = (wave * GM_X_SLOTS + i) * 64;          // first slot of this instruction (uniform)
+  for (int i = 0; i < MI; ++i) {
+    const int first = (wave * MI + i) * 64;                  // first slot of this instruction (uniform)
     const int slot = first + lane;
     const int row = slot >> 3, sigma = (slot & 7) ^ x_swizzle(row);
     const int k = stage_k<F>(c, hh, sigma);
@@ -121,9 +126,9 @@ __host__ __device__ constexpr int seg_k(int sigma) {   // stage_k without the ch
   return (F == FAST) ? 32 * (sigma >> 1) + 8 * (sigma & 1) : 16 * sigma;
 }
 
-template <int F>
+template <int F, int MI>
 __device__ __forceinline__ void load_offsets(LoadOffs& o, int K, int nchunk, int wave, int lane) {
-  const int row = wave * 64 + (lane >> 3);              // slot 0 of the lane: row of x in the tile
+  const int row = wave * 8 * MI + (lane >> 3);          // slot 0 of the lane: row of x in the tile
   const int sigma = (lane & 7) ^ x_swizzle(row);
   o.x[0] = (uint32_t)(row * K + seg_k<F>(sigma)) * 2u;
   o.x[1] = (uint32_t)(row * K + seg_k<F>(sigma ^ 1)) * 2u;
@@ -135,7 +140,7 @@ __device__ __forceinline__ void load_offsets(LoadOffs& o, int K, int nchunk, int
 // Part P (0, 1, 2) of stage h's direct loads (K a multiple of 128): x slots 3P .. 3P + 2 (the last part
 // has two), then in part 1 the weight pieces and in part 2 the scale bytes. Spreading a stage's loads over
 // three k-steps keeps each burst of vector-memory issue short.
-template <int F, int P>
+template <int F, int MI, int P>
 __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
                                                  int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
@@ -143,8 +148,8 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
   const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
   const uint32_t xrow8 = (uint32_t)K * 16u;                 // 8 rows of bf16
 #pragma unroll
-  for (int i = 3 * P; i < 3 * P + 3 && i < GM_X_SLOTS; ++i) {
-    const int first = (wave * GM_X_SLOTS + i) * 64;
+  for (int i = 3 * P; i < 3 * P + 3 && i < MI; ++i) {
+    const int first = (wave * MI + i) * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(stage + first * 16), 16,
                                              o.x[i & 1] + i * xrow8, xs, 0, 0);
   }
@@ -167,27 +172,27 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
   }
 }
 
-// Load I (0 .. 11) of stage h's direct loads (K a multiple of 128): x slots 0-7, the two weight pieces, then
-// the scale loads (two for 16-weight groups, one for FAST; I = 11 issues nothing for FAST). Issued one at a
-// time between MFMAs so that no burst of vector-memory instructions holds up the wave.
-template <int F, int I>
+// Load I (0 .. MI + 3) of stage h's direct loads (K a multiple of 128): x slots 0 .. MI - 1, the two weight
+// pieces, then the scale loads (two for 16-weight groups, one for FAST). Issued one or two at a time between
+// MFMAs so that no burst of vector-memory instructions holds up the wave.
+template <int F, int MI, int I>
 __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOffs& o, uint8_t* stage, int h, int K,
                                                 int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
-  if constexpr (I < GM_X_SLOTS) {
+  if constexpr (I < MI) {
     const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
     const uint32_t xrow8 = (uint32_t)K * 16u;               // 8 rows of bf16
-    const int first = (wave * GM_X_SLOTS + I) * 64;
+    const int first = (wave * MI + I) * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(stage + first * 16), 16,
                                              o.x[I & 1] + I * xrow8, xs, 0, 0);
-  } else if constexpr (I < GM_X_SLOTS + 2) {
-    constexpr int part = I - GM_X_SLOTS;
+  } else if constexpr (I < MI + 2) {
+    constexpr int part = I - MI;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16,
         o.w + (uint32_t)(part * 2 * nchunk * UNIT_Q), c * UNIT_Q + 512 * hh, 0, 0);
   } else {
     constexpr int us = unit_s(F), parts = 4 * (us / 4) / 64;
-    constexpr int part = I - GM_X_SLOTS - 2;
+    constexpr int part = I - MI - 2;
     if constexpr (part < parts)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256),
@@ -196,16 +201,16 @@ __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOf
 }
 
 // All of stage h's loads: the three parts, or the per-slot path when K is ragged.
-template <int F, bool RAGGED>
+template <int F, int MI, bool RAGGED>
 __device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
                                             int nchunk, int wave, int lane) {
   if constexpr (RAGGED) {
-    issue_x<F, RAGGED>(src, ring, h, K, wave, lane);
+    issue_x<F, MI, RAGGED>(src, ring, h, K, wave, lane);
     issue_w<F>(src, ring, h, nchunk, wave, lane);
   } else {
-    issue_stage_part<F, 0>(src, o, ring, h, K, nchunk, wave);
-    issue_stage_part<F, 1>(src, o, ring, h, K, nchunk, wave);
-    issue_stage_part<F, 2>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 0>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 1>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 2>(src, o, ring, h, K, nchunk, wave);
   }
 }
 
@@ -335,26 +340,47 @@ __device__ __forceinline__ bf16x8 a_frag(const uint8_t* stage, int lane, int i) 
 }
 
 // Operands of one k-step, double-buffered across k-steps.
+template <int MI>
 struct KOps {
-  bf16x8 a[8];
+  bf16x8 a[MI];
   u32x4 b[2];
 };
 
-// The next k-step's operands, prepared in eight slices; slice g runs between MFMA groups g and g + 1.
-template <int F, int S, int G>
-__device__ __forceinline__ void prep_slice(KOps& nx, BDec (&d)[2], const WRegs& r, const uint8_t* stage, int lane) {
+// The next k-step's operands, prepared in eight slices (x fragment G when the tile has it, and quarter G % 4
+// of B operand G / 4).
+template <int F, int MI, int S, int G>
+__device__ __forceinline__ void prep_slice(KOps<MI>& nx, BDec (&d)[2], const WRegs& r, const uint8_t* stage, int lane) {
   const int kh = lane >> 5;
-  nx.a[G] = a_frag<S>(stage, lane, G);
+  if constexpr (G < MI) nx.a[G] = a_frag<S>(stage, lane, G);
   b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2, kh);
 }
 
-template <int G, int J>
-__device__ __forceinline__ void mfma_one(f32x16 (&acc)[8][2], const KOps& k) {
+// The B dequantization pieces (b_sub) that run after MFMA slot SLOT (0 .. 2 MI - 1) of a k-step. With 16
+// MFMAs (MI = 8) slot s takes piece s % 8 of operand s / 8; with 12 (MI = 6) each operand's six slots take
+// pieces 0, 1, 2, 3, then 4 and 5, then 6 and 7.
+template <int F, int MI, int S, int SLOT>
+__device__ __forceinline__ void b_slot(BDec (&d)[2], u32x4 (&b)[2], const WRegs& r, int kh) {
+  if constexpr (MI == 8) {
+    constexpr int t = SLOT >> 3, q = SLOT & 7;
+    b_sub<F, S, q>(d[t], b[t], r, t, kh);
+  } else {
+    constexpr int t = SLOT / 6, q = SLOT % 6;
+    if constexpr (q < 4) {
+      b_sub<F, S, q>(d[t], b[t], r, t, kh);
+    } else {
+      b_sub<F, S, 4 + 2 * (q - 4)>(d[t], b[t], r, t, kh);
+      b_sub<F, S, 5 + 2 * (q - 4)>(d[t], b[t], r, t, kh);
+    }
+  }
+}
+
+template <int MI, int G, int J>
+__device__ __forceinline__ void mfma_one(f32x16 (&acc)[MI][2], const KOps<MI>& k) {
   acc[G][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], __builtin_bit_cast(bf16x8, k.b[J]), acc[G][J], 0, 0, 0);
 }
 
-template <int G>
-__device__ __forceinline__ void mfma_group(f32x16 (&acc)[8][2], const KOps& k) {
+template <int MI, int G>
+__device__ __forceinline__ void mfma_group(f32x16 (&acc)[MI][2], const KOps<MI>& k) {
   const bf16x8 b0 = __builtin_bit_cast(bf16x8, k.b[0]), b1 = __builtin_bit_cast(bf16x8, k.b[1]);
   acc[G][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], b0, acc[G][0], 0, 0, 0);
   acc[G][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], b1, acc[G][1], 0, 0, 0);
@@ -369,68 +395,82 @@ struct StageLoads {
   int h, K, nchunk, wave, lane;
 };
 
-// Loads issued after MFMA group G of k-step S: with K ragged, all of the stage at once (k-step 0, group 1);
-// otherwise load 4 S + G / 2 of the stage after each odd group of k-steps 0-2.
-template <int F, bool RAGGED, int S, int G>
-__device__ __forceinline__ void issue_part(const StageLoads& L) {
-  if constexpr (RAGGED) {
-    if constexpr (S == 0 && G == 1) issue_stage<F, true>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
-  } else {
-    if constexpr (S < 3 && (G & 1)) issue_stage_one<F, 4 * S + (G >> 1)>(*L.src, *L.o, L.dst, L.h, L.K, L.nchunk, L.wave);
+// The loads of issue point Q (0 .. 3 MI / 2 - 1): load I goes out at point I * points / loads, so the
+// stage's loads spread evenly (one per point with MI = 8, where the points and the loads are both 12; the
+// first point takes two with MI = 6).
+template <int F, int MI, int Q, int I = 0>
+__device__ __forceinline__ void issue_point(const StageLoads& L) {
+  constexpr int NL = gm_loads_per_stage(F, MI), NP = 3 * MI / 2;
+  if constexpr (I < NL) {
+    if constexpr (I * NP / NL == Q) issue_stage_one<F, MI, I>(*L.src, *L.o, L.dst, L.h, L.K, L.nchunk, L.wave);
+    issue_point<F, MI, Q, I + 1>(L);
   }
 }
 
-// One k-step of the wave's 256 x 64 tile: 8 groups of 2 MFMAs (x fragment G against both column tiles),
-// each followed by one slice of the next k-step's operands (k-step S + 1 of this stage); after group 1
-// the wave issues part S of the loads of two stages ahead. Scheduling fences keep that order, so the
-// slices' LDS reads and VALU work and the loads run while the matrix core is busy.
-template <int F, bool RAGGED, int S, bool LOAD>
-__device__ __forceinline__ void kstep(f32x16 (&acc)[8][2], const KOps& cur, KOps& nx, const WRegs& r,
+// Loads issued after MFMA group G of k-step S: with K ragged, all of the stage at once (k-step 0, group 1);
+// otherwise issue point S MI / 2 + G / 2 after each odd group of k-steps 0-2.
+template <int F, int MI, bool RAGGED, int S, int G>
+__device__ __forceinline__ void issue_part(const StageLoads& L) {
+  if constexpr (RAGGED) {
+    if constexpr (S == 0 && G == 1) issue_stage<F, MI, true>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
+  } else {
+    if constexpr (S < 3 && (G & 1)) issue_point<F, MI, S * (MI / 2) + (G >> 1)>(L);
+  }
+}
+
+// One k-step of the wave's 32 MI x 64 tile: MI groups of 2 MFMAs (x fragment G against both column
+// tiles), each MFMA followed by its share of the next k-step's operands (k-step S + 1 of this stage); after
+// odd groups of k-steps 0-2 the wave issues loads of two stages ahead. Scheduling fences keep that order,
+// so the LDS reads, VALU work and loads run while the matrix core is busy.
+template <int F, int MI, bool RAGGED, int S, bool LOAD>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur, KOps<MI>& nx, const WRegs& r,
                                       const uint8_t* stage, int lane, const StageLoads& L) {
   BDec d[2];
   const int kh = lane >> 5;
 #define FP4_GROUP(G)                                                      \
-  mfma_one<G, 0>(acc, cur);                                               \
-  nx.a[G] = a_frag<S + 1>(stage, lane, G);                                \
-  b_sub<F, S + 1, (2 * (G)) & 7>(d[(G) >> 2], nx.b[(G) >> 2], r, (G) >> 2, kh); \
-  __builtin_amdgcn_sched_barrier(0);                                      \
-  mfma_one<G, 1>(acc, cur);                                               \
-  b_sub<F, S + 1, (2 * (G) + 1) & 7>(d[(G) >> 2], nx.b[(G) >> 2], r, (G) >> 2, kh); \
-  if constexpr (LOAD) issue_part<F, RAGGED, S, G>(L);                     \
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr ((G) < MI) {                                               \
+    mfma_one<MI, G, 0>(acc, cur);                                         \
+    nx.a[G] = a_frag<S + 1>(stage, lane, G);                              \
+    b_slot<F, MI, S + 1, 2 * (G)>(d, nx.b, r, kh);                        \
+    __builtin_amdgcn_sched_barrier(0);                                    \
+    mfma_one<MI, G, 1>(acc, cur);                                         \
+    b_slot<F, MI, S + 1, 2 * (G) + 1>(d, nx.b, r, kh);                    \
+    if constexpr (LOAD) issue_part<F, MI, RAGGED, S, G>(L);               \
+    __builtin_amdgcn_sched_barrier(0);                                    \
+  }
   FP4_GROUP(0) FP4_GROUP(1) FP4_GROUP(2) FP4_GROUP(3) FP4_GROUP(4) FP4_GROUP(5) FP4_GROUP(6) FP4_GROUP(7)
 #undef FP4_GROUP
 }
 
 // Operands of k-step 0 of a stage, all at once (the first stage only; later stages prepare them inside
 // the previous stage's last k-step).
-template <int F>
-__device__ __forceinline__ void prep_all0(KOps& k, const WRegs& r, const uint8_t* stage, int lane) {
+template <int F, int MI>
+__device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uint8_t* stage, int lane) {
   BDec d[2];
-  prep_slice<F, 0, 0>(k, d, r, stage, lane); prep_slice<F, 0, 1>(k, d, r, stage, lane);
-  prep_slice<F, 0, 2>(k, d, r, stage, lane); prep_slice<F, 0, 3>(k, d, r, stage, lane);
-  prep_slice<F, 0, 4>(k, d, r, stage, lane); prep_slice<F, 0, 5>(k, d, r, stage, lane);
-  prep_slice<F, 0, 6>(k, d, r, stage, lane); prep_slice<F, 0, 7>(k, d, r, stage, lane);
+  prep_slice<F, MI, 0, 0>(k, d, r, stage, lane); prep_slice<F, MI, 0, 1>(k, d, r, stage, lane);
+  prep_slice<F, MI, 0, 2>(k, d, r, stage, lane); prep_slice<F, MI, 0, 3>(k, d, r, stage, lane);
+  prep_slice<F, MI, 0, 4>(k, d, r, stage, lane); prep_slice<F, MI, 0, 5>(k, d, r, stage, lane);
+  prep_slice<F, MI, 0, 6>(k, d, r, stage, lane); prep_slice<F, MI, 0, 7>(k, d, r, stage, lane);
 }
 
 // Stage h of the K loop (see the kernel). LOAD: the stage issues stage h + 2's loads; MORE: there is a
 // stage h + 1, whose k-step 0 operands this stage prepares into ka. SLOT = h % 3 when known at compile
 // time (the ring offsets are then constants), else -1.
-template <int F, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1>
-__device__ __forceinline__ void stage_body(f32x16 (&acc)[8][2], KOps& ka, KOps& kb, WRegs& r, const GemmSrc& src,
-                                           const LoadOffs& lo, uint8_t* ring, int h, int K, int nchunk, int wave,
-                                           int lane) {
-  constexpr int LPS = gm_loads_per_stage(F);
+template <int F, int MI, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1>
+__device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, KOps<MI>& kb, WRegs& r,
+                                           const GemmSrc& src, const LoadOffs& lo, uint8_t* ring, int h, int K,
+                                           int nchunk, int wave, int lane) {
+  constexpr int LPS = gm_loads_per_stage(F, MI);
   const int s0 = SLOT >= 0 ? SLOT : h % GM_RING;
   const int s1 = SLOT >= 0 ? (SLOT + 1) % GM_RING : (s0 == GM_RING - 1 ? 0 : s0 + 1);
   const int s2 = SLOT >= 0 ? (SLOT + 2) % GM_RING : (s1 == GM_RING - 1 ? 0 : s1 + 1);
   const uint8_t* stage = ring + s0 * GM_STAGE_BYTES;
   const StageLoads L{&src, &lo, ring, ring + s2 * GM_STAGE_BYTES, h + 2, K, nchunk, wave, lane};
-  kstep<F, RAGGED, 0, LOAD>(acc, ka, kb, r, stage, lane, L);
-  kstep<F, RAGGED, 1, LOAD>(acc, kb, ka, r, stage, lane, L);
-  kstep<F, RAGGED, 2, LOAD>(acc, ka, kb, r, stage, lane, L);
+  kstep<F, MI, RAGGED, 0, LOAD>(acc, ka, kb, r, stage, lane, L);
+  kstep<F, MI, RAGGED, 1, LOAD>(acc, kb, ka, r, stage, lane, L);
+  kstep<F, MI, RAGGED, 2, LOAD>(acc, ka, kb, r, stage, lane, L);
   // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
-  mfma_group<0>(acc, kb);
+  mfma_group<MI, 0>(acc, kb);
   __builtin_amdgcn_sched_barrier(0);
   const uint8_t* next = ring + s1 * GM_STAGE_BYTES;
   if constexpr (MORE) {
@@ -444,54 +484,51 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[8][2], KOps& ka, KOps& 
   __builtin_amdgcn_sched_barrier(0);
   BDec d[2];
   const int kh = lane >> 5;
-  // MFMA groups 1-7 of k-step 3 carry the preparation of stage h + 1's k-step 0 (its pieces 0-6 here,
-  // piece 7 after the loop body)
-#define FP4_LAST(G)                                                                                   \
-  mfma_one<G, 0>(acc, kb);                                                                            \
-  if constexpr (MORE) {                                                                               \
-    ka.a[G - 1] = a_frag<0>(next, lane, G - 1);                                                       \
-    b_sub<F, 0, (2 * (G - 1)) & 7>(d[(G - 1) >> 2], ka.b[(G - 1) >> 2], r, (G - 1) >> 2, kh);         \
-  }                                                                                                   \
-  __builtin_amdgcn_sched_barrier(0);                                                                  \
-  mfma_one<G, 1>(acc, kb);                                                                            \
-  if constexpr (MORE) b_sub<F, 0, (2 * (G - 1) + 1) & 7>(d[(G - 1) >> 2], ka.b[(G - 1) >> 2], r, (G - 1) >> 2, kh); \
-  __builtin_amdgcn_sched_barrier(0);
+  // MFMA groups 1 .. MI - 1 of k-step 3 carry the preparation of stage h + 1's k-step 0 (the shares of
+  // groups 0 .. MI - 2 here, the last group's share after the loop body)
+#define FP4_LAST(G)                                                                \
+  if constexpr ((G) < MI) {                                                        \
+    mfma_one<MI, G, 0>(acc, kb);                                                   \
+    if constexpr (MORE) {                                                          \
+      ka.a[(G) - 1] = a_frag<0>(next, lane, (G) - 1);                              \
+      b_slot<F, MI, 0, 2 * ((G) - 1)>(d, ka.b, r, kh);                             \
+    }                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                             \
+    mfma_one<MI, G, 1>(acc, kb);                                                   \
+    if constexpr (MORE) b_slot<F, MI, 0, 2 * ((G) - 1) + 1>(d, ka.b, r, kh);       \
+    __builtin_amdgcn_sched_barrier(0);                                             \
+  }
   FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
 #undef FP4_LAST
   if constexpr (MORE) {
-    ka.a[7] = a_frag<0>(next, lane, 7);
-    b_sub<F, 0, 6>(d[1], ka.b[1], r, 1, kh);
-    b_sub<F, 0, 7>(d[1], ka.b[1], r, 1, kh);
+    ka.a[MI - 1] = a_frag<0>(next, lane, MI - 1);
+    b_slot<F, MI, 0, 2 * (MI - 1)>(d, ka.b, r, kh);
+    b_slot<F, MI, 0, 2 * (MI - 1) + 1>(d, ka.b, r, kh);
   }
 }
 
-template <int F, bool RAGGED>
-__global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restrict__ qp,
-                                                          const uint8_t* __restrict__ sp,
-                                                          const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                          int M, int N, int K, int nchunk, int tiles_m, float gscale) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+// One tile of y: rows m0 .. m0 + 32 MI - 1, columns n0 .. n0 + 255 (see the kernel).
+template <int F, int MI, bool RAGGED>
+__device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
+                                          const uint16_t* __restrict__ x, float* __restrict__ y, int M, int N, int K,
+                                          int nchunk, int m0, int n0, float gscale) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave: keeps descriptors scalar
-  // consecutive workgroups go to different XCDs (block b runs on XCD b % 8); with tiles_m = 8 the
-  // workgroups of one XCD share an x tile in its L2
-  const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
-  const int m0 = bm * GM_BM, n0 = bn * GM_BN;
   const int wrow0 = n0 + 64 * wave;            // this wave's 64 weight rows (4 tiles of 16)
   const int ntiles = (N + TILE_N - 1) / TILE_N;
 
   GemmSrc src;
-  const int mrows = min(M - m0, GM_BM);
+  const int mrows = min(M - m0, 32 * MI);
   src.x = make_rsrc(x + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
   const int tiles_here = max(0, min(ntiles - wrow0 / TILE_N, 4));
   src.q = make_rsrc(qp + (int64_t)(wrow0 / TILE_N) * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
   src.s = make_rsrc(sp + (int64_t)(wrow0 / TILE_N) * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
   LoadOffs lo;
-  load_offsets<F>(lo, K, nchunk, wave, lane);
+  load_offsets<F, MI>(lo, K, nchunk, wave, lane);
 
-  f32x16 acc[8][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
@@ -502,33 +539,33 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
   // at a barrier (every wave's share of stage h + 1 is then in LDS, and every wave is done reading stage
   // h), reads stage h + 1's packed weights and prepares its k-step 0 -- still between MFMAs.
   const int H = 2 * nchunk;
-  constexpr int LPS = gm_loads_per_stage(F);
-  issue_stage<F, RAGGED>(src, lo, ring, 0, K, nchunk, wave, lane);
-  if (1 < H) issue_stage<F, RAGGED>(src, lo, ring, 1, K, nchunk, wave, lane);
+  constexpr int LPS = gm_loads_per_stage(F, MI);
+  issue_stage<F, MI, RAGGED>(src, lo, ring, 0, K, nchunk, wave, lane);
+  if (1 < H) issue_stage<F, MI, RAGGED>(src, lo, ring, 1, K, nchunk, wave, lane);
   if (1 < H) wait_vmcnt<LPS>();
   else wait_vmcnt<0>();
   workgroup_barrier();
   WRegs r;
-  KOps ka, kb;
+  KOps<MI> ka, kb;
   read_w(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
-  prep_all0<F>(ka, r, ring, lane);
+  prep_all0<F, MI>(ka, r, ring, lane);
 
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
   // body is compiled for each case, so the loop has no per-group branches.
   int h = 0;
   // three stages per iteration (the ring period), so that every ring offset is a constant
   for (; h + 4 < H; h += 3) {
-    stage_body<F, RAGGED, true, true, 0>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
-    stage_body<F, RAGGED, true, true, 1>(acc, ka, kb, r, src, lo, ring, h + 1, K, nchunk, wave, lane);
-    stage_body<F, RAGGED, true, true, 2>(acc, ka, kb, r, src, lo, ring, h + 2, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 0>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 1>(acc, ka, kb, r, src, lo, ring, h + 1, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 2>(acc, ka, kb, r, src, lo, ring, h + 2, K, nchunk, wave, lane);
   }
-  for (; h + 2 < H; ++h) stage_body<F, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
-  if (h + 1 < H) stage_body<F, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, h++, K, nchunk, wave, lane);
-  stage_body<F, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
+  for (; h + 2 < H; ++h) stage_body<F, MI, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
+  if (h + 1 < H) stage_body<F, MI, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, h++, K, nchunk, wave, lane);
+  stage_body<F, MI, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
 
   // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -539,17 +576,82 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
       }
 }
 
+// Tiles. The first nbig workgroups take 256-row tiles, the rest (if any) 192-row tiles; the host picks the
+// split so that a grid of between one and two rounds of 256-row tiles becomes two rounds whose second is
+// made of the shorter tiles (the slowest CU then does 1.75 tiles of work, not 2).
+//  * 192-row tiles: rows 0 .. 1535 (8 bands) of column tiles 0 .. ns - 1; workgroup nbig + i takes band
+//    i % 8 and column tile i / 8.
+//  * 256-row tiles: first column tiles ns .. tiles_n - 1 over all tiles_m bands (band = i % tiles_m), then
+//    rows 1536 .. M - 1 (tiles_m - 6 bands) of column tiles 0 .. ns - 1.
+// With ns = 0 every tile is 256 rows: workgroup i takes band i % tiles_m and column tile i / tiles_m.
+// Block b runs on XCD b % 8, so with 8 bands the workgroups of one XCD share an x band in its L2.
+template <int F, bool RAGGED>
+__global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restrict__ qp,
+                                                          const uint8_t* __restrict__ sp,
+                                                          const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                          int M, int N, int K, int nchunk, int tiles_m, int ns,
+                                                          int nbig, float gscale) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  const int b = (int)blockIdx.x;
+  if (b < nbig) {
+    const int tiles_n = (N + GM_BN - 1) / GM_BN;
+    const int nwide = tiles_m * (tiles_n - ns);
+    int m0, n0;
+    if (b < nwide) {
+      m0 = (b % tiles_m) * GM_BM;
+      n0 = (ns + b / tiles_m) * GM_BN;
+    } else {
+      const int i = b - nwide, bands = tiles_m - GM_SHORT_BANDS * GM_SHORT_ROWS / GM_BM;
+      m0 = GM_SHORT_BANDS * GM_SHORT_ROWS + (i % bands) * GM_BM;
+      n0 = (i / bands) * GM_BN;
+    }
+    gemm_tile<F, 8, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, m0, n0, gscale);
+  } else {
+    const int i = b - nbig;
+    gemm_tile<F, 6, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, (i % GM_SHORT_BANDS) * GM_SHORT_ROWS,
+                            (i / GM_SHORT_BANDS) * GM_BN, gscale);
+  }
+}
+
+// Compute units of the current device (cached per device).
+static int gemm_device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 template <int F, bool RAGGED>
 static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
                           int N, int K, float g) {
   const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const int tiles_m = (M + GM_BM - 1) / GM_BM;
   const int tiles_n = (N + GM_BN - 1) / GM_BN;
+  // Between one and two rounds of 256-row tiles: 8 s columns' worth of rows 0 .. 1535 go to s = 8 ns
+  // 192-row tiles (3/4 of the work each), chosen so that the grid is two rounds (s = 4 (2 cus - U), at
+  // most every column tile), the second made of short tiles.
+  const int cus = gemm_device_cus();
+  const int64_t U = (int64_t)tiles_m * tiles_n;
+  int ns = 0;
+  if (M % GM_BM == 0 && M >= GM_SHORT_BANDS * GM_SHORT_ROWS && U > cus && U < 2 * cus) {
+    ns = (int)(4 * (2 * cus - U) / GM_SHORT_BANDS);
+    if (ns > tiles_n) ns = tiles_n;
+  }
+  if (const char* e = getenv("FP4_GEMM_SHORT")) {  // tuning override: 0 = 256-row tiles only
+    if (atoi(e) == 0) ns = 0;
+  }
+  const int nbig = (int)(U - (int64_t)(GM_SHORT_BANDS * GM_SHORT_ROWS / GM_BM) * ns);
+  const int grid = nbig + GM_SHORT_BANDS * ns;
   static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, GM_LDS) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(tiles_m * tiles_n), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M,
-                     N, K, nchunk, tiles_m, g);
+  hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K, nchunk,
+                     tiles_m, ns, nbig, g);
 }
 
 template <int F>

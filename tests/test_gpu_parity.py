@@ -333,6 +333,33 @@ def test_gemm_multi_tile(fmt, k):
 
 
 @pytest.mark.parametrize("fmt", gc.FMTS)
+def test_gemm_short_tiles(fmt, monkeypatch):
+    # 7 x 37 tiles of 256 x 256 are between one and two rounds on a 256-CU GPU, so rows 0-1535 of every
+    # column tile run as 192-row tiles (the rest as 256-row tiles); K = 672 is ragged. Sampled columns over
+    # all rows against the oracle, and the whole output against the launch with 256-row tiles only
+    # (the same products in the same order: bitwise equal).
+    m, n, k = 1792, 37 * 256, 672
+    _announce("gemm-short", fmt, m, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=61, mat=k)
+    del w
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.activations(m, k, cfg=61, mat=1)
+    x = gc.x_tensor(x_bits)
+    y = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    rng = np.random.default_rng(61)
+    cols = np.unique(np.concatenate([[0, 255, 256, 8191, 8192, n - 1], rng.choice(n, 40, replace=False)]))
+    gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"gemm-short {fmt}")
+    monkeypatch.setenv("FP4_GEMM_SHORT", "0")
+    y_plain = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_plain)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_plain)
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
 def test_gemm_identity_returns_weights_exactly(fmt):
     # x = I (M = K) gives y = W32^T exactly
     n, k = 96, 256
