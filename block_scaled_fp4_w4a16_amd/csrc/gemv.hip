@@ -359,6 +359,27 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
   }
 
   // cross-wave reduction in a fixed order, then y = g * sum
+  if constexpr (MC >= 1 && MC <= 4) {
+    // at most 4 x rows: the stored C rows 0 .. MC - 1 are elements 0 .. MC - 1 of lanes 0-15, so only
+    // they go through LDS: red[wave][t][r][16]
+    if (lane < 16) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < MC; ++r) red[((wave * T + t) * MC + r) * 16 + lane] = acc[t][r];
+    }
+    __syncthreads();
+    constexpr int per_wave = T * MC * 16;
+    if ((int)threadIdx.x < per_wave) {
+      const int e = threadIdx.x, t = e / (MC * 16), r = (e >> 4) % MC, col = (tile0 + t) * TILE_N + (e & 15);
+      if (col < N) {
+        float sum = 0.f;
+        for (int w = 0; w < W; ++w) sum += red[w * per_wave + e];
+        y[(int64_t)r * N + col] = sum * gscale;
+      }
+    }
+    return;
+  }
   float* mine = red + ((size_t)wave * T * 64 + lane) * 4;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -467,17 +488,14 @@ __device__ __forceinline__ void gemv_ring_body(const uint8_t* __restrict__ qp, c
     }
   }
 
-  // cross-wave reduction in a fixed order, then y = g * sum
-  *reinterpret_cast<f32x4*>(red + ((size_t)wave * 64 + lane) * 4) = acc;
+  // cross-wave reduction in a fixed order, then y = g * sum (only C row 0, lanes 0-15, is stored)
+  if (lane < 16) red[wave * 16 + lane] = acc[0];
   __syncthreads();
-  const int total = 64 * 4;
-  for (int e = threadIdx.x; e < total; e += nthr) {
-    const int l = (e >> 2) & 63, r = e & 3;
-    const int mrow = 4 * (l >> 4) + r;
-    const int col = tile * TILE_N + (l & 15);
-    if (mrow < 1 && col < N) {
+  if ((int)threadIdx.x < 16) {
+    const int col = tile * TILE_N + (int)threadIdx.x;
+    if (col < N) {
       float sum = 0.f;
-      for (int w = 0; w < W; ++w) sum += red[(size_t)w * total + e];
+      for (int w = 0; w < W; ++w) sum += red[w * 16 + (int)threadIdx.x];
       y[col] = sum * gscale;
     }
   }
