@@ -798,6 +798,8 @@ static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     using O3 = GemvLaunch<F, 1, 1, 3, 1, MAXI, 1, true>;
     using O4 = GemvLaunch<F, 1, 1, 4, 1, MAXI, 1, true>;
     int W = pick_waves<O4>(nwg, min_chunks, M, wmax);
+    // 8 waves of up to 4 chunks beat 16 waves of 2 (K = 4096: 3-10% faster, fewer waves to reduce)
+    if (W == 16 && (max_chunks + 7) / 8 <= 4 && !getenv("FP4_GEMV_WAVES")) W = 8;
     int U = (max_chunks + W - 1) / W;
     if (const char* e = getenv("FP4_GEMV_U")) {  // tuning override, read at each call
       if (atoi(e) >= 2 && atoi(e) <= 4 && atoi(e) * W >= max_chunks) U = atoi(e);
