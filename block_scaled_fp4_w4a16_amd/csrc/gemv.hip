@@ -1,4 +1,4 @@
-// Decode-shaped W4A16 product (1 <= M <= 16).
+// Decode-shaped W4A16 product (1 <= M <= 16), and the mid-M product (M <= 64) further down.
 //
 // One workgroup owns T consecutive 16-row tiles of W and the whole K range; its W waves
 // split the 128-wide K chunks (wave w takes chunks w, w + W, ...). Per chunk a lane loads
@@ -6,7 +6,8 @@
 // scale bytes, decodes to exact bf16 levels and issues one MFMA per scale group:
 //   A = x fragment (row m = lane % 16, zero for m >= M), B = unscaled levels, C = 0,
 // then folds the group scale into FP32: acc += scale * C. The waves' partial sums are
-// reduced through LDS in a fixed order, multiplied by the global scale and stored.
+// reduced through LDS in a fixed order, multiplied by the global scale and stored. Long K at M = 1
+// on large grids uses a variant that keeps a ring of chunks in flight per wave (gemv_ring_kernel).
 #include "common.h"
 #include "launch.h"
 #include "fp4w4a16.h"
@@ -258,8 +259,9 @@ struct GemvItem {
   int pad;
 };
 
-// start[i] is item i's first workgroup (INT_MAX for unused entries); the starts sit together ahead of the
-// items so that a workgroup finds its matrix from two wide scalar loads.
+// start[i] is item i's first workgroup (INT_MAX for unused entries). Launches of up to 4 matrices also
+// pass starts 1..3 as preloaded scalars; larger ones read them here, together ahead of the items, with
+// wide scalar loads.
 template <int MAXI>
 struct GemvBatch {
   int count;
@@ -268,7 +270,8 @@ struct GemvBatch {
 };
 
 // Dynamic LDS: [W waves][U chunks][4 lane groups][M rows][64 B] of staged x, then the
-// cross-wave reduction buffer [W][T][64 lanes][4] floats.
+// cross-wave reduction buffer: [W][T][64 lanes][4] floats, or with M <= 4 fixed at compile time only the
+// stored C rows, [W][T][M][16] floats.
 // MC > 0 fixes M = MC at compile time (the x address arithmetic then reduces to shifts and masks);
 // MC = 0 takes M from mw (at most MX). mw = M | W << 8, W = waves per workgroup. ONE: every wave's
 // chunks fit in one batch (nchunk <= U * W for every matrix of the launch), so there is no next batch
