@@ -298,6 +298,8 @@ def main():
     ap.add_argument("--gemm-steps", type=int, default=200)
     ap.add_argument("--gemm-warmup", type=int, default=200)
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-spec", action="store_true", help="skip the speculative-verify shapes (M = 1, 9, 16)")
+    ap.add_argument("--spec-steps", type=int, default=2000)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=50)
     ap.add_argument("--sweep-warmup", type=int, default=20)
@@ -331,6 +333,25 @@ def main():
         gm = bench_gemm(fp4, torch, synth, "rocmfp4_fast", args.gemm_steps, args.gemm_warmup)
         print(f"# gemm FAST M=2048: {gm['per_launch_s'] * 1e6:.1f} us/launch, {gm['tflops']:.1f} TFLOP/s "
               f"({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
+        t1 = time.time()
+        gm_nv = bench_gemm(fp4, torch, synth, "nvfp4", args.gemm_steps, args.gemm_warmup)
+        print(f"# gemm NVFP4 M=2048: {gm_nv['per_launch_s'] * 1e6:.1f} us/launch, {gm_nv['tflops']:.1f} TFLOP/s "
+              f"({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
+
+    spec = None
+    if not args.no_spec:
+        # speculative verify / small batch: gate- and down-shaped matrices at M = 1, 9 (1 token + 8 drafts), 16
+        t3 = time.time()
+        spec = {}
+        for fmt in ("nvfp4", "rocmfp4_dual"):
+            for shape in ("gate_9728x2560", "down_2560x9728"):
+                for m in (1, 9, 16):
+                    name = f"{fmt}_{shape}_m{m}"
+                    r = bench_gemv(fp4, torch, synth, name, args.spec_steps, args.spec_steps // 10)
+                    spec[name] = {"us_per_launch": round(r["per_launch_s"] * 1e6, 3), "GB/s": round(r["gbs"], 1),
+                                  "frac": round(r["gbs"] / HBM_PEAK_GBS, 4)}
+        print(f"# speculative-verify shapes: {len(spec)} workloads ({time.time() - t3:.1f}s)", file=sys.stderr,
+              flush=True)
 
     sw = None
     if not args.no_sweep:
@@ -376,7 +397,13 @@ def main():
                         "roofline": {"bound": "mfma", "achieved": round(gm["tflops"], 2),
                                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                      "frac": round(gm["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
-                                     "traffic": traffic_from_profiles("gemm.hip", "rocmfp4_fast_prefill_m2048")}}
+                                     "traffic": traffic_from_profiles("gemm.hip", "rocmfp4_fast_prefill_m2048")},
+                        "nvfp4": {"workload": "nvfp4_prefill_m2048_k4096_n14336", "value": round(gm_nv["tflops"], 2),
+                                  "us_per_launch": round(gm_nv["per_launch_s"] * 1e6, 2),
+                                  "frac": round(gm_nv["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}}
+    if spec:
+        line["spec_verify"] = {"workload": "speculative verify, gate 9728x2560 and down 2560x9728, M = 1, 9, 16",
+                               "unit": "GB/s of weight + scale bytes", "steps": args.spec_steps, "results": spec}
     if sw:
         gbs = sw["bytes"] / sw["grouped"] / 1e9
         line["decode_sweep"] = {
