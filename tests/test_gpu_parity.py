@@ -91,6 +91,22 @@ def test_gemv_small_shapes(fmt, m):
 
 
 @pytest.mark.parametrize("fmt", gc.FMTS_ALL)
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_gemv_long_k_batches(fmt, m):
+    # K = 8288: 65 chunks, the last partial, so each wave runs several batches of chunk slots with the next
+    # batch prefetched (the ring kernel is not picked at this grid size)
+    n, k = 40, 8288
+    _announce("gemv-long-k", fmt, m, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=64, mat=m)
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.activations(m, k, cfg=64, mat=k + m)
+    y = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_gemv(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    gc.check_product(fmt, packed, x_bits, y, label=f"gemv-long-k {fmt} M={m}")
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 def test_gemv_ring_forced(fmt, monkeypatch):
     # The long-K ring kernel (M = 1), switched on for small grids: a ragged last tile, a partial last
     # 128-wide chunk, chunk counts that are not a multiple of 16 waves x 3 slots, waves with no chunk at
