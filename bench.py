@@ -309,8 +309,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a design "
-                                   "note, not code (run with --gpus 1)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; sharding across GPUs is "
+                                   "described, not implemented (run with --gpus 1)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
