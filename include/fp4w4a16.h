@@ -149,8 +149,8 @@ int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const 
                  float global_scale, const void* x_bf16, float* y, void* stream);
 
 /*
- * Dequantize the kernel layout to FP32 W[N][K] (the pages' dequant-at-load, EdgeRock card
- * "Load on a CUDA GPU"): W = fl32(fl32(level*scale)*g), bit-exact. For checking and tools.
+ * Dequantize the kernel layout to FP32 W[N][K] (the pages' dequant-at-load, EdgeRock card,
+ * section on loading on a CUDA GPU): W = fl32(fl32(level*scale)*g), bit-exact. For checking and tools.
  */
 int fp4_dequant_f32(int fmt, int64_t N, int64_t K, const void* q, const void* s,
                     float global_scale, float* w, void* stream);

@@ -16,7 +16,7 @@
  *    beyond 9 s the level clips to 10; with s = 0 every level is 0;
  *  - E(c) = sum_i v_i * (|w_i| - L_i s)^2 accumulated in index order; (w - sign*L*s)^2
  *    equals (|w| - L*s)^2 exactly because rounding to nearest is symmetric;
- *  - "expand from the start, keep a strictly better candidate": candidates are visited
+ *  - the search widens outward from the start and keeps a strictly better candidate: candidates are visited
  *    at distance 0, 1, 2, ... from start, lower code first, and a candidate replaces the
  *    best only if its error is strictly smaller. This equals the lexicographic minimum
  *    of (E, |c - start|, c) over all 127 codes; nothing is pruned.

@@ -5,7 +5,7 @@ Sources:
   4-bit values with one FP8 E4M3 scale per 16 values and an FP32 global scale.
   The E2M1 and E4M3 value sets are the OCP microscaling / OCP FP8 definitions
   those names refer to.
-* ROCmFP4 design page (npu.ciru.ai "rocmwhy"), section 01 "values" and the
+* ROCmFP4 design page, section 01 (values) and the
   format comparison table: the Codebook10 grid 0, +-1, +-2, +-3, +-4, +-6, +-8,
   +-10, E2M1-derived with the outer magnitude retuned from 12 to 10; scales
   are unsigned E4M3 (UE4M3) and the search scores the finite candidates.
