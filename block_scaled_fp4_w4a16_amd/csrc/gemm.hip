@@ -331,12 +331,25 @@ __device__ __forceinline__ void b_sub(BDec& d, u32x4& out, const WRegs& r, int j
   }
 }
 
-// x fragment i (rows 32 i .. 32 i + 31) of k-step S: segment sigma = 4 kh + S of the lane's row.
-template <int S>
-__device__ __forceinline__ bf16x8 a_frag(const uint8_t* stage, int lane, int i) {
-  const int sigma = 4 * (lane >> 5) + S;
-  const int row = 32 * i + (lane & 31);
-  return *reinterpret_cast<const bf16x8*>(stage + row * GM_ROW_BYTES + 16 * (sigma ^ x_swizzle(row)));
+// Per-lane LDS offsets of x fragment 0 for each ring slot and k-step S: row r = lane % 32, segment
+// sigma = 4 kh + S, swizzled. Fragment i (rows 32 i + r) has r's swizzle (the swizzle reads bits 0-3 of
+// the row), so it sits a constant 32 rows further: reads need no per-fragment address arithmetic.
+struct XBase {
+  uint32_t v[GM_RING][4];
+};
+
+__device__ __forceinline__ void x_bases(XBase& xb, int lane) {
+  const int r = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int slot = 0; slot < GM_RING; ++slot)
+#pragma unroll
+    for (int S = 0; S < 4; ++S)
+      xb.v[slot][S] = (uint32_t)(slot * GM_STAGE_BYTES + r * GM_ROW_BYTES + 16 * ((4 * kh + S) ^ x_swizzle(r)));
+}
+
+// x fragment i (rows 32 i .. 32 i + 31) at per-lane offset `base` of fragment 0.
+__device__ __forceinline__ bf16x8 a_frag(const uint8_t* ring, uint32_t base, int i) {
+  return *reinterpret_cast<const bf16x8*>(ring + base + 32 * GM_ROW_BYTES * i);
 }
 
 // Operands of one k-step, double-buffered across k-steps.
@@ -349,9 +362,10 @@ struct KOps {
 // The next k-step's operands, prepared in eight slices (x fragment G when the tile has it, and quarter G % 4
 // of B operand G / 4).
 template <int F, int MI, int S, int G>
-__device__ __forceinline__ void prep_slice(KOps<MI>& nx, BDec (&d)[2], const WRegs& r, const uint8_t* stage, int lane) {
+__device__ __forceinline__ void prep_slice(KOps<MI>& nx, BDec (&d)[2], const WRegs& r, const uint8_t* ring,
+                                           uint32_t xbase, int lane) {
   const int kh = lane >> 5;
-  if constexpr (G < MI) nx.a[G] = a_frag<S>(stage, lane, G);
+  if constexpr (G < MI) nx.a[G] = a_frag(ring, xbase, G);
   b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2, kh);
 }
 
@@ -424,13 +438,13 @@ __device__ __forceinline__ void issue_part(const StageLoads& L) {
 // so the LDS reads, VALU work and loads run while the matrix core is busy.
 template <int F, int MI, bool RAGGED, int S, bool LOAD>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur, KOps<MI>& nx, const WRegs& r,
-                                      const uint8_t* stage, int lane, const StageLoads& L) {
+                                      const uint8_t* ring, const uint32_t (&xc)[4], int lane, const StageLoads& L) {
   BDec d[2];
   const int kh = lane >> 5;
 #define FP4_GROUP(G)                                                      \
   if constexpr ((G) < MI) {                                               \
     mfma_one<MI, G, 0>(acc, cur);                                         \
-    nx.a[G] = a_frag<S + 1>(stage, lane, G);                              \
+    nx.a[G] = a_frag(ring, xc[S + 1], G);                                 \
     b_slot<F, MI, S + 1, 2 * (G)>(d, nx.b, r, kh);                        \
     __builtin_amdgcn_sched_barrier(0);                                    \
     mfma_one<MI, G, 1>(acc, cur);                                         \
@@ -445,12 +459,12 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur,
 // Operands of k-step 0 of a stage, all at once (the first stage only; later stages prepare them inside
 // the previous stage's last k-step).
 template <int F, int MI>
-__device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uint8_t* stage, int lane) {
+__device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uint8_t* ring, uint32_t xb0, int lane) {
   BDec d[2];
-  prep_slice<F, MI, 0, 0>(k, d, r, stage, lane); prep_slice<F, MI, 0, 1>(k, d, r, stage, lane);
-  prep_slice<F, MI, 0, 2>(k, d, r, stage, lane); prep_slice<F, MI, 0, 3>(k, d, r, stage, lane);
-  prep_slice<F, MI, 0, 4>(k, d, r, stage, lane); prep_slice<F, MI, 0, 5>(k, d, r, stage, lane);
-  prep_slice<F, MI, 0, 6>(k, d, r, stage, lane); prep_slice<F, MI, 0, 7>(k, d, r, stage, lane);
+  prep_slice<F, MI, 0, 0>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 1>(k, d, r, ring, xb0, lane);
+  prep_slice<F, MI, 0, 2>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 3>(k, d, r, ring, xb0, lane);
+  prep_slice<F, MI, 0, 4>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 5>(k, d, r, ring, xb0, lane);
+  prep_slice<F, MI, 0, 6>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 7>(k, d, r, ring, xb0, lane);
 }
 
 // Stage h of the K loop (see the kernel). LOAD: the stage issues stage h + 2's loads; MORE: there is a
@@ -458,17 +472,28 @@ __device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uin
 // time (the ring offsets are then constants), else -1.
 template <int F, int MI, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1>
 __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, KOps<MI>& kb, WRegs& r,
-                                           const GemmSrc& src, const LoadOffs& lo, uint8_t* ring, int h, int K,
+                                           const GemmSrc& src, const LoadOffs& lo, uint8_t* ring, const XBase& xb, int h, int K,
                                            int nchunk, int wave, int lane) {
   constexpr int LPS = gm_loads_per_stage(F, MI);
   const int s0 = SLOT >= 0 ? SLOT : h % GM_RING;
   const int s1 = SLOT >= 0 ? (SLOT + 1) % GM_RING : (s0 == GM_RING - 1 ? 0 : s0 + 1);
   const int s2 = SLOT >= 0 ? (SLOT + 2) % GM_RING : (s1 == GM_RING - 1 ? 0 : s1 + 1);
-  const uint8_t* stage = ring + s0 * GM_STAGE_BYTES;
   const StageLoads L{&src, &lo, ring, ring + s2 * GM_STAGE_BYTES, h + 2, K, nchunk, wave, lane};
-  kstep<F, MI, RAGGED, 0, LOAD>(acc, ka, kb, r, stage, lane, L);
-  kstep<F, MI, RAGGED, 1, LOAD>(acc, kb, ka, r, stage, lane, L);
-  kstep<F, MI, RAGGED, 2, LOAD>(acc, ka, kb, r, stage, lane, L);
+  // this stage's and the next stage's per-lane fragment offsets (registers when the slot is known)
+  uint32_t xc[4], xn[4];
+#pragma unroll
+  for (int S = 0; S < 4; ++S) {
+    if constexpr (SLOT >= 0) {
+      xc[S] = xb.v[SLOT][S];
+      xn[S] = xb.v[(SLOT + 1) % GM_RING][S];
+    } else {
+      xc[S] = xb.v[0][S] + (uint32_t)(s0 * GM_STAGE_BYTES);
+      xn[S] = xb.v[0][S] + (uint32_t)(s1 * GM_STAGE_BYTES);
+    }
+  }
+  kstep<F, MI, RAGGED, 0, LOAD>(acc, ka, kb, r, ring, xc, lane, L);
+  kstep<F, MI, RAGGED, 1, LOAD>(acc, kb, ka, r, ring, xc, lane, L);
+  kstep<F, MI, RAGGED, 2, LOAD>(acc, ka, kb, r, ring, xc, lane, L);
   // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
   mfma_group<MI, 0>(acc, kb);
   __builtin_amdgcn_sched_barrier(0);
@@ -490,7 +515,7 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
   if constexpr ((G) < MI) {                                                        \
     mfma_one<MI, G, 0>(acc, kb);                                                   \
     if constexpr (MORE) {                                                          \
-      ka.a[(G) - 1] = a_frag<0>(next, lane, (G) - 1);                              \
+      ka.a[(G) - 1] = a_frag(ring, xn[0], (G) - 1);                               \
       b_slot<F, MI, 0, 2 * ((G) - 1)>(d, ka.b, r, kh);                             \
     }                                                                              \
     __builtin_amdgcn_sched_barrier(0);                                             \
@@ -501,7 +526,7 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
   FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
 #undef FP4_LAST
   if constexpr (MORE) {
-    ka.a[MI - 1] = a_frag<0>(next, lane, MI - 1);
+    ka.a[MI - 1] = a_frag(ring, xn[0], MI - 1);
     b_slot<F, MI, 0, 2 * (MI - 1)>(d, ka.b, r, kh);
     b_slot<F, MI, 0, 2 * (MI - 1) + 1>(d, ka.b, r, kh);
   }
@@ -548,20 +573,22 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
   WRegs r;
   KOps<MI> ka, kb;
   read_w(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
-  prep_all0<F, MI>(ka, r, ring, lane);
+  XBase xb;
+  x_bases(xb, lane);
+  prep_all0<F, MI>(ka, r, ring, xb.v[0][0], lane);
 
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
   // body is compiled for each case, so the loop has no per-group branches.
   int h = 0;
   // three stages per iteration (the ring period), so that every ring offset is a constant
   for (; h + 4 < H; h += 3) {
-    stage_body<F, MI, RAGGED, true, true, 0>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
-    stage_body<F, MI, RAGGED, true, true, 1>(acc, ka, kb, r, src, lo, ring, h + 1, K, nchunk, wave, lane);
-    stage_body<F, MI, RAGGED, true, true, 2>(acc, ka, kb, r, src, lo, ring, h + 2, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 0>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 1>(acc, ka, kb, r, src, lo, ring, xb, h + 1, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 2>(acc, ka, kb, r, src, lo, ring, xb, h + 2, K, nchunk, wave, lane);
   }
-  for (; h + 2 < H; ++h) stage_body<F, MI, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
-  if (h + 1 < H) stage_body<F, MI, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, h++, K, nchunk, wave, lane);
-  stage_body<F, MI, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, h, K, nchunk, wave, lane);
+  for (; h + 2 < H; ++h) stage_body<F, MI, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
+  if (h + 1 < H) stage_body<F, MI, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, xb, h++, K, nchunk, wave, lane);
+  stage_body<F, MI, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
 
   // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]; y is written
   // once and not read back here, so the stores are nontemporal (about 1% faster than plain ones)
