@@ -176,6 +176,39 @@ def test_gemv_canary_and_determinism():
     assert torch.all(buf[:32] == 12345.0) and torch.all(buf[32 + m * n:] == 12345.0)
 
 
+def test_products_on_side_streams():
+    # The library keeps no per-call state: the GEMV, mid-M kernel and GEMM launched on two side streams at
+    # once, each call with its own output, give the bytes they give on the current stream one at a time.
+    fmt, n, k = "rocmfp4_dual", 400, 1024
+    _announce("side-streams", fmt)
+    cases = []
+    for mat, m in enumerate((1, 9, 96)):
+        w, packed = gc.make_case(fmt, n, k, cfg=66, mat=mat)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=66, mat=mat)
+        x = gc.x_tensor(x_bits)
+        ref_y = torch.full((m, n), float("nan"), device="cuda")
+        fp4.w4a16_matmul(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, ref_y)
+        torch.cuda.synchronize()
+        gc.check_product(fmt, packed, x_bits, ref_y, label=f"side-streams M={m}")
+        cases.append((m, pw, x, ref_y))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full((m, n), float("nan"), device="cuda") for (m, _, _, _) in cases for _ in streams]
+    for rep in range(3):
+        i = 0
+        for (m, pw, x, _) in cases:
+            for st in streams:
+                st.wait_stream(torch.cuda.current_stream())
+                fp4.w4a16_matmul(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, outs[i], stream=st)
+                i += 1
+    torch.cuda.synchronize()
+    i = 0
+    for (m, pw, x, ref_y) in cases:
+        for st in streams:
+            assert torch.equal(outs[i], ref_y), f"M={m}: side-stream result differs"
+            i += 1
+
+
 def test_gemv_m0_is_noop():
     y = torch.full((4,), 7.0, device="cuda")
     q = torch.zeros(1024, dtype=torch.uint8, device="cuda")
