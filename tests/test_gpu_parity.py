@@ -435,6 +435,32 @@ def test_matmul_dispatch(m):
     gc.check_product(fmt, packed, x_bits, y, label=f"matmul M={m}")
 
 
+def _random_shapes(fmt, count, seed):
+    # Seeded shapes across all three product paths (GEMV M <= 16, mid-M 17..64, GEMM above), with ragged
+    # N (any value) and K (any multiple of the format's block), so tile and chunk tails land anywhere.
+    rng = np.random.default_rng(seed)
+    kmul = 16 if fmt == "nvfp4" else 32
+    bands = [(1, 16)] if fmt == "q4_0" else [(1, 16), (17, 64), (65, 300)]
+    out = []
+    for i in range(count):
+        lo, hi = bands[i % len(bands)]
+        out.append((int(rng.integers(lo, hi + 1)), int(rng.integers(1, 641)), kmul * int(rng.integers(1, 2560 // kmul + 1))))
+    return out
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
+def test_matmul_random_shapes(fmt):
+    for case, (m, n, k) in enumerate(_random_shapes(fmt, 9, seed=1000 + gc.FMTS_ALL.index(fmt))):
+        _announce("matmul-random", fmt, m, n, k)
+        w, packed = gc.make_case(fmt, n, k, cfg=67, mat=case)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=67, mat=case)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        fp4.w4a16_matmul(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+        torch.cuda.synchronize()
+        gc.check_product(fmt, packed, x_bits, y, label=f"matmul {fmt} M={m} N={n} K={k}")
+
+
 # ------------------------------------------------------------------ device packers (byte-exact)
 
 @pytest.mark.parametrize("fmt", gc.FMTS_ALL)
