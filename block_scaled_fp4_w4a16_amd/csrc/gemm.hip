@@ -42,10 +42,12 @@ constexpr int GM_SHORT_BANDS = 8;    // MI = 6 tiles cover rows 0 .. 8 * 192 - 1
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // This lane's weight bytes for one stage, read back from LDS: for each of the wave's two 32-row column
-// tiles, dwords 2 kh and 2 kh + 1 of the row's two lane pieces, and the row's scale bytes of the chunk.
+// tiles, dwords 2 kh and 2 kh + 1 of the row's two lane pieces, and the row's scale bytes of the chunk that
+// its k half (kh) uses: bytes 4 kh .. 4 kh + 3 of 8 (16-weight groups), or 2 kh, 2 kh + 1 of 4 (FAST), so
+// that the byte a k-step needs is a constant index.
 struct WRegs {
   u32x2 w[2][2];
-  u32x2 sc[2];
+  uint32_t sc[2];
 };
 
 // Buffer descriptors (raw, stride 0): loads past num_records return zeros.
@@ -224,8 +226,8 @@ __device__ __forceinline__ void read_w(WRegs& r, const uint8_t* stage, int F_spr
     r.w[j][0] = *reinterpret_cast<const u32x2*>(wb);
     r.w[j][1] = *reinterpret_cast<const u32x2*>(wb + 256);
     const uint8_t* sb = stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + t * F_us + n * F_spr;
-    if (F_spr == 4) r.sc[j] = u32x2{*reinterpret_cast<const uint32_t*>(sb), 0u};
-    else r.sc[j] = *reinterpret_cast<const u32x2*>(sb);
+    if (F_spr == 4) r.sc[j] = *reinterpret_cast<const uint16_t*>(sb + 2 * kh);
+    else r.sc[j] = *reinterpret_cast<const uint32_t*>(sb + 4 * kh);
   }
 }
 
@@ -254,12 +256,9 @@ struct BDec {
 };
 
 template <int F, int S, int SL>
-__device__ __forceinline__ void b_slice(BDec& d, u32x4& out, const WRegs& r, int j, int kh) {
+__device__ __forceinline__ void b_slice(BDec& d, u32x4& out, const WRegs& r, int j) {
   if constexpr (SL == 0) {
-    const int sigma = 4 * kh + S;
-    const int gi = (F == FAST) ? (sigma >> 1) : sigma;     // scale byte of this k-step
-    const uint32_t sw = (gi & 4) ? r.sc[j][1] : r.sc[j][0];
-    d.sc = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * (gi & 3)), 0);
+    d.sc = __builtin_amdgcn_cvt_f32_fp8(r.sc[j], F == FAST ? (S >> 1) : S);   // scale byte of this k-step
     const u32x2 w0 = r.w[j][0], w1 = r.w[j][1];
     if constexpr (F == FAST) {
       const uint32_t w = (S & 1) ? w1[S >> 1] : w0[S >> 1];
@@ -296,13 +295,10 @@ __device__ __forceinline__ void b_slice(BDec& d, u32x4& out, const WRegs& r, int
 // in the shadow of a single MFMA: scale and low lookup, high lookup, two pair converts each, then the
 // four "times scale, pack" steps.
 template <int F, int S, int SUB>
-__device__ __forceinline__ void b_sub(BDec& d, u32x4& out, const WRegs& r, int j, int kh) {
+__device__ __forceinline__ void b_sub(BDec& d, u32x4& out, const WRegs& r, int j) {
   const u32x2 w0 = r.w[j][0], w1 = r.w[j][1];
   if constexpr (SUB == 0) {
-    const int sigma = 4 * kh + S;
-    const int gi = (F == FAST) ? (sigma >> 1) : sigma;
-    const uint32_t sw = (gi & 4) ? r.sc[j][1] : r.sc[j][0];
-    d.sc = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * (gi & 3)), 0);
+    d.sc = __builtin_amdgcn_cvt_f32_fp8(r.sc[j], F == FAST ? (S >> 1) : S);
     if constexpr (F == FAST) d.q0 = cb10_quad<false>((S & 1) ? w1[S >> 1] : w0[S >> 1]);
     else if constexpr (F == DUAL) d.q0 = cb10_quad<(S & 1) != 0>(w0[S >> 1]);
     else d.q0 = __builtin_amdgcn_perm(w1[S >> 1], w0[S >> 1], (S & 1) ? 0x07060302u : 0x05040100u);
@@ -364,26 +360,25 @@ struct KOps {
 template <int F, int MI, int S, int G>
 __device__ __forceinline__ void prep_slice(KOps<MI>& nx, BDec (&d)[2], const WRegs& r, const uint8_t* ring,
                                            uint32_t xbase, int lane) {
-  const int kh = lane >> 5;
   if constexpr (G < MI) nx.a[G] = a_frag(ring, xbase, G);
-  b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2, kh);
+  b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2);
 }
 
 // The B dequantization pieces (b_sub) that run after MFMA slot SLOT (0 .. 2 MI - 1) of a k-step. With 16
 // MFMAs (MI = 8) slot s takes piece s % 8 of operand s / 8; with 12 (MI = 6) each operand's six slots take
 // pieces 0, 1, 2, 3, then 4 and 5, then 6 and 7.
 template <int F, int MI, int S, int SLOT>
-__device__ __forceinline__ void b_slot(BDec (&d)[2], u32x4 (&b)[2], const WRegs& r, int kh) {
+__device__ __forceinline__ void b_slot(BDec (&d)[2], u32x4 (&b)[2], const WRegs& r) {
   if constexpr (MI == 8) {
     constexpr int t = SLOT >> 3, q = SLOT & 7;
-    b_sub<F, S, q>(d[t], b[t], r, t, kh);
+    b_sub<F, S, q>(d[t], b[t], r, t);
   } else {
     constexpr int t = SLOT / 6, q = SLOT % 6;
     if constexpr (q < 4) {
-      b_sub<F, S, q>(d[t], b[t], r, t, kh);
+      b_sub<F, S, q>(d[t], b[t], r, t);
     } else {
-      b_sub<F, S, 4 + 2 * (q - 4)>(d[t], b[t], r, t, kh);
-      b_sub<F, S, 5 + 2 * (q - 4)>(d[t], b[t], r, t, kh);
+      b_sub<F, S, 4 + 2 * (q - 4)>(d[t], b[t], r, t);
+      b_sub<F, S, 5 + 2 * (q - 4)>(d[t], b[t], r, t);
     }
   }
 }
@@ -440,15 +435,14 @@ template <int F, int MI, bool RAGGED, int S, bool LOAD>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur, KOps<MI>& nx, const WRegs& r,
                                       const uint8_t* ring, const uint32_t (&xc)[4], int lane, const StageLoads& L) {
   BDec d[2];
-  const int kh = lane >> 5;
 #define FP4_GROUP(G)                                                      \
   if constexpr ((G) < MI) {                                               \
     mfma_one<MI, G, 0>(acc, cur);                                         \
     nx.a[G] = a_frag(ring, xc[S + 1], G);                                 \
-    b_slot<F, MI, S + 1, 2 * (G)>(d, nx.b, r, kh);                        \
+    b_slot<F, MI, S + 1, 2 * (G)>(d, nx.b, r);                        \
     __builtin_amdgcn_sched_barrier(0);                                    \
     mfma_one<MI, G, 1>(acc, cur);                                         \
-    b_slot<F, MI, S + 1, 2 * (G) + 1>(d, nx.b, r, kh);                    \
+    b_slot<F, MI, S + 1, 2 * (G) + 1>(d, nx.b, r);                    \
     if constexpr (LOAD) issue_part<F, MI, RAGGED, S, G>(L);               \
     __builtin_amdgcn_sched_barrier(0);                                    \
   }
@@ -508,7 +502,6 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
   }
   __builtin_amdgcn_sched_barrier(0);
   BDec d[2];
-  const int kh = lane >> 5;
   // MFMA groups 1 .. MI - 1 of k-step 3 carry the preparation of stage h + 1's k-step 0 (the shares of
   // groups 0 .. MI - 2 here, the last group's share after the loop body)
 #define FP4_LAST(G)                                                                \
@@ -516,19 +509,19 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
     mfma_one<MI, G, 0>(acc, kb);                                                   \
     if constexpr (MORE) {                                                          \
       ka.a[(G) - 1] = a_frag(ring, xn[0], (G) - 1);                               \
-      b_slot<F, MI, 0, 2 * ((G) - 1)>(d, ka.b, r, kh);                             \
+      b_slot<F, MI, 0, 2 * ((G) - 1)>(d, ka.b, r);                             \
     }                                                                              \
     __builtin_amdgcn_sched_barrier(0);                                             \
     mfma_one<MI, G, 1>(acc, kb);                                                   \
-    if constexpr (MORE) b_slot<F, MI, 0, 2 * ((G) - 1) + 1>(d, ka.b, r, kh);       \
+    if constexpr (MORE) b_slot<F, MI, 0, 2 * ((G) - 1) + 1>(d, ka.b, r);       \
     __builtin_amdgcn_sched_barrier(0);                                             \
   }
   FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
 #undef FP4_LAST
   if constexpr (MORE) {
     ka.a[MI - 1] = a_frag(ring, xn[0], MI - 1);
-    b_slot<F, MI, 0, 2 * (MI - 1)>(d, ka.b, r, kh);
-    b_slot<F, MI, 0, 2 * (MI - 1) + 1>(d, ka.b, r, kh);
+    b_slot<F, MI, 0, 2 * (MI - 1)>(d, ka.b, r);
+    b_slot<F, MI, 0, 2 * (MI - 1) + 1>(d, ka.b, r);
   }
 }
 
