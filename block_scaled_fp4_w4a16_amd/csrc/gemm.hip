@@ -359,7 +359,7 @@ struct KOps {
 // of B operand G / 4).
 template <int F, int MI, int S, int G>
 __device__ __forceinline__ void prep_slice(KOps<MI>& nx, BDec (&d)[2], const WRegs& r, const uint8_t* ring,
-                                           uint32_t xbase, int lane) {
+                                           uint32_t xbase) {
   if constexpr (G < MI) nx.a[G] = a_frag(ring, xbase, G);
   b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2);
 }
@@ -433,7 +433,7 @@ __device__ __forceinline__ void issue_part(const StageLoads& L) {
 // so the LDS reads, VALU work and loads run while the matrix core is busy.
 template <int F, int MI, bool RAGGED, int S, bool LOAD>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur, KOps<MI>& nx, const WRegs& r,
-                                      const uint8_t* ring, const uint32_t (&xc)[4], int lane, const StageLoads& L) {
+                                      const uint8_t* ring, const uint32_t (&xc)[4], const StageLoads& L) {
   BDec d[2];
 #define FP4_GROUP(G)                                                      \
   if constexpr ((G) < MI) {                                               \
@@ -453,12 +453,12 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur,
 // Operands of k-step 0 of a stage, all at once (the first stage only; later stages prepare them inside
 // the previous stage's last k-step).
 template <int F, int MI>
-__device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uint8_t* ring, uint32_t xb0, int lane) {
+__device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uint8_t* ring, uint32_t xb0) {
   BDec d[2];
-  prep_slice<F, MI, 0, 0>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 1>(k, d, r, ring, xb0, lane);
-  prep_slice<F, MI, 0, 2>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 3>(k, d, r, ring, xb0, lane);
-  prep_slice<F, MI, 0, 4>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 5>(k, d, r, ring, xb0, lane);
-  prep_slice<F, MI, 0, 6>(k, d, r, ring, xb0, lane); prep_slice<F, MI, 0, 7>(k, d, r, ring, xb0, lane);
+  prep_slice<F, MI, 0, 0>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 1>(k, d, r, ring, xb0);
+  prep_slice<F, MI, 0, 2>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 3>(k, d, r, ring, xb0);
+  prep_slice<F, MI, 0, 4>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 5>(k, d, r, ring, xb0);
+  prep_slice<F, MI, 0, 6>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 7>(k, d, r, ring, xb0);
 }
 
 // Stage h of the K loop (see the kernel). LOAD: the stage issues stage h + 2's loads; MORE: there is a
@@ -485,9 +485,9 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
       xn[S] = xb.v[0][S] + (uint32_t)(s1 * GM_STAGE_BYTES);
     }
   }
-  kstep<F, MI, RAGGED, 0, LOAD>(acc, ka, kb, r, ring, xc, lane, L);
-  kstep<F, MI, RAGGED, 1, LOAD>(acc, kb, ka, r, ring, xc, lane, L);
-  kstep<F, MI, RAGGED, 2, LOAD>(acc, ka, kb, r, ring, xc, lane, L);
+  kstep<F, MI, RAGGED, 0, LOAD>(acc, ka, kb, r, ring, xc, L);
+  kstep<F, MI, RAGGED, 1, LOAD>(acc, kb, ka, r, ring, xc, L);
+  kstep<F, MI, RAGGED, 2, LOAD>(acc, ka, kb, r, ring, xc, L);
   // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
   mfma_group<MI, 0>(acc, kb);
   __builtin_amdgcn_sched_barrier(0);
@@ -568,7 +568,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
   read_w(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
   XBase xb;
   x_bases(xb, lane);
-  prep_all0<F, MI>(ka, r, ring, xb.v[0][0], lane);
+  prep_all0<F, MI>(ka, r, ring, xb.v[0][0]);
 
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
   // body is compiled for each case, so the loop has no per-group branches.
