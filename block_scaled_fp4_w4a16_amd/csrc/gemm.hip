@@ -668,9 +668,8 @@ static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, co
   }
   const int nbig = (int)(U - (int64_t)(GM_SHORT_BANDS * GM_SHORT_ROWS / GM_BM) * ns);
   const int grid = nbig + GM_SHORT_BANDS * ns;
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, GM_LDS) == hipSuccess;
-  (void)attr;
+  static Fp4LdsLimit lds_limit;
+  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
   hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K, nchunk,
                      tiles_m, ns, nbig, g);
 }

@@ -520,8 +520,8 @@ struct RingLaunch {
   static const void* fn() { return reinterpret_cast<const void*>(&gemv_ring_kernel<F, D>); }
   static size_t lds(int W, int nchunk) { return (size_t)nchunk * 256 + (size_t)W * 64 * 4 * sizeof(float); }
   static void launch(const GemvItem& it, int W, hipStream_t st) {
-    static const bool ok = hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
-    (void)ok;
+    static Fp4LdsLimit lds_limit;
+    lds_limit.ensure(fn(), GEMV_LDS_MAX);
     const int nchunk = (it.K + CHUNK_K - 1) / CHUNK_K, ntiles = (it.N + TILE_N - 1) / TILE_N;
     hipLaunchKernelGGL((gemv_ring_kernel<F, D>), dim3(ntiles), dim3(64 * W), lds(W, nchunk), st, it.q, it.s, it.x, it.y,
                        it.N, it.K, it.g, 1 | (W << 8));
@@ -733,10 +733,10 @@ struct GemvLaunch {
     }
     return r;
   }
-  // allow more than 64 KiB of dynamic LDS for this instantiation (once; thread-safe static init)
+  // allow more than 64 KiB of dynamic LDS for this instantiation (once per device)
   static void attr() {
-    static const bool ok = hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
-    (void)ok;
+    static Fp4LdsLimit lds_limit;
+    lds_limit.ensure(fn(), GEMV_LDS_MAX);
   }
   static void launch(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
     attr();
@@ -871,9 +871,8 @@ static void launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* 
   const int ntiles = (N + TILE_N - 1) / TILE_N;
   const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
   const size_t lds = stage > red ? stage : red;
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&midm_kernel<F, MB, T, WMAX>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_MAX) == hipSuccess;
-  (void)attr;
+  static Fp4LdsLimit lds_limit;
+  lds_limit.ensure(reinterpret_cast<const void*>(&midm_kernel<F, MB, T, WMAX>), GEMV_LDS_MAX);
   hipLaunchKernelGGL((midm_kernel<F, MB, T, WMAX>), dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, N, K,
                      g, M | (W << 8));
 }

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <atomic>
 
 static inline bool fp4_valid_format(int f) { return f >= 1 && f <= 4; }
 
@@ -18,3 +19,20 @@ static inline int fp4_check_nk(int fmt, int64_t N, int64_t K) {
 
 // Launch status of the last kernel enqueued by this thread.
 static inline int fp4_launch_status() { return hipGetLastError() == hipSuccess ? 0 : -6; }
+
+// A kernel's dynamic-LDS limit raised to `bytes` once per device: the attribute is set for the device
+// current at the call, so a process that launches on several GPUs needs it on each. One static object
+// per kernel instantiation; a race only repeats the call.
+struct Fp4LdsLimit {
+  std::atomic<int> done[64];
+  void ensure(const void* fn, int bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+      (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      return;
+    }
+    if (done[dev].load(std::memory_order_acquire)) return;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess)
+      done[dev].store(1, std::memory_order_release);
+  }
+};
