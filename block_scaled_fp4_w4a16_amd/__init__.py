@@ -9,6 +9,7 @@ without the built library fails loudly.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -107,6 +108,36 @@ def _stream(stream) -> int | None:
     return int(stream)
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _device(*ts) -> torch.device:
+    """The one GPU that every given tensor (None entries skipped) lives on; the call runs there."""
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if len(devs) != 1:
+        raise ValueError(f"tensors must all live on one GPU (got {sorted(str(d) for d in devs)})")
+    d = devs.pop()
+    if d.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    return d
+
+
+@functools.lru_cache(maxsize=4096)
+def _plane_bytes(f: int, N: int, K: int) -> tuple[int, int]:
+    q = ctypes.c_size_t()
+    s = ctypes.c_size_t()
+    _check(lib().fp4_layout_bytes(f, N, K, ctypes.byref(q), ctypes.byref(s)), "fp4_layout_bytes")
+    return q.value, s.value
+
+
+def _check_planes(f: int, N: int, K: int, q, s):
+    qb, sb = _plane_bytes(f, N, K)
+    if _nbytes(q) < qb or _nbytes(s) < sb:
+        raise ValueError(f"packed planes too small for N={N} K={K}: need {qb} + {sb} bytes, "
+                         f"got {_nbytes(q)} + {_nbytes(s)}")
+
+
 def fp4_abi_version() -> int:
     return lib().fp4_abi_version()
 
@@ -123,8 +154,22 @@ def fp4_layout_bytes(fmt, N: int, K: int) -> tuple[int, int]:
 
 
 def fp4_pack_layout(fmt, N, K, src_q, src_s, dst_q, dst_s, stream=None):
-    _check(lib().fp4_pack_layout(_fmt(fmt), N, K, _ptr(src_q), _ptr(src_s), _ptr(dst_q), _ptr(dst_s),
-                                 _stream(stream)), "fp4_pack_layout")
+    f = _fmt(fmt)
+    dev = _device(src_q, src_s, dst_q, dst_s)
+    if N > 0 and K > 0 and K % 16 == 0:
+        if f == 1:
+            need = (N * K // 2, N * K // 16)
+            if _nbytes(src_q) < need[0] or (src_s is not None and _nbytes(src_s) < need[1]):
+                raise ValueError(f"canonical NVFP4 planes too small: need {need[0]} + {need[1]} bytes")
+        elif K % 32 == 0 and f in (2, 3, 4):
+            need = N * (K // 32) * {2: 18, 3: 17, 4: 18}[f]
+            if _nbytes(src_q) < need:
+                raise ValueError(f"canonical blocks too small: need {need} bytes, got {_nbytes(src_q)}")
+        if f in (1, 2, 3, 4) and (f == 1 or K % 32 == 0):
+            _check_planes(f, N, K, dst_q, dst_s)
+    with torch.cuda.device(dev):
+        _check(lib().fp4_pack_layout(f, N, K, _ptr(src_q), _ptr(src_s), _ptr(dst_q), _ptr(dst_s), _stream(stream)),
+               "fp4_pack_layout")
 
 
 def _product(name, fmt, M, N, K, q, s, global_scale, x, y, stream):
@@ -132,8 +177,13 @@ def _product(name, fmt, M, N, K, q, s, global_scale, x, y, stream):
         raise TypeError("x must be bfloat16 and y float32")
     if x.numel() < M * K or y.numel() < M * N:
         raise ValueError("x or y is smaller than M x K / M x N")
-    _check(getattr(lib(), name)(_fmt(fmt), M, N, K, _ptr(q), _ptr(s), float(global_scale), _ptr(x), _ptr(y),
-                                _stream(stream)), name)
+    f = _fmt(fmt)
+    dev = _device(q, s, x, y)
+    if M > 0 and N > 0 and K > 0:
+        _check_planes(f, N, K, q, s)
+    with torch.cuda.device(dev):
+        _check(getattr(lib(), name)(f, M, N, K, _ptr(q), _ptr(s), float(global_scale), _ptr(x), _ptr(y),
+                                    _stream(stream)), name)
 
 
 def w4a16_gemv(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
@@ -143,13 +193,19 @@ def w4a16_gemv(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
 def w4a16_gemv_batched(fmt, M, items, stream=None):
     """items: sequence of (q, s, global_scale, x, y, N, K), one per matrix; all share fmt and M."""
     arr = (GemvItem * max(1, len(items)))()
+    f = _fmt(fmt)
+    tensors = []
     for i, (q, s, g, x, y, n, k) in enumerate(items):
         if x.dtype != torch.bfloat16 or y.dtype != torch.float32:
             raise TypeError("x must be bfloat16 and y float32")
         if x.numel() < M * k or y.numel() < M * n:
             raise ValueError("x or y is smaller than M x K / M x N")
+        if M > 0 and n > 0 and k > 0:
+            _check_planes(f, n, k, q, s)
+        tensors += [q, s, x, y]
         arr[i] = GemvItem(_ptr(q), _ptr(s), _ptr(x), _ptr(y), n, k, float(g))
-    _check(lib().w4a16_gemv_batched(_fmt(fmt), M, len(items), arr, _stream(stream)), "w4a16_gemv_batched")
+    with torch.cuda.device(_device(*tensors) if tensors else torch.cuda.current_device()):
+        _check(lib().w4a16_gemv_batched(f, M, len(items), arr, _stream(stream)), "w4a16_gemv_batched")
 
 
 def w4a16_gemm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
@@ -167,8 +223,13 @@ def w4a16_matmul(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
 def fp4_dequant_f32(fmt, N, K, q, s, global_scale, w, stream=None):
     if w.dtype != torch.float32 or w.numel() < N * K:
         raise ValueError("w must be float32 with N x K elements")
-    _check(lib().fp4_dequant_f32(_fmt(fmt), N, K, _ptr(q), _ptr(s), float(global_scale), _ptr(w),
-                                 _stream(stream)), "fp4_dequant_f32")
+    f = _fmt(fmt)
+    dev = _device(q, s, w)
+    if N > 0 and K > 0:
+        _check_planes(f, N, K, q, s)
+    with torch.cuda.device(dev):
+        _check(lib().fp4_dequant_f32(f, N, K, _ptr(q), _ptr(s), float(global_scale), _ptr(w), _stream(stream)),
+               "fp4_dequant_f32")
 
 
 def fp4_quantize_nvfp4(N, K, w, wq, ws, g_out, stream=None):
@@ -176,8 +237,9 @@ def fp4_quantize_nvfp4(N, K, w, wq, ws, g_out, stream=None):
         raise TypeError("w and g_out must be float32")
     if w.numel() < N * K or wq.numel() < N * K // 2 or ws.numel() < N * K // 16 or g_out.numel() < 1:
         raise ValueError("buffer too small")
-    _check(lib().fp4_quantize_nvfp4(N, K, _ptr(w), _ptr(wq), _ptr(ws), _ptr(g_out), _stream(stream)),
-           "fp4_quantize_nvfp4")
+    with torch.cuda.device(_device(w, wq, ws, g_out)):
+        _check(lib().fp4_quantize_nvfp4(N, K, _ptr(w), _ptr(wq), _ptr(ws), _ptr(g_out), _stream(stream)),
+               "fp4_quantize_nvfp4")
 
 
 def fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream=None):
@@ -187,8 +249,9 @@ def fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream=None):
     bb = 18 if f == 2 else 17
     if w.numel() < N * K or blocks.numel() < N * (K // 32) * bb:
         raise ValueError("buffer too small")
-    _check(lib().fp4_quantize_rocmfp4(f, N, K, _ptr(w), _ptr(importance), _ptr(blocks), _stream(stream)),
-           "fp4_quantize_rocmfp4")
+    with torch.cuda.device(_device(w, importance, blocks)):
+        _check(lib().fp4_quantize_rocmfp4(f, N, K, _ptr(w), _ptr(importance), _ptr(blocks), _stream(stream)),
+               "fp4_quantize_rocmfp4")
 
 
 def fp4_quantize_q4_0(N, K, w, blocks, stream=None):
@@ -196,7 +259,8 @@ def fp4_quantize_q4_0(N, K, w, blocks, stream=None):
         raise TypeError("w must be float32")
     if w.numel() < N * K or blocks.numel() < N * (K // 32) * 18:
         raise ValueError("buffer too small")
-    _check(lib().fp4_quantize_q4_0(N, K, _ptr(w), _ptr(blocks), _stream(stream)), "fp4_quantize_q4_0")
+    with torch.cuda.device(_device(w, blocks)):
+        _check(lib().fp4_quantize_q4_0(N, K, _ptr(w), _ptr(blocks), _stream(stream)), "fp4_quantize_q4_0")
 
 
 # ----------------------------------------------------------------------------------------------

@@ -209,6 +209,31 @@ def test_products_on_side_streams():
             i += 1
 
 
+def test_binding_rejects_short_planes_and_mixed_devices():
+    # The binding checks buffer sizes the C ABI cannot see (raw pointers) before anything is launched.
+    fmt, n, k = "rocmfp4_dual", 64, 256
+    w, packed = gc.make_case(fmt, n, k, cfg=68)
+    pw = gc.upload(fmt, n, k, packed)
+    x = torch.zeros((1, k), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((1, n), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fp4.w4a16_matmul(fmt, 1, n, k, pw.q[:-16], pw.s, 1.0, x, y)
+    with pytest.raises(ValueError):
+        fp4.w4a16_matmul(fmt, 1, n, k, pw.q, pw.s[:-1], 1.0, x, y)
+    with pytest.raises(ValueError):
+        fp4.w4a16_matmul(fmt, 1, n, k, pw.q, pw.s, 1.0, x.cpu(), y)
+    with pytest.raises(ValueError):
+        fp4.fp4_dequant_f32(fmt, n, k, pw.q[:100], pw.s, 1.0, torch.empty(n * k, device="cuda"))
+    blocks = torch.zeros(n * (k // 32) * 18, dtype=torch.uint8, device="cuda")
+    dq, ds = torch.empty_like(pw.q), torch.empty_like(pw.s)
+    with pytest.raises(ValueError):
+        fp4.fp4_pack_layout(fmt, n, k, blocks[:-1], None, dq, ds)
+    with pytest.raises(ValueError):
+        fp4.fp4_pack_layout(fmt, n, k, blocks, None, dq[:-1], ds)
+    fp4.fp4_pack_layout(fmt, n, k, blocks, None, dq, ds)   # the full-size call still goes through
+    torch.cuda.synchronize()
+
+
 def test_gemv_m0_is_noop():
     y = torch.full((4,), 7.0, device="cuda")
     q = torch.zeros(1024, dtype=torch.uint8, device="cuda")
