@@ -529,7 +529,7 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
 template <int F, int MI, bool RAGGED>
 __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                           const uint16_t* __restrict__ x, float* __restrict__ y, int M, int N, int K,
-                                          int nchunk, int m0, int n0, float gscale) {
+                                          int nchunk, int m0, int n0, float gscale, int hb, int he, bool add_out) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave: keeps descriptors scalar
   const int wrow0 = n0 + 64 * wave;            // this wave's 64 weight rows (4 tiles of 16)
@@ -556,11 +556,12 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
   // between their MFMAs. In k-step 3 the wave waits for its share of stage h + 1, meets the other waves
   // at a barrier (every wave's share of stage h + 1 is then in LDS, and every wave is done reading stage
   // h), reads stage h + 1's packed weights and prepares its k-step 0 -- still between MFMAs.
-  const int H = 2 * nchunk;
+  // Stages hb .. he - 1 (all of K, or one part of a split K); hb is a multiple of the ring period, so
+  // stage h sits in ring slot h % 3 as when hb = 0.
   constexpr int LPS = gm_loads_per_stage(F, MI);
-  issue_stage<F, MI, RAGGED>(src, lo, ring, 0, K, nchunk, wave, lane);
-  if (1 < H) issue_stage<F, MI, RAGGED>(src, lo, ring, 1, K, nchunk, wave, lane);
-  if (1 < H) wait_vmcnt<LPS>();
+  issue_stage<F, MI, RAGGED>(src, lo, ring, hb, K, nchunk, wave, lane);
+  if (hb + 1 < he) issue_stage<F, MI, RAGGED>(src, lo, ring, hb + 1, K, nchunk, wave, lane);
+  if (hb + 1 < he) wait_vmcnt<LPS>();
   else wait_vmcnt<0>();
   workgroup_barrier();
   WRegs r;
@@ -572,19 +573,34 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
   // body is compiled for each case, so the loop has no per-group branches.
-  int h = 0;
+  int h = hb;
   // three stages per iteration (the ring period), so that every ring offset is a constant
-  for (; h + 4 < H; h += 3) {
+  for (; h + 4 < he; h += 3) {
     stage_body<F, MI, RAGGED, true, true, 0>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
     stage_body<F, MI, RAGGED, true, true, 1>(acc, ka, kb, r, src, lo, ring, xb, h + 1, K, nchunk, wave, lane);
     stage_body<F, MI, RAGGED, true, true, 2>(acc, ka, kb, r, src, lo, ring, xb, h + 2, K, nchunk, wave, lane);
   }
-  for (; h + 2 < H; ++h) stage_body<F, MI, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
-  if (h + 1 < H) stage_body<F, MI, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, xb, h++, K, nchunk, wave, lane);
+  for (; h + 2 < he; ++h) stage_body<F, MI, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
+  if (h + 1 < he) stage_body<F, MI, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, xb, h++, K, nchunk, wave, lane);
   stage_body<F, MI, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
 
   // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]; y is written
-  // once and not read back here, so the stores are nontemporal (about 1% faster than plain ones)
+  // once and not read back here, so the stores are nontemporal (about 1% faster than plain ones). A
+  // part of a split K adds its g-scaled sum into the zeroed y instead (FP32 atomics in L2): with two parts
+  // every element is fl(0 + a + b) in either order, so the result does not depend on which part is first.
+  if (add_out) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int col = wrow0 + 32 * j + (lane & 31);
+          if (row < M && col < N) unsafeAtomicAdd(y + (int64_t)row * N + col, acc[i][j][e] * gscale);
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -605,15 +621,24 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 //  * 256-row tiles: first column tiles ns .. tiles_n - 1 over all tiles_m bands (band = i % tiles_m), then
 //    rows 1536 .. M - 1 (tiles_m - 6 bands) of column tiles 0 .. ns - 1.
 // With ns = 0 every tile is 256 rows: workgroup i takes band i % tiles_m and column tile i / tiles_m.
+// ksplit > 0 (grids of at most a quarter of the CUs, ns = 0): workgroup b < nbig takes stages 0 .. ksplit
+// - 1 of tile b, workgroup nbig + b the rest, and both add into the zeroed y.
 // Block b runs on XCD b % 8, so with 8 bands the workgroups of one XCD share an x band in its L2.
 template <int F, bool RAGGED>
 __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restrict__ qp,
                                                           const uint8_t* __restrict__ sp,
                                                           const uint16_t* __restrict__ x, float* __restrict__ y,
                                                           int M, int N, int K, int nchunk, int tiles_m, int ns,
-                                                          int nbig, float gscale) {
+                                                          int nbig, float gscale, int ksplit) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
-  const int b = (int)blockIdx.x;
+  int b = (int)blockIdx.x;
+  int hb = 0, he = 2 * nchunk;
+  if (ksplit > 0) {
+    const bool second = b >= nbig;
+    if (second) b -= nbig;
+    hb = second ? ksplit : 0;
+    he = second ? he : ksplit;
+  }
   if (b < nbig) {
     const int tiles_n = (N + GM_BN - 1) / GM_BN;
     const int nwide = tiles_m * (tiles_n - ns);
@@ -626,12 +651,18 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
       m0 = GM_SHORT_BANDS * GM_SHORT_ROWS + (i % bands) * GM_BM;
       n0 = (i / bands) * GM_BN;
     }
-    gemm_tile<F, 8, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, m0, n0, gscale);
+    gemm_tile<F, 8, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, m0, n0, gscale, hb, he, ksplit > 0);
   } else {
     const int i = b - nbig;
     gemm_tile<F, 6, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, (i % GM_SHORT_BANDS) * GM_SHORT_ROWS,
-                            (i / GM_SHORT_BANDS) * GM_BN, gscale);
+                            (i / GM_SHORT_BANDS) * GM_BN, gscale, hb, he, false);
   }
+}
+
+// y = 0 before the parts of a split K add into it (a kernel, not a memset, so that the call can be
+// captured in a graph).
+__global__ void gemm_zero_kernel(float* __restrict__ y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) y[i] = 0.f;
 }
 
 // Compute units of the current device (cached per device).
@@ -667,11 +698,26 @@ static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, co
     if (atoi(e) == 0) ns = 0;
   }
   const int nbig = (int)(U - (int64_t)(GM_SHORT_BANDS * GM_SHORT_ROWS / GM_BM) * ns);
-  const int grid = nbig + GM_SHORT_BANDS * ns;
+  // Grids of at most a quarter of the CUs split K in two (at a multiple of the 3-stage ring period, each
+  // part at least 6 stages) so that twice the workgroups run; y is zeroed first and both parts add into
+  // it. On larger grids zeroing and adding y costs more than the extra workgroups gain (prefill N =
+  // 14336 at M = 512, 112 tiles: 91 us split against 79 us whole).
+  int ksplit = 0;
+  const int H = 2 * nchunk;
+  if (ns == 0 && 4 * U <= cus && H >= 12) ksplit = 3 * (H / 6);
+  if (const char* e = getenv("FP4_GEMM_SPLIT")) {  // tuning override: 0 = whole K per workgroup
+    if (atoi(e) == 0) ksplit = 0;
+  }
+  const int grid = ksplit ? 2 * nbig : nbig + GM_SHORT_BANDS * ns;
+  if (ksplit) {
+    const int64_t total = (int64_t)M * N;
+    const int zb = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    hipLaunchKernelGGL(gemm_zero_kernel, dim3(zb), dim3(256), 0, st, y, total);
+  }
   static Fp4LdsLimit lds_limit;
   lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
   hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K, nchunk,
-                     tiles_m, ns, nbig, g);
+                     tiles_m, ns, nbig, g, ksplit);
 }
 
 template <int F>

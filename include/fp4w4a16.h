@@ -129,6 +129,11 @@ int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items
  * Prefill-shaped product, any M >= 1, intended for M >= 64: stages x tiles
  * and packed weight tiles, dequantizes each weight tile once into LDS as exact bf16
  * level*scale, contracts with bf16 MFMA in FP32 and multiplies by g in the epilogue.
+ * When y has few 256x256 tiles (at most a quarter of the device's compute units) and K spans
+ * at least 6 chunks of 128, K is split in two: the call enqueues a kernel that zeroes y, then
+ * the product, whose two halves add their g-scaled sums into y with FP32 atomics. Two addends
+ * onto zero give the same sum in either order, so the result is still bit-reproducible; it
+ * differs from the whole-K sum only by rounding. Both kernels run on `stream`.
  */
 int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);

@@ -434,6 +434,32 @@ def test_gemm_short_tiles(fmt, monkeypatch):
 
 
 @pytest.mark.parametrize("fmt", gc.FMTS)
+@pytest.mark.parametrize("m,n,k", [(100, 600, 1152), (256, 512, 2048), (257, 37, 4000)])
+def test_gemm_split_k(fmt, m, n, k, monkeypatch):
+    # Grids of at most half the CUs split K in two parts that add into the zeroed y: against the oracle,
+    # repeatable to the bit (two addends onto zero give the same sum in either order), and within the
+    # tolerance of the whole-K launch (FP4_GEMM_SPLIT=0).
+    _announce("gemm-split", fmt, m, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=69, mat=k)
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.activations(m, k, cfg=69, mat=m)
+    x = gc.x_tensor(x_bits)
+    ys = []
+    for _ in range(3):
+        y = torch.full((m, n), float("nan"), device="cuda")
+        fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    gc.check_product(fmt, packed, x_bits, ys[0], label=f"gemm-split {fmt} M={m} {n}x{k}")
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+    monkeypatch.setenv("FP4_GEMM_SPLIT", "0")
+    y_whole = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_whole)
+    torch.cuda.synchronize()
+    gc.check_product(fmt, packed, x_bits, y_whole, label=f"gemm-whole {fmt} M={m} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", gc.FMTS)
 def test_gemm_identity_returns_weights_exactly(fmt):
     # x = I (M = K) gives y = W32^T exactly
     n, k = 96, 256
