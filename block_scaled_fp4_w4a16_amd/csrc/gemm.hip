@@ -366,12 +366,17 @@ __device__ __forceinline__ void prep_slice(KOps<MI>& nx, BDec (&d)[2], const WRe
 
 // The B dequantization pieces (b_sub) that run after MFMA slot SLOT (0 .. 2 MI - 1) of a k-step. With 16
 // MFMAs (MI = 8) slot s takes piece s % 8 of operand s / 8; with 12 (MI = 6) each operand's six slots take
-// pieces 0, 1, 2, 3, then 4 and 5, then 6 and 7.
+// pieces 0, 1, 2, 3, then 4 and 5, then 6 and 7; with 8 (MI = 4) slot s takes pieces 2 (s % 4) and
+// 2 (s % 4) + 1 of operand s / 4.
 template <int F, int MI, int S, int SLOT>
 __device__ __forceinline__ void b_slot(BDec (&d)[2], u32x4 (&b)[2], const WRegs& r) {
   if constexpr (MI == 8) {
     constexpr int t = SLOT >> 3, q = SLOT & 7;
     b_sub<F, S, q>(d[t], b[t], r, t);
+  } else if constexpr (MI == 4) {
+    constexpr int t = SLOT >> 2, q = 2 * (SLOT & 3);
+    b_sub<F, S, q>(d[t], b[t], r, t);
+    b_sub<F, S, q + 1>(d[t], b[t], r, t);
   } else {
     constexpr int t = SLOT / 6, q = SLOT % 6;
     if constexpr (q < 4) {
@@ -622,14 +627,16 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 //    rows 1536 .. M - 1 (tiles_m - 6 bands) of column tiles 0 .. ns - 1.
 // With ns = 0 every tile is 256 rows: workgroup i takes band i % tiles_m and column tile i / tiles_m.
 // ksplit > 0 (grids of at most a quarter of the CUs, ns = 0): workgroup b < nbig takes stages 0 .. ksplit
-// - 1 of tile b, workgroup nbig + b the rest, and both add into the zeroed y.
+// - 1 of tile b, workgroup nbig + b the rest, and both add into the zeroed y. rows128 (M <= 128, one band,
+// ns = 0): every tile is 128 rows (4 MFMA row blocks per wave), so no MFMA multiplies padding rows 128 ..
+// 255.
 // Block b runs on XCD b % 8, so with 8 bands the workgroups of one XCD share an x band in its L2.
 template <int F, bool RAGGED>
 __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restrict__ qp,
                                                           const uint8_t* __restrict__ sp,
                                                           const uint16_t* __restrict__ x, float* __restrict__ y,
                                                           int M, int N, int K, int nchunk, int tiles_m, int ns,
-                                                          int nbig, float gscale, int ksplit) {
+                                                          int nbig, float gscale, int ksplit, int rows128) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   int b = (int)blockIdx.x;
   int hb = 0, he = 2 * nchunk;
@@ -639,7 +646,9 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
     hb = second ? ksplit : 0;
     he = second ? he : ksplit;
   }
-  if (b < nbig) {
+  if (rows128) {
+    gemm_tile<F, 4, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, 0, b * GM_BN, gscale, hb, he, ksplit > 0);
+  } else if (b < nbig) {
     const int tiles_n = (N + GM_BN - 1) / GM_BN;
     const int nwide = tiles_m * (tiles_n - ns);
     int m0, n0;
@@ -716,8 +725,12 @@ static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, co
   }
   static Fp4LdsLimit lds_limit;
   lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
+  int rows128 = (M <= 128) ? 1 : 0;  // one band (tiles_m = 1, ns = 0)
+  if (const char* e = getenv("FP4_GEMM_ROWS128")) {  // tuning override: 0 = 256-row tiles
+    if (atoi(e) == 0) rows128 = 0;
+  }
   hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K, nchunk,
-                     tiles_m, ns, nbig, g, ksplit);
+                     tiles_m, ns, nbig, g, ksplit, rows128);
 }
 
 template <int F>
