@@ -627,16 +627,16 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 //    rows 1536 .. M - 1 (tiles_m - 6 bands) of column tiles 0 .. ns - 1.
 // With ns = 0 every tile is 256 rows: workgroup i takes band i % tiles_m and column tile i / tiles_m.
 // ksplit > 0 (grids of at most a quarter of the CUs, ns = 0): workgroup b < nbig takes stages 0 .. ksplit
-// - 1 of tile b, workgroup nbig + b the rest, and both add into the zeroed y. rows128 (M <= 128, one band,
-// ns = 0): every tile is 128 rows (4 MFMA row blocks per wave), so no MFMA multiplies padding rows 128 ..
-// 255.
+// - 1 of tile b, workgroup nbig + b the rest, and both add into the zeroed y. band_rows = 128 or 192
+// (M at most that, one band, ns = 0): every tile is that many rows (4 or 6 MFMA row blocks per wave), so
+// fewer MFMAs multiply padding rows.
 // Block b runs on XCD b % 8, so with 8 bands the workgroups of one XCD share an x band in its L2.
 template <int F, bool RAGGED>
 __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restrict__ qp,
                                                           const uint8_t* __restrict__ sp,
                                                           const uint16_t* __restrict__ x, float* __restrict__ y,
                                                           int M, int N, int K, int nchunk, int tiles_m, int ns,
-                                                          int nbig, float gscale, int ksplit, int rows128) {
+                                                          int nbig, float gscale, int ksplit, int band_rows) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   int b = (int)blockIdx.x;
   int hb = 0, he = 2 * nchunk;
@@ -646,8 +646,10 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
     hb = second ? ksplit : 0;
     he = second ? he : ksplit;
   }
-  if (rows128) {
+  if (band_rows == 128) {
     gemm_tile<F, 4, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, 0, b * GM_BN, gscale, hb, he, ksplit > 0);
+  } else if (band_rows == 192) {
+    gemm_tile<F, 6, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, 0, b * GM_BN, gscale, hb, he, ksplit > 0);
   } else if (b < nbig) {
     const int tiles_n = (N + GM_BN - 1) / GM_BN;
     const int nwide = tiles_m * (tiles_n - ns);
@@ -725,12 +727,13 @@ static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, co
   }
   static Fp4LdsLimit lds_limit;
   lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
-  int rows128 = (M <= 128) ? 1 : 0;  // one band (tiles_m = 1, ns = 0)
-  if (const char* e = getenv("FP4_GEMM_ROWS128")) {  // tuning override: 0 = 256-row tiles
-    if (atoi(e) == 0) rows128 = 0;
+  // one band (tiles_m = 1, ns = 0): tiles only as high as M needs, 128 or 192 rows
+  int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
+  if (const char* e = getenv("FP4_GEMM_BAND_ROWS")) {  // tuning override: 0 = 256-row tiles
+    if (atoi(e) == 0) band_rows = 0;
   }
   hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K, nchunk,
-                     tiles_m, ns, nbig, g, ksplit, rows128);
+                     tiles_m, ns, nbig, g, ksplit, band_rows);
 }
 
 template <int F>

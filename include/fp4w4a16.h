@@ -133,8 +133,8 @@ int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items
  * at least 6 chunks of 128, K is split in two: the call enqueues a kernel that zeroes y, then
  * the product, whose two halves add their g-scaled sums into y with FP32 atomics. Two addends
  * onto zero give the same sum in either order, so the result is still bit-reproducible; it
- * differs from the whole-K sum only by rounding. Both kernels run on `stream`. For M <= 128 the
- * tiles are 128 rows high (same products, same order, same bits as 256-row tiles).
+ * differs from the whole-K sum only by rounding. Both kernels run on `stream`. For M <= 128 (192)
+ * the tiles are 128 (192) rows high: same products, same order, same bits as 256-row tiles.
  */
 int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);

@@ -460,12 +460,13 @@ def test_gemm_split_k(fmt, m, n, k, monkeypatch):
 
 
 @pytest.mark.parametrize("fmt", gc.FMTS)
-@pytest.mark.parametrize("m", [65, 128])
-def test_gemm_rows128_tiles(fmt, m, monkeypatch):
-    # M <= 128 runs 128-row tiles: the same products in the same order as the 256-row tiling whose padding
-    # rows it skips, so the outputs are bitwise equal (K = 1152 also takes the two-way split).
+@pytest.mark.parametrize("m", [65, 128, 129, 192])
+def test_gemm_band_row_tiles(fmt, m, monkeypatch):
+    # M <= 128 runs 128-row tiles and M <= 192 192-row tiles: the same products in the same order as the
+    # 256-row tiling whose padding rows they skip, so the outputs are bitwise equal (K = 1152 also takes the
+    # two-way split).
     n, k = 600, 1152
-    _announce("gemm-rows128", fmt, m, n, k)
+    _announce("gemm-band-rows", fmt, m, n, k)
     w, packed = gc.make_case(fmt, n, k, cfg=70, mat=m)
     pw = gc.upload(fmt, n, k, packed)
     x_bits = synth.activations(m, k, cfg=70, mat=m)
@@ -473,8 +474,8 @@ def test_gemm_rows128_tiles(fmt, m, monkeypatch):
     y = torch.full((m, n), float("nan"), device="cuda")
     fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
     torch.cuda.synchronize()
-    gc.check_product(fmt, packed, x_bits, y, label=f"gemm-rows128 {fmt} M={m}")
-    monkeypatch.setenv("FP4_GEMM_ROWS128", "0")
+    gc.check_product(fmt, packed, x_bits, y, label=f"gemm-band-rows {fmt} M={m}")
+    monkeypatch.setenv("FP4_GEMM_BAND_ROWS", "0")
     y256 = torch.full((m, n), float("nan"), device="cuda")
     fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y256)
     torch.cuda.synchronize()
