@@ -626,31 +626,16 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 //  * 256-row tiles: first column tiles ns .. tiles_n - 1 over all tiles_m bands (band = i % tiles_m), then
 //    rows 1536 .. M - 1 (tiles_m - 6 bands) of column tiles 0 .. ns - 1.
 // With ns = 0 every tile is 256 rows: workgroup i takes band i % tiles_m and column tile i / tiles_m.
-// ksplit > 0 (grids of at most a quarter of the CUs, ns = 0): workgroup b < nbig takes stages 0 .. ksplit
-// - 1 of tile b, workgroup nbig + b the rest, and both add into the zeroed y. band_rows = 128 or 192
-// (M at most that, one band, ns = 0): every tile is that many rows (4 or 6 MFMA row blocks per wave), so
-// fewer MFMAs multiply padding rows.
 // Block b runs on XCD b % 8, so with 8 bands the workgroups of one XCD share an x band in its L2.
 template <int F, bool RAGGED>
 __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restrict__ qp,
                                                           const uint8_t* __restrict__ sp,
                                                           const uint16_t* __restrict__ x, float* __restrict__ y,
                                                           int M, int N, int K, int nchunk, int tiles_m, int ns,
-                                                          int nbig, float gscale, int ksplit, int band_rows) {
+                                                          int nbig, float gscale) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
-  int b = (int)blockIdx.x;
-  int hb = 0, he = 2 * nchunk;
-  if (ksplit > 0) {
-    const bool second = b >= nbig;
-    if (second) b -= nbig;
-    hb = second ? ksplit : 0;
-    he = second ? he : ksplit;
-  }
-  if (band_rows == 128) {
-    gemm_tile<F, 4, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, 0, b * GM_BN, gscale, hb, he, ksplit > 0);
-  } else if (band_rows == 192) {
-    gemm_tile<F, 6, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, 0, b * GM_BN, gscale, hb, he, ksplit > 0);
-  } else if (b < nbig) {
+  const int b = (int)blockIdx.x;
+  if (b < nbig) {
     const int tiles_n = (N + GM_BN - 1) / GM_BN;
     const int nwide = tiles_m * (tiles_n - ns);
     int m0, n0;
@@ -662,12 +647,36 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
       m0 = GM_SHORT_BANDS * GM_SHORT_ROWS + (i % bands) * GM_BM;
       n0 = (i / bands) * GM_BN;
     }
-    gemm_tile<F, 8, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, m0, n0, gscale, hb, he, ksplit > 0);
+    gemm_tile<F, 8, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, m0, n0, gscale, 0, 2 * nchunk, false);
   } else {
     const int i = b - nbig;
     gemm_tile<F, 6, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, (i % GM_SHORT_BANDS) * GM_SHORT_ROWS,
-                            (i / GM_SHORT_BANDS) * GM_BN, gscale, hb, he, false);
+                            (i / GM_SHORT_BANDS) * GM_BN, gscale, 0, 2 * nchunk, false);
   }
+}
+
+// Grids of at most a quarter of the CUs (a kernel of its own, so that the prefill kernel above keeps its
+// code): tiles of 32 MI rows (MI = 4 or 6 when M fits one such band, else 8), tile t taking band t %
+// tiles_m and column tile t / tiles_m. ksplit > 0: workgroup t < ntiles takes stages 0 .. ksplit - 1 of
+// tile t, workgroup ntiles + t the rest, and both add into the zeroed y.
+template <int F, bool RAGGED, int MI>
+__global__ __launch_bounds__(GM_THREADS) void gemm_small_kernel(const uint8_t* __restrict__ qp,
+                                                                const uint8_t* __restrict__ sp,
+                                                                const uint16_t* __restrict__ x,
+                                                                float* __restrict__ y, int M, int N, int K,
+                                                                int nchunk, int tiles_m, int ntiles, float gscale,
+                                                                int ksplit) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  int t = (int)blockIdx.x;
+  int hb = 0, he = 2 * nchunk;
+  if (ksplit > 0) {
+    const bool second = t >= ntiles;
+    if (second) t -= ntiles;
+    hb = second ? ksplit : 0;
+    he = second ? he : ksplit;
+  }
+  gemm_tile<F, MI, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, (t % tiles_m) * 32 * MI, (t / tiles_m) * GM_BN, gscale,
+                           hb, he, ksplit > 0);
 }
 
 // y = 0 before the parts of a split K add into it (a kernel, not a memset, so that the call can be
@@ -687,6 +696,15 @@ static int gemm_device_cus() {
     cache[dev].store(c, std::memory_order_relaxed);
   }
   return c;
+}
+
+template <int F, bool RAGGED, int MI>
+static void launch_gemm_small(hipStream_t st, int grid, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                              int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit) {
+  static Fp4LdsLimit lds_limit;
+  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI>), GM_LDS);
+  hipLaunchKernelGGL((gemm_small_kernel<F, RAGGED, MI>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K,
+                     nchunk, tiles_m, ntiles, g, ksplit);
 }
 
 template <int F, bool RAGGED>
@@ -719,21 +737,27 @@ static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, co
   if (const char* e = getenv("FP4_GEMM_SPLIT")) {  // tuning override: 0 = whole K per workgroup
     if (atoi(e) == 0) ksplit = 0;
   }
-  const int grid = ksplit ? 2 * nbig : nbig + GM_SHORT_BANDS * ns;
+  // one band: tiles only as high as M needs, 128 or 192 rows
+  int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
+  if (const char* e = getenv("FP4_GEMM_BAND_ROWS")) {  // tuning override: 0 = 256-row tiles
+    if (atoi(e) == 0) band_rows = 0;
+  }
+  if (ksplit == 0 && band_rows == 0) {
+    static Fp4LdsLimit lds_limit;
+    lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
+    hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(nbig + GM_SHORT_BANDS * ns), dim3(GM_THREADS), GM_LDS, st, q, s,
+                       x, y, M, N, K, nchunk, tiles_m, ns, nbig, g);
+    return;
+  }
   if (ksplit) {
     const int64_t total = (int64_t)M * N;
     const int zb = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
     hipLaunchKernelGGL(gemm_zero_kernel, dim3(zb), dim3(256), 0, st, y, total);
   }
-  static Fp4LdsLimit lds_limit;
-  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
-  // one band (tiles_m = 1, ns = 0): tiles only as high as M needs, 128 or 192 rows
-  int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
-  if (const char* e = getenv("FP4_GEMM_BAND_ROWS")) {  // tuning override: 0 = 256-row tiles
-    if (atoi(e) == 0) band_rows = 0;
-  }
-  hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K, nchunk,
-                     tiles_m, ns, nbig, g, ksplit, band_rows);
+  const int grid = ksplit ? 2 * (int)U : (int)U;
+  if (band_rows == 128) launch_gemm_small<F, RAGGED, 4>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
+  else if (band_rows) launch_gemm_small<F, RAGGED, 6>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
+  else launch_gemm_small<F, RAGGED, 8>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)U, g, ksplit);
 }
 
 template <int F>
