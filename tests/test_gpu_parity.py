@@ -482,6 +482,32 @@ def test_gemm_band_row_tiles(fmt, m, monkeypatch):
     assert torch.equal(y, y256)
 
 
+def test_gemm_split_in_graph():
+    # The split-K GEMM enqueues a zero-fill kernel and the product: captured in a graph (on torch's capture
+    # stream) and replayed several times, with eager work and synchronizations between the replays, every
+    # replay gives the eager result bit for bit.
+    fmt, m, n, k = "rocmfp4_fast", 128, 512, 2048
+    _announce("gemm-split-graph", fmt, m, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=71)
+    pw = gc.upload(fmt, n, k, packed)
+    x = gc.x_tensor(synth.activations(m, k, cfg=71))
+    y_eager = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_eager)
+    torch.cuda.synchronize()
+    y = torch.full((m, n), float("nan"), device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+    for rep in range(4):
+        y.fill_(float("nan") if rep % 2 else 7.0)
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {rep} differs"
+        del junk
+
+
 @pytest.mark.parametrize("fmt", gc.FMTS)
 def test_gemm_identity_returns_weights_exactly(fmt):
     # x = I (M = K) gives y = W32^T exactly
