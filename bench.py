@@ -161,13 +161,13 @@ def bench_gemv(fp4, torch, synth, name: str, steps: int, warmup: int):
                 gbs=abytes / per_launch / 1e9, y0=y0.cpu().numpy(), x_bits=x_bits, w_np=w_np)
 
 
-def bench_gemm(fp4, torch, synth, fmt: str, steps: int, warmup: int):
+def bench_gemm(fp4, torch, synth, fmt: str, steps: int, warmup: int, m: int = 2048, pw=None):
     cfg, mat = 4, 0
     n, k = synth.WORKLOADS[cfg]["shapes"][mat]
-    m = 2048
-    w_np = synth.workload_weights(cfg, mat)
-    pw = pack_on_gpu(fp4, torch, fmt, w_np)
-    del w_np
+    if pw is None:
+        w_np = synth.workload_weights(cfg, mat)
+        pw = pack_on_gpu(fp4, torch, fmt, w_np)
+        del w_np
     x_bits = synth.workload_activations(cfg, mat, m)
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
@@ -179,7 +179,7 @@ def bench_gemm(fp4, torch, synth, fmt: str, steps: int, warmup: int):
     secs = time_launches(torch, launch, copies, steps, warmup)
     per = secs / steps
     flops = 2.0 * m * n * k
-    return dict(fmt=fmt, m=m, n=n, k=k, per_launch_s=per, tflops=flops / per / 1e12)
+    return dict(fmt=fmt, m=m, n=n, k=k, per_launch_s=per, tflops=flops / per / 1e12, pw=pw)
 
 
 def host_threads() -> int:
@@ -298,6 +298,7 @@ def main():
     ap.add_argument("--gemm-steps", type=int, default=200)
     ap.add_argument("--gemm-warmup", type=int, default=200)
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-gemm-small", action="store_true", help="skip the M = 128, 256, 512 GEMM figures")
     ap.add_argument("--no-spec", action="store_true", help="skip the speculative-verify shapes (M = 1, 9, 16)")
     ap.add_argument("--spec-steps", type=int, default=2000)
     ap.add_argument("--no-cpu", action="store_true")
@@ -337,6 +338,15 @@ def main():
         gm_nv = bench_gemm(fp4, torch, synth, "nvfp4", args.gemm_steps, args.gemm_warmup)
         print(f"# gemm NVFP4 M=2048: {gm_nv['per_launch_s'] * 1e6:.1f} us/launch, {gm_nv['tflops']:.1f} TFLOP/s "
               f"({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
+        # the same FAST matrix at prefill-chunk sizes (small grids: two-way K split, 128/192-row tiles);
+        # one weight copy, so the weights stay in the last-level cache between launches
+        t1 = time.time()
+        gm_small = {}
+        for m_small in (() if args.no_gemm_small else (128, 256, 512)):
+            r = bench_gemm(fp4, torch, synth, "rocmfp4_fast", 400, 200, m=m_small, pw=gm["pw"])
+            gm_small[f"m{m_small}"] = {"us_per_launch": round(r["per_launch_s"] * 1e6, 2),
+                                       "TFLOP/s": round(r["tflops"], 1)}
+        print(f"# gemm FAST small M: {gm_small} ({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
 
     spec = None
     if not args.no_spec:
@@ -400,7 +410,8 @@ def main():
                                      "traffic": traffic_from_profiles("gemm.hip", "rocmfp4_fast_prefill_m2048")},
                         "nvfp4": {"workload": "nvfp4_prefill_m2048_k4096_n14336", "value": round(gm_nv["tflops"], 2),
                                   "us_per_launch": round(gm_nv["per_launch_s"] * 1e6, 2),
-                                  "frac": round(gm_nv["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}}
+                                  "frac": round(gm_nv["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)},
+                        "small_m": {"workload": "rocmfp4_fast k4096 n14336 at M = 128, 256, 512", **gm_small}}
     if spec:
         line["spec_verify"] = {"workload": "speculative verify, gate 9728x2560 and down 2560x9728, M = 1, 9, 16",
                                "unit": "GB/s of weight + scale bytes", "steps": args.spec_steps, "results": spec}
