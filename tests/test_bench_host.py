@@ -1,0 +1,48 @@
+"""Host-side logic of bench.py (CPU only): algorithmic byte counts, the stale-counter rule, --gpus."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_match_the_format_densities():
+    # 4.5 bits per weight for NVFP4 (4-bit code + one 8-bit scale per 16) and Dual (18 B per 32 weights),
+    # 4.25 for FAST (17 B per 32)
+    assert bench.algorithmic_bytes("nvfp4", 2048, 2048) == 2048 * 2048 * 9 // 16 == 2_359_296
+    assert bench.algorithmic_bytes("rocmfp4_dual", 4096, 4096) == 4096 * 128 * 18 == 9_437_184
+    assert bench.algorithmic_bytes("rocmfp4_fast", 14336, 4096) == 14336 * 128 * 17 == 31_195_136
+    assert bench.algorithmic_bytes("nvfp4", 14336, 4096) == 33_030_144
+    assert bench.algorithmic_bytes("rocmfp4_dual", 9728, 2560) == bench.algorithmic_bytes("nvfp4", 9728, 2560)
+    assert bench.algorithmic_bytes("rocmfp4_fast", 9728, 2560) == 9728 * 80 * 17
+
+
+def test_decode_sweep_bytes():
+    # 36 layers of q, k, v, o, gate, up, down in NVFP4
+    total = sum(bench.algorithmic_bytes("nvfp4", n, k) for (n, k) in synth.WORKLOADS[2]["shapes"])
+    assert len(synth.WORKLOADS[2]["shapes"]) == 252
+    assert total == 36 * (2 * 5_898_240 + 2 * 1_474_560 + 3 * 14_008_320) == 2_043_740_160
+
+
+def test_traffic_is_dropped_when_the_kernel_source_changed(monkeypatch):
+    # a counter figure is reported only while the kernel source it was taken on is unchanged
+    real = bench.kernel_source_hash("gemv.hip")
+    got = bench.traffic_from_profiles("gemv.hip", "rocmfp4_dual_4096x4096_m1")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda name: real[::-1])
+    assert bench.traffic_from_profiles("gemv.hip", "rocmfp4_dual_4096x4096_m1") is None
+    monkeypatch.undo()
+    if got is not None:
+        assert 9_437_184 <= got < 2 * 9_437_184
+    assert bench.traffic_from_profiles("gemv.hip", "no_such_workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout
