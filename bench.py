@@ -1,23 +1,39 @@
 """Benchmark of the W4A16 hot path on one MI355X.
 
-Default workload: ROCmFP4 Dual 4096 x 4096, M = 1 (decode GEMV), plus the prefill GEMM
-(ROCmFP4 FAST, M = 2048, K = 4096, N = 14336) reported in the same JSON line.
+Headline (`value`): ROCmFP4 Dual 4096 x 4096, M = 1 (a decode GEMV), in GB/s of weight + scale bytes.
+The same JSON line carries every other workload, each with its own roofline fraction:
+  * NVFP4 2048 x 2048, M = 1;
+  * the 4B-class decode sweep (36 layers x q, k, v, o, gate, up, down; NVFP4, M = 1), grouped launches
+    and one launch per matrix;
+  * speculative verify / small batch: gate 9728 x 2560 and down 2560 x 9728 at M = 1, 9, 16 in NVFP4,
+    Dual and FAST (M = 9 is one token plus eight n-gram drafts);
+  * the prefill GEMM, M = 2048, K = 4096, N = 14336, in FAST and NVFP4 (TFLOP/s), and the same matrix at
+    M = 128, 256, 512;
+  * a plain streaming read of the same byte counts (the ceiling launch cost and memory latency leave).
 
-A step is one GEMV launch over one packed matrix. Weights are drawn by `synth`, packed on the
-GPU by the library's own packer (fp4_quantize_*), repacked to kernel layout and replicated into
-enough distinct copies (>= 1 GiB) that every launch reads its matrix from HBM rather than from
-the 256 MB last-level cache. Launches are recorded into HIP graphs on torch's current stream and
-timed with HIP events on that stream between synchronisations; `value` is weight + scale bytes
-per launch divided by the average launch time.
+A step of a GEMV workload is one launch over one packed matrix. Weights are drawn by `synth`, packed on
+the GPU by the library's own packers and replicated into distinct copies totalling >= 1 GiB, so every
+launch reads its matrix from HBM, not from the 256 MB last-level cache. Launch i reads copy i % copies.
 
-The `cpu_baseline` leg times the CPU oracle (exact dequantisation + FP64 product) on a bounded
-row sample of the same workload, packed by the oracle itself.
+Timing protocol (per workload): K timed steps are captured in HIP graphs (one graph of min(K, copies)
+launches, replayed, plus one for the remainder); every graph is replayed during warm-up before any
+timing. Each of R repetitions replays an untimed filler graph (the other copies, so that the timed
+copies are cold and the GPU queue is never empty at the start event), then the timed graphs between two
+HIP events on torch's current stream (the stream the graphs launch on). Reported: the median per-step
+time over the R repetitions, min, max, max/min and the raw samples, and the shader clock read by a probe
+kernel enqueued right after each timed block.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+The CPU baseline (`cpu_baseline`) times the oracle (exact dequantisation + FP64 product) on a bounded
+row sample of each workload, packed by the oracle's own packers, on every core of this process's
+affinity mask, and compares the GPU output on the same rows with it: a workload whose sample fails that
+check is reported with "parity": false and no throughput.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--only NAME[,NAME...]]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -29,29 +45,27 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 COLD_BYTES = 1 << 30            # 4x the 256 MB last-level cache
 BLOCK_BYTES = {"rocmfp4_dual": 18, "rocmfp4_fast": 17, "q4_0": 18}
+HEADLINE = "rocmfp4_dual_4096x4096_m1"
 
+# One-matrix GEMV workloads: name -> (synth workload id, matrix index, fmt, M)
 WORKLOADS = {
-    # name: (synth cfg, matrix index, fmt, M)
     "rocmfp4_dual_4096x4096_m1": (1, 0, "rocmfp4_dual", 1),
     "nvfp4_2048x2048_m1": (0, 0, "nvfp4", 1),
-    "nvfp4_gate_9728x2560_m1": (3, 0, "nvfp4", 1),
-    "rocmfp4_dual_gate_9728x2560_m1": (3, 0, "rocmfp4_dual", 1),
-    "rocmfp4_fast_gate_9728x2560_m1": (3, 0, "rocmfp4_fast", 1),
-    "nvfp4_down_2560x9728_m1": (3, 1, "nvfp4", 1),
-    "rocmfp4_dual_down_2560x9728_m1": (3, 1, "rocmfp4_dual", 1),
-    "rocmfp4_fast_down_2560x9728_m1": (3, 1, "rocmfp4_fast", 1),
+    "q4_0_4096x4096_m1": (1, 0, "q4_0", 1),          # the Dual matrix in stock Q4_0 (same bytes)
 }
-WORKLOADS["q4_0_4096x4096_m1"] = (1, 0, "q4_0", 1)          # the Dual matrix in stock Q4_0 (same bytes)
-WORKLOADS["q4_0_gate_9728x2560_m1"] = (3, 0, "q4_0", 1)
-WORKLOADS["q4_0_down_2560x9728_m1"] = (3, 1, "q4_0", 1)
-for _m in (9, 16):
-    for _f in ("nvfp4", "rocmfp4_dual", "rocmfp4_fast", "q4_0"):
-        WORKLOADS[f"{_f}_gate_9728x2560_m{_m}"] = (3, 0, _f, _m)
-        WORKLOADS[f"{_f}_down_2560x9728_m{_m}"] = (3, 1, _f, _m)
+SPEC_FMTS = ("nvfp4", "rocmfp4_dual", "rocmfp4_fast")
+SPEC_SHAPES = (("gate_9728x2560", 0), ("down_2560x9728", 1))
+SPEC_MS = (1, 9, 16)
+for _f in SPEC_FMTS + ("q4_0",):
+    for _shape, _mat in SPEC_SHAPES:
+        for _m in SPEC_MS:
+            WORKLOADS[f"{_f}_{_shape}_m{_m}"] = (3, _mat, _f, _m)
+
+SECTIONS = ("headline", "nvfp4_2048", "spec", "gemm", "gemm_small", "sweep", "read_probe")
 
 
 def algorithmic_bytes(fmt: str, n: int, k: int) -> int:
@@ -83,30 +97,68 @@ def traffic_from_profiles(kernel_file: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
+def host_threads() -> int:
+    """Host cores this process may run on (its affinity mask)."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 # ----------------------------------------------------------------------------------------------
-def pack_on_gpu(fp4, torch, fmt: str, w_np: np.ndarray):
-    """synth fp32 weights -> device packer -> kernel layout (all on the GPU, no oracle)."""
-    w = torch.from_numpy(w_np).cuda()
-    pw = fp4.PackedWeight.quantize(fmt, w)
-    del w
-    return pw
+class Probes:
+    """The benchmark's measurement kernels (libfp4probe.so): a plain streaming read and a clock probe."""
 
+    def __init__(self, torch):
+        path = os.path.join(ROOT, "block_scaled_fp4_w4a16_amd", "libfp4probe.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with block_scaled_fp4_w4a16_amd/build.py")
+        self.torch = torch
+        self.lib = ctypes.CDLL(path)
+        self.lib.fp4probe_read.restype = ctypes.c_int
+        self.lib.fp4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.fp4probe_clock.restype = ctypes.c_int
+        self.lib.fp4probe_clock.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+        self.clk = torch.zeros(2, dtype=torch.int64, device="cuda")
 
-def replicate(torch, pw, copies: int):
-    qs = [pw.q] + [pw.q.clone() for _ in range(copies - 1)]
-    ss = [pw.s] + [pw.s.clone() for _ in range(copies - 1)]
-    return qs, ss
+    def read(self, ptr: int, nbytes: int):
+        rc = self.lib.fp4probe_read(ptr, nbytes, self.sink.data_ptr(), self.torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"read probe launch failed ({rc})")
+
+    def clock_launch(self, ticks: int = 300):
+        """Enqueue the clock probe (a busy wait of `ticks` 100 MHz ticks) on the current stream."""
+        rc = self.lib.fp4probe_clock(ticks, self.clk.data_ptr(), self.torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"clock probe launch failed ({rc})")
+
+    def clock_mhz(self) -> float:
+        cycles, ticks = (int(v) for v in self.clk.cpu().tolist())
+        return 100.0 * cycles / ticks if ticks > 0 else float("nan")
 
 
 def graph_of(torch, fn, launches):
-    """Capture `launches` calls fn(i) into one HIP graph (the library launches on the capture stream)."""
+    """Capture fn(i) for i in `launches` into one HIP graph (the library launches on the capture stream)."""
+    launches = list(launches)
+    if not launches:
+        return None
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for i in launches:  # warm the code path outside capture once
-            fn(i)
-            break
+        fn(launches[0])  # warm the host code path outside capture once
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
@@ -116,89 +168,143 @@ def graph_of(torch, fn, launches):
     return g
 
 
-def time_launches(torch, fn, copies: int, steps: int, warmup: int):
-    """Run `steps` launches (launch i uses copy i % copies) as graph replays; return seconds."""
-    g_full = graph_of(torch, fn, range(copies))
-    rem = steps % copies
-    g_rem = graph_of(torch, fn, range(rem)) if rem else None
-    for _ in range(max(1, warmup // copies)):
-        g_full.replay()
+def time_steps(torch, fn, copies: int, steps: int, warmup: int, reps: int, probes=None, filler: int | None = None):
+    """Time `steps` launches fn(i) (launch i reads copy i % copies) `reps` times; see the module docstring.
+
+    Returns per-step seconds (median, min, max, samples), the shader clock after each timed block, and the
+    graph shape."""
+    L = max(1, min(steps, copies))
+    q, r = divmod(steps, L)
+    g_main = graph_of(torch, fn, range(L))
+    g_rem = graph_of(torch, fn, range(r))
+    fill = range(L, copies) if L < copies else range(filler if filler is not None else copies)
+    g_fill = graph_of(torch, fn, fill)
+    graphs = [g for g in (g_fill, g_main, g_rem) if g is not None]
+    per_round = len(fill) + L + r
+    done = 0
+    while done < max(warmup, 1):
+        for g in graphs:
+            g.replay()
+        done += per_round
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps // copies):
-        g_full.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3
+    samples, clocks = [], []
+    for _ in range(reps):
+        if g_fill is not None:
+            g_fill.replay()
+        start.record()
+        for _ in range(q):
+            g_main.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        end.record()
+        if probes is not None:
+            probes.clock_launch()
+        torch.cuda.synchronize()
+        samples.append(start.elapsed_time(end) / 1e3 / steps)
+        if probes is not None:
+            clocks.append(probes.clock_mhz())
+    med = float(np.median(samples))
+    return dict(median_s=med, min_s=float(min(samples)), max_s=float(max(samples)), samples_s=samples,
+                clock_mhz=float(np.median(clocks)) if clocks else None, launches_per_graph=L,
+                graph_replays_per_rep=q + (1 if r else 0), reps=reps, steps=steps)
 
 
-def bench_gemv(fp4, torch, synth, name: str, steps: int, warmup: int):
+def timing_fields(t: dict) -> dict:
+    return {"us_median": round(t["median_s"] * 1e6, 3), "us_min": round(t["min_s"] * 1e6, 3),
+            "us_max": round(t["max_s"] * 1e6, 3), "spread": round(t["max_s"] / t["min_s"], 4),
+            "samples_us": [round(v * 1e6, 3) for v in t["samples_s"]], "reps": t["reps"],
+            "steps_per_rep": t["steps"], "launches_per_graph": t["launches_per_graph"],
+            "shader_clock_mhz": None if t["clock_mhz"] is None else round(t["clock_mhz"], 1)}
+
+
+def hbm_roofline(nbytes: int, t: dict, traffic=None) -> dict:
+    gbs = nbytes / t["median_s"] / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+# ----------------------------------------------------------------------------------------------
+def pack_on_gpu(fp4, torch, fmt: str, w_np: np.ndarray):
+    """synth fp32 weights -> the library's device packer -> kernel layout (no oracle)."""
+    w = torch.from_numpy(w_np).cuda()
+    pw = fp4.PackedWeight.quantize(fmt, w)
+    del w
+    return pw
+
+
+def bench_gemv(fp4, torch, synth, name: str, steps: int, warmup: int, reps: int, probes):
     cfg, mat, fmt, m = WORKLOADS[name]
     n, k = synth.WORKLOADS[cfg]["shapes"][mat]
     w_np = synth.workload_weights(cfg, mat)
     pw = pack_on_gpu(fp4, torch, fmt, w_np)
     plane_bytes = pw.q.numel() + pw.s.numel()
     copies = max(2, -(-COLD_BYTES // plane_bytes))
-    qs, ss = replicate(torch, pw, copies)
+    qs = [pw.q] + [pw.q.clone() for _ in range(copies - 1)]
+    ss = [pw.s] + [pw.s.clone() for _ in range(copies - 1)]
     x_bits = synth.workload_activations(cfg, mat, m)
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
     ys = [torch.empty((m, n), dtype=torch.float32, device="cuda") for _ in range(min(copies, 8))]
 
     def launch(i):
-        fp4.w4a16_gemv(fmt, m, n, k, qs[i], ss[i], pw.global_scale, x, ys[i % len(ys)])
+        fp4.w4a16_gemv(fmt, m, n, k, qs[i % copies], ss[i % copies], pw.global_scale, x, ys[i % len(ys)])
 
-    secs = time_launches(torch, launch, copies, steps, warmup)
-    per_launch = secs / steps
-    abytes = algorithmic_bytes(fmt, n, k)
+    t = time_steps(torch, launch, copies, steps, warmup, reps, probes)
     y0 = torch.empty((m, n), dtype=torch.float32, device="cuda")
     fp4.w4a16_gemv(fmt, m, n, k, qs[0], ss[0], pw.global_scale, x, y0)
     torch.cuda.synchronize()
-    return dict(fmt=fmt, n=n, k=k, m=m, copies=copies, per_launch_s=per_launch, bytes=abytes,
-                gbs=abytes / per_launch / 1e9, y0=y0.cpu().numpy(), x_bits=x_bits, w_np=w_np)
+    del qs, ss
+    return dict(name=name, fmt=fmt, n=n, k=k, m=m, copies=copies, bytes=algorithmic_bytes(fmt, n, k), t=t,
+                y=y0.cpu().numpy(), x_bits=x_bits, w_np=w_np, global_scale=pw.global_scale)
 
 
-def bench_gemm(fp4, torch, synth, fmt: str, steps: int, warmup: int, m: int = 2048, pw=None):
-    cfg, mat = 4, 0
-    n, k = synth.WORKLOADS[cfg]["shapes"][mat]
+def bench_gemm(fp4, torch, synth, fmt: str, m: int, steps: int, warmup: int, reps: int, probes, pw=None):
+    n, k = synth.WORKLOADS[4]["shapes"][0]
     if pw is None:
-        w_np = synth.workload_weights(cfg, mat)
-        pw = pack_on_gpu(fp4, torch, fmt, w_np)
-        del w_np
-    x_bits = synth.workload_activations(cfg, mat, m)
+        pw = pack_on_gpu(fp4, torch, fmt, synth.workload_weights(4, 0))
+    x_bits = synth.workload_activations(4, 0, m)
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
 
-    def launch(i):
+    def launch(_):
         fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
 
-    copies = 1
-    secs = time_launches(torch, launch, copies, steps, warmup)
-    per = secs / steps
+    # the weights and x stay resident in the last-level cache between launches (one copy): the product
+    # is bound by the matrix cores, not by reading them
+    t = time_steps(torch, launch, steps, steps, warmup, reps, probes, filler=min(steps, 20))
+    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+    torch.cuda.synchronize()
     flops = 2.0 * m * n * k
-    return dict(fmt=fmt, m=m, n=n, k=k, per_launch_s=per, tflops=flops / per / 1e12, pw=pw)
+    return dict(fmt=fmt, m=m, n=n, k=k, t=t, tflops=flops / t["median_s"] / 1e12, pw=pw, x_bits=x_bits,
+                y=y.cpu().numpy())
 
 
-def host_threads() -> int:
-    """Host cores this process may use (the affinity mask), at most 16."""
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+def bench_read_probe(torch, probes, nbytes: int, steps: int, warmup: int, reps: int):
+    """The plain streaming read of `nbytes` per launch over >= 1 GiB of distinct slices."""
+    slot = -(-nbytes // 256) * 256
+    copies = max(2, -(-COLD_BYTES // slot))
+    buf = torch.empty(copies * slot, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    base = buf.data_ptr()
+
+    def launch(i):
+        probes.read(base + (i % copies) * slot, nbytes)
+
+    t = time_steps(torch, launch, copies, steps, warmup, reps, probes)
+    del buf
+    return t
 
 
-def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int):
+def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int, reps: int, probes):
     """The 4B-class decode sweep: 36 layers x {q, k, v, o, gate, up, down}, NVFP4, M = 1.
 
     Weights are N(0, 0.02) drawn on the GPU (synth.device_weights) and packed by the library's NVFP4
     packer; all 252 matrices (2.04 GB) stay resident, so each sweep streams them from HBM. A sweep is
     launched per layer the way a decoder consumes it: one grouped launch for q|k|v (same x), one for
     o, one grouped launch for gate|up (same x), one for down -- 144 launches. The same sweep with one
-    launch per matrix (252 launches) is timed beside it. Both are recorded as HIP graphs.
+    launch per matrix (252 launches), and a plain streaming read with the 144 grouped launches' byte
+    counts over the same 2.04 GB, are timed beside it.
     """
     cfg = 2
     layer = synth.DECODE_4B_LAYER
@@ -215,10 +321,12 @@ def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int):
     torch.cuda.synchronize()
 
     def xb(k, mat):
-        return torch.from_numpy(synth.activations(1, k, cfg=cfg, mat=mat).view(np.int16)).view(torch.bfloat16).cuda()
+        return synth.activations(1, k, cfg=cfg, mat=mat)
 
-    xs = [dict(attn=xb(2560, 4 * li), o=xb(4096, 4 * li + 1), mlp=xb(2560, 4 * li + 2), down=xb(9728, 4 * li + 3))
-          for li in range(36)]
+    x_host = [dict(attn=xb(2560, 4 * li), o=xb(4096, 4 * li + 1), mlp=xb(2560, 4 * li + 2), down=xb(9728, 4 * li + 3))
+              for li in range(36)]
+    xs = [{key: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for key, v in d.items()}
+          for d in x_host]
     ys = [[torch.empty((1, n), dtype=torch.float32, device="cuda") for (_, n, _) in layer] for _ in range(36)]
     which_x = ("attn", "attn", "attn", "o", "mlp", "mlp", "down")
 
@@ -226,12 +334,12 @@ def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int):
         pw = mats[li][pi]
         return (pw.q, pw.s, pw.global_scale, xs[li][which_x[pi]], ys[li][pi], pw.N, pw.K)
 
+    groups = ((0, 1, 2), (3,), (4, 5), (6,))
+
     def sweep_grouped(_):
         for li in range(36):
-            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 0), item(li, 1), item(li, 2)])
-            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 3)])
-            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 4), item(li, 5)])
-            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, 6)])
+            for grp in groups:
+                fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, pi) for pi in grp])
 
     def sweep_single(_):
         for li in range(36):
@@ -241,70 +349,107 @@ def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int):
 
     out = dict(bytes=total_bytes)
     for name, fn in (("grouped", sweep_grouped), ("single", sweep_single)):
-        secs = time_launches(torch, fn, 1, steps, warmup)
-        out[name] = secs / steps
+        out[name] = time_steps(torch, fn, 1, steps, warmup, reps, probes, filler=1)
+    # outputs of the grouped sweep for the oracle check (layer 0)
+    sweep_grouped(0)
+    torch.cuda.synchronize()
+    out["layer0_y"] = [ys[0][pi].cpu().numpy() for pi in range(7)]
+    out["layer0_x"] = [x_host[0][which_x[pi]] for pi in range(7)]
+    del mats
+    torch.cuda.empty_cache()
+    # the same 144 launches as plain streaming reads of each launch's bytes, over a 2.04 GB buffer
+    sizes = []
+    for _ in range(36):
+        for grp in groups:
+            sizes.append(sum(algorithmic_bytes("nvfp4", layer[pi][1], layer[pi][2]) for pi in grp))
+    offs = np.concatenate([[0], np.cumsum([-(-b // 256) * 256 for b in sizes])]).astype(np.int64)
+    buf = torch.empty(int(offs[-1]), dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    base = buf.data_ptr()
+
+    def probe_sweep(_):
+        for j, b in enumerate(sizes):
+            probes.read(base + int(offs[j]), b)
+
+    out["read_probe"] = time_steps(torch, probe_sweep, 1, steps, warmup, reps, probes, filler=1)
+
+    def one_read(_):
+        probes.read(base, total_bytes)
+
+    out["read_probe_one_launch"] = time_steps(torch, one_read, 1, steps, warmup, reps, probes, filler=1)
+    del buf
     return out
 
 
-def cpu_baseline(fmt: str, w_np: np.ndarray, x_bits: np.ndarray, y_gpu: np.ndarray, budget_s: float = 12.0):
-    """The CPU oracle on a row sample of the same matrix: oracle-packed, exact dequant + FP64 product."""
+# ----------------------------------------------------------------------------------------------
+# CPU baseline and the parity gate (the only part of this file that uses the oracle)
+
+def _oracle_pack_rows(fmt: str, w_full: np.ndarray, rows: np.ndarray):
+    """Oracle-packed canonical bytes of `rows` of w_full (NVFP4's global scale comes from the whole matrix)."""
+    from oracle import pack
+    if fmt == "nvfp4":
+        return pack.pack_nvfp4_rows(w_full[rows], pack.nvfp4_global_scale(w_full))
+    return pack.pack(fmt, np.ascontiguousarray(w_full[rows]))
+
+
+def oracle_sample(fmt: str, w_full: np.ndarray, rows: np.ndarray, x_bits: np.ndarray, y_gpu: np.ndarray,
+                  threads: int, budget_s: float, time_it: bool = True):
+    """Time the oracle's exact dequant + FP64 product on `rows` of the matrix (on `threads` host threads, a
+    slab of rows each) and compare y_gpu[:, rows] with it. Packing is input preparation, not timed."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
-    from oracle import pack, ref
-    threads = host_threads()
-    rows = np.arange(0, w_np.shape[0], max(1, w_np.shape[0] // 512))[:512]
-    sample_w = np.ascontiguousarray(w_np[rows])
-    packed = pack.pack(fmt, sample_w)                       # input preparation, not timed
-    n, k = sample_w.shape
-    abytes = algorithmic_bytes(fmt, n, k)
+    from oracle import ref
+    packed = _oracle_pack_rows(fmt, w_full, rows)
+    parts = [p for p in np.array_split(np.arange(len(rows)), threads) if len(p)]
+    chunks = [ref.rows(fmt, packed, p) for p in parts]
+
+    def one(chunk):
+        return ref.matmul(x_bits, ref.dequant(fmt, chunk))
+
     times = []
-    with threadpool_limits(limits=threads):
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=len(chunks)) as ex:
         t_end = time.perf_counter() + budget_s
-        while time.perf_counter() < t_end or len(times) < 3:
+        while True:
             t0 = time.perf_counter()
-            w64 = ref.dequant(fmt, packed)
-            y_ref = ref.matmul(x_bits, w64)
+            y_ref = np.concatenate(list(ex.map(one, chunks)), axis=1)
             times.append(time.perf_counter() - t0)
+            if not time_it or (time.perf_counter() >= t_end and len(times) >= 3):
+                break
+    w64 = ref.dequant(fmt, packed)
+    ok, worst = ref.check(y_gpu[:, rows], y_ref, ref.bound(x_bits, w64))
+    n, k = len(rows), w_full.shape[1]
     med = float(np.median(times))
-    b = ref.bound(x_bits, w64)
-    ok, worst = ref.check(y_gpu[:, rows], y_ref, b)
-    return dict(value=abytes / med / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{n} of {w_np.shape[0]} rows x K={k} ({fmt}, M={x_bits.shape[0]}), exact dequant "
-                       f"(numpy, one thread) + FP64 product (BLAS, {threads} threads), median of "
-                       f"{len(times)} runs",
-                ms=med * 1e3, parity_on_sample=ok, worst_error_ratio=worst)
+    m = x_bits.shape[0]
+    return dict(parity=bool(ok), worst_error_ratio=round(float(worst), 5), rows=int(n), K=int(k), M=int(m),
+                ms=round(med * 1e3, 3), runs=len(times),
+                gbs=algorithmic_bytes(fmt, n, k) / med / 1e9, gflops=2.0 * m * n * k / med / 1e9)
 
 
-def copy_calibration(torch, mib: int = 256, reps: int = 5):
-    """A plain device copy of known size, run so that rocprofv3 counters can be scaled to bytes."""
-    n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 256)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    for _ in range(reps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "reps": reps}}), flush=True)
+def sample_rows(n: int, count: int) -> np.ndarray:
+    return np.unique(np.linspace(0, n - 1, min(n, count)).astype(np.int64))
 
 
+# ----------------------------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=11400)
-    ap.add_argument("--warmup", type=int, default=1140)
-    ap.add_argument("--workload", default="rocmfp4_dual_4096x4096_m1", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=2000, help="timed launches of the headline GEMV per repetition")
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--reps", type=int, default=5, help="timed repetitions per workload (median and spread)")
+    ap.add_argument("--only", default="", help=f"comma-separated sections to run, of {','.join(SECTIONS)}")
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS),
+                    help="the one-matrix GEMV workload of the headline figure")
     # The GEMM's clocks take tens of milliseconds of matrix-core load to settle (from ~245 to ~207 us per
-    # launch on MI355X); the default warmup covers that, so the timed launches measure steady state.
-    ap.add_argument("--gemm-steps", type=int, default=200)
+    # launch on MI355X); the default warm-up covers that, so the timed launches measure steady state.
+    ap.add_argument("--gemm-steps", type=int, default=100)
     ap.add_argument("--gemm-warmup", type=int, default=200)
-    ap.add_argument("--no-gemm", action="store_true")
-    ap.add_argument("--no-gemm-small", action="store_true", help="skip the M = 128, 256, 512 GEMM figures")
-    ap.add_argument("--no-spec", action="store_true", help="skip the speculative-verify shapes (M = 1, 9, 16)")
-    ap.add_argument("--spec-steps", type=int, default=2000)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--sweep-steps", type=int, default=50)
-    ap.add_argument("--sweep-warmup", type=int, default=20)
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--spec-steps", type=int, default=400)
+    ap.add_argument("--sweep-steps", type=int, default=10)
+    ap.add_argument("--sweep-warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=1.5, help="seconds of oracle timing per sampled workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline and the parity gate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (scale factor for HBM byte counters)")
     args = ap.parse_args()
@@ -313,6 +458,10 @@ def main():
         print(json.dumps({"error": "the library and this benchmark run on one GPU; sharding across GPUs is "
                                    "described, not implemented (run with --gpus 1)", "n_gpus": args.gpus}))
         sys.exit(2)
+    only = set(s for s in args.only.split(",") if s) or set(SECTIONS)
+    unknown = only - set(SECTIONS)
+    if unknown:
+        ap.error(f"unknown sections {sorted(unknown)}")
 
     import torch
     import block_scaled_fp4_w4a16_amd as fp4
@@ -321,111 +470,216 @@ def main():
     torch.cuda.set_device(0)
     torch.cuda.synchronize()
     if args.copy_calibration:
-        copy_calibration(torch)
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 256)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "reps": 5}}), flush=True)
         return
-    t0 = time.time()
-    gv = bench_gemv(fp4, torch, synth, args.workload, args.steps, args.warmup)
-    print(f"# gemv {args.workload}: {gv['per_launch_s'] * 1e6:.3f} us/launch, {gv['gbs']:.1f} GB/s "
-          f"({gv['copies']} cold copies, {time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
 
-    gm = None
-    if not args.no_gemm:
-        t1 = time.time()
-        gm = bench_gemm(fp4, torch, synth, "rocmfp4_fast", args.gemm_steps, args.gemm_warmup)
-        print(f"# gemm FAST M=2048: {gm['per_launch_s'] * 1e6:.1f} us/launch, {gm['tflops']:.1f} TFLOP/s "
-              f"({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
-        t1 = time.time()
-        gm_nv = bench_gemm(fp4, torch, synth, "nvfp4", args.gemm_steps, args.gemm_warmup)
-        print(f"# gemm NVFP4 M=2048: {gm_nv['per_launch_s'] * 1e6:.1f} us/launch, {gm_nv['tflops']:.1f} TFLOP/s "
-              f"({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
-        # the same FAST matrix at prefill-chunk sizes (small grids: two-way K split, 128/192-row tiles);
-        # one weight copy, so the weights stay in the last-level cache between launches
-        t1 = time.time()
-        gm_small = {}
-        for m_small in (() if args.no_gemm_small else (128, 256, 512)):
-            r = bench_gemm(fp4, torch, synth, "rocmfp4_fast", 400, 200, m=m_small, pw=gm["pw"])
-            gm_small[f"m{m_small}"] = {"us_per_launch": round(r["per_launch_s"] * 1e6, 2),
-                                       "TFLOP/s": round(r["tflops"], 1)}
-        print(f"# gemm FAST small M: {gm_small} ({time.time() - t1:.1f}s)", file=sys.stderr, flush=True)
+    probes = Probes(torch)
+    reps = max(1, args.reps)
 
-    spec = None
-    if not args.no_spec:
-        # speculative verify / small batch: gate- and down-shaped matrices at M = 1, 9 (1 token + 8 drafts), 16
-        t3 = time.time()
-        spec = {}
-        for fmt in ("nvfp4", "rocmfp4_dual"):
-            for shape in ("gate_9728x2560", "down_2560x9728"):
-                for m in (1, 9, 16):
+    def log(msg):
+        print(f"# {msg}", file=sys.stderr, flush=True)
+
+    gemv_rows = {}          # name -> bench_gemv result
+    read_probe = {}
+    if "headline" in only:
+        t0 = time.time()
+        r = bench_gemv(fp4, torch, synth, args.workload, args.steps, args.warmup, reps, probes)
+        gemv_rows[args.workload] = r
+        log(f"gemv {args.workload}: {r['t']['median_s'] * 1e6:.3f} us/launch median "
+            f"[{r['t']['min_s'] * 1e6:.3f}, {r['t']['max_s'] * 1e6:.3f}], "
+            f"{r['bytes'] / r['t']['median_s'] / 1e9:.1f} GB/s, clock {r['t']['clock_mhz']:.0f} MHz "
+            f"({r['copies']} cold copies, {time.time() - t0:.1f}s)")
+    if "nvfp4_2048" in only:
+        r = bench_gemv(fp4, torch, synth, "nvfp4_2048x2048_m1", args.steps, args.warmup, reps, probes)
+        gemv_rows[r["name"]] = r
+        log(f"gemv nvfp4_2048x2048_m1: {r['t']['median_s'] * 1e6:.3f} us/launch median")
+    if "spec" in only:
+        t0 = time.time()
+        for fmt in SPEC_FMTS:
+            for shape, _ in SPEC_SHAPES:
+                for m in SPEC_MS:
                     name = f"{fmt}_{shape}_m{m}"
-                    r = bench_gemv(fp4, torch, synth, name, args.spec_steps, args.spec_steps // 10)
-                    spec[name] = {"us_per_launch": round(r["per_launch_s"] * 1e6, 3), "GB/s": round(r["gbs"], 1),
-                                  "frac": round(r["gbs"] / HBM_PEAK_GBS, 4)}
-        print(f"# speculative-verify shapes: {len(spec)} workloads ({time.time() - t3:.1f}s)", file=sys.stderr,
-              flush=True)
+                    r = bench_gemv(fp4, torch, synth, name, args.spec_steps, args.spec_steps // 4, reps, probes)
+                    gemv_rows[name] = r
+        log(f"speculative-verify shapes: {len(SPEC_FMTS) * len(SPEC_SHAPES) * len(SPEC_MS)} workloads "
+            f"({time.time() - t0:.1f}s)")
+    if "read_probe" in only:
+        t0 = time.time()
+        sizes = sorted({algorithmic_bytes("nvfp4", 2048, 2048), algorithmic_bytes("rocmfp4_dual", 4096, 4096),
+                        algorithmic_bytes("nvfp4", 9728, 2560), algorithmic_bytes("rocmfp4_fast", 9728, 2560)})
+        for b in sizes:
+            read_probe[b] = bench_read_probe(torch, probes, b, args.steps, args.warmup, reps)
+        log(f"read probe: {len(sizes)} sizes ({time.time() - t0:.1f}s)")
+
+    gemm = {}
+    if "gemm" in only:
+        for fmt in ("rocmfp4_fast", "nvfp4"):
+            t0 = time.time()
+            gemm[fmt] = bench_gemm(fp4, torch, synth, fmt, 2048, args.gemm_steps, args.gemm_warmup, reps, probes)
+            log(f"gemm {fmt} M=2048: {gemm[fmt]['t']['median_s'] * 1e6:.1f} us/launch median, "
+                f"{gemm[fmt]['tflops']:.1f} TFLOP/s, clock {gemm[fmt]['t']['clock_mhz']:.0f} MHz "
+                f"({time.time() - t0:.1f}s)")
+    gemm_small = {}
+    if "gemm_small" in only:
+        t0 = time.time()
+        pw = gemm["rocmfp4_fast"]["pw"] if "rocmfp4_fast" in gemm else None
+        for m in (128, 256, 512):
+            r = bench_gemm(fp4, torch, synth, "rocmfp4_fast", m, 200, 100, reps, probes, pw=pw)
+            pw = r["pw"]
+            gemm_small[m] = r
+        log(f"gemm FAST small M ({time.time() - t0:.1f}s)")
+    for r in gemm.values():
+        r.pop("pw", None)
+    for r in gemm_small.values():
+        r.pop("pw", None)
 
     sw = None
-    if not args.no_sweep:
-        t2 = time.time()
-        sw = bench_decode_sweep(fp4, torch, synth, args.sweep_steps, args.sweep_warmup)
-        print(f"# decode sweep NVFP4 M=1 (252 matrices, {sw['bytes'] / 1e9:.3f} GB): grouped "
-              f"{sw['grouped'] * 1e6:.1f} us ({sw['bytes'] / sw['grouped'] / 1e9:.1f} GB/s), one launch per matrix "
-              f"{sw['single'] * 1e6:.1f} us ({sw['bytes'] / sw['single'] / 1e9:.1f} GB/s) ({time.time() - t2:.1f}s)",
-              file=sys.stderr, flush=True)
+    if "sweep" in only:
+        t0 = time.time()
+        sw = bench_decode_sweep(fp4, torch, synth, args.sweep_steps, args.sweep_warmup, reps, probes)
+        log(f"decode sweep: grouped {sw['grouped']['median_s'] * 1e6:.1f} us, single "
+            f"{sw['single']['median_s'] * 1e6:.1f} us, read probe {sw['read_probe']['median_s'] * 1e6:.1f} us "
+            f"({time.time() - t0:.1f}s)")
 
-    cpu = None
+    # ------------------------------------------------------------------ oracle: CPU baseline + parity gate
+    cpu = {}
+    threads = host_threads()
     if not args.no_cpu:
-        cpu = cpu_baseline(gv["fmt"], gv["w_np"], gv["x_bits"], gv["y0"])
-        print(f"# cpu oracle: {cpu['value']:.4f} GB/s on the sample, parity {cpu['parity_on_sample']}",
-              file=sys.stderr, flush=True)
+        t0 = time.time()
+        budget = args.cpu_budget
+        for name, r in gemv_rows.items():
+            timed = (name in (HEADLINE, "nvfp4_2048x2048_m1") or r["m"] == 9)
+            cpu[name] = oracle_sample(r["fmt"], r["w_np"], sample_rows(r["n"], 512), r["x_bits"], r["y"], threads,
+                                      budget, time_it=timed)
+        if gemm or gemm_small:
+            w_pref = synth.workload_weights(4, 0)
+            for fmt, r in gemm.items():
+                cpu[f"{fmt}_prefill_m2048"] = oracle_sample(fmt, w_pref, sample_rows(r["n"], 64), r["x_bits"], r["y"],
+                                                            threads, budget)
+            for m, r in gemm_small.items():
+                cpu[f"rocmfp4_fast_prefill_m{m}"] = oracle_sample("rocmfp4_fast", w_pref, sample_rows(r["n"], 64),
+                                                                  r["x_bits"], r["y"], threads, budget, time_it=False)
+            del w_pref
+        if sw is not None:
+            layer = synth.DECODE_4B_LAYER
+            res = []
+            for pi, (_, n, k) in enumerate(layer):
+                w = synth.device_weights(n, k, cfg=2, mat=pi).cpu().numpy()
+                res.append(oracle_sample("nvfp4", w, sample_rows(n, 256), sw["layer0_x"][pi], sw["layer0_y"][pi],
+                                         threads, budget / 7))
+            cpu["decode_sweep_layer0"] = dict(
+                parity=all(x["parity"] for x in res), worst_error_ratio=max(x["worst_error_ratio"] for x in res),
+                rows=sum(x["rows"] for x in res), ms=round(sum(x["ms"] for x in res), 3),
+                gbs=sum(algorithmic_bytes("nvfp4", x["rows"], x["K"]) for x in res) / (sum(x["ms"] for x in res) / 1e3) / 1e9)
+        log(f"oracle samples: {len(cpu)} ({time.time() - t0:.1f}s), parity "
+            f"{'ok' if all(c['parity'] for c in cpu.values()) else 'FAILED: ' + str([k for k, c in cpu.items() if not c['parity']])}")
 
-    line = {
-        "metric": "W4A16 GEMV weight GB/s & % HBM peak (M=1); GEMM TFLOP/s & % MFMA (M=2048)",
-        "value": round(gv["gbs"], 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": gv["per_launch_s"] * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded Student-t weights packed on the GPU by the library's packer; bf16 N(0,1) x)",
-        "config": {"workload": args.workload, "fmt": gv["fmt"], "M": gv["m"], "N": gv["n"], "K": gv["k"],
-                   "bytes_per_launch": gv["bytes"], "cold_copies": gv["copies"]},
-        "roofline": {"bound": "hbm", "achieved": round(gv["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gv["gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles("gemv.hip", args.workload)},
-        "cpu_baseline": cpu and {k_: cpu[k_] for k_ in ("value", "unit", "cores", "kind", "sample")},
-    }
-    if cpu:
-        line["cpu_baseline"]["parity_on_sample"] = cpu["parity_on_sample"]
-    if gm:
-        line["gemm"] = {"workload": "rocmfp4_fast_prefill_m2048_k4096_n14336", "value": round(gm["tflops"], 2),
-                        "unit": "TFLOP/s", "us_per_launch": round(gm["per_launch_s"] * 1e6, 2),
-                        "steps": args.gemm_steps, "warmup": args.gemm_warmup,
-                        "roofline": {"bound": "mfma", "achieved": round(gm["tflops"], 2),
-                                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                     "frac": round(gm["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
-                                     "traffic": traffic_from_profiles("gemm.hip", "rocmfp4_fast_prefill_m2048")},
-                        "nvfp4": {"workload": "nvfp4_prefill_m2048_k4096_n14336", "value": round(gm_nv["tflops"], 2),
-                                  "us_per_launch": round(gm_nv["per_launch_s"] * 1e6, 2),
-                                  "frac": round(gm_nv["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)},
-                        "small_m": {"workload": "rocmfp4_fast k4096 n14336 at M = 128, 256, 512", **gm_small}}
-    if spec:
-        line["spec_verify"] = {"workload": "speculative verify, gate 9728x2560 and down 2560x9728, M = 1, 9, 16",
-                               "unit": "GB/s of weight + scale bytes", "steps": args.spec_steps, "results": spec}
+    def parity_of(key):
+        c = cpu.get(key)
+        return None if c is None else c["parity"]
+
+    def gated(value, key):
+        """No throughput for a workload whose oracle check failed."""
+        return None if parity_of(key) is False else value
+
+    # ------------------------------------------------------------------ the JSON line
+    line = {"metric": "W4A16 GEMV weight GB/s & % HBM peak (M=1); GEMM TFLOP/s & % MFMA (M=2048)"}
+    head = gemv_rows.get(args.workload)
+    if head is not None:
+        gbs = head["bytes"] / head["t"]["median_s"] / 1e9
+        line.update({
+            "value": gated(round(gbs, 2), args.workload),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": head["t"]["median_s"] * 1e3,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded Student-t weights packed on the GPU by the library's packers; bf16 N(0,1) x)",
+            "config": {"workload": args.workload, "fmt": head["fmt"], "M": head["m"], "N": head["n"],
+                       "K": head["k"], "bytes_per_launch": head["bytes"], "cold_copies": head["copies"]},
+            "roofline": hbm_roofline(head["bytes"], head["t"], traffic_from_profiles("gemv.hip", args.workload)),
+            "timing": timing_fields(head["t"]),
+            "parity": parity_of(args.workload),
+        })
+        if head["bytes"] in read_probe:
+            rp = read_probe[head["bytes"]]
+            line["roofline"]["vs_read_probe"] = round(rp["median_s"] / head["t"]["median_s"], 4)
+    if not args.no_cpu and args.workload in cpu:
+        c = cpu[args.workload]
+        line["cpu_baseline"] = {
+            "value": c["gbs"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{c['rows']} of {head['n']} rows x K={c['K']} ({head['fmt']}, M={c['M']}): exact dequant + "
+                      f"FP64 product, one row slab per thread on {threads} threads, median of {c['runs']} runs "
+                      f"({c['ms']} ms)",
+            "cpu_model": cpu_model(),
+            "per_workload": {k_: {f: v_[f] for f in ("ms", "gbs", "gflops", "rows", "M", "K", "runs", "parity",
+                                                     "worst_error_ratio") if f in v_}
+                             for k_, v_ in cpu.items()},
+        }
+    workloads = {}
+    for name, r in gemv_rows.items():
+        if name == args.workload:
+            continue
+        gbs = r["bytes"] / r["t"]["median_s"] / 1e9
+        entry = {"fmt": r["fmt"], "N": r["n"], "K": r["k"], "M": r["m"], "bytes_per_launch": r["bytes"],
+                 "GB/s": gated(round(gbs, 2), name), "roofline": hbm_roofline(r["bytes"], r["t"]),
+                 "timing": timing_fields(r["t"]), "parity": parity_of(name), "cold_copies": r["copies"]}
+        if r["bytes"] in read_probe:
+            entry["roofline"]["vs_read_probe"] = round(read_probe[r["bytes"]]["median_s"] / r["t"]["median_s"], 4)
+        if name == "nvfp4_2048x2048_m1":
+            entry["roofline"]["traffic"] = traffic_from_profiles("gemv.hip", name)
+        workloads[name] = entry
+    if workloads:
+        line["gemv_workloads"] = workloads
+    if read_probe:
+        line["read_probe"] = {
+            "what": "plain streaming read of the same bytes per launch (16-byte nontemporal loads), cold copies",
+            "results": {str(b): {"GB/s": round(b / t["median_s"] / 1e9, 2),
+                                 "frac": round(b / t["median_s"] / 1e9 / HBM_PEAK_GBS, 4), **timing_fields(t)}
+                        for b, t in read_probe.items()}}
+    if gemm:
+        line["gemm"] = {}
+        for fmt, r in gemm.items():
+            key = f"{fmt}_prefill_m2048"
+            line["gemm"][f"{fmt}_prefill_m2048_k4096_n14336"] = {
+                "TFLOP/s": gated(round(r["tflops"], 2), key),
+                "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "traffic": traffic_from_profiles("gemm.hip", f"{fmt}_prefill_m2048")},
+                "timing": timing_fields(r["t"]), "parity": parity_of(key)}
+    if gemm_small:
+        line["gemm_small_m"] = {
+            f"rocmfp4_fast_m{m}_k4096_n14336": {
+                "TFLOP/s": gated(round(r["tflops"], 2), f"rocmfp4_fast_prefill_m{m}"),
+                "frac": round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4), "timing": timing_fields(r["t"]),
+                "parity": parity_of(f"rocmfp4_fast_prefill_m{m}")} for m, r in gemm_small.items()}
     if sw:
-        gbs = sw["bytes"] / sw["grouped"] / 1e9
+        g = sw["grouped"]
+        gbs = sw["bytes"] / g["median_s"] / 1e9
         line["decode_sweep"] = {
             "workload": "nvfp4_4b_decode_sweep_m1 (36 layers x q,k,v,o,gate,up,down)",
-            "value": round(gbs, 2), "unit": "GB/s", "us_per_sweep": round(sw["grouped"] * 1e6, 2),
-            "launches_per_sweep": 144, "bytes_per_sweep": sw["bytes"],
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
-            "one_launch_per_matrix": {"value": round(sw["bytes"] / sw["single"] / 1e9, 2),
-                                      "us_per_sweep": round(sw["single"] * 1e6, 2), "launches_per_sweep": 252},
+            "GB/s": gated(round(gbs, 2), "decode_sweep_layer0"), "bytes_per_sweep": sw["bytes"],
+            "launches_per_sweep": 144, "roofline": hbm_roofline(sw["bytes"], g), "timing": timing_fields(g),
+            "parity": parity_of("decode_sweep_layer0"),
+            "one_launch_per_matrix": {"GB/s": round(sw["bytes"] / sw["single"]["median_s"] / 1e9, 2),
+                                      "launches_per_sweep": 252, "timing": timing_fields(sw["single"])},
+            "read_probe_144_launches": {"GB/s": round(sw["bytes"] / sw["read_probe"]["median_s"] / 1e9, 2),
+                                        "timing": timing_fields(sw["read_probe"])},
+            "read_probe_one_launch": {"GB/s": round(sw["bytes"] / sw["read_probe_one_launch"]["median_s"] / 1e9, 2),
+                                      "timing": timing_fields(sw["read_probe_one_launch"])},
         }
+        line["decode_sweep"]["roofline"]["vs_read_probe"] = round(sw["read_probe"]["median_s"] / g["median_s"], 4)
     print(json.dumps(line), flush=True)
 
 

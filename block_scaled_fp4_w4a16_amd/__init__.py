@@ -41,7 +41,7 @@ _SIGS = {
     "fp4_abi_version": (_c, []),
     "fp4_status_string": (ctypes.c_char_p, [_c]),
     "fp4_layout_bytes": (_c, [_c, _i64, _i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
-    "fp4_pack_layout": (_c, [_c, _i64, _i64, _p, _p, _p, _p, _p]),
+    "fp4_pack_layout": (_c, [_c, _i64, _i64, _p, _p, _p, _p, _c, _p]),
     "w4a16_gemv": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "w4a16_gemv_batched": (_c, [_c, _i64, _c, ctypes.POINTER(GemvItem), _p]),
     "w4a16_gemm": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
@@ -153,7 +153,10 @@ def fp4_layout_bytes(fmt, N: int, K: int) -> tuple[int, int]:
     return q.value, s.value
 
 
-def fp4_pack_layout(fmt, N, K, src_q, src_s, dst_q, dst_s, stream=None):
+def fp4_pack_layout(fmt, N, K, src_q, src_s, dst_q, dst_s, validate=False, stream=None):
+    """Canonical bytes -> kernel layout. validate=True first checks every scale code on the device
+    (waits for the stream) and raises RuntimeError with the library's FP4_ERR_INVALID_SCALE status,
+    leaving dst_q / dst_s untouched, if one is NaN (or, for Q4_0, not finite)."""
     f = _fmt(fmt)
     dev = _device(src_q, src_s, dst_q, dst_s)
     if N > 0 and K > 0 and K % 16 == 0:
@@ -168,8 +171,8 @@ def fp4_pack_layout(fmt, N, K, src_q, src_s, dst_q, dst_s, stream=None):
         if f in (1, 2, 3, 4) and (f == 1 or K % 32 == 0):
             _check_planes(f, N, K, dst_q, dst_s)
     with torch.cuda.device(dev):
-        _check(lib().fp4_pack_layout(f, N, K, _ptr(src_q), _ptr(src_s), _ptr(dst_q), _ptr(dst_s), _stream(stream)),
-               "fp4_pack_layout")
+        _check(lib().fp4_pack_layout(f, N, K, _ptr(src_q), _ptr(src_s), _ptr(dst_q), _ptr(dst_s), int(bool(validate)),
+                                     _stream(stream)), "fp4_pack_layout")
 
 
 def _product(name, fmt, M, N, K, q, s, global_scale, x, y, stream):
@@ -284,9 +287,9 @@ class PackedWeight:
 
     @staticmethod
     def from_canonical(fmt: str, N: int, K: int, src_q: torch.Tensor, src_s: torch.Tensor | None,
-                       global_scale: float = 1.0, stream=None) -> "PackedWeight":
+                       global_scale: float = 1.0, stream=None, validate: bool = False) -> "PackedWeight":
         pw = PackedWeight.empty(fmt, N, K, global_scale, device=src_q.device)
-        fp4_pack_layout(fmt, N, K, src_q, src_s, pw.q, pw.s, stream)
+        fp4_pack_layout(fmt, N, K, src_q, src_s, pw.q, pw.s, validate, stream)
         return pw
 
     @staticmethod
@@ -300,7 +303,7 @@ class PackedWeight:
             g = torch.empty(1, dtype=torch.float32, device=w.device)
             fp4_quantize_nvfp4(N, K, w, wq, ws, g, stream)
             gs = float(g.item())
-            return PackedWeight.from_canonical(fmt, N, K, wq, ws, gs, stream)
+            return PackedWeight.from_canonical(fmt, N, K, wq, ws, gs, stream=stream)
         blocks = torch.empty(N * (K // 32) * BLOCK_BYTES[fmt], dtype=torch.uint8, device=w.device)
         if fmt == "q4_0":
             if importance is not None:
@@ -308,7 +311,7 @@ class PackedWeight:
             fp4_quantize_q4_0(N, K, w, blocks, stream)
         else:
             fp4_quantize_rocmfp4(fmt, N, K, w, importance, blocks, stream)
-        return PackedWeight.from_canonical(fmt, N, K, blocks, None, 1.0, stream)
+        return PackedWeight.from_canonical(fmt, N, K, blocks, None, 1.0, stream=stream)
 
     def matmul(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         M = x.shape[0]

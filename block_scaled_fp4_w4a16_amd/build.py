@@ -1,4 +1,5 @@
-"""Compile the HIP library libfp4w4a16.so for gfx950, in place (hipcc; no GPU needed)."""
+"""Compile the HIP library libfp4w4a16.so for gfx950, in place (hipcc; no GPU needed), and the
+benchmark's measurement probes, libfp4probe.so (a separate library outside the C ABI)."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp4w4a16.so")
+PROBE_LIB = os.path.join(HERE, "libfp4probe.so")
+PROBE_SOURCES = ["probe.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "layout.hip", "gemv.hip", "gemm.hip", "quantize.hip"]
 ARCH = os.environ.get("FP4_OFFLOAD_ARCH", "gfx950")
@@ -34,18 +37,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + f".tmp{os.getpid()}"
     r = subprocess.run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs,
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
         print(LIB)
+        print(PROBE_LIB)
     return LIB
 
 

@@ -685,30 +685,17 @@ __global__ void gemm_zero_kernel(float* __restrict__ y, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) y[i] = 0.f;
 }
 
-// Compute units of the current device (cached per device).
-static int gemm_device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int c = cache[dev].load(std::memory_order_relaxed);
-  if (c <= 0) {
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cache[dev].store(c, std::memory_order_relaxed);
-  }
-  return c;
-}
-
 template <int F, bool RAGGED, int MI>
-static void launch_gemm_small(hipStream_t st, int grid, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
-                              int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit) {
+static int launch_gemm_small(hipStream_t st, int grid, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                             int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit) {
   static Fp4LdsLimit lds_limit;
   lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI>), GM_LDS);
-  hipLaunchKernelGGL((gemm_small_kernel<F, RAGGED, MI>), dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K,
-                     nchunk, tiles_m, ntiles, g, ksplit);
+  return fp4_launch(gemm_small_kernel<F, RAGGED, MI>, dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K,
+                    nchunk, tiles_m, ntiles, g, ksplit);
 }
 
 template <int F, bool RAGGED>
-static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
+static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
                           int N, int K, float g) {
   const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const int tiles_m = (M + GM_BM - 1) / GM_BM;
@@ -716,16 +703,15 @@ static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, co
   // Between one and two rounds of 256-row tiles: 8 s columns' worth of rows 0 .. 1535 go to s = 8 ns
   // 192-row tiles (3/4 of the work each), chosen so that the grid is two rounds (s = 4 (2 cus - U), at
   // most every column tile), the second made of short tiles.
-  const int cus = gemm_device_cus();
+  const int cus = fp4_device_cus();
+  const Fp4Tuning& tu = fp4_tuning();
   const int64_t U = (int64_t)tiles_m * tiles_n;
   int ns = 0;
   if (M % GM_BM == 0 && M >= GM_SHORT_BANDS * GM_SHORT_ROWS && U > cus && U < 2 * cus) {
     ns = (int)(4 * (2 * cus - U) / GM_SHORT_BANDS);
     if (ns > tiles_n) ns = tiles_n;
   }
-  if (const char* e = getenv("FP4_GEMM_SHORT")) {  // tuning override: 0 = 256-row tiles only
-    if (atoi(e) == 0) ns = 0;
-  }
+  if (tu.gemm_short == 0) ns = 0;  // tuning override: 256-row tiles only
   const int nbig = (int)(U - (int64_t)(GM_SHORT_BANDS * GM_SHORT_ROWS / GM_BM) * ns);
   // Grids of at most a quarter of the CUs split K in two (at a multiple of the 3-stage ring period, each
   // part at least 6 stages) so that twice the workgroups run; y is zeroed first and both parts add into
@@ -734,37 +720,33 @@ static void launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, co
   int ksplit = 0;
   const int H = 2 * nchunk;
   if (ns == 0 && 4 * U <= cus && H >= 12) ksplit = 3 * (H / 6);
-  if (const char* e = getenv("FP4_GEMM_SPLIT")) {  // tuning override: 0 = whole K per workgroup
-    if (atoi(e) == 0) ksplit = 0;
-  }
+  if (tu.gemm_split == 0) ksplit = 0;  // tuning override: whole K per workgroup
   // one band: tiles only as high as M needs, 128 or 192 rows
   int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
-  if (const char* e = getenv("FP4_GEMM_BAND_ROWS")) {  // tuning override: 0 = 256-row tiles
-    if (atoi(e) == 0) band_rows = 0;
-  }
+  if (tu.gemm_band_rows == 0) band_rows = 0;  // tuning override: 256-row tiles
   if (ksplit == 0 && band_rows == 0) {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
-    hipLaunchKernelGGL((gemm_kernel<F, RAGGED>), dim3(nbig + GM_SHORT_BANDS * ns), dim3(GM_THREADS), GM_LDS, st, q, s,
-                       x, y, M, N, K, nchunk, tiles_m, ns, nbig, g);
-    return;
+    return fp4_launch(gemm_kernel<F, RAGGED>, dim3(nbig + GM_SHORT_BANDS * ns), dim3(GM_THREADS), GM_LDS, st, q, s, x,
+                      y, M, N, K, nchunk, tiles_m, ns, nbig, g);
   }
   if (ksplit) {
     const int64_t total = (int64_t)M * N;
     const int zb = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    hipLaunchKernelGGL(gemm_zero_kernel, dim3(zb), dim3(256), 0, st, y, total);
+    const int rc = fp4_launch(gemm_zero_kernel, dim3(zb), dim3(256), 0, st, y, total);
+    if (rc) return rc;
   }
   const int grid = ksplit ? 2 * (int)U : (int)U;
-  if (band_rows == 128) launch_gemm_small<F, RAGGED, 4>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
-  else if (band_rows) launch_gemm_small<F, RAGGED, 6>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
-  else launch_gemm_small<F, RAGGED, 8>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)U, g, ksplit);
+  if (band_rows == 128) return launch_gemm_small<F, RAGGED, 4>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
+  if (band_rows) return launch_gemm_small<F, RAGGED, 6>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
+  return launch_gemm_small<F, RAGGED, 8>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)U, g, ksplit);
 }
 
 template <int F>
-static void launch_gemm(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
-                        int N, int K, float g) {
-  if (K % CHUNK_K == 0) launch_gemm_t<F, false>(st, q, s, x, y, M, N, K, g);
-  else launch_gemm_t<F, true>(st, q, s, x, y, M, N, K, g);
+static int launch_gemm(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M, int N,
+                       int K, float g) {
+  if (K % CHUNK_K == 0) return launch_gemm_t<F, false>(st, q, s, x, y, M, N, K, g);
+  return launch_gemm_t<F, true>(st, q, s, x, y, M, N, K, g);
 }
 
 }  // namespace fp4
@@ -790,11 +772,10 @@ extern "C" int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   const uint8_t* ss = (const uint8_t*)s;
   const uint16_t* xx = (const uint16_t*)x_bf16;
   switch (fmt) {
-    case NVFP4: launch_gemm<NVFP4>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale); break;
-    case DUAL:  launch_gemm<DUAL>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale); break;
-    default:    launch_gemm<FAST>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale); break;
+    case NVFP4: return launch_gemm<NVFP4>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale);
+    case DUAL:  return launch_gemm<DUAL>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale);
+    default:    return launch_gemm<FAST>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale);
   }
-  return fp4_launch_status();
 }
 
 extern "C" int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,

@@ -519,12 +519,12 @@ template <int F, int D>
 struct RingLaunch {
   static const void* fn() { return reinterpret_cast<const void*>(&gemv_ring_kernel<F, D>); }
   static size_t lds(int W, int nchunk) { return (size_t)nchunk * 256 + (size_t)W * 64 * 4 * sizeof(float); }
-  static void launch(const GemvItem& it, int W, hipStream_t st) {
+  static int launch(const GemvItem& it, int W, hipStream_t st) {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(fn(), GEMV_LDS_MAX);
     const int nchunk = (it.K + CHUNK_K - 1) / CHUNK_K, ntiles = (it.N + TILE_N - 1) / TILE_N;
-    hipLaunchKernelGGL((gemv_ring_kernel<F, D>), dim3(ntiles), dim3(64 * W), lds(W, nchunk), st, it.q, it.s, it.x, it.y,
-                       it.N, it.K, it.g, 1 | (W << 8));
+    return fp4_launch(gemv_ring_kernel<F, D>, dim3(ntiles), dim3(64 * W), lds(W, nchunk), st, it.q, it.s, it.x, it.y,
+                      it.N, it.K, it.g, 1 | (W << 8));
   }
 };
 
@@ -691,19 +691,6 @@ __global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restri
   }
 }
 
-// Compute units of the current device (queried once per device).
-static int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int c = cus[dev].load(std::memory_order_relaxed);
-  if (c <= 0) {
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cus[dev].store(c, std::memory_order_relaxed);
-  }
-  return c;
-}
-
 // Workgroups of W waves of kernel `k` that one compute unit holds at once, with `lds` bytes of dynamic
 // LDS each (from the occupancy calculator; remembered per wave count and LDS size class).
 static int resident_per_cu(const void* k, int W, size_t lds) {
@@ -721,15 +708,17 @@ struct GemvLaunch {
   static size_t lds(int W, int M) { return (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float); }
   // workgroups resident per CU for W = 1, 2, 4, 8, 16 at this M (computed once per M class)
   static int resident(int W, int M) {
-    static std::atomic<int> cache[5][17];
+    static std::atomic<int> cache[64][5][17];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     int wi = 0;
     while ((1 << wi) < W) ++wi;
     const int mi = M > 16 ? 16 : M;
-    int r = cache[wi][mi].load(std::memory_order_relaxed);
+    int r = cache[dev][wi][mi].load(std::memory_order_relaxed);
     if (r <= 0) {
       attr();
       r = resident_per_cu(fn(), W, lds(W, M));
-      cache[wi][mi].store(r, std::memory_order_relaxed);
+      cache[dev][wi][mi].store(r, std::memory_order_relaxed);
     }
     return r;
   }
@@ -738,17 +727,17 @@ struct GemvLaunch {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(fn(), GEMV_LDS_MAX);
   }
-  static void launch(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
+  static int launch(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
     attr();
     if constexpr (MAXI == 1) {
       const GemvItem& i0 = b.it[0];
-      hipLaunchKernelGGL((gemv_kernel<F, T, RU, U, MX, MC, ONE>), dim3(nwg), dim3(64 * W), lds(W, M), st, i0.q, i0.s,
-                         i0.x, i0.y, i0.N, i0.K, i0.g, M | (W << 8));
+      return fp4_launch(gemv_kernel<F, T, RU, U, MX, MC, ONE>, dim3(nwg), dim3(64 * W), lds(W, M), st, i0.q, i0.s, i0.x,
+                        i0.y, i0.N, i0.K, i0.g, M | (W << 8));
     } else {
       const int inf = 0x7fffffff;
-      hipLaunchKernelGGL((gemv_group_kernel<F, T, RU, U, MX, MAXI, MC, ONE>), dim3(nwg), dim3(64 * W), lds(W, M), st,
-                         MAXI > 1 ? b.start[1 % MAXI] : inf, MAXI > 2 ? b.start[2 % MAXI] : inf,
-                         MAXI > 3 ? b.start[3 % MAXI] : inf, M | (W << 8), b);
+      return fp4_launch(gemv_group_kernel<F, T, RU, U, MX, MAXI, MC, ONE>, dim3(nwg), dim3(64 * W), lds(W, M), st,
+                        MAXI > 1 ? b.start[1 % MAXI] : inf, MAXI > 2 ? b.start[2 % MAXI] : inf,
+                        MAXI > 3 ? b.start[3 % MAXI] : inf, M | (W << 8), b);
     }
   }
 };
@@ -757,22 +746,21 @@ struct GemvLaunch {
 // two K chunks and, for M > 1, keep the whole grid resident at once (one round of workgroups).
 template <class L>
 static int pick_waves(int nwg, int min_chunks, int M, int wmax) {
-  const int cus = device_cus();
+  const int cus = fp4_device_cus();
   int W = 16;
   // M = 1 (single-batch kernels, high occupancy): the most waves that keep two chunks per wave, even when
   // the grid then takes a second round (a wave working through more chunks costs more than the round).
   const bool fit = M > 1;
   while (W > 1 && (W > wmax || min_chunks < 2 * W || (fit && (int64_t)nwg > (int64_t)L::resident(W, M) * cus)))
     W >>= 1;
-  if (const char* e = getenv("FP4_GEMV_WAVES")) {  // tuning override, read at each call
-    if (atoi(e) > 0 && atoi(e) <= 16) W = atoi(e);
-  }
+  const int tw = fp4_tuning().gemv_waves;  // tuning override
+  if (tw > 0 && tw <= 16) W = tw;
   return W;
 }
 
 // Fills in the workgroup ranges, picks the variant and wave count, and launches. Every item has N, K >= 1.
 template <int F, int MAXI>
-static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
+static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   // With more than 4 x rows a workgroup takes two tiles (they share the staged x) when there are enough
   // tiles for one such workgroup per CU; otherwise one.
   int total_tiles = 0;
@@ -802,50 +790,48 @@ static void dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     using O4 = GemvLaunch<F, 1, 1, 4, 1, MAXI, 1, true>;
     int W = pick_waves<O4>(nwg, min_chunks, M, wmax);
     // 8 waves of up to 4 chunks beat 16 waves of 2 (K = 4096: 3-10% faster, fewer waves to reduce)
-    if (W == 16 && (max_chunks + 7) / 8 <= 4 && !getenv("FP4_GEMV_WAVES")) W = 8;
+    const Fp4Tuning& tu = fp4_tuning();
+    if (W == 16 && (max_chunks + 7) / 8 <= 4 && tu.gemv_waves < 0) W = 8;
     int U = (max_chunks + W - 1) / W;
-    if (const char* e = getenv("FP4_GEMV_U")) {  // tuning override, read at each call
-      if (atoi(e) >= 2 && atoi(e) <= 4 && atoi(e) * W >= max_chunks) U = atoi(e);
-    }
+    if (tu.gemv_u >= 2 && tu.gemv_u <= 4 && tu.gemv_u * W >= max_chunks) U = tu.gemv_u;  // tuning override
     using L2 = GemvLaunch<F, 1, 1, 2, 1, MAXI, 1>;
-    const char* one = getenv("FP4_GEMV_ONE");  // tuning override: 0 = batch loop with prefetch
+    const bool batch_loop = tu.gemv_one == 0;  // tuning override: batch loop with prefetch
     // Long K on a grid of at least two workgroups per CU: the ring kernel (3 chunks in flight per wave,
     // so two 16-wave workgroups fit on a CU where the batch loop fits one).
-    const char* rg = getenv("FP4_GEMV_RING");   // tuning override: 0 = never, 1 = whenever it applies
     const bool ring_fits = MAXI == 1 && max_chunks <= RING_MAX_CHUNKS;
-    const bool ring = ring_fits && (rg ? atoi(rg) == 1 : (U > 4 && nwg >= 2 * device_cus()));
-    if (ring) RingLaunch<F, 3>::launch(b.it[0], RING_WAVES, st);
-    else if (one && atoi(one) == 0 && U <= 2) L2::launch(b, nwg, W, M, st);
-    else if (one && atoi(one) == 0 && U <= 4) L4::launch(b, nwg, W, M, st);
-    else if (U <= 2) O2::launch(b, nwg, W, M, st);
-    else if (U == 3) O3::launch(b, nwg, W, M, st);
-    else if (U == 4) O4::launch(b, nwg, W, M, st);
-    else L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+    const bool ring = ring_fits && (tu.gemv_ring >= 0 ? tu.gemv_ring == 1 : (U > 4 && nwg >= 2 * fp4_device_cus()));
+    if (ring) return RingLaunch<F, 3>::launch(b.it[0], RING_WAVES, st);
+    if (batch_loop && U <= 2) return L2::launch(b, nwg, W, M, st);
+    if (batch_loop && U <= 4) return L4::launch(b, nwg, W, M, st);
+    if (U <= 2) return O2::launch(b, nwg, W, M, st);
+    if (U == 3) return O3::launch(b, nwg, W, M, st);
+    if (U == 4) return O4::launch(b, nwg, W, M, st);
+    return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
   } else if (M == 2) {
     using L4 = GemvLaunch<F, 1, 2, 4, 2, MAXI, 2>;
-    L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+    return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
   } else if (M == 3) {
     using L4 = GemvLaunch<F, 1, 4, 4, 3, MAXI, 3>;
-    L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+    return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
   } else if (M == 4) {
     using L4 = GemvLaunch<F, 1, 4, 4, 4, MAXI, 4>;
-    L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+    return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
   } else if (T == 2) {
     using L = GemvLaunch<F, 2, 4, 2, 16, MAXI, 0>;
-    L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
+    return L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
   } else {
     using L = GemvLaunch<F, 1, 4, 2, 16, MAXI, 0>;
-    L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
+    return L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
   }
 }
 
 template <int MAXI>
-static void dispatch_fmt(int fmt, GemvBatch<MAXI>& b, int M, hipStream_t st) {
+static int dispatch_fmt(int fmt, GemvBatch<MAXI>& b, int M, hipStream_t st) {
   switch (fmt) {
-    case NVFP4: dispatch_gemv<NVFP4>(b, M, st); break;
-    case DUAL:  dispatch_gemv<DUAL>(b, M, st); break;
-    case FAST:  dispatch_gemv<FAST>(b, M, st); break;
-    default:    dispatch_gemv<Q4_0>(b, M, st); break;
+    case NVFP4: return dispatch_gemv<NVFP4>(b, M, st);
+    case DUAL:  return dispatch_gemv<DUAL>(b, M, st);
+    case FAST:  return dispatch_gemv<FAST>(b, M, st);
+    default:    return dispatch_gemv<Q4_0>(b, M, st);
   }
 }
 
@@ -866,19 +852,19 @@ static int check_item(int fmt, int64_t M, int64_t N, int64_t K, const void* q, c
 }
 
 template <int F, int MB, int T, int WMAX = 8>
-static void launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
-                        int M, int N, int K, float g) {
+static int launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                       int M, int N, int K, float g) {
   const int ntiles = (N + TILE_N - 1) / TILE_N;
   const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
   const size_t lds = stage > red ? stage : red;
   static Fp4LdsLimit lds_limit;
   lds_limit.ensure(reinterpret_cast<const void*>(&midm_kernel<F, MB, T, WMAX>), GEMV_LDS_MAX);
-  hipLaunchKernelGGL((midm_kernel<F, MB, T, WMAX>), dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, N, K,
-                     g, M | (W << 8));
+  return fp4_launch(midm_kernel<F, MB, T, WMAX>, dim3((ntiles + T - 1) / T), dim3(64 * W), lds, st, q, s, x, y, N, K, g,
+                    M | (W << 8));
 }
 
 template <int F, int MB>
-static void dispatch_midm_mb(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+static int dispatch_midm_mb(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                              int N, int K, float g) {
   const int nchunk = (K + CHUNK_K - 1) / CHUNK_K, ntiles = (N + TILE_N - 1) / TILE_N;
   // Two tiles per workgroup share the staged x (half the x traffic) when that still leaves two
@@ -893,32 +879,25 @@ static void dispatch_midm_mb(int M, hipStream_t st, const uint8_t* q, const uint
   const int wmax = (MB == 1 && T == 1) ? 16 : 8;
   int W = wmax;
   while (W > 1 && (nchunk < 2 * W || nwg * W > resident)) W >>= 1;
-  if (const char* e = getenv("FP4_MIDM_WAVES")) {  // tuning override, read at each call
-    if (atoi(e) > 0 && atoi(e) <= wmax) W = atoi(e);
-  }
+  const int tw = fp4_tuning().midm_waves;  // tuning override
+  if (tw > 0 && tw <= wmax) W = tw;
   if constexpr (MB == 1) {
-    if (T == 1 && W > 8) {
-      launch_midm<F, 1, 1, 16>(W, st, q, s, x, y, M, N, K, g);
-      return;
-    }
+    if (T == 1 && W > 8) return launch_midm<F, 1, 1, 16>(W, st, q, s, x, y, M, N, K, g);
   }
   if constexpr (MB <= 3) {
-    if (T == 2) {
-      launch_midm<F, MB, 2>(W, st, q, s, x, y, M, N, K, g);
-      return;
-    }
+    if (T == 2) return launch_midm<F, MB, 2>(W, st, q, s, x, y, M, N, K, g);
   }
-  launch_midm<F, MB, 1>(W, st, q, s, x, y, M, N, K, g);
+  return launch_midm<F, MB, 1>(W, st, q, s, x, y, M, N, K, g);
 }
 
 template <int F>
-static void dispatch_midm(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
-                          int N, int K, float g) {
+static int dispatch_midm(int M, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
+                         int N, int K, float g) {
   const int mb = (M + 15) / 16;
-  if (mb == 1)      dispatch_midm_mb<F, 1>(M, st, q, s, x, y, N, K, g);
-  else if (mb == 2) dispatch_midm_mb<F, 2>(M, st, q, s, x, y, N, K, g);
-  else if (mb == 3) dispatch_midm_mb<F, 3>(M, st, q, s, x, y, N, K, g);
-  else              dispatch_midm_mb<F, 4>(M, st, q, s, x, y, N, K, g);
+  if (mb == 1) return dispatch_midm_mb<F, 1>(M, st, q, s, x, y, N, K, g);
+  if (mb == 2) return dispatch_midm_mb<F, 2>(M, st, q, s, x, y, N, K, g);
+  if (mb == 3) return dispatch_midm_mb<F, 3>(M, st, q, s, x, y, N, K, g);
+  return dispatch_midm_mb<F, 4>(M, st, q, s, x, y, N, K, g);
 }
 
 
@@ -941,18 +920,16 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
     const uint8_t* ss = (const uint8_t*)s;
     const uint16_t* xx = (const uint16_t*)x_bf16;
     switch (fmt) {
-      case NVFP4: dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
-      case DUAL:  dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
-      default:    dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
+      case NVFP4: return dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
+      case DUAL:  return dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
+      default:    return dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
     }
-    return fp4_launch_status();
   }
   GemvBatch<1> b;
   b.count = 1;
   b.it[0] = GemvItem{(const uint8_t*)q, (const uint8_t*)s, (const uint16_t*)x_bf16, y, (int)N, (int)K, 0, 0,
                      global_scale, 0};
-  dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
-  return fp4_launch_status();
+  return dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
 }
 
 template <int MAXI>
@@ -984,17 +961,16 @@ extern "C" int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_
   if (count == 1) {
     GemvBatch<1> b;
     fill_batch(b, count, items);
-    dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
-  } else if (count <= 4) {
+    return dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
+  }
+  if (count <= 4) {
     GemvBatch<4> b;
     fill_batch(b, count, items);
-    dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
-  } else {
-    GemvBatch<FP4_GEMV_MAX_ITEMS> b;
-    fill_batch(b, count, items);
-    dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
+    return dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
   }
-  return fp4_launch_status();
+  GemvBatch<FP4_GEMV_MAX_ITEMS> b;
+  fill_batch(b, count, items);
+  return dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
 }
 
 // Mid-M entry point (17 <= M <= 64 through w4a16_matmul; any 1 <= M <= 64 accepted).
@@ -1015,9 +991,8 @@ extern "C" int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   const uint8_t* ss = (const uint8_t*)s;
   const uint16_t* xx = (const uint16_t*)x_bf16;
   switch (fmt) {
-    case NVFP4: dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
-    case DUAL:  dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;
-    default:    dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale); break;  // FAST
+    case NVFP4: return dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
+    case DUAL:  return dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
+    default:    return dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
   }
-  return fp4_launch_status();
 }

@@ -1,8 +1,11 @@
-// Host-side argument checks shared by the entry points.
+// Host-side helpers shared by the entry points: argument checks, checked launches, the tuning
+// overrides and per-device caches.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <atomic>
+#include <tuple>
+#include <utility>
 
 static inline bool fp4_valid_format(int f) { return f >= 1 && f <= 4; }
 
@@ -17,8 +20,38 @@ static inline int fp4_check_nk(int fmt, int64_t N, int64_t K) {
   return 0;
 }
 
-// Launch status of the last kernel enqueued by this thread.
-static inline int fp4_launch_status() { return hipGetLastError() == hipSuccess ? 0 : -6; }
+// Launches kernel `k` through hipLaunchKernel and returns 0, or FP4_ERR_HIP (-6) when the runtime
+// rejects this launch. The status is the launch's own return value: an error left behind by an
+// earlier, unrelated HIP call is neither reported nor cleared here. Each argument is converted to
+// the kernel's parameter type before its address is passed.
+template <typename... P, typename... A, size_t... I>
+static inline int fp4_launch_impl(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                                  std::index_sequence<I...>, A&&... a) {
+  std::tuple<P...> args(static_cast<P>(std::forward<A>(a))...);
+  void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {static_cast<void*>(&std::get<I>(args))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, lds, st) == hipSuccess ? 0 : -6;
+}
+
+template <typename... P, typename... A>
+static inline int fp4_launch(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  return fp4_launch_impl(k, grid, block, lds, st, std::index_sequence_for<P...>{}, std::forward<A>(a)...);
+}
+
+// Tuning overrides, read once from the environment at the first call that needs them (a
+// thread-safe static initialisation in api.hip) and fixed for the life of the process. -1 = unset.
+// They exist for A/B timing and for tests that force one path; nothing sets them by default.
+struct Fp4Tuning {
+  int gemv_waves;      // FP4_GEMV_WAVES: 1..16 waves per GEMV workgroup
+  int gemv_u;          // FP4_GEMV_U: 2..4 chunk slots per wave (M = 1)
+  int gemv_one;        // FP4_GEMV_ONE=0: batch loop with prefetch instead of one batch per wave
+  int gemv_ring;       // FP4_GEMV_RING=0/1: never / whenever it applies, the long-K ring kernel
+  int midm_waves;      // FP4_MIDM_WAVES: waves per mid-M workgroup
+  int gemm_short;      // FP4_GEMM_SHORT=0: 256-row tiles only
+  int gemm_split;      // FP4_GEMM_SPLIT=0: whole K per workgroup
+  int gemm_band_rows;  // FP4_GEMM_BAND_ROWS=0: 256-row tiles at M <= 192
+};
+const Fp4Tuning& fp4_tuning();
 
 // A kernel's dynamic-LDS limit raised to `bytes` once per device: the attribute is set for the device
 // current at the call, so a process that launches on several GPUs needs it on each. One static object
@@ -36,3 +69,6 @@ struct Fp4LdsLimit {
       done[dev].store(1, std::memory_order_release);
   }
 };
+
+// Compute units of the current device (queried once per device).
+int fp4_device_cus();

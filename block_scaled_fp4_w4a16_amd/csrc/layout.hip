@@ -2,6 +2,8 @@
 #include "common.h"
 #include "launch.h"
 #include "fp4w4a16.h"
+#include <atomic>
+#include <mutex>
 
 namespace fp4 {
 
@@ -120,9 +122,74 @@ __global__ void dequant_kernel(int N, int K, int nchunk, int64_t npieces, const 
   }
 }
 
+// Scale validation (fp4_pack_layout with validate != 0): one thread per scale of the canonical input.
+// A NaN E4M3 / UE4M3 code (low 7 bits all ones; UE4M3's bit 7 is ignored as on decode) or a Q4_0 FP16
+// scale with an all-ones exponent sets *bad. Every writer stores the same value, so the races are benign.
+template <int F>
+__global__ void validate_scales_kernel(int64_t nscales, const uint8_t* __restrict__ src_q,
+                                       const uint8_t* __restrict__ src_s, unsigned int* __restrict__ bad) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nscales; i += (int64_t)gridDim.x * blockDim.x) {
+    bool nonfinite;
+    if (F == NVFP4) {
+      nonfinite = (src_s[i] & 0x7F) == 0x7F;
+    } else if (F == DUAL) {           // two scale bytes at the head of each 18-byte block
+      nonfinite = (src_q[(i >> 1) * 18 + (i & 1)] & 0x7F) == 0x7F;
+    } else if (F == FAST) {           // one scale byte at the head of each 17-byte block
+      nonfinite = (src_q[i * 17] & 0x7F) == 0x7F;
+    } else {                          // Q4_0: FP16 scale, little-endian, at the head of each 18-byte block
+      const unsigned hi = src_q[i * 18 + 1];
+      nonfinite = ((hi >> 2) & 31) == 31;
+    }
+    if (nonfinite) *bad = 1u;
+  }
+}
+
+__global__ void clear_word_kernel(unsigned int* w) { *w = 0u; }
+
+// One 4-byte word per device for the validation result. In host code `fp4_bad_scale_word` is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned int fp4_bad_scale_word;
+
 }  // namespace fp4
 
 using namespace fp4;
+
+namespace {
+std::mutex g_validate_lock[64];
+std::atomic<unsigned int*> g_validate_word[64];
+
+// The device address of the validation word on the current device (or nullptr).
+unsigned int* validate_word(int dev) {
+  unsigned int* p = g_validate_word[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* a = nullptr;
+  if (hipGetSymbolAddress(&a, HIP_SYMBOL(fp4::fp4_bad_scale_word)) != hipSuccess || !a) return nullptr;
+  p = static_cast<unsigned int*>(a);
+  g_validate_word[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+template <int F>
+int validate_scales(int64_t N, int64_t K, const uint8_t* sq, const uint8_t* ss, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -6;
+  std::lock_guard<std::mutex> guard(g_validate_lock[dev]);
+  unsigned int* word = validate_word(dev);
+  if (!word) return -6;
+  const int64_t nscales = (F == NVFP4) ? N * (K / 16) : (F == DUAL ? 2 : 1) * N * (K / 32);
+  const int threads = 256;
+  const int64_t want = (nscales + threads - 1) / threads;
+  const unsigned blocks = (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+  int rc = fp4_launch(clear_word_kernel, dim3(1), dim3(1), 0, st, word);
+  if (rc) return rc;
+  rc = fp4_launch(validate_scales_kernel<F>, dim3(blocks), dim3(threads), 0, st, nscales, sq, ss, word);
+  if (rc) return rc;
+  unsigned int host = 0;
+  if (hipMemcpyAsync(&host, word, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess) return -6;
+  if (hipStreamSynchronize(st) != hipSuccess) return -6;
+  return host ? -5 : 0;
+}
+}  // namespace
 
 extern "C" int fp4_layout_bytes(int fmt, int64_t N, int64_t K, size_t* q_bytes, size_t* s_bytes) {
   if (!fp4_valid_format(fmt) || !q_bytes || !s_bytes) return -1;
@@ -135,7 +202,7 @@ extern "C" int fp4_layout_bytes(int fmt, int64_t N, int64_t K, size_t* q_bytes, 
 }
 
 extern "C" int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q, const void* src_s,
-                               void* dst_q, void* dst_s, void* stream) {
+                               void* dst_q, void* dst_s, int validate, void* stream) {
   if (!fp4_valid_format(fmt) || !src_q || !dst_q || !dst_s) return -1;
   if (fmt == NVFP4 && !src_s) return -1;
   if (fmt != NVFP4 && src_s) return -1;
@@ -153,13 +220,22 @@ extern "C" int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q,
   const uint8_t* ss = (const uint8_t*)src_s;
   uint8_t* dq = (uint8_t*)dst_q;
   uint8_t* ds = (uint8_t*)dst_s;
-  switch (fmt) {
-    case NVFP4: hipLaunchKernelGGL(pack_layout_kernel<NVFP4>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
-    case DUAL:  hipLaunchKernelGGL(pack_layout_kernel<DUAL>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
-    case FAST:  hipLaunchKernelGGL(pack_layout_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
-    default:    hipLaunchKernelGGL(pack_layout_kernel<Q4_0>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds); break;
+  if (validate) {
+    switch (fmt) {
+      case NVFP4: rc = validate_scales<NVFP4>(N, K, sq, ss, st); break;
+      case DUAL:  rc = validate_scales<DUAL>(N, K, sq, ss, st); break;
+      case FAST:  rc = validate_scales<FAST>(N, K, sq, ss, st); break;
+      default:    rc = validate_scales<Q4_0>(N, K, sq, ss, st); break;
+    }
+    if (rc) return rc;
   }
-  return fp4_launch_status();
+  const dim3 grid((unsigned)blocks), block(threads);
+  switch (fmt) {
+    case NVFP4: return fp4_launch(pack_layout_kernel<NVFP4>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds);
+    case DUAL:  return fp4_launch(pack_layout_kernel<DUAL>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds);
+    case FAST:  return fp4_launch(pack_layout_kernel<FAST>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds);
+    default:    return fp4_launch(pack_layout_kernel<Q4_0>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, sq, ss, dq, ds);
+  }
 }
 
 extern "C" int fp4_dequant_f32(int fmt, int64_t N, int64_t K, const void* q, const void* s, float global_scale,
@@ -177,11 +253,11 @@ extern "C" int fp4_dequant_f32(int fmt, int64_t N, int64_t K, const void* q, con
   hipStream_t st = (hipStream_t)stream;
   const uint8_t* qq = (const uint8_t*)q;
   const uint8_t* sp = (const uint8_t*)s;
+  const dim3 grid((unsigned)blocks), block(threads);
   switch (fmt) {
-    case NVFP4: hipLaunchKernelGGL(dequant_kernel<NVFP4>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
-    case DUAL:  hipLaunchKernelGGL(dequant_kernel<DUAL>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
-    case FAST:  hipLaunchKernelGGL(dequant_kernel<FAST>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
-    default:    hipLaunchKernelGGL(dequant_kernel<Q4_0>, dim3((unsigned)blocks), dim3(threads), 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w); break;
+    case NVFP4: return fp4_launch(dequant_kernel<NVFP4>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w);
+    case DUAL:  return fp4_launch(dequant_kernel<DUAL>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w);
+    case FAST:  return fp4_launch(dequant_kernel<FAST>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w);
+    default:    return fp4_launch(dequant_kernel<Q4_0>, grid, block, 0, st, (int)N, (int)K, nchunk, npieces, qq, sp, global_scale, w);
   }
-  return fp4_launch_status();
 }

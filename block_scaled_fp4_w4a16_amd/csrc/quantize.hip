@@ -254,14 +254,16 @@ extern "C" int fp4_quantize_nvfp4(int64_t N, int64_t K, const float* w, void* wq
   if (!fp4_aligned(w, 16) || !fp4_aligned(wq, 8) || !fp4_aligned(g_out, 4)) return -3;
   hipStream_t st = (hipStream_t)stream;
   const int64_t count = N * K, nblocks = count / 16;
-  hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(1), 0, st, g_out);
+  rc = fp4_launch(nvfp4_zero_kernel, dim3(1), dim3(1), 0, st, g_out);
+  if (rc) return rc;
   int grid = (int)((count + 255) / 256);
   if (grid > 4096) grid = 4096;
-  hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(grid), dim3(256), 0, st, w, count, g_out);
-  hipLaunchKernelGGL(nvfp4_pack_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st, w, nblocks,
-                     (const float*)g_out, (uint8_t*)wq, (uint8_t*)ws);
-  hipLaunchKernelGGL(nvfp4_finish_kernel, dim3(1), dim3(1), 0, st, g_out);
-  return fp4_launch_status();
+  rc = fp4_launch(nvfp4_amax_kernel, dim3(grid), dim3(256), 0, st, w, count, g_out);
+  if (rc) return rc;
+  rc = fp4_launch(nvfp4_pack_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st, w, nblocks,
+                  (const float*)g_out, (uint8_t*)wq, (uint8_t*)ws);
+  if (rc) return rc;
+  return fp4_launch(nvfp4_finish_kernel, dim3(1), dim3(1), 0, st, g_out);
 }
 
 extern "C" int fp4_quantize_rocmfp4(int fmt, int64_t N, int64_t K, const float* w, const float* importance,
@@ -275,12 +277,10 @@ extern "C" int fp4_quantize_rocmfp4(int fmt, int64_t N, int64_t K, const float* 
   const int64_t grid = (nblocks * 64 + 255) / 256;
   if (grid > 0x7fffffffLL) return -4;
   if (fmt == DUAL)
-    hipLaunchKernelGGL(rocm_pack_kernel<DUAL>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
-                       (uint8_t*)blocks);
-  else
-    hipLaunchKernelGGL(rocm_pack_kernel<FAST>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
-                       (uint8_t*)blocks);
-  return fp4_launch_status();
+    return fp4_launch(rocm_pack_kernel<DUAL>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
+                      (uint8_t*)blocks);
+  return fp4_launch(rocm_pack_kernel<FAST>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
+                    (uint8_t*)blocks);
 }
 
 extern "C" int fp4_quantize_q4_0(int64_t N, int64_t K, const float* w, void* blocks, void* stream) {
@@ -291,7 +291,6 @@ extern "C" int fp4_quantize_q4_0(int64_t N, int64_t K, const float* w, void* blo
   const int64_t nblocks = N * K / 32;
   const int64_t grid = (nblocks + 255) / 256;
   if (grid > 0x7fffffffLL) return -4;
-  hipLaunchKernelGGL(q4_0_pack_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w, nblocks,
-                     (uint8_t*)blocks);
-  return fp4_launch_status();
+  return fp4_launch(q4_0_pack_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w, nblocks,
+                    (uint8_t*)blocks);
 }

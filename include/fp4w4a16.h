@@ -24,7 +24,18 @@
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; a return of FP4_OK means the launch was accepted.
  *  - Arguments are validated before anything is enqueued; a negative status is returned
- *    and nothing runs. No entry point prints, aborts or keeps mutable global state.
+ *    and nothing runs. A launch the HIP runtime rejects returns FP4_ERR_HIP (each launch's
+ *    own return code is checked; errors left by earlier, unrelated HIP calls are neither
+ *    reported nor cleared). No entry point prints or aborts.
+ *  - State kept between calls: per-device caches of facts about the device (compute-unit
+ *    count, occupancy of each kernel variant, whether a kernel's dynamic-LDS limit has been
+ *    raised), filled on first use and never changed afterwards; the tuning overrides read
+ *    once from the environment at the first call (FP4_GEMV_WAVES, FP4_GEMV_U, FP4_GEMV_ONE,
+ *    FP4_GEMV_RING, FP4_MIDM_WAVES, FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS; none
+ *    set by default); and one 4-byte device word per GPU, a static device variable, that
+ *    fp4_pack_layout uses when asked to validate (serialised by a per-device host lock).
+ *    Apart from that word, which only the validation path touches, concurrent calls on
+ *    different streams share no mutable state.
  *  - Shapes: W is N x K (N outputs, K inputs); x is M x K bf16 row-major; y is M x N
  *    fp32 row-major. K must be a multiple of 16 (NVFP4) or 32 (ROCmFP4). M = 0 is a
  *    no-op. x and the planes must be 16-byte aligned; y must be 4-byte aligned and must
@@ -40,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP4W4A16_ABI_VERSION 1
+#define FP4W4A16_ABI_VERSION 2
 
 /* Weight formats. */
 enum {
@@ -57,7 +68,9 @@ enum {
   FP4_ERR_SHAPE = -2,        /* bad M, N or K                                    */
   FP4_ERR_ALIGN = -3,        /* a pointer is not aligned as required             */
   FP4_ERR_UNSUPPORTED = -4,  /* shape outside what the entry point handles       */
-  FP4_ERR_HIP = -6           /* the HIP runtime rejected a launch                */
+  FP4_ERR_INVALID_SCALE = -5,/* a scale code is NaN or infinite (fp4_pack_layout
+                                with validation on)                               */
+  FP4_ERR_HIP = -6           /* the HIP runtime rejected a launch or a copy      */
 };
 
 /* Version of this interface (FP4W4A16_ABI_VERSION). */
@@ -70,12 +83,20 @@ const char* fp4_status_string(int status);
  * Bytes of the two device planes ("kernel layout") that fp4_pack_layout writes for an
  * N x K matrix of format `fmt`: the nibble plane and the scale plane. Rows are padded to
  * a multiple of 16 and K to a multiple of 128; padding holds zero codes and zero scales.
- * q_bytes and s_bytes are HOST pointers.
+ * For N a multiple of 16 and K of 128 the two planes hold exactly the canonical bytes:
+ * 18, 17 and 18 bytes per 32 weights for Dual, FAST and Q4_0 (ROCmFP4 design page, format
+ * comparison table: block size and density) and K/2 + K/16 bytes per row for NVFP4 (one
+ * nibble per weight and one scale byte per 16: EdgeRock-4B-NVFP4 card, description).
+ * q_bytes and s_bytes are HOST pointers. Errors: FP4_ERR_ARG (unknown format, null
+ * pointer), FP4_ERR_SHAPE / FP4_ERR_UNSUPPORTED (N or K out of range).
  */
 int fp4_layout_bytes(int fmt, int64_t N, int64_t K, size_t* q_bytes, size_t* s_bytes);
 
 /*
- * Repack canonical packed weights into the kernel layout (load time, once per matrix).
+ * Repack canonical packed weights into the kernel layout (load time, once per matrix; the
+ * pages handle their packed data and scales once, when a checkpoint is loaded: EdgeRock-4B-
+ * NVFP4 card, "Load on a CUDA GPU"; block contents from the ROCmFP4 design page, format
+ * comparison table, and section 02 on the two half-block scales).
  * Canonical input (device memory):
  *   NVFP4:    src_q = wq uint8[N][K/2], byte j holds element 2j (bits 0-3) and 2j+1
  *             (bits 4-7); src_s = ws uint8[N][K/16] E4M3 scales.
@@ -86,17 +107,37 @@ int fp4_layout_bytes(int fmt, int64_t N, int64_t K, size_t* q_bytes, size_t* s_b
  *             same qs order; src_s must be NULL.
  * Output: dst_q / dst_s of the sizes fp4_layout_bytes reports (16-byte aligned). The
  * layout's internal order is private to this library and may change with the ABI version.
+ * validate != 0: before anything is written, every scale code is checked on the device
+ * (both formats define their scales as finite numbers: EdgeRock-4B-NVFP4 card, description,
+ * which gives E4M3 scale bytes; ROCmFP4 design page, section 02, where the scale bytes are
+ * E4M3 without a sign, and section 03, whose search ranges over finite scale values only).
+ * An E4M3 / UE4M3 code whose low 7 bits are all ones (NaN), or a Q4_0 FP16
+ * scale with an all-ones exponent (infinity or NaN), makes the call return
+ * FP4_ERR_INVALID_SCALE and leave dst_q / dst_s untouched. Validation waits for `stream`
+ * (the call returns only after the check has run) and is meant for load time.
+ * validate == 0: no check and no wait; such codes then decode to NaN (or infinity) as the
+ * format defines them.
+ * Errors: FP4_ERR_ARG (unknown format; null src_q, dst_q or dst_s; src_s null for NVFP4 or
+ * non-null otherwise), FP4_ERR_SHAPE / FP4_ERR_UNSUPPORTED (N, K), FP4_ERR_ALIGN (dst not
+ * 16-byte aligned), FP4_ERR_INVALID_SCALE, FP4_ERR_HIP.
  */
 int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q, const void* src_s,
-                    void* dst_q, void* dst_s, void* stream);
+                    void* dst_q, void* dst_s, int validate, void* stream);
 
 /*
- * Decode-shaped product, 1 <= M <= 16: streams each nibble and scale byte
+ * Decode-shaped product, 1 <= M <= 16 (one token, or one token plus n-gram draft tokens:
+ * Nanbeige4.2-3B-NVFP4A16 card, serving notes; its speed is set by the weight bytes read:
+ * same card, speed notes, and Gemma-4-E4B-it-ROCmFP4-GGUF card, bandwidth sanity check).
+ * y = x * W^T with W as defined at the top (EdgeRock-4B-NVFP4 card, description; ROCmFP4
+ * design page, sections 01 and 02). Streams each nibble and scale byte
  * once, decodes to exact bf16 levels, contracts against x on the matrix cores, applies
  * the group scales to the FP32 partial sums, reduces the K split inside the workgroup and
  * multiplies by g. From M = 5 on (NVFP4, Dual, FAST) it runs the w4a16_midm kernel instead,
  * which decodes each weight once into exact bf16 level*scale shared by all rows of x.
- * q/s are fp4_pack_layout output. Deterministic (no atomics).
+ * q/s are fp4_pack_layout output (device); x is M x K bf16 bit patterns and y M x N fp32,
+ * both row-major on the device. Deterministic (no atomics). Errors: FP4_ERR_ARG,
+ * FP4_ERR_SHAPE (M < 0, N or K), FP4_ERR_UNSUPPORTED (M > 16, K > 2^24), FP4_ERR_ALIGN,
+ * FP4_ERR_HIP.
  */
 int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);
@@ -126,7 +167,10 @@ typedef struct fp4_gemv_item {
 int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items, void* stream);
 
 /*
- * Prefill-shaped product, any M >= 1, intended for M >= 64: stages x tiles
+ * Prefill-shaped product, any M >= 1, intended for M >= 64 (a prompt of many tokens against
+ * the same packed weights; W as defined at the top: EdgeRock-4B-NVFP4 card, description;
+ * ROCmFP4 design page, sections 01 and 02, and the technical-boundaries note that the levels
+ * are exact integers, which lets level*scale be exact in bf16): stages x tiles
  * and packed weight tiles, dequantizes each weight tile once into LDS as exact bf16
  * level*scale, contracts with bf16 MFMA in FP32 and multiplies by g in the epilogue.
  * When y has few 256x256 tiles (at most a quarter of the device's compute units) and K spans
@@ -135,6 +179,8 @@ int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items
  * onto zero give the same sum in either order, so the result is still bit-reproducible; it
  * differs from the whole-K sum only by rounding. Both kernels run on `stream`. For M <= 128 (192)
  * the tiles are 128 (192) rows high: same products, same order, same bits as 256-row tiles.
+ * Q4_0 gives FP4_ERR_UNSUPPORTED (its level*scale is not exact in bf16). Other errors:
+ * FP4_ERR_ARG, FP4_ERR_SHAPE, FP4_ERR_UNSUPPORTED (K > 2^22), FP4_ERR_ALIGN, FP4_ERR_HIP.
  */
 int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);

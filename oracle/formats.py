@@ -1,8 +1,8 @@
 """Codes of the two 4-bit weight formats and their scale bytes (FP64, exact).
 
 Sources:
-* EdgeRock-4B-NVFP4 model card, opening description: NVFP4 weights are E2M1
-  4-bit values with one FP8 E4M3 scale per 16 values and an FP32 global scale.
+* EdgeRock-4B-NVFP4 model card, opening description: NVFP4 stores E2M1 codes,
+  an E4M3 scale byte for each group of 16 weights, and a per-matrix FP32 factor.
   The E2M1 and E4M3 value sets are the OCP microscaling / OCP FP8 definitions
   those names refer to.
 * ROCmFP4 design page, section 01 (values) and the
@@ -18,7 +18,7 @@ Readings (the pages leave these open):
 * UE4M3: the byte's bit 7 is ignored (masked); 0x7F is NaN and never emitted,
   so the finite candidates are the 127 codes 0x00..0x7E, zero included.
 * Q4_0: the 16 codes are the consecutive integers -8..7 (code q is level q - 8),
-  the usual stock Q4_0 grid that "uniform integer steps" in 4 bits describes.
+  the usual stock Q4_0 grid: the comparison table's evenly spaced integers in 4 bits.
 """
 from __future__ import annotations
 

@@ -90,13 +90,21 @@ def _nvfp4_rows(w: np.ndarray, g: np.float32):
     return layouts.nvfp4_join(codes), scale_codes.reshape(n, k // 16)
 
 
-def pack_nvfp4(w: np.ndarray, rows_per_slab: int = 512):
-    w = np.ascontiguousarray(w, dtype=np.float32)
+def nvfp4_global_scale(w: np.ndarray) -> np.float32:
+    """Step 1: g = fl32(amax / 2688) of the whole matrix (0 when amax is 0)."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(w))) if w.size else np.float32(0)
+    return np.float32(amax) / np.float32(6 * 448) if amax > 0 else np.float32(0)
+
+
+def pack_nvfp4_rows(w_rows: np.ndarray, g: np.float32, rows_per_slab: int = 512):
+    """Steps 2-3 for some rows of a matrix whose global scale g (step 1, over the whole matrix) is
+    given: rows are packed independently once g is known, so a row sample packs to exactly the bytes
+    those rows get in the whole matrix."""
+    w = np.ascontiguousarray(w_rows, dtype=np.float32)
     n, k = w.shape
     if k % layouts.NVFP4_GROUP:
         raise ValueError("K must be a multiple of 16 for NVFP4")
-    amax = np.float32(np.max(np.abs(w))) if w.size else np.float32(0)
-    g = np.float32(amax) / np.float32(6 * 448) if amax > 0 else np.float32(0)
     if not (g > 0):
         return (np.zeros((n, k // 2), np.uint8), np.zeros((n, k // 16), np.uint8), np.float32(1.0))
     wq = np.empty((n, k // 2), np.uint8)
@@ -104,6 +112,13 @@ def pack_nvfp4(w: np.ndarray, rows_per_slab: int = 512):
     for r0 in range(0, n, rows_per_slab):
         wq[r0:r0 + rows_per_slab], ws[r0:r0 + rows_per_slab] = _nvfp4_rows(w[r0:r0 + rows_per_slab], g)
     return (wq, ws, np.float32(g))
+
+
+def pack_nvfp4(w: np.ndarray, rows_per_slab: int = 512):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.shape[1] % layouts.NVFP4_GROUP:
+        raise ValueError("K must be a multiple of 16 for NVFP4")
+    return pack_nvfp4_rows(w, nvfp4_global_scale(w), rows_per_slab)
 
 
 def rocmfp4_search(w_groups: np.ndarray, importance: np.ndarray | None = None):

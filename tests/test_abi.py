@@ -11,7 +11,7 @@ HEADER = os.path.join(ROOT, "include", "fp4w4a16.h")
 
 fp4 = pytest.importorskip("block_scaled_fp4_w4a16_amd")
 
-OK, ARG, SHAPE, ALIGN, UNSUP = 0, -1, -2, -3, -4
+OK, ARG, SHAPE, ALIGN, UNSUP, INVALID_SCALE, HIP = 0, -1, -2, -3, -4, -5, -6
 FAKE = 1 << 20   # a 16-byte-aligned non-null address; never dereferenced by these calls
 NVFP4, DUAL, FAST, Q4_0 = 1, 2, 3, 4
 
@@ -31,9 +31,23 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert fp4.fp4_abi_version() == 1
-    for st in (OK, ARG, SHAPE, ALIGN, UNSUP, -6, 12345):
+    assert fp4.fp4_abi_version() == 2
+    for st in (OK, ARG, SHAPE, ALIGN, UNSUP, INVALID_SCALE, HIP, 12345):
         assert isinstance(fp4.fp4_status_string(st), str) and fp4.fp4_status_string(st)
+    # every status has its own text
+    texts = [fp4.fp4_status_string(st) for st in (OK, ARG, SHAPE, ALIGN, UNSUP, INVALID_SCALE, HIP)]
+    assert len(set(texts)) == len(texts)
+    assert "scale" in fp4.fp4_status_string(INVALID_SCALE)
+    assert fp4.fp4_status_string(12345) == "unknown status"
+
+
+def test_header_declares_status_codes():
+    text = open(HEADER).read()
+    for name, value in (("FP4_OK", 0), ("FP4_ERR_ARG", -1), ("FP4_ERR_SHAPE", -2), ("FP4_ERR_ALIGN", -3),
+                        ("FP4_ERR_UNSUPPORTED", -4), ("FP4_ERR_INVALID_SCALE", -5), ("FP4_ERR_HIP", -6)):
+        assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
+    assert re.search(r"FP4W4A16_ABI_VERSION\s+2\b", text)
+    assert re.search(r"int fp4_pack_layout\([^)]*int validate, void\* stream\)", text)
 
 
 def test_layout_bytes():
@@ -98,14 +112,19 @@ def test_product_argument_errors(fn):
         assert call(M=65) == UNSUP
 
 
-def test_pack_layout_argument_errors():
+@pytest.mark.parametrize("validate", [0, 1])
+def test_pack_layout_argument_errors(validate):
+    # argument checks come before the validation pass, so these fail on the host with or without it
     f = _raw().fp4_pack_layout
-    assert f(Q4_0, 16, 64, FAKE, FAKE, FAKE, FAKE, None) == ARG       # Q4_0 carries scales in blocks
-    assert f(NVFP4, 16, 64, FAKE, None, FAKE, FAKE, None) == ARG      # NVFP4 needs the scale plane
-    assert f(DUAL, 16, 64, FAKE, FAKE, FAKE, FAKE, None) == ARG       # ROCmFP4 carries scales in blocks
-    assert f(FAST, 16, 48, FAKE, None, FAKE, FAKE, None) == SHAPE
-    assert f(FAST, 16, 64, FAKE, None, FAKE + 4, FAKE, None) == ALIGN
-    assert f(9, 16, 64, FAKE, None, FAKE, FAKE, None) == ARG
+    v = validate
+    assert f(Q4_0, 16, 64, FAKE, FAKE, FAKE, FAKE, v, None) == ARG       # Q4_0 carries scales in blocks
+    assert f(NVFP4, 16, 64, FAKE, None, FAKE, FAKE, v, None) == ARG      # NVFP4 needs the scale plane
+    assert f(DUAL, 16, 64, FAKE, FAKE, FAKE, FAKE, v, None) == ARG       # ROCmFP4 carries scales in blocks
+    assert f(FAST, 16, 48, FAKE, None, FAKE, FAKE, v, None) == SHAPE
+    assert f(FAST, 16, 64, FAKE, None, FAKE + 4, FAKE, v, None) == ALIGN
+    assert f(9, 16, 64, FAKE, None, FAKE, FAKE, v, None) == ARG
+    assert f(DUAL, 16, 64, None, None, FAKE, FAKE, v, None) == ARG
+    assert f(DUAL, 0, 64, FAKE, None, FAKE, FAKE, v, None) == SHAPE
 
 
 def test_dequant_and_quantize_argument_errors():

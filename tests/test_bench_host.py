@@ -5,6 +5,8 @@ import os
 import subprocess
 import sys
 
+import numpy as np
+
 import bench
 import synth
 
@@ -46,3 +48,25 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stdout
+
+
+def test_oracle_sample_gate_passes_the_oracle_and_fails_a_perturbed_output():
+    # the parity gate of the CPU-baseline leg: the oracle's own product passes, a product with one
+    # element off by more than the tolerance is flagged (so that workload's throughput is withheld)
+    from oracle import pack, ref
+    w = synth.weights(64, 256, dist="t", nu=5.0, cfg=95)
+    x_bits = synth.activations(3, 256, cfg=95, mat=1)
+    for fmt in ("nvfp4", "rocmfp4_dual", "rocmfp4_fast"):
+        y = ref.matmul(x_bits, ref.dequant(fmt, pack.pack(fmt, w))).astype(np.float32)
+        rows = bench.sample_rows(64, 16)
+        good = bench.oracle_sample(fmt, w, rows, x_bits, y, threads=3, budget_s=0.0)
+        assert good["parity"] and good["rows"] == len(rows) and good["runs"] >= 3
+        bad_y = y.copy()
+        bad_y[1, rows[5]] += 0.5
+        assert not bench.oracle_sample(fmt, w, rows, x_bits, bad_y, threads=2, budget_s=0.0, time_it=False)["parity"]
+
+
+def test_sample_rows_cover_both_ends():
+    r = bench.sample_rows(4096, 512)
+    assert r[0] == 0 and r[-1] == 4095 and len(r) == 512 and np.all(np.diff(r) > 0)
+    assert list(bench.sample_rows(5, 512)) == [0, 1, 2, 3, 4]

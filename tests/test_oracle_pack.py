@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
+import synth
 from oracle import formats, layouts, pack, ref
 from tests import golden_io
 
@@ -268,3 +269,16 @@ def test_q4_0_zero_block():
     blocks, _ = pack.pack_q4_0(np.zeros((2, 32), np.float32))
     codes, d = layouts.q4_0_split(blocks)
     assert np.all(codes == 8) and np.all(d == 0)
+
+
+def test_nvfp4_row_sample_packs_like_the_whole_matrix():
+    # rows are packed independently once the whole-matrix global scale is known, so packing a row
+    # sample with that scale gives exactly those rows of the whole matrix's bytes
+    w = synth.weights(48, 128, dist="t", nu=5.0, cfg=96)
+    wq, ws, g = pack.pack_nvfp4(w)
+    rows = np.array([0, 7, 8, 31, 47])
+    sq, ss, sg = pack.pack_nvfp4_rows(w[rows], pack.nvfp4_global_scale(w))
+    assert sg == g
+    assert np.array_equal(sq, wq[rows]) and np.array_equal(ss, ws[rows])
+    # a sample packed on its own would take its own (smaller) amax: different bytes in general
+    assert pack.nvfp4_global_scale(w[rows]) <= g
