@@ -20,8 +20,8 @@ launches, replayed, plus one for the remainder); every graph is replayed during 
 timing. Each of R repetitions replays an untimed filler graph (the other copies, so that the timed
 copies are cold and the GPU queue is never empty at the start event), then the timed graphs between two
 HIP events on torch's current stream (the stream the graphs launch on). Reported: the median per-step
-time over the R repetitions, min, max, max/min and the raw samples, and the shader clock read by a probe
-kernel enqueued right after each timed block.
+time over the R repetitions, min, max, max/min and the raw samples, and the shader clock from the SMU's
+metrics (amdsmi) sampled while each timed block runs.
 
 The CPU baseline (`cpu_baseline`) times the oracle (exact dequantisation + FP64 product) on a bounded
 row sample of each workload, packed by the oracle's own packers, on every core of this process's
@@ -118,7 +118,7 @@ def cpu_model() -> str:
 
 # ----------------------------------------------------------------------------------------------
 class Probes:
-    """The benchmark's measurement kernels (libfp4probe.so): a plain streaming read and a clock probe."""
+    """The benchmark's measurement kernel (libfp4probe.so): a plain streaming read."""
 
     def __init__(self, torch):
         path = os.path.join(ROOT, "block_scaled_fp4_w4a16_amd", "libfp4probe.so")
@@ -128,25 +128,44 @@ class Probes:
         self.lib = ctypes.CDLL(path)
         self.lib.fp4probe_read.restype = ctypes.c_int
         self.lib.fp4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
-        self.lib.fp4probe_clock.restype = ctypes.c_int
-        self.lib.fp4probe_clock.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
         self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
-        self.clk = torch.zeros(2, dtype=torch.int64, device="cuda")
 
     def read(self, ptr: int, nbytes: int):
         rc = self.lib.fp4probe_read(ptr, nbytes, self.sink.data_ptr(), self.torch.cuda.current_stream().cuda_stream)
         if rc:
             raise RuntimeError(f"read probe launch failed ({rc})")
 
-    def clock_launch(self, ticks: int = 300):
-        """Enqueue the clock probe (a busy wait of `ticks` 100 MHz ticks) on the current stream."""
-        rc = self.lib.fp4probe_clock(ticks, self.clk.data_ptr(), self.torch.cuda.current_stream().cuda_stream)
-        if rc:
-            raise RuntimeError(f"clock probe launch failed ({rc})")
 
-    def clock_mhz(self) -> float:
-        cycles, ticks = (int(v) for v in self.clk.cpu().tolist())
-        return 100.0 * cycles / ticks if ticks > 0 else float("nan")
+class ClockSampler:
+    """The GPU's current shader (gfx) clock from the SMU metrics table (amdsmi), sampled while a timed block
+    runs: the host enqueues the block's graphs and samples before waiting for them, so the reading falls
+    inside the block whenever the block is longer than the enqueue (milliseconds here)."""
+
+    def __init__(self):
+        self.smi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self.smi = amdsmi
+        except Exception:
+            self.smi = None
+
+    def sample(self):
+        if self.smi is None:
+            return None
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        except Exception:
+            return None
+        vals = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and 0 < v < 10000]
+        if vals:
+            return float(np.mean(vals))
+        v = m.get("current_gfxclk")
+        return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
+
+
+CLOCK = None   # a ClockSampler once main() runs (amdsmi is not touched at import)
 
 
 def graph_of(torch, fn, launches):
@@ -171,7 +190,7 @@ def graph_of(torch, fn, launches):
 def time_steps(torch, fn, copies: int, steps: int, warmup: int, reps: int, probes=None, filler: int | None = None):
     """Time `steps` launches fn(i) (launch i reads copy i % copies) `reps` times; see the module docstring.
 
-    Returns per-step seconds (median, min, max, samples), the shader clock after each timed block, and the
+    Returns per-step seconds (median, min, max, samples), the shader clock sampled during the timed blocks, and the
     graph shape."""
     L = max(1, min(steps, copies))
     q, r = divmod(steps, L)
@@ -199,12 +218,11 @@ def time_steps(torch, fn, copies: int, steps: int, warmup: int, reps: int, probe
         if g_rem is not None:
             g_rem.replay()
         end.record()
-        if probes is not None:
-            probes.clock_launch()
+        c = CLOCK.sample() if CLOCK is not None else None
         torch.cuda.synchronize()
         samples.append(start.elapsed_time(end) / 1e3 / steps)
-        if probes is not None:
-            clocks.append(probes.clock_mhz())
+        if c is not None:
+            clocks.append(c)
     med = float(np.median(samples))
     return dict(median_s=med, min_s=float(min(samples)), max_s=float(max(samples)), samples_s=samples,
                 clock_mhz=float(np.median(clocks)) if clocks else None, launches_per_graph=L,
@@ -422,7 +440,7 @@ def oracle_sample(fmt: str, w_full: np.ndarray, rows: np.ndarray, x_bits: np.nda
     n, k = len(rows), w_full.shape[1]
     med = float(np.median(times))
     m = x_bits.shape[0]
-    return dict(parity=bool(ok), worst_error_ratio=round(float(worst), 5), rows=int(n), K=int(k), M=int(m),
+    return dict(parity=bool(ok), worst_error_ratio=float(f"{float(worst):.4g}"), rows=int(n), K=int(k), M=int(m),
                 ms=round(med * 1e3, 3), runs=len(times),
                 gbs=algorithmic_bytes(fmt, n, k) / med / 1e9, gflops=2.0 * m * n * k / med / 1e9)
 
@@ -480,6 +498,8 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "reps": 5}}), flush=True)
         return
 
+    global CLOCK
+    CLOCK = ClockSampler()
     probes = Probes(torch)
     reps = max(1, args.reps)
 
@@ -494,7 +514,7 @@ def main():
         gemv_rows[args.workload] = r
         log(f"gemv {args.workload}: {r['t']['median_s'] * 1e6:.3f} us/launch median "
             f"[{r['t']['min_s'] * 1e6:.3f}, {r['t']['max_s'] * 1e6:.3f}], "
-            f"{r['bytes'] / r['t']['median_s'] / 1e9:.1f} GB/s, clock {r['t']['clock_mhz']:.0f} MHz "
+            f"{r['bytes'] / r['t']['median_s'] / 1e9:.1f} GB/s, clock {r['t']['clock_mhz']} MHz "
             f"({r['copies']} cold copies, {time.time() - t0:.1f}s)")
     if "nvfp4_2048" in only:
         r = bench_gemv(fp4, torch, synth, "nvfp4_2048x2048_m1", args.steps, args.warmup, reps, probes)
@@ -524,7 +544,7 @@ def main():
             t0 = time.time()
             gemm[fmt] = bench_gemm(fp4, torch, synth, fmt, 2048, args.gemm_steps, args.gemm_warmup, reps, probes)
             log(f"gemm {fmt} M=2048: {gemm[fmt]['t']['median_s'] * 1e6:.1f} us/launch median, "
-                f"{gemm[fmt]['tflops']:.1f} TFLOP/s, clock {gemm[fmt]['t']['clock_mhz']:.0f} MHz "
+                f"{gemm[fmt]['tflops']:.1f} TFLOP/s, clock {gemm[fmt]['t']['clock_mhz']} MHz "
                 f"({time.time() - t0:.1f}s)")
     gemm_small = {}
     if "gemm_small" in only:

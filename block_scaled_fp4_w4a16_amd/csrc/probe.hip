@@ -1,12 +1,9 @@
-// Measurement probes for the benchmark (built into libfp4probe.so, separate from the library and its C
-// ABI; nothing in the library calls them).
+// Measurement probe for the benchmark (built into libfp4probe.so, separate from the library and its C
+// ABI; nothing in the library calls it).
 //  * fp4probe_read: a kernel that only streams `bytes` from HBM, with the GEMV's load form (16-byte
 //    nontemporal buffer loads, four per lane, 256-lane workgroups, one 16 KiB slice per workgroup). Its
 //    rate at a given size is the ceiling that launch cost and memory latency leave for any kernel that
 //    must read those bytes once.
-//  * fp4probe_clock: the shader clock, from the shader-clock cycle counter against the constant 100 MHz
-//    counter over a short busy wait; launched right after a workload, it reads the clock the workload
-//    ran at.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,20 +40,6 @@ __global__ __launch_bounds__(PROBE_THREADS) void read_probe_kernel(const uint8_t
   if (x == 0x9E3779B9u) sink[threadIdx.x] = x;
 }
 
-// One wave: cycles of the shader clock and ticks of the 100 MHz constant clock over a busy wait of at
-// least `ticks` constant-clock ticks (the loop is bounded by 2^24 iterations as well).
-__global__ void clock_probe_kernel(uint64_t ticks, uint64_t* __restrict__ out) {
-  const uint64_t c0 = __builtin_amdgcn_s_memtime();
-  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-  uint64_t r1 = r0;
-  for (int i = 0; i < (1 << 24) && r1 - r0 < ticks; ++i) r1 = __builtin_amdgcn_s_memrealtime();
-  const uint64_t c1 = __builtin_amdgcn_s_memtime();
-  if (threadIdx.x == 0) {
-    out[0] = c1 - c0;
-    out[1] = r1 - r0;
-  }
-}
-
 }  // namespace
 
 extern "C" int fp4probe_read(const void* p, uint64_t bytes, void* sink, void* stream) {
@@ -66,11 +49,4 @@ extern "C" int fp4probe_read(const void* p, uint64_t bytes, void* sink, void* st
   void* args[] = {&p, &bytes, &sink};
   return hipLaunchKernel(reinterpret_cast<const void*>(&read_probe_kernel), dim3((unsigned)blocks),
                          dim3(PROBE_THREADS), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : -6;
-}
-
-extern "C" int fp4probe_clock(uint64_t ticks, void* out, void* stream) {
-  if (!out) return -1;
-  void* args[] = {&ticks, &out};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&clock_probe_kernel), dim3(1), dim3(64), args, 0,
-                         (hipStream_t)stream) == hipSuccess ? 0 : -6;
 }
