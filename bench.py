@@ -20,8 +20,9 @@ launches, replayed, plus one for the remainder); every graph is replayed during 
 timing. Each of R repetitions replays an untimed filler graph (the other copies, so that the timed
 copies are cold and the GPU queue is never empty at the start event), then the timed graphs between two
 HIP events on torch's current stream (the stream the graphs launch on). Reported: the median per-step
-time over the R repetitions, min, max, max/min and the raw samples, and the shader clock from the SMU's
-metrics (amdsmi) sampled while each timed block runs.
+time over the R repetitions, min, max, max/min and the raw samples. (The shader clock is not sampled here:
+the SMU metrics table read through amdsmi does not follow the load on these boards; the counter-based
+clock, GRBM_GUI_ACTIVE over the traced kernel time, is recorded with the rocprofv3 summaries.)
 
 The CPU baseline (`cpu_baseline`) times the oracle (exact dequantisation + FP64 product) on a bounded
 row sample of each workload, packed by the oracle's own packers, on every core of this process's
@@ -136,38 +137,6 @@ class Probes:
             raise RuntimeError(f"read probe launch failed ({rc})")
 
 
-class ClockSampler:
-    """The GPU's current shader (gfx) clock from the SMU metrics table (amdsmi), sampled while a timed block
-    runs: the host enqueues the block's graphs and samples before waiting for them, so the reading falls
-    inside the block whenever the block is longer than the enqueue (milliseconds here)."""
-
-    def __init__(self):
-        self.smi = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
-            self.smi = amdsmi
-        except Exception:
-            self.smi = None
-
-    def sample(self):
-        if self.smi is None:
-            return None
-        try:
-            m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
-        except Exception:
-            return None
-        vals = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and 0 < v < 10000]
-        if vals:
-            return float(np.mean(vals))
-        v = m.get("current_gfxclk")
-        return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
-
-
-CLOCK = None   # a ClockSampler once main() runs (amdsmi is not touched at import)
-
-
 def graph_of(torch, fn, launches):
     """Capture fn(i) for i in `launches` into one HIP graph (the library launches on the capture stream)."""
     launches = list(launches)
@@ -190,8 +159,7 @@ def graph_of(torch, fn, launches):
 def time_steps(torch, fn, copies: int, steps: int, warmup: int, reps: int, probes=None, filler: int | None = None):
     """Time `steps` launches fn(i) (launch i reads copy i % copies) `reps` times; see the module docstring.
 
-    Returns per-step seconds (median, min, max, samples), the shader clock sampled during the timed blocks, and the
-    graph shape."""
+    Returns per-step seconds (median, min, max, samples) and the graph shape."""
     L = max(1, min(steps, copies))
     q, r = divmod(steps, L)
     g_main = graph_of(torch, fn, range(L))
@@ -208,7 +176,7 @@ def time_steps(torch, fn, copies: int, steps: int, warmup: int, reps: int, probe
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    samples, clocks = [], []
+    samples = []
     for _ in range(reps):
         if g_fill is not None:
             g_fill.replay()
@@ -218,14 +186,11 @@ def time_steps(torch, fn, copies: int, steps: int, warmup: int, reps: int, probe
         if g_rem is not None:
             g_rem.replay()
         end.record()
-        c = CLOCK.sample() if CLOCK is not None else None
         torch.cuda.synchronize()
         samples.append(start.elapsed_time(end) / 1e3 / steps)
-        if c is not None:
-            clocks.append(c)
     med = float(np.median(samples))
     return dict(median_s=med, min_s=float(min(samples)), max_s=float(max(samples)), samples_s=samples,
-                clock_mhz=float(np.median(clocks)) if clocks else None, launches_per_graph=L,
+                launches_per_graph=L,
                 graph_replays_per_rep=q + (1 if r else 0), reps=reps, steps=steps)
 
 
@@ -233,8 +198,7 @@ def timing_fields(t: dict) -> dict:
     return {"us_median": round(t["median_s"] * 1e6, 3), "us_min": round(t["min_s"] * 1e6, 3),
             "us_max": round(t["max_s"] * 1e6, 3), "spread": round(t["max_s"] / t["min_s"], 4),
             "samples_us": [round(v * 1e6, 3) for v in t["samples_s"]], "reps": t["reps"],
-            "steps_per_rep": t["steps"], "launches_per_graph": t["launches_per_graph"],
-            "shader_clock_mhz": None if t["clock_mhz"] is None else round(t["clock_mhz"], 1)}
+            "steps_per_rep": t["steps"], "launches_per_graph": t["launches_per_graph"]}
 
 
 def hbm_roofline(nbytes: int, t: dict, traffic=None) -> dict:
@@ -365,13 +329,26 @@ def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int, reps: int, pr
                 q, s_, g, x, y, n, k = item(li, pi)
                 fp4.w4a16_gemv("nvfp4", 1, n, k, q, s_, g, x, y)
 
-    out = dict(bytes=total_bytes)
-    for name, fn in (("grouped", sweep_grouped), ("single", sweep_single)):
+    # the 252 products as a device list: launches of up to 32 matrices each, in layer order (the
+    # benchmark's products are independent, so they may share a launch; a decoder's layers could not)
+    flat = [(li, pi) for li in range(36) for pi in range(7)]
+    lists = [flat[i:i + 32] for i in range(0, len(flat), 32)]
+
+    def sweep_list(_):
+        for lst in lists:
+            fp4.w4a16_gemv_batched("nvfp4", 1, [item(li, pi) for (li, pi) in lst])
+
+    out = dict(bytes=total_bytes, list_launches=len(lists))
+    for name, fn in (("grouped", sweep_grouped), ("single", sweep_single), ("device_list", sweep_list)):
         out[name] = time_steps(torch, fn, 1, steps, warmup, reps, probes, filler=1)
-    # outputs of the grouped sweep for the oracle check (layer 0)
-    sweep_grouped(0)
-    torch.cuda.synchronize()
-    out["layer0_y"] = [ys[0][pi].cpu().numpy() for pi in range(7)]
+    # outputs of each launch pattern for the oracle check (layer 0)
+    for name, fn in (("grouped", sweep_grouped), ("device_list", sweep_list)):
+        for li in range(36):
+            for y_ in ys[li]:
+                y_.fill_(float("nan"))
+        fn(0)
+        torch.cuda.synchronize()
+        out[f"layer0_y_{name}"] = [ys[0][pi].cpu().numpy() for pi in range(7)]
     out["layer0_x"] = [x_host[0][which_x[pi]] for pi in range(7)]
     del mats
     torch.cuda.empty_cache()
@@ -498,8 +475,6 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "reps": 5}}), flush=True)
         return
 
-    global CLOCK
-    CLOCK = ClockSampler()
     probes = Probes(torch)
     reps = max(1, args.reps)
 
@@ -514,7 +489,7 @@ def main():
         gemv_rows[args.workload] = r
         log(f"gemv {args.workload}: {r['t']['median_s'] * 1e6:.3f} us/launch median "
             f"[{r['t']['min_s'] * 1e6:.3f}, {r['t']['max_s'] * 1e6:.3f}], "
-            f"{r['bytes'] / r['t']['median_s'] / 1e9:.1f} GB/s, clock {r['t']['clock_mhz']} MHz "
+            f"{r['bytes'] / r['t']['median_s'] / 1e9:.1f} GB/s "
             f"({r['copies']} cold copies, {time.time() - t0:.1f}s)")
     if "nvfp4_2048" in only:
         r = bench_gemv(fp4, torch, synth, "nvfp4_2048x2048_m1", args.steps, args.warmup, reps, probes)
@@ -544,7 +519,7 @@ def main():
             t0 = time.time()
             gemm[fmt] = bench_gemm(fp4, torch, synth, fmt, 2048, args.gemm_steps, args.gemm_warmup, reps, probes)
             log(f"gemm {fmt} M=2048: {gemm[fmt]['t']['median_s'] * 1e6:.1f} us/launch median, "
-                f"{gemm[fmt]['tflops']:.1f} TFLOP/s, clock {gemm[fmt]['t']['clock_mhz']} MHz "
+                f"{gemm[fmt]['tflops']:.1f} TFLOP/s "
                 f"({time.time() - t0:.1f}s)")
     gemm_small = {}
     if "gemm_small" in only:
@@ -565,7 +540,8 @@ def main():
         t0 = time.time()
         sw = bench_decode_sweep(fp4, torch, synth, args.sweep_steps, args.sweep_warmup, reps, probes)
         log(f"decode sweep: grouped {sw['grouped']['median_s'] * 1e6:.1f} us, single "
-            f"{sw['single']['median_s'] * 1e6:.1f} us, read probe {sw['read_probe']['median_s'] * 1e6:.1f} us "
+            f"{sw['single']['median_s'] * 1e6:.1f} us, device list {sw['device_list']['median_s'] * 1e6:.1f} us, "
+            f"read probe {sw['read_probe']['median_s'] * 1e6:.1f} us "
             f"({time.time() - t0:.1f}s)")
 
     # ------------------------------------------------------------------ oracle: CPU baseline + parity gate
@@ -589,15 +565,18 @@ def main():
             del w_pref
         if sw is not None:
             layer = synth.DECODE_4B_LAYER
-            res = []
-            for pi, (_, n, k) in enumerate(layer):
-                w = synth.device_weights(n, k, cfg=2, mat=pi).cpu().numpy()
-                res.append(oracle_sample("nvfp4", w, sample_rows(n, 256), sw["layer0_x"][pi], sw["layer0_y"][pi],
-                                         threads, budget / 7))
-            cpu["decode_sweep_layer0"] = dict(
-                parity=all(x["parity"] for x in res), worst_error_ratio=max(x["worst_error_ratio"] for x in res),
-                rows=sum(x["rows"] for x in res), ms=round(sum(x["ms"] for x in res), 3),
-                gbs=sum(algorithmic_bytes("nvfp4", x["rows"], x["K"]) for x in res) / (sum(x["ms"] for x in res) / 1e3) / 1e9)
+            for mode in ("grouped", "device_list"):
+                res = []
+                for pi, (_, n, k) in enumerate(layer):
+                    w = synth.device_weights(n, k, cfg=2, mat=pi).cpu().numpy()
+                    res.append(oracle_sample("nvfp4", w, sample_rows(n, 256), sw["layer0_x"][pi],
+                                             sw[f"layer0_y_{mode}"][pi], threads, budget / 7,
+                                             time_it=(mode == "grouped")))
+                cpu[f"decode_sweep_layer0_{mode}"] = dict(
+                    parity=all(x["parity"] for x in res), worst_error_ratio=max(x["worst_error_ratio"] for x in res),
+                    rows=sum(x["rows"] for x in res), ms=round(sum(x["ms"] for x in res), 3),
+                    gbs=sum(algorithmic_bytes("nvfp4", x["rows"], x["K"]) for x in res)
+                    / (sum(x["ms"] for x in res) / 1e3) / 1e9)
         log(f"oracle samples: {len(cpu)} ({time.time() - t0:.1f}s), parity "
             f"{'ok' if all(c['parity'] for c in cpu.values()) else 'FAILED: ' + str([k for k, c in cpu.items() if not c['parity']])}")
 
@@ -689,9 +668,16 @@ def main():
         gbs = sw["bytes"] / g["median_s"] / 1e9
         line["decode_sweep"] = {
             "workload": "nvfp4_4b_decode_sweep_m1 (36 layers x q,k,v,o,gate,up,down)",
-            "GB/s": gated(round(gbs, 2), "decode_sweep_layer0"), "bytes_per_sweep": sw["bytes"],
+            "GB/s": gated(round(gbs, 2), "decode_sweep_layer0_grouped"), "bytes_per_sweep": sw["bytes"],
             "launches_per_sweep": 144, "roofline": hbm_roofline(sw["bytes"], g), "timing": timing_fields(g),
-            "parity": parity_of("decode_sweep_layer0"),
+            "parity": parity_of("decode_sweep_layer0_grouped"),
+            "device_list": {
+                "what": "the 252 products in launches of up to 32 matrices each (independent products; a decoder's "
+                        "layers depend on each other and could not share launches)",
+                "GB/s": gated(round(sw["bytes"] / sw["device_list"]["median_s"] / 1e9, 2),
+                              "decode_sweep_layer0_device_list"),
+                "launches_per_sweep": sw["list_launches"], "roofline": hbm_roofline(sw["bytes"], sw["device_list"]),
+                "timing": timing_fields(sw["device_list"]), "parity": parity_of("decode_sweep_layer0_device_list")},
             "one_launch_per_matrix": {"GB/s": round(sw["bytes"] / sw["single"]["median_s"] / 1e9, 2),
                                       "launches_per_sweep": 252, "timing": timing_fields(sw["single"])},
             "read_probe_144_launches": {"GB/s": round(sw["bytes"] / sw["read_probe"]["median_s"] / 1e9, 2),
