@@ -66,7 +66,7 @@ for _f in SPEC_FMTS + ("q4_0",):
         for _m in SPEC_MS:
             WORKLOADS[f"{_f}_{_shape}_m{_m}"] = (3, _mat, _f, _m)
 
-SECTIONS = ("headline", "nvfp4_2048", "spec", "gemm", "gemm_small", "sweep", "read_probe")
+SECTIONS = ("headline", "nvfp4_2048", "spec", "gemm", "gemm_small", "sweep", "read_probe", "packers")
 
 
 def algorithmic_bytes(fmt: str, n: int, k: int) -> int:
@@ -376,6 +376,34 @@ def bench_decode_sweep(fp4, torch, synth, steps: int, warmup: int, reps: int, pr
     return out
 
 
+def bench_packers(fp4, torch, synth, reps: int):
+    """Throughput of the device packers on the 4096 x 4096 Dual workload's fp32 weights (load time, not the
+    product): each packer call timed over a few launches, in weights per second and fp32 input GB/s."""
+    n, k = synth.WORKLOADS[1]["shapes"][0]
+    w = torch.from_numpy(synth.workload_weights(1, 0)).cuda()
+    out = {}
+    for fmt in ("rocmfp4_dual", "rocmfp4_fast", "nvfp4", "q4_0"):
+        if fmt == "nvfp4":
+            wq = torch.empty(n * k // 2, dtype=torch.uint8, device="cuda")
+            ws = torch.empty(n * k // 16, dtype=torch.uint8, device="cuda")
+            gb = torch.empty(1, dtype=torch.float32, device="cuda")
+
+            def launch(_):
+                fp4.fp4_quantize_nvfp4(n, k, w, wq, ws, gb)
+        else:
+            blocks = torch.empty(n * (k // 32) * BLOCK_BYTES[fmt], dtype=torch.uint8, device="cuda")
+            if fmt == "q4_0":
+                def launch(_):
+                    fp4.fp4_quantize_q4_0(n, k, w, blocks)
+            else:
+                def launch(_, fmt=fmt):
+                    fp4.fp4_quantize_rocmfp4(fmt, n, k, w, None, blocks)
+        t = time_steps(torch, launch, 5, 5, 2, reps, None, filler=1)
+        out[fmt] = {"ms": round(t["median_s"] * 1e3, 4), "Gweights/s": round(n * k / t["median_s"] / 1e9, 2),
+                    "fp32_input_GB/s": round(4 * n * k / t["median_s"] / 1e9, 1), "timing": timing_fields(t)}
+    return out
+
+
 # ----------------------------------------------------------------------------------------------
 # CPU baseline and the parity gate (the only part of this file that uses the oracle)
 
@@ -544,6 +572,13 @@ def main():
             f"read probe {sw['read_probe']['median_s'] * 1e6:.1f} us "
             f"({time.time() - t0:.1f}s)")
 
+    packers = None
+    if "packers" in only:
+        t0 = time.time()
+        packers = bench_packers(fp4, torch, synth, reps)
+        log(f"packers 4096x4096: " + ", ".join(f"{f} {v['ms']} ms" for f, v in packers.items())
+            + f" ({time.time() - t0:.1f}s)")
+
     # ------------------------------------------------------------------ oracle: CPU baseline + parity gate
     cpu = {}
     threads = host_threads()
@@ -686,6 +721,9 @@ def main():
                                       "timing": timing_fields(sw["read_probe_one_launch"])},
         }
         line["decode_sweep"]["roofline"]["vs_read_probe"] = round(sw["read_probe"]["median_s"] / g["median_s"], 4)
+    if packers:
+        line["packers"] = {"workload": "device packers on the 4096 x 4096 fp32 weights (load time; ROCmFP4 with the "
+                                       "pruned exhaustive-equivalent scale search)", "results": packers}
     print(json.dumps(line), flush=True)
 
 

@@ -4,11 +4,12 @@
 // card, description): global amax -> g = fl32(amax / 2688); per 16-weight block an E4M3 scale,
 // rounded to nearest-even from blockmax / (6 g) in FP64; per weight the nearest E2M1 magnitude.
 //
-// ROCmFP4, exhaustive finite-UE4M3 MSE search (ROCmFP4 design page, section 03): one wave per
-// 32-weight block; for each scale group (two 16-weight halves for Dual, the whole block for
-// FAST) the 64 lanes score the 127 candidate codes, two each, in FP64 with the terms summed in
-// index order, then a wave reduction keeps the smallest error, breaking ties by distance to the
-// start code (E4M3 RNE of max|w| / 10) and then by the lower code.
+// ROCmFP4, finite-UE4M3 MSE search (ROCmFP4 design page, section 03): for each scale group (two
+// 16-weight halves for Dual, the whole block for FAST) the winner among the 127 candidate codes is the
+// smallest error E(c) (FP64, terms summed in index order), ties broken by distance to the start code
+// (E4M3 RNE of max|w| / 10) and then by the lower code. The default kernel runs one thread per block and
+// visits the candidates outward from the start with safe pruning (below); the exhaustive kernel (one wave
+// per block, the 64 lanes scoring two candidates each, then a wave reduction) is kept for comparison.
 //
 // Q4_0, signed abs-max (ROCmFP4 design page, comparison table, stock Q4_0 reference scale): one thread
 // per 32-weight block; m = the first weight of largest magnitude, d = m / -8 (exact), stored as FP16
@@ -166,7 +167,142 @@ __device__ int search_group(const float* wv, const float* iv, int lane) {
   return bc;
 }
 
-// one wave (64 threads) per 32-weight block
+// Safe pruning (ROCmFP4 design page, section 03: pruning may only skip work that cannot change the selected
+// scale). Two lower bounds of E(c), each a sum of some of E(c)'s own terms, computed with E's operations in
+// E's order (so each is <= the computed E(c)), and each only growing as the scale moves away from the start:
+//  * smaller scales: every weight with |w| > 10 s takes level 10, term v (|w| - 10 s)^2 -- more such weights,
+//    each with a larger term, as s falls;
+//  * larger scales: every weight with |w| <= s / 2 takes level 0, term v w^2 -- more such weights as s grows.
+// Candidates are visited outward from the start code (distance d = 1, 2, ...; the lower code first). A
+// candidate visited later can only replace the best one with a strictly smaller error (it is not nearer to
+// the start, and at equal distance not lower), so once a direction's bound reaches the best error no code in
+// that direction can win and the direction is dropped. The winner is the exhaustive search's. Pruning is off
+// (every candidate scored) for groups with a non-finite weight or an importance that is negative or NaN.
+template <int G>
+__device__ __forceinline__ double bound_down(const float* wv, const float* iv, double s) {
+  double e = 0.0;
+  for (int i = 0; i < G; ++i) {
+    const double a = fabs((double)wv[i]);
+    if (a > 10.0 * s) {
+      const double dlt = a - 10.0 * s;
+      double t = dlt * dlt;
+      if (iv) t = (double)iv[i] * t;
+      e = e + t;
+    }
+  }
+  return e;
+}
+
+template <int G>
+__device__ __forceinline__ double bound_up(const float* wv, const float* iv, double s) {
+  double e = 0.0;
+  for (int i = 0; i < G; ++i) {
+    const double a = fabs((double)wv[i]);
+    if (a <= 0.5 * s) {
+      const double dlt = a - 0.0 * s;
+      double t = dlt * dlt;
+      if (iv) t = (double)iv[i] * t;
+      e = e + t;
+    }
+  }
+  return e;
+}
+
+template <int G>
+__device__ int search_group_pruned(const float* wv, const float* iv) {
+  double amax = 0.0;
+  bool prune = true;
+  for (int i = 0; i < G; ++i) {
+    amax = fmax(amax, fabs((double)wv[i]));
+    if (!(fabs((double)wv[i]) <= 1.0e308)) prune = false;
+    if (iv && !(iv[i] >= 0.f)) prune = false;
+  }
+  const int start = e4m3_rne(fmin(amax / 10.0, 448.0));
+  int bc = start;
+  double be = group_error<G>(wv, iv, e4m3_value(start));
+  bool down = true, up = true;
+  for (int d = 1; d <= 126 && (down || up); ++d) {
+    if (down) {
+      const int c = start - d;
+      if (c < 0) {
+        down = false;
+      } else {
+        const double sc = e4m3_value(c);
+        if (prune && bound_down<G>(wv, iv, sc) >= be) {
+          down = false;
+        } else {
+          const double e = group_error<G>(wv, iv, sc);
+          if (better(e, c, be, bc, start)) { be = e; bc = c; }
+        }
+      }
+    }
+    if (up) {
+      const int c = start + d;
+      if (c > 126) {
+        up = false;
+      } else {
+        const double sc = e4m3_value(c);
+        if (prune && bound_up<G>(wv, iv, sc) >= be) {
+          up = false;
+        } else {
+          const double e = group_error<G>(wv, iv, sc);
+          if (better(e, c, be, bc, start)) { be = e; bc = c; }
+        }
+      }
+    }
+  }
+  return bc;
+}
+
+// the block's packed bytes from its scale codes
+template <int F>
+__device__ __forceinline__ void rocm_write_block(uint8_t* ob, const float* wv, const int (&sc)[2], int j) {
+  constexpr int NS = (F == DUAL) ? 2 : 1;
+  const double s_lo = e4m3_value(sc[0]), s_hi = e4m3_value(sc[1]);
+  const int c_lo = cb10_nearest(fabs((double)wv[j]), s_lo);
+  const int c_hi = cb10_nearest(fabs((double)wv[j + 16]), s_hi);
+  const int n_lo = c_lo | ((wv[j] < 0.f && c_lo) ? 8 : 0);
+  const int n_hi = c_hi | ((wv[j + 16] < 0.f && c_hi) ? 8 : 0);
+  ob[NS + j] = (uint8_t)(n_lo | (n_hi << 4));
+}
+
+// one thread per 32-weight block, pruned search
+template <int F>
+__global__ __launch_bounds__(256) void rocm_pack_pruned_kernel(const float* __restrict__ w, const float* __restrict__ imp,
+                                                               int64_t nblocks, uint8_t* __restrict__ out) {
+  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= nblocks) return;
+  float wv[32], iv[32];
+  const f32x4* src = reinterpret_cast<const f32x4*>(w + blk * 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 t = src[i];
+    wv[4 * i] = t[0]; wv[4 * i + 1] = t[1]; wv[4 * i + 2] = t[2]; wv[4 * i + 3] = t[3];
+  }
+  if (imp) {
+    const f32x4* isrc = reinterpret_cast<const f32x4*>(imp + blk * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 t = isrc[i];
+      iv[4 * i] = t[0]; iv[4 * i + 1] = t[1]; iv[4 * i + 2] = t[2]; iv[4 * i + 3] = t[3];
+    }
+  }
+  constexpr int BB = (F == DUAL) ? 18 : 17;
+  int sc[2];
+  if constexpr (F == DUAL) {
+    sc[0] = search_group_pruned<16>(wv, imp ? iv : nullptr);
+    sc[1] = search_group_pruned<16>(wv + 16, imp ? iv + 16 : nullptr);
+  } else {
+    sc[0] = search_group_pruned<32>(wv, imp ? iv : nullptr);
+    sc[1] = sc[0];
+  }
+  uint8_t* ob = out + blk * BB;
+  ob[0] = (uint8_t)sc[0];
+  if (F == DUAL) ob[1] = (uint8_t)sc[1];
+  for (int j = 0; j < 16; ++j) rocm_write_block<F>(ob, wv, sc, j);
+}
+
+// one wave (64 threads) per 32-weight block, every candidate scored (two per lane)
 template <int F>
 __global__ __launch_bounds__(256) void rocm_pack_kernel(const float* __restrict__ w, const float* __restrict__ imp,
                                                         int64_t nblocks, uint8_t* __restrict__ out) {
@@ -198,14 +334,7 @@ __global__ __launch_bounds__(256) void rocm_pack_kernel(const float* __restrict_
     sc[1] = sc[0];
   }
   uint8_t* ob = out + blk * BB;
-  if (lane < 16) {
-    const double s_lo = e4m3_value(sc[0]), s_hi = e4m3_value(sc[1]);
-    const int c_lo = cb10_nearest(fabs((double)wv[lane]), s_lo);
-    const int c_hi = cb10_nearest(fabs((double)wv[lane + 16]), s_hi);
-    const int n_lo = c_lo | ((wv[lane] < 0.f && c_lo) ? 8 : 0);
-    const int n_hi = c_hi | ((wv[lane + 16] < 0.f && c_hi) ? 8 : 0);
-    ob[NS + lane] = (uint8_t)(n_lo | (n_hi << 4));
-  }
+  if (lane < 16) rocm_write_block<F>(ob, wv, sc, lane);
   if (lane == 0) {
     ob[0] = (uint8_t)sc[0];
     if (NS == 2) ob[1] = (uint8_t)sc[1];
@@ -276,11 +405,14 @@ extern "C" int fp4_quantize_rocmfp4(int fmt, int64_t N, int64_t K, const float* 
   const int64_t nblocks = N * K / 32;
   const int64_t grid = (nblocks * 64 + 255) / 256;
   if (grid > 0x7fffffffLL) return -4;
-  if (fmt == DUAL)
-    return fp4_launch(rocm_pack_kernel<DUAL>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
-                      (uint8_t*)blocks);
-  return fp4_launch(rocm_pack_kernel<FAST>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks,
-                    (uint8_t*)blocks);
+  uint8_t* ob = (uint8_t*)blocks;
+  if (fp4_tuning().quant_exhaustive == 1) {  // tuning override: every candidate of every group scored
+    if (fmt == DUAL) return fp4_launch(rocm_pack_kernel<DUAL>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks, ob);
+    return fp4_launch(rocm_pack_kernel<FAST>, dim3((unsigned)grid), dim3(256), 0, st, w, importance, nblocks, ob);
+  }
+  const dim3 pg((unsigned)((nblocks + 255) / 256));
+  if (fmt == DUAL) return fp4_launch(rocm_pack_pruned_kernel<DUAL>, pg, dim3(256), 0, st, w, importance, nblocks, ob);
+  return fp4_launch(rocm_pack_pruned_kernel<FAST>, pg, dim3(256), 0, st, w, importance, nblocks, ob);
 }
 
 extern "C" int fp4_quantize_q4_0(int64_t N, int64_t K, const float* w, void* blocks, void* stream) {

@@ -31,7 +31,8 @@
  *    count, occupancy of each kernel variant, whether a kernel's dynamic-LDS limit has been
  *    raised), filled on first use and never changed afterwards; the tuning overrides read
  *    once from the environment at the first call (FP4_GEMV_WAVES, FP4_GEMV_U, FP4_GEMV_ONE,
- *    FP4_GEMV_RING, FP4_MIDM_WAVES, FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS, FP4_GEMM_LDS; none
+ *    FP4_GEMV_RING, FP4_MIDM_WAVES, FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS, FP4_GEMM_LDS,
+ *    FP4_QUANT_EXHAUSTIVE; none
  *    set by default); and one 4-byte device word per GPU, a static device variable, that
  *    fp4_pack_layout uses when asked to validate (serialised by a per-device host lock).
  *    Apart from that word, which only the validation path touches, concurrent calls on
@@ -226,6 +227,11 @@ int fp4_quantize_nvfp4(int64_t N, int64_t K, const float* w, void* wq, void* ws,
  * nearest Codebook10 level (ties to the even level, clipping at 10); the smallest E wins,
  * ties broken by distance from the start code (E4M3 RNE of max|w|/10) then by the lower
  * code. importance (v) may be NULL (all ones). Output: canonical blocks uint8[N][K/32][B].
+ * The candidates are visited outward from the start code with safe pruning (same section: work that cannot
+ * change the selected scale may be skipped): a direction is dropped once a lower bound of E made of E's own
+ * terms (weights that must clip to level 10 below the scale, or round to 0 above it) reaches the best error,
+ * so the result is the exhaustive winner. Groups with a non-finite weight or a negative or NaN importance
+ * score every candidate.
  */
 int fp4_quantize_rocmfp4(int fmt, int64_t N, int64_t K, const float* w, const float* importance,
                          void* blocks, void* stream);

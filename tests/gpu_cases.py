@@ -50,3 +50,28 @@ def check_product(fmt, packed, x_bits, y_gpu, cols=None, label=""):
     ok, worst = ref.check(y, y_ref, b)
     assert ok, f"{label}: worst error / allowance = {worst}"
     return worst
+
+
+def save_case(folder, name, entry, fmt, m, n, k, pw, x_bits):
+    """Write one product's inputs for tests/variant_child.py."""
+    import os
+    np.savez(os.path.join(str(folder), name + ".npz"), entry=entry, fmt=fmt, m=m, n=n, k=k, q=pw.q.cpu().numpy(),
+             s=pw.s.cpu().numpy(), g=np.float32(pw.global_scale), x=x_bits)
+
+
+def run_variant(folder, env_overrides: dict) -> dict:
+    """Run the saved cases in a child process with the given tuning overrides; returns {name: y}."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, **env_overrides)
+    r = subprocess.run([sys.executable, os.path.join(root, "tests", "variant_child.py"), str(folder)], env=env,
+                       capture_output=True, text=True, timeout=600)
+    print(r.stdout[-3000:], r.stderr[-3000:], flush=True)
+    assert r.returncode == 0, f"variant child failed with status {r.returncode}"
+    out = {}
+    for f in os.listdir(str(folder)):
+        if f.endswith(".y.npy"):
+            out[f[:-6]] = np.load(os.path.join(str(folder), f))
+    return out

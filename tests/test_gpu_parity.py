@@ -106,21 +106,24 @@ def test_gemv_long_k_batches(fmt, m):
     gc.check_product(fmt, packed, x_bits, y, label=f"gemv-long-k {fmt} M={m}")
 
 
-@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
-def test_gemv_ring_forced(fmt, monkeypatch):
-    # The long-K ring kernel (M = 1), switched on for small grids: a ragged last tile, a partial last
-    # 128-wide chunk, chunk counts that are not a multiple of 16 waves x 3 slots, waves with no chunk at
-    # all (10 chunks for 16 waves), and the largest K it takes (256 chunks, 64 KiB of staged x).
-    monkeypatch.setenv("FP4_GEMV_RING", "1")
-    for n, k in [(200, 8288), (37, 1184), (16, 32768)]:
-        _announce("gemv-ring", fmt, n, k)
-        w, packed = gc.make_case(fmt, n, k, cfg=59, mat=n)
-        pw = gc.upload(fmt, n, k, packed)
-        x_bits = synth.activations(1, k, cfg=59, mat=k)
-        y = torch.full((1, n), float("nan"), device="cuda")
-        fp4.w4a16_gemv(fmt, 1, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
-        torch.cuda.synchronize()
-        gc.check_product(fmt, packed, x_bits, y, label=f"gemv-ring {fmt} {n}x{k}")
+def test_gemv_ring_forced(tmp_path):
+    # The long-K ring kernel (M = 1), switched on for small grids (FP4_GEMV_RING=1, in a child process: the
+    # library reads its tuning overrides once per process): a ragged last tile, a partial last 128-wide chunk,
+    # chunk counts that are not a multiple of 16 waves x 3 slots, waves with no chunk at all (10 chunks for
+    # 16 waves), and the largest K it takes (256 chunks, 64 KiB of staged x).
+    cases = {}
+    for fmt in gc.FMTS_ALL:
+        for n, k in [(200, 8288), (37, 1184), (16, 32768)]:
+            _announce("gemv-ring", fmt, n, k)
+            w, packed = gc.make_case(fmt, n, k, cfg=59, mat=n)
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(1, k, cfg=59, mat=k)
+            name = f"{fmt}_{n}_{k}"
+            gc.save_case(tmp_path, name, "gemv", fmt, 1, n, k, pw, x_bits)
+            cases[name] = (fmt, packed, x_bits)
+    ys = gc.run_variant(tmp_path, {"FP4_GEMV_RING": "1"})
+    for name, (fmt, packed, x_bits) in cases.items():
+        gc.check_product(fmt, packed, x_bits, torch.from_numpy(ys[name]), label=f"gemv-ring {name}")
 
 
 def test_gemv_ring_full_grid():
@@ -406,80 +409,83 @@ def test_gemm_multi_tile(fmt, k):
     gc.check_product(fmt, packed, x_bits, y, label=f"gemm-multi {fmt} M={m} {n}x{k}")
 
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
-def test_gemm_short_tiles(fmt, monkeypatch):
+def test_gemm_short_tiles(tmp_path):
     # 7 x 37 tiles of 256 x 256 are between one and two rounds on a 256-CU GPU, so rows 0-1535 of every
     # column tile run as 192-row tiles (the rest as 256-row tiles); K = 672 is ragged. Sampled columns over
     # all rows against the oracle, and the whole output against the launch with 256-row tiles only
-    # (the same products in the same order: bitwise equal).
+    # (FP4_GEMM_SHORT=0 in a child process; the same products in the same order: bitwise equal).
     m, n, k = 1792, 37 * 256, 672
-    _announce("gemm-short", fmt, m, n, k)
-    w, packed = gc.make_case(fmt, n, k, cfg=61, mat=k)
-    del w
-    pw = gc.upload(fmt, n, k, packed)
-    x_bits = synth.activations(m, k, cfg=61, mat=1)
-    x = gc.x_tensor(x_bits)
-    y = torch.full((m, n), float("nan"), device="cuda")
-    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
-    torch.cuda.synchronize()
-    assert not torch.isnan(y).any()
-    rng = np.random.default_rng(61)
-    cols = np.unique(np.concatenate([[0, 255, 256, 8191, 8192, n - 1], rng.choice(n, 40, replace=False)]))
-    gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"gemm-short {fmt}")
-    monkeypatch.setenv("FP4_GEMM_SHORT", "0")
-    y_plain = torch.full((m, n), float("nan"), device="cuda")
-    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_plain)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y_plain)
-
-
-@pytest.mark.parametrize("fmt", gc.FMTS)
-@pytest.mark.parametrize("m,n,k", [(100, 600, 1152), (256, 512, 2048), (257, 37, 4000)])
-def test_gemm_split_k(fmt, m, n, k, monkeypatch):
-    # Grids of at most half the CUs split K in two parts that add into the zeroed y: against the oracle,
-    # repeatable to the bit (two addends onto zero give the same sum in either order), and within the
-    # tolerance of the whole-K launch (FP4_GEMM_SPLIT=0).
-    _announce("gemm-split", fmt, m, n, k)
-    w, packed = gc.make_case(fmt, n, k, cfg=69, mat=k)
-    pw = gc.upload(fmt, n, k, packed)
-    x_bits = synth.activations(m, k, cfg=69, mat=m)
-    x = gc.x_tensor(x_bits)
-    ys = []
-    for _ in range(3):
+    want = {}
+    for fmt in gc.FMTS:
+        _announce("gemm-short", fmt, m, n, k)
+        w, packed = gc.make_case(fmt, n, k, cfg=61, mat=k)
+        del w
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=61, mat=1)
         y = torch.full((m, n), float("nan"), device="cuda")
-        fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
-        ys.append(y)
-    torch.cuda.synchronize()
-    gc.check_product(fmt, packed, x_bits, ys[0], label=f"gemm-split {fmt} M={m} {n}x{k}")
-    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
-    monkeypatch.setenv("FP4_GEMM_SPLIT", "0")
-    y_whole = torch.full((m, n), float("nan"), device="cuda")
-    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_whole)
-    torch.cuda.synchronize()
-    gc.check_product(fmt, packed, x_bits, y_whole, label=f"gemm-whole {fmt} M={m} {n}x{k}")
+        fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any()
+        rng = np.random.default_rng(61)
+        cols = np.unique(np.concatenate([[0, 255, 256, 8191, 8192, n - 1], rng.choice(n, 40, replace=False)]))
+        gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"gemm-short {fmt}")
+        gc.save_case(tmp_path, fmt, "gemm", fmt, m, n, k, pw, x_bits)
+        want[fmt] = y.cpu().numpy()
+    ys = gc.run_variant(tmp_path, {"FP4_GEMM_SHORT": "0"})
+    for fmt, y in want.items():
+        assert np.array_equal(y.view(np.uint32), ys[fmt].view(np.uint32)), fmt
 
 
-@pytest.mark.parametrize("fmt", gc.FMTS)
-@pytest.mark.parametrize("m", [65, 128, 129, 192])
-def test_gemm_band_row_tiles(fmt, m, monkeypatch):
+def test_gemm_split_k(tmp_path):
+    # Grids of at most a quarter of the CUs split K in two parts that add into the zeroed y: against the
+    # oracle, repeatable to the bit (two addends onto zero give the same sum in either order), and the
+    # whole-K launch (FP4_GEMM_SPLIT=0, in a child process) within the tolerance too.
+    cases = {}
+    for fmt in gc.FMTS:
+        for (m, n, k) in [(100, 600, 1152), (256, 512, 2048), (257, 37, 4000)]:
+            _announce("gemm-split", fmt, m, n, k)
+            w, packed = gc.make_case(fmt, n, k, cfg=69, mat=k)
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(m, k, cfg=69, mat=m)
+            x = gc.x_tensor(x_bits)
+            ys = []
+            for _ in range(3):
+                y = torch.full((m, n), float("nan"), device="cuda")
+                fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+                ys.append(y)
+            torch.cuda.synchronize()
+            gc.check_product(fmt, packed, x_bits, ys[0], label=f"gemm-split {fmt} M={m} {n}x{k}")
+            assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+            name = f"{fmt}_{m}_{n}_{k}"
+            gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
+            cases[name] = (fmt, packed, x_bits)
+    whole = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0"})
+    for name, (fmt, packed, x_bits) in cases.items():
+        gc.check_product(fmt, packed, x_bits, torch.from_numpy(whole[name]), label=f"gemm-whole {name}")
+
+
+def test_gemm_band_row_tiles(tmp_path):
     # M <= 128 runs 128-row tiles and M <= 192 192-row tiles: the same products in the same order as the
-    # 256-row tiling whose padding rows they skip, so the outputs are bitwise equal (K = 1152 also takes the
-    # two-way split).
+    # 256-row tiling whose padding rows they skip (FP4_GEMM_BAND_ROWS=0, in a child process), so the outputs
+    # are bitwise equal (K = 1152 also takes the two-way split).
     n, k = 600, 1152
-    _announce("gemm-band-rows", fmt, m, n, k)
-    w, packed = gc.make_case(fmt, n, k, cfg=70, mat=m)
-    pw = gc.upload(fmt, n, k, packed)
-    x_bits = synth.activations(m, k, cfg=70, mat=m)
-    x = gc.x_tensor(x_bits)
-    y = torch.full((m, n), float("nan"), device="cuda")
-    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
-    torch.cuda.synchronize()
-    gc.check_product(fmt, packed, x_bits, y, label=f"gemm-band-rows {fmt} M={m}")
-    monkeypatch.setenv("FP4_GEMM_BAND_ROWS", "0")
-    y256 = torch.full((m, n), float("nan"), device="cuda")
-    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y256)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y256)
+    want = {}
+    for fmt in gc.FMTS:
+        for m in (65, 128, 129, 192):
+            _announce("gemm-band-rows", fmt, m, n, k)
+            w, packed = gc.make_case(fmt, n, k, cfg=70, mat=m)
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(m, k, cfg=70, mat=m)
+            y = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+            torch.cuda.synchronize()
+            gc.check_product(fmt, packed, x_bits, y, label=f"gemm-band-rows {fmt} M={m}")
+            name = f"{fmt}_{m}"
+            gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
+            want[name] = y.cpu().numpy()
+    ys = gc.run_variant(tmp_path, {"FP4_GEMM_BAND_ROWS": "0"})
+    for name, y in want.items():
+        assert np.array_equal(y.view(np.uint32), ys[name].view(np.uint32)), name
 
 
 def test_gemm_split_in_graph():
