@@ -618,287 +618,6 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
       }
 }
 
-// ---------------------------------------------------------------------------------------------------
-// Shared-decode GEMM (K a multiple of 128). A workgroup of 8 waves computes a 256 x 256 tile of y. In each
-// stage of 64 positions every wave decodes one eighth of the tile's weights (32 weight rows) once into
-// exact bf16 level * scale and writes them to an LDS tile that all 8 waves read as MFMA B operands; x
-// arrives by direct-to-LDS loads in the same swizzled segment order as in gemm_kernel, and the weight tile
-// uses that order too. Wave w owns rows 128 (w / 4) .. + 127 and weight rows 64 (w % 4) .. + 63 of the tile
-// (4 x 2 MFMA blocks of 32 x 32: 128 accumulators), so two waves share each SIMD and one wave's decode
-// and LDS traffic run while the other's MFMAs keep the matrix core busy.
-//
-// LDS holds 3 x slots and 2 W slots of 32 KiB (256 rows x 64 positions of bf16 each), 160 KiB in all.
-// Stage s reads x slot s % 3 and W slot s % 2. During stage s each wave
-//  * decodes stage s + 1's weights (its packed bytes, loaded into registers two stages earlier) into W
-//    slot (s + 1) % 2, which stage s - 1 read;
-//  * issues the direct loads of stage s + 2's x into x slot (s + 2) % 3, which stage s - 1 read;
-//  * issues the loads of stage s + 3's packed weights into register set s % 3 (its stage s weights were
-//    decoded during stage s - 1).
-// A barrier ends each stage: after it, stage s + 1's x and W are complete in LDS and stage s's slots free.
-// Loads for stages past the last read zeros (out-of-range buffer offsets) into slots nobody reads.
-constexpr int GL_WAVES = 8, GL_THREADS = 64 * GL_WAVES;
-constexpr int GL_SLOT = 256 * GM_ROW_BYTES;            // 32 KiB
-constexpr int GL_XS = 3, GL_WS = 2;
-constexpr int GL_LDS = (GL_XS + GL_WS) * GL_SLOT;      // 160 KiB
-constexpr int GL_X_LOADS = 256 * 8 / GL_THREADS;       // 16-byte x slots per thread per stage: 4
-constexpr uint32_t GL_OOB = 0x80000000u;               // a buffer offset past every descriptor here
-
-// One stage of this lane's packed weights: dwords 2 jh and 2 jh + 1 of its weight row's lane pieces 2 hh (a)
-// and 2 hh + 1 (b) -- segments 4 jh .. 4 jh + 3 of the stage -- and the row's scale dword of the chunk.
-struct GLPacked {
-  u32x2 a, b;
-  uint32_t s;
-};
-
-// Per-lane offsets, fixed for the tile.
-struct GLLane {
-  uint32_t woff, soff;   // packed-weight and scale offsets of the lane's weight row (stage term added per stage)
-  uint32_t wlds;         // byte offset of the lane's weight row in a W slot
-  uint32_t wswz;         // its segment swizzle
-  uint32_t xoff[2];      // x direct loads: offsets of the lane's first two slots (later ones 8 rows apart)
-  uint32_t ops[4];       // operand reads of k-step S: row / weight row r = lane % 32, segment 4 (lane / 32) + S
-  int jh;
-};
-
-template <int F>
-__device__ __forceinline__ void gl_lane(GLLane& L, int K, int nchunk, int wave, int lane) {
-  // producer: weight row n of tile tt (of the wave's two), segment half jh
-  const int tt = lane >> 5, jh = (lane >> 4) & 1, n = lane & 15;
-  L.jh = jh;
-  L.woff = (uint32_t)(tt * nchunk) * UNIT_Q + n * 16 + 8 * jh;
-  L.soff = (uint32_t)(tt * nchunk) * unit_s(F) + n * (unit_s(F) / TILE_N) + (F == FAST ? 0 : 4 * jh);
-  L.wlds = (uint32_t)(32 * wave + 16 * tt + n) * GM_ROW_BYTES;
-  L.wswz = (uint32_t)x_swizzle(n);
-  // x: load i of the lane fills slot (4 wave + i) * 64 + lane: row 8 (4 wave + i) + lane / 8, physical
-  // segment lane % 8, logical segment (lane % 8) ^ swizzle(row)
-  const int row = 32 * wave + (lane >> 3);
-  const int sigma = (lane & 7) ^ x_swizzle(row);
-  L.xoff[0] = (uint32_t)(row * K + seg_k<F>(sigma)) * 2u;
-  L.xoff[1] = (uint32_t)(row * K + seg_k<F>(sigma ^ 1)) * 2u;
-  const int r = lane & 31, kh = lane >> 5;
-#pragma unroll
-  for (int S = 0; S < 4; ++S) L.ops[S] = (uint32_t)(r * GM_ROW_BYTES + 16 * ((4 * kh + S) ^ x_swizzle(r)));
-}
-
-template <int F>
-__device__ __forceinline__ void gl_load_w(GLPacked& p, const GemmSrc& src, const GLLane& L, int h, int H) {
-  const bool ok = h < H;
-  const int c = h >> 1, hh = h & 1;
-  const uint32_t qo = ok ? L.woff + (uint32_t)c * UNIT_Q + 512u * hh : GL_OOB;
-  const uint32_t so = ok ? L.soff + (uint32_t)c * unit_s(F) : GL_OOB;
-  p.a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(src.q, qo, 0, 0));
-  p.b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(src.q, ok ? qo + 256u : GL_OOB, 0, 0));
-  p.s = __builtin_amdgcn_raw_buffer_load_b32(src.s, so, 0, 0);
-}
-
-// x direct load I (0..3) of stage h into its slot.
-template <int F, int I>
-__device__ __forceinline__ void gl_load_x(const GemmSrc& src, const GLLane& L, uint8_t* slot, int h, int H, int K,
-                                          int wave) {
-  const bool ok = h < H;
-  const int c = h >> 1, hh = h & 1;
-  const int xs = ok ? 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8)) : 0;
-  const uint32_t off = ok ? L.xoff[I & 1] + (uint32_t)I * (uint32_t)K * 16u : GL_OOB;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(slot + (4 * wave + I) * 1024),
-                                           16, off, xs, 0, 0);
-}
-
-// Decode of segment jj (0..3) of this lane's weight row in four pieces: scale and nibble selection, pair
-// converts, then the two halves of "times scale, pack to bf16" (exact), the second followed by the LDS write.
-template <int F, int JJ, int PIECE>
-__device__ __forceinline__ void gl_decode(BDec& d, u32x4& out, const GLPacked& p, const GLLane& L, uint8_t* wslot) {
-  if constexpr (PIECE == 0) {
-    if constexpr (F == FAST) {
-      d.sc = __builtin_amdgcn_cvt_f32_fp8(p.s >> (16 * L.jh), JJ >> 1);
-      const uint32_t w = (JJ & 1) ? p.b[JJ >> 1] : p.a[JJ >> 1];
-      d.q0 = cb10_quad<false>(w);
-      d.q1 = cb10_quad<true>(w);
-    } else if constexpr (F == DUAL) {
-      d.sc = __builtin_amdgcn_cvt_f32_fp8(p.s, JJ);
-      d.q0 = cb10_quad<(JJ & 1) != 0>(p.a[JJ >> 1]);
-      d.q1 = cb10_quad<(JJ & 1) != 0>(p.b[JJ >> 1]);
-    } else {
-      d.sc = __builtin_amdgcn_cvt_f32_fp8(p.s, JJ);
-      d.q0 = __builtin_amdgcn_perm(p.b[JJ >> 1], p.a[JJ >> 1], (JJ & 1) ? 0x07060302u : 0x05040100u);
-    }
-  } else if constexpr (PIECE == 1) {
-    if constexpr (F == NVFP4) {
-      d.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 0);
-      d.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 1);
-      d.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 2);
-      d.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d.q0, 1.0f, 3);
-    } else {
-      d.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q0, 1.0f, false);
-      d.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q0, 1.0f, true);
-      d.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q1, 1.0f, false);
-      d.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.q1, 1.0f, true);
-    }
-  } else if constexpr (PIECE == 2) {
-    out[0] = pack_bf16x2(d.p[0][0] * d.sc, d.p[0][1] * d.sc);
-    out[1] = pack_bf16x2(d.p[1][0] * d.sc, d.p[1][1] * d.sc);
-  } else {
-    out[2] = pack_bf16x2(d.p[2][0] * d.sc, d.p[2][1] * d.sc);
-    out[3] = pack_bf16x2(d.p[3][0] * d.sc, d.p[3][1] * d.sc);
-    const uint32_t seg = (uint32_t)(4 * L.jh + JJ) ^ L.wswz;
-    *reinterpret_cast<u32x4*>(wslot + L.wlds + 16 * seg) = out;
-  }
-}
-
-struct GLOps {
-  bf16x8 a[4];
-  bf16x8 b[2];
-};
-
-template <int S>
-__device__ __forceinline__ void gl_read(GLOps& o, int q, const uint8_t* xslot, const uint8_t* wslot, const GLLane& L,
-                                        int mh, int nq) {
-  if (q < 4) o.a[q] = *reinterpret_cast<const bf16x8*>(xslot + (128 * mh + 32 * q) * GM_ROW_BYTES + L.ops[S]);
-  else o.b[q - 4] = *reinterpret_cast<const bf16x8*>(wslot + (64 * nq + 32 * (q - 4)) * GM_ROW_BYTES + L.ops[S]);
-}
-
-// One stage (see above). SL = s % 6 fixes the slots at compile time.
-template <int F, int SL>
-__device__ __forceinline__ void gl_stage(f32x16 (&acc)[4][2], GLPacked (&pk)[3], const GemmSrc& src, const GLLane& L,
-                                         uint8_t* lds, int s, int H, int K, int wave, int mh, int nq) {
-  constexpr int XS = SL % 3, WS = SL % 2, WN = (SL + 1) % 2, XL = (SL + 2) % 3, PD = (SL + 1) % 3, PL = SL % 3;
-  const uint8_t* xslot = lds + XS * GL_SLOT;
-  const uint8_t* wslot = lds + (GL_XS + WS) * GL_SLOT;
-  uint8_t* wnext = lds + (GL_XS + WN) * GL_SLOT;
-  uint8_t* xload = lds + XL * GL_SLOT;
-  GLOps cur, nx;
-#pragma unroll
-  for (int q = 0; q < 6; ++q) gl_read<0>(cur, q, xslot, wslot, L, mh, nq);
-  // this stage's decode needs stage s + 1's packed weights: 7 younger loads (stage s + 1's x, stage s + 2's
-  // weights) may still be in flight
-  wait_vmcnt<GL_X_LOADS + 3>();
-  BDec d;
-  u32x4 out;
-#define FP4_GL_KSTEP(S)                                                                                        \
-  {                                                                                                            \
-    _Pragma("unroll") for (int mm = 0; mm < 8; ++mm) {                                                         \
-      acc[mm >> 1][mm & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[mm >> 1], cur.b[mm & 1],            \
-                                                                     acc[mm >> 1][mm & 1], 0, 0, 0);          \
-      if (S < 3 && mm < 6) gl_read<(S + 1) & 3>(nx, mm, xslot, wslot, L, mh, nq);                              \
-      if (mm == 0) gl_decode<F, S, 0>(d, out, pk[PD], L, wnext);                                              \
-      if (mm == 2) gl_decode<F, S, 1>(d, out, pk[PD], L, wnext);                                              \
-      if (mm == 4) gl_decode<F, S, 2>(d, out, pk[PD], L, wnext);                                              \
-      if (mm == 6) gl_decode<F, S, 3>(d, out, pk[PD], L, wnext);                                              \
-      if (S == 0 && (mm & 1)) {                                                                                \
-        if (mm == 1) gl_load_x<F, 0>(src, L, xload, s + 2, H, K, wave);                                       \
-        if (mm == 3) gl_load_x<F, 1>(src, L, xload, s + 2, H, K, wave);                                       \
-        if (mm == 5) gl_load_x<F, 2>(src, L, xload, s + 2, H, K, wave);                                       \
-        if (mm == 7) gl_load_x<F, 3>(src, L, xload, s + 2, H, K, wave);                                       \
-      }                                                                                                        \
-      if (S == 1 && mm == 1) gl_load_w<F>(pk[PL], src, L, s + 3, H);                                          \
-      __builtin_amdgcn_sched_barrier(0);                                                                       \
-    }                                                                                                          \
-    if (S < 3) cur = nx;                                                                                       \
-  }
-  FP4_GL_KSTEP(0) FP4_GL_KSTEP(1) FP4_GL_KSTEP(2) FP4_GL_KSTEP(3)
-#undef FP4_GL_KSTEP
-  // stage s + 1's x (issued during stage s - 1) is in LDS once at most 10 younger loads remain (stage s + 2's
-  // weights, then this stage's x and weights); then every wave's W and x writes are done at the barrier
-  wait_vmcnt<3 + GL_X_LOADS + 3>();
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  workgroup_barrier();
-}
-
-template <int F>
-__global__ __launch_bounds__(GL_THREADS) void gemm_lds_kernel(const uint8_t* __restrict__ qp,
-                                                              const uint8_t* __restrict__ sp,
-                                                              const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                              int M, int N, int K, int nchunk, int tiles_m,
-                                                              float gscale) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int b = (int)blockIdx.x;
-  const int m0 = (b % tiles_m) * GM_BM, n0 = (b / tiles_m) * GM_BN;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int mh = wave >> 2, nq = wave & 3;
-  const int ntiles = (N + TILE_N - 1) / TILE_N;
-  const int H = 2 * nchunk;
-
-  GemmSrc src;
-  const int mrows = min(M - m0, GM_BM);
-  src.x = make_rsrc(x + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
-  const int wt0 = n0 / TILE_N + 2 * wave;                 // the wave's two weight tiles (decode)
-  const int tiles_here = max(0, min(ntiles - wt0, 2));
-  src.q = make_rsrc(qp + (int64_t)wt0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
-  src.s = make_rsrc(sp + (int64_t)wt0 * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
-  GLLane L;
-  gl_lane<F>(L, K, nchunk, wave, lane);
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  // prologue, in the order the steady state has in flight: weights 0, x 0, weights 1, x 1, weights 2
-  GLPacked pk[3];
-  gl_load_w<F>(pk[0], src, L, 0, H);
-  gl_load_x<F, 0>(src, L, lds, 0, H, K, wave);
-  gl_load_x<F, 1>(src, L, lds, 0, H, K, wave);
-  gl_load_x<F, 2>(src, L, lds, 0, H, K, wave);
-  gl_load_x<F, 3>(src, L, lds, 0, H, K, wave);
-  gl_load_w<F>(pk[1], src, L, 1, H);
-  gl_load_x<F, 0>(src, L, lds + GL_SLOT, 1, H, K, wave);
-  gl_load_x<F, 1>(src, L, lds + GL_SLOT, 1, H, K, wave);
-  gl_load_x<F, 2>(src, L, lds + GL_SLOT, 1, H, K, wave);
-  gl_load_x<F, 3>(src, L, lds + GL_SLOT, 1, H, K, wave);
-  gl_load_w<F>(pk[2], src, L, 2, H);
-  wait_vmcnt<2 * GL_X_LOADS + 6>();        // stage 0's weights
-  {
-    BDec d;
-    u32x4 out;
-    uint8_t* w0 = lds + GL_XS * GL_SLOT;
-    gl_decode<F, 0, 0>(d, out, pk[0], L, w0); gl_decode<F, 0, 1>(d, out, pk[0], L, w0);
-    gl_decode<F, 0, 2>(d, out, pk[0], L, w0); gl_decode<F, 0, 3>(d, out, pk[0], L, w0);
-    gl_decode<F, 1, 0>(d, out, pk[0], L, w0); gl_decode<F, 1, 1>(d, out, pk[0], L, w0);
-    gl_decode<F, 1, 2>(d, out, pk[0], L, w0); gl_decode<F, 1, 3>(d, out, pk[0], L, w0);
-    gl_decode<F, 2, 0>(d, out, pk[0], L, w0); gl_decode<F, 2, 1>(d, out, pk[0], L, w0);
-    gl_decode<F, 2, 2>(d, out, pk[0], L, w0); gl_decode<F, 2, 3>(d, out, pk[0], L, w0);
-    gl_decode<F, 3, 0>(d, out, pk[0], L, w0); gl_decode<F, 3, 1>(d, out, pk[0], L, w0);
-    gl_decode<F, 3, 2>(d, out, pk[0], L, w0); gl_decode<F, 3, 3>(d, out, pk[0], L, w0);
-  }
-  wait_vmcnt<GL_X_LOADS + 6>();            // stage 0's x
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  workgroup_barrier();
-
-  int s = 0;
-  for (; s + 6 <= H; s += 6) {
-    gl_stage<F, 0>(acc, pk, src, L, lds, s, H, K, wave, mh, nq);
-    gl_stage<F, 1>(acc, pk, src, L, lds, s + 1, H, K, wave, mh, nq);
-    gl_stage<F, 2>(acc, pk, src, L, lds, s + 2, H, K, wave, mh, nq);
-    gl_stage<F, 3>(acc, pk, src, L, lds, s + 3, H, K, wave, mh, nq);
-    gl_stage<F, 4>(acc, pk, src, L, lds, s + 4, H, K, wave, mh, nq);
-    gl_stage<F, 5>(acc, pk, src, L, lds, s + 5, H, K, wave, mh, nq);
-  }
-  // H is even: 0, 2 or 4 stages remain
-  if (s + 2 <= H) {
-    gl_stage<F, 0>(acc, pk, src, L, lds, s, H, K, wave, mh, nq);
-    gl_stage<F, 1>(acc, pk, src, L, lds, s + 1, H, K, wave, mh, nq);
-    s += 2;
-    if (s + 2 <= H) {
-      gl_stage<F, 2>(acc, pk, src, L, lds, s, H, K, wave, mh, nq);
-      gl_stage<F, 3>(acc, pk, src, L, lds, s + 1, H, K, wave, mh, nq);
-    }
-  }
-  wait_vmcnt<0>();  // the loads for stages past the last (zeros into free slots) have landed
-
-  // epilogue: acc[i][j][e] = C[128 mh + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][64 nq + 32 j + lane % 32]
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + 128 * mh + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int col = n0 + 64 * nq + 32 * j + (lane & 31);
-        if (row < M && col < N) __builtin_nontemporal_store(acc[i][j][e] * gscale, y + (int64_t)row * N + col);
-      }
-}
-
 // Tiles. The first nbig workgroups take 256-row tiles, the rest (if any) 192-row tiles; the host picks the
 // split so that a grid of between one and two rounds of 256-row tiles becomes two rounds whose second is
 // made of the shorter tiles (the slowest CU then does 1.75 tiles of work, not 2).
@@ -1005,14 +724,6 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   // one band: tiles only as high as M needs, 128 or 192 rows
   int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
   if (tu.gemm_band_rows == 0) band_rows = 0;  // tuning override: 256-row tiles
-  // the shared-decode kernel (whole K, 256 x 256 tiles, K a multiple of 128)
-  const bool lds_kernel = !RAGGED && ksplit == 0 && band_rows == 0 && tu.gemm_lds == 1;
-  if (lds_kernel) {
-    static Fp4LdsLimit lds_limit;
-    lds_limit.ensure(reinterpret_cast<const void*>(&gemm_lds_kernel<F>), GL_LDS);
-    return fp4_launch(gemm_lds_kernel<F>, dim3((unsigned)U), dim3(GL_THREADS), GL_LDS, st, q, s, x, y, M, N, K, nchunk,
-                      tiles_m, g);
-  }
   if (ksplit == 0 && band_rows == 0) {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);

@@ -1,7 +1,5 @@
 """GPU: kernel variants that a tuning override selects, each in a child process (the library reads its
 overrides once per process), against the default kernels:
-  * the shared-decode GEMM kernel (each weight tile decoded once into a bf16 LDS tile that 8 waves read as
-    MFMA B operands), FP4_GEMM_LDS=1: the same products summed in the same order, so bitwise equal;
   * the exhaustive ROCmFP4 packer (every candidate scored), FP4_QUANT_EXHAUSTIVE=1, against the default
     pruned search: byte-equal blocks, on groups that exercise both pruned directions, ties, zero and
     negative importance (negative importance switches pruning off) and extreme magnitudes."""
@@ -17,35 +15,11 @@ pytestmark = pytest.mark.gpu
 
 fp4 = pytest.importorskip("block_scaled_fp4_w4a16_amd")
 
-# (M, N, K): one tile, a ragged grid, several bands with a ragged last band, ragged N
-CASES = [(256, 256, 128), (300, 700, 512), (1200, 4352, 2048), (2048, 2304, 1024)]
-
 
 @pytest.fixture(autouse=True, scope="module")
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def test_shared_decode_gemm_matches_default_kernel_bitwise(tmp_path):
-    want = {}
-    for fmt in gc.FMTS:
-        for (m, n, k) in CASES:
-            name = f"{fmt}_{m}_{n}_{k}"
-            print("CASE default", name, flush=True)
-            w, packed = gc.make_case(fmt, n, k, cfg=98, mat=m)
-            pw = gc.upload(fmt, n, k, packed)
-            xb = synth.activations(m, k, cfg=98, mat=m)
-            y = torch.empty(m, n, dtype=torch.float32, device="cuda")
-            fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(xb), y)
-            torch.cuda.synchronize()
-            cols = np.unique(np.linspace(0, n - 1, 24).astype(int))
-            gc.check_product(fmt, packed, xb, y, cols=cols, label=f"default {name}")
-            want[name] = y.cpu().numpy()
-            gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, xb)
-    ys = gc.run_variant(tmp_path, {"FP4_GEMM_LDS": "1"})
-    for name, y0 in want.items():
-        assert np.array_equal(y0.view(np.uint32), ys[name].view(np.uint32)), name
 
 
 def test_pruned_packer_matches_exhaustive_kernel(tmp_path):

@@ -1,5 +1,5 @@
 """Child process of the GPU tests that force a kernel variant. The library reads its tuning overrides
-(FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS, FP4_GEMM_LDS, FP4_GEMV_RING, ...) once per process, so
+(FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS, FP4_GEMV_RING, FP4_QUANT_EXHAUSTIVE, ...) once per process, so
 a forced variant needs a process of its own: this one runs the products the parent saved in `folder`
 (one .npz per case: entry, fmt, m, n, k, planes q and s, global scale g, x; or, for the ROCmFP4 packer,
 weights w and optionally importance imp) and saves each output as <case>.y.npy beside it."""
