@@ -35,7 +35,12 @@ constexpr int GM_LDS = GM_RING * GM_STAGE_BYTES;      // 126 KiB
 // A tile has 32 MI rows of x: MI = 8 (256 rows) or 6 (192 rows, the shorter tiles that even out the last
 // round of a grid). A thread then has MI 16-byte x slots per stage (each 8 rows below the previous).
 // Vector-memory instructions per thread per stage: x slots, 2 weight loads, scale loads (512 or 256 bytes).
-__host__ __device__ constexpr int gm_loads_per_stage(int f, int mi) { return mi + 2 + (f == FAST ? 1 : 2); }
+// NB = 32-column blocks of weight rows per wave: 2 (256-column tiles) or 1 (128-column tiles for small grids).
+// Scale-byte loads per stage: 4-byte loads of the 2 NB tiles' scale rows, 64 lanes each (at least one).
+__host__ __device__ constexpr int gm_scale_parts(int f, int nb) {
+  return 2 * nb * (unit_s(f) / 4) / 64 > 1 ? 2 * nb * (unit_s(f) / 4) / 64 : 1;
+}
+__host__ __device__ constexpr int gm_loads_per_stage(int f, int mi, int nb = 2) { return mi + nb + gm_scale_parts(f, nb); }
 constexpr int GM_SHORT_ROWS = 192;   // rows of an MI = 6 tile
 constexpr int GM_SHORT_BANDS = 8;    // MI = 6 tiles cover rows 0 .. 8 * 192 - 1 of their columns
 
@@ -88,12 +93,12 @@ __device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h
 
 // Weights of stage h: the two lane pieces 2 hh, 2 hh + 1 of a unit are 512 contiguous bytes, so the wave's four
 // tiles take 2 KiB (two 16-byte direct loads per lane), plus the scale bytes of the same four tiles.
-template <int F>
+template <int F, int NB = 2>
 __device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h, int nchunk, int wave, int lane) {
   const int c = h >> 1, hh = h & 1;
   uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
 #pragma unroll
-  for (int part = 0; part < 2; ++part) {
+  for (int part = 0; part < NB; ++part) {
     const int tt = 2 * part + (lane >> 5);
     const uint32_t off = (uint32_t)(tt * nchunk + c) * UNIT_Q + 512 * hh + (lane & 31) * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -102,7 +107,7 @@ __device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h
   }
   constexpr int us = unit_s(F);                   // 128 (16-weight groups) or 64 (FAST) bytes per unit
   constexpr int lanes_per_tile = us / 4;          // 4-byte loads
-  constexpr int parts = 4 * lanes_per_tile / 64;  // 2 or 1
+  constexpr int parts = gm_scale_parts(F, NB);    // 2 or 1
 #pragma unroll
   for (int part = 0; part < parts; ++part) {
     const int idx = part * 64 + lane;
@@ -142,7 +147,7 @@ __device__ __forceinline__ void load_offsets(LoadOffs& o, int K, int nchunk, int
 // Part P (0, 1, 2) of stage h's direct loads (K a multiple of 128): x slots 3P .. 3P + 2 (the last part
 // has two), then in part 1 the weight pieces and in part 2 the scale bytes. Spreading a stage's loads over
 // three k-steps keeps each burst of vector-memory issue short.
-template <int F, int MI, int P>
+template <int F, int MI, int P, int NB = 2>
 __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
                                                  int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
@@ -158,13 +163,13 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
   if constexpr (P == 1) {
     const int ws = c * UNIT_Q + 512 * hh;
 #pragma unroll
-    for (int part = 0; part < 2; ++part)
+    for (int part = 0; part < NB; ++part)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16,
           o.w + (uint32_t)(part * 2 * nchunk * UNIT_Q), ws, 0, 0);
   }
   if constexpr (P == 2) {
-    constexpr int us = unit_s(F), parts = 4 * (us / 4) / 64;
+    constexpr int us = unit_s(F), parts = gm_scale_parts(F, NB);
     const int ss = c * us;
 #pragma unroll
     for (int part = 0; part < parts; ++part)
@@ -177,7 +182,7 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
 // Load I (0 .. MI + 3) of stage h's direct loads (K a multiple of 128): x slots 0 .. MI - 1, the two weight
 // pieces, then the scale loads (two for 16-weight groups, one for FAST). Issued one or two at a time between
 // MFMAs so that no burst of vector-memory instructions holds up the wave.
-template <int F, int MI, int I>
+template <int F, int MI, int I, int NB = 2>
 __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOffs& o, uint8_t* stage, int h, int K,
                                                 int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
@@ -187,14 +192,14 @@ __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOf
     const int first = (wave * MI + I) * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (__attribute__((address_space(3))) void*)(stage + first * 16), 16,
                                              o.x[I & 1] + I * xrow8, xs, 0, 0);
-  } else if constexpr (I < MI + 2) {
+  } else if constexpr (I < MI + NB) {
     constexpr int part = I - MI;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16,
         o.w + (uint32_t)(part * 2 * nchunk * UNIT_Q), c * UNIT_Q + 512 * hh, 0, 0);
   } else {
-    constexpr int us = unit_s(F), parts = 4 * (us / 4) / 64;
-    constexpr int part = I - MI - 2;
+    constexpr int us = unit_s(F), parts = gm_scale_parts(F, NB);
+    constexpr int part = I - MI - NB;
     if constexpr (part < parts)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256),
@@ -203,23 +208,24 @@ __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOf
 }
 
 // All of stage h's loads: the three parts, or the per-slot path when K is ragged.
-template <int F, int MI, bool RAGGED>
+template <int F, int MI, bool RAGGED, int NB = 2>
 __device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
                                             int nchunk, int wave, int lane) {
   if constexpr (RAGGED) {
     issue_x<F, MI, RAGGED>(src, ring, h, K, wave, lane);
-    issue_w<F>(src, ring, h, nchunk, wave, lane);
+    issue_w<F, NB>(src, ring, h, nchunk, wave, lane);
   } else {
-    issue_stage_part<F, MI, 0>(src, o, ring, h, K, nchunk, wave);
-    issue_stage_part<F, MI, 1>(src, o, ring, h, K, nchunk, wave);
-    issue_stage_part<F, MI, 2>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 0, NB>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 1, NB>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 2, NB>(src, o, ring, h, K, nchunk, wave);
   }
 }
 
+template <int NB = 2>
 __device__ __forceinline__ void read_w(WRegs& r, const uint8_t* stage, int F_spr, int F_us, int wave, int lane) {
   const int kh = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NB; ++j) {
     const int rl = 32 * j + (lane & 31);
     const int t = rl >> 4, n = rl & 15;
     const uint8_t* wb = stage + GM_X_BYTES + wave * 2048 + t * 512 + n * 16 + 8 * kh;
@@ -357,11 +363,11 @@ struct KOps {
 
 // The next k-step's operands, prepared in eight slices (x fragment G when the tile has it, and quarter G % 4
 // of B operand G / 4).
-template <int F, int MI, int S, int G>
+template <int F, int MI, int S, int G, int NB = 2>
 __device__ __forceinline__ void prep_slice(KOps<MI>& nx, BDec (&d)[2], const WRegs& r, const uint8_t* ring,
                                            uint32_t xbase) {
   if constexpr (G < MI) nx.a[G] = a_frag(ring, xbase, G);
-  b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2);
+  if constexpr ((G >> 2) < NB) b_slice<F, S, G & 3>(d[G >> 2], nx.b[G >> 2], r, G >> 2);
 }
 
 // The B dequantization pieces (b_sub) that run after MFMA slot SLOT (0 .. 2 MI - 1) of a k-step. With 16
@@ -393,11 +399,14 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[MI][2], const KOps<MI>& k
   acc[G][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], __builtin_bit_cast(bf16x8, k.b[J]), acc[G][J], 0, 0, 0);
 }
 
-template <int MI, int G>
+template <int MI, int G, int NB = 2>
 __device__ __forceinline__ void mfma_group(f32x16 (&acc)[MI][2], const KOps<MI>& k) {
-  const bf16x8 b0 = __builtin_bit_cast(bf16x8, k.b[0]), b1 = __builtin_bit_cast(bf16x8, k.b[1]);
+  const bf16x8 b0 = __builtin_bit_cast(bf16x8, k.b[0]);
   acc[G][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], b0, acc[G][0], 0, 0, 0);
-  acc[G][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], b1, acc[G][1], 0, 0, 0);
+  if constexpr (NB == 2) {
+    const bf16x8 b1 = __builtin_bit_cast(bf16x8, k.b[1]);
+    acc[G][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.a[G], b1, acc[G][1], 0, 0, 0);
+  }
 }
 
 // Direct loads to issue during a k-step: part P of stage h (nothing when h is past the last stage).
@@ -412,23 +421,24 @@ struct StageLoads {
 // The loads of issue point Q (0 .. 3 MI / 2 - 1): load I goes out at point I * points / loads, so the
 // stage's loads spread evenly (one per point with MI = 8, where the points and the loads are both 12; the
 // first point takes two with MI = 6).
-template <int F, int MI, int Q, int I = 0>
+template <int F, int MI, int Q, int NB = 2, int I = 0>
 __device__ __forceinline__ void issue_point(const StageLoads& L) {
-  constexpr int NL = gm_loads_per_stage(F, MI), NP = 3 * MI / 2;
+  constexpr int NL = gm_loads_per_stage(F, MI, NB), NP = 3 * MI / 2;
   if constexpr (I < NL) {
-    if constexpr (I * NP / NL == Q) issue_stage_one<F, MI, I>(*L.src, *L.o, L.dst, L.h, L.K, L.nchunk, L.wave);
-    issue_point<F, MI, Q, I + 1>(L);
+    if constexpr (I * NP / NL == Q) issue_stage_one<F, MI, I, NB>(*L.src, *L.o, L.dst, L.h, L.K, L.nchunk, L.wave);
+    issue_point<F, MI, Q, NB, I + 1>(L);
   }
 }
 
 // Loads issued after MFMA group G of k-step S: with K ragged, all of the stage at once (k-step 0, group 1);
 // otherwise issue point S MI / 2 + G / 2 after each odd group of k-steps 0-2.
-template <int F, int MI, bool RAGGED, int S, int G>
+template <int F, int MI, bool RAGGED, int S, int G, int NB = 2>
 __device__ __forceinline__ void issue_part(const StageLoads& L) {
   if constexpr (RAGGED) {
-    if constexpr (S == 0 && G == 1) issue_stage<F, MI, true>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
+    if constexpr (S == 0 && G == 1)
+      issue_stage<F, MI, true, NB>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
   } else {
-    if constexpr (S < 3 && (G & 1)) issue_point<F, MI, S * (MI / 2) + (G >> 1)>(L);
+    if constexpr (S < 3 && (G & 1)) issue_point<F, MI, S * (MI / 2) + (G >> 1), NB>(L);
   }
 }
 
@@ -436,19 +446,24 @@ __device__ __forceinline__ void issue_part(const StageLoads& L) {
 // tiles), each MFMA followed by its share of the next k-step's operands (k-step S + 1 of this stage); after
 // odd groups of k-steps 0-2 the wave issues loads of two stages ahead. Scheduling fences keep that order,
 // so the LDS reads, VALU work and loads run while the matrix core is busy.
-template <int F, int MI, bool RAGGED, int S, bool LOAD>
+template <int F, int MI, bool RAGGED, int S, bool LOAD, int NB = 2>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur, KOps<MI>& nx, const WRegs& r,
                                       const uint8_t* ring, const uint32_t (&xc)[4], const StageLoads& L) {
   BDec d[2];
+  // NB = 2: two MFMAs per x fragment G, each followed by a B-operand piece; NB = 1: one MFMA and one slot
 #define FP4_GROUP(G)                                                      \
   if constexpr ((G) < MI) {                                               \
     mfma_one<MI, G, 0>(acc, cur);                                         \
     nx.a[G] = a_frag(ring, xc[S + 1], G);                                 \
-    b_slot<F, MI, S + 1, 2 * (G)>(d, nx.b, r);                        \
-    __builtin_amdgcn_sched_barrier(0);                                    \
-    mfma_one<MI, G, 1>(acc, cur);                                         \
-    b_slot<F, MI, S + 1, 2 * (G) + 1>(d, nx.b, r);                    \
-    if constexpr (LOAD) issue_part<F, MI, RAGGED, S, G>(L);               \
+    if constexpr (NB == 2) {                                              \
+      b_slot<F, MI, S + 1, 2 * (G)>(d, nx.b, r);                          \
+      __builtin_amdgcn_sched_barrier(0);                                  \
+      mfma_one<MI, G, 1>(acc, cur);                                       \
+      b_slot<F, MI, S + 1, 2 * (G) + 1>(d, nx.b, r);                      \
+    } else {                                                              \
+      b_slot<F, MI, S + 1, G>(d, nx.b, r);                                \
+    }                                                                     \
+    if constexpr (LOAD) issue_part<F, MI, RAGGED, S, G, NB>(L);           \
     __builtin_amdgcn_sched_barrier(0);                                    \
   }
   FP4_GROUP(0) FP4_GROUP(1) FP4_GROUP(2) FP4_GROUP(3) FP4_GROUP(4) FP4_GROUP(5) FP4_GROUP(6) FP4_GROUP(7)
@@ -457,23 +472,23 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[MI][2], const KOps<MI>& cur,
 
 // Operands of k-step 0 of a stage, all at once (the first stage only; later stages prepare them inside
 // the previous stage's last k-step).
-template <int F, int MI>
+template <int F, int MI, int NB = 2>
 __device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uint8_t* ring, uint32_t xb0) {
   BDec d[2];
-  prep_slice<F, MI, 0, 0>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 1>(k, d, r, ring, xb0);
-  prep_slice<F, MI, 0, 2>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 3>(k, d, r, ring, xb0);
-  prep_slice<F, MI, 0, 4>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 5>(k, d, r, ring, xb0);
-  prep_slice<F, MI, 0, 6>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 7>(k, d, r, ring, xb0);
+  prep_slice<F, MI, 0, 0, NB>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 1, NB>(k, d, r, ring, xb0);
+  prep_slice<F, MI, 0, 2, NB>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 3, NB>(k, d, r, ring, xb0);
+  prep_slice<F, MI, 0, 4, NB>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 5, NB>(k, d, r, ring, xb0);
+  prep_slice<F, MI, 0, 6, NB>(k, d, r, ring, xb0); prep_slice<F, MI, 0, 7, NB>(k, d, r, ring, xb0);
 }
 
 // Stage h of the K loop (see the kernel). LOAD: the stage issues stage h + 2's loads; MORE: there is a
 // stage h + 1, whose k-step 0 operands this stage prepares into ka. SLOT = h % 3 when known at compile
 // time (the ring offsets are then constants), else -1.
-template <int F, int MI, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1>
+template <int F, int MI, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1, int NB = 2>
 __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, KOps<MI>& kb, WRegs& r,
                                            const GemmSrc& src, const LoadOffs& lo, uint8_t* ring, const XBase& xb, int h, int K,
                                            int nchunk, int wave, int lane) {
-  constexpr int LPS = gm_loads_per_stage(F, MI);
+  constexpr int LPS = gm_loads_per_stage(F, MI, NB);
   const int s0 = SLOT >= 0 ? SLOT : h % GM_RING;
   const int s1 = SLOT >= 0 ? (SLOT + 1) % GM_RING : (s0 == GM_RING - 1 ? 0 : s0 + 1);
   const int s2 = SLOT >= 0 ? (SLOT + 2) % GM_RING : (s1 == GM_RING - 1 ? 0 : s1 + 1);
@@ -490,11 +505,11 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
       xn[S] = xb.v[0][S] + (uint32_t)(s1 * GM_STAGE_BYTES);
     }
   }
-  kstep<F, MI, RAGGED, 0, LOAD>(acc, ka, kb, r, ring, xc, L);
-  kstep<F, MI, RAGGED, 1, LOAD>(acc, kb, ka, r, ring, xc, L);
-  kstep<F, MI, RAGGED, 2, LOAD>(acc, ka, kb, r, ring, xc, L);
+  kstep<F, MI, RAGGED, 0, LOAD, NB>(acc, ka, kb, r, ring, xc, L);
+  kstep<F, MI, RAGGED, 1, LOAD, NB>(acc, kb, ka, r, ring, xc, L);
+  kstep<F, MI, RAGGED, 2, LOAD, NB>(acc, ka, kb, r, ring, xc, L);
   // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
-  mfma_group<MI, 0>(acc, kb);
+  mfma_group<MI, 0, NB>(acc, kb);
   __builtin_amdgcn_sched_barrier(0);
   const uint8_t* next = ring + s1 * GM_STAGE_BYTES;
   if constexpr (MORE) {
@@ -503,7 +518,7 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads of stage h are done
     workgroup_barrier();
-    read_w(r, next, scales_per_row_chunk(F), unit_s(F), wave, lane);
+    read_w<NB>(r, next, scales_per_row_chunk(F), unit_s(F), wave, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
   BDec d[2];
@@ -514,36 +529,38 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
     mfma_one<MI, G, 0>(acc, kb);                                                   \
     if constexpr (MORE) {                                                          \
       ka.a[(G) - 1] = a_frag(ring, xn[0], (G) - 1);                               \
-      b_slot<F, MI, 0, 2 * ((G) - 1)>(d, ka.b, r);                             \
+      b_slot<F, MI, 0, NB * ((G) - 1)>(d, ka.b, r);                                \
     }                                                                              \
     __builtin_amdgcn_sched_barrier(0);                                             \
-    mfma_one<MI, G, 1>(acc, kb);                                                   \
-    if constexpr (MORE) b_slot<F, MI, 0, 2 * ((G) - 1) + 1>(d, ka.b, r);       \
-    __builtin_amdgcn_sched_barrier(0);                                             \
+    if constexpr (NB == 2) {                                                       \
+      mfma_one<MI, G, 1>(acc, kb);                                                 \
+      if constexpr (MORE) b_slot<F, MI, 0, 2 * ((G) - 1) + 1>(d, ka.b, r);         \
+      __builtin_amdgcn_sched_barrier(0);                                           \
+    }                                                                              \
   }
   FP4_LAST(1) FP4_LAST(2) FP4_LAST(3) FP4_LAST(4) FP4_LAST(5) FP4_LAST(6) FP4_LAST(7)
 #undef FP4_LAST
   if constexpr (MORE) {
     ka.a[MI - 1] = a_frag(ring, xn[0], MI - 1);
-    b_slot<F, MI, 0, 2 * (MI - 1)>(d, ka.b, r);
-    b_slot<F, MI, 0, 2 * (MI - 1) + 1>(d, ka.b, r);
+    b_slot<F, MI, 0, NB * (MI - 1)>(d, ka.b, r);
+    if constexpr (NB == 2) b_slot<F, MI, 0, 2 * (MI - 1) + 1>(d, ka.b, r);
   }
 }
 
-// One tile of y: rows m0 .. m0 + 32 MI - 1, columns n0 .. n0 + 255 (see the kernel).
-template <int F, int MI, bool RAGGED>
+// One tile of y: rows m0 .. m0 + 32 MI - 1, columns n0 .. n0 + 128 NB - 1 (see the kernel).
+template <int F, int MI, bool RAGGED, int NB = 2>
 __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                           const uint16_t* __restrict__ x, float* __restrict__ y, int M, int N, int K,
                                           int nchunk, int m0, int n0, float gscale, int hb, int he, bool add_out) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave: keeps descriptors scalar
-  const int wrow0 = n0 + 64 * wave;            // this wave's 64 weight rows (4 tiles of 16)
+  const int wrow0 = n0 + 32 * NB * wave;       // this wave's 32 NB weight rows (2 NB tiles of 16)
   const int ntiles = (N + TILE_N - 1) / TILE_N;
 
   GemmSrc src;
   const int mrows = min(M - m0, 32 * MI);
   src.x = make_rsrc(x + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
-  const int tiles_here = max(0, min(ntiles - wrow0 / TILE_N, 4));
+  const int tiles_here = max(0, min(ntiles - wrow0 / TILE_N, 2 * NB));
   src.q = make_rsrc(qp + (int64_t)(wrow0 / TILE_N) * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
   src.s = make_rsrc(sp + (int64_t)(wrow0 / TILE_N) * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
   LoadOffs lo;
@@ -563,31 +580,33 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
   // h), reads stage h + 1's packed weights and prepares its k-step 0 -- still between MFMAs.
   // Stages hb .. he - 1 (all of K, or one part of a split K); hb is a multiple of the ring period, so
   // stage h sits in ring slot h % 3 as when hb = 0.
-  constexpr int LPS = gm_loads_per_stage(F, MI);
-  issue_stage<F, MI, RAGGED>(src, lo, ring, hb, K, nchunk, wave, lane);
-  if (hb + 1 < he) issue_stage<F, MI, RAGGED>(src, lo, ring, hb + 1, K, nchunk, wave, lane);
+  constexpr int LPS = gm_loads_per_stage(F, MI, NB);
+  issue_stage<F, MI, RAGGED, NB>(src, lo, ring, hb, K, nchunk, wave, lane);
+  if (hb + 1 < he) issue_stage<F, MI, RAGGED, NB>(src, lo, ring, hb + 1, K, nchunk, wave, lane);
   if (hb + 1 < he) wait_vmcnt<LPS>();
   else wait_vmcnt<0>();
   workgroup_barrier();
   WRegs r;
   KOps<MI> ka, kb;
-  read_w(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
+  read_w<NB>(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
   XBase xb;
   x_bases(xb, lane);
-  prep_all0<F, MI>(ka, r, ring, xb.v[0][0]);
+  prep_all0<F, MI, NB>(ka, r, ring, xb.v[0][0]);
 
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
   // body is compiled for each case, so the loop has no per-group branches.
   int h = hb;
   // three stages per iteration (the ring period), so that every ring offset is a constant
   for (; h + 4 < he; h += 3) {
-    stage_body<F, MI, RAGGED, true, true, 0>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
-    stage_body<F, MI, RAGGED, true, true, 1>(acc, ka, kb, r, src, lo, ring, xb, h + 1, K, nchunk, wave, lane);
-    stage_body<F, MI, RAGGED, true, true, 2>(acc, ka, kb, r, src, lo, ring, xb, h + 2, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 0, NB>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 1, NB>(acc, ka, kb, r, src, lo, ring, xb, h + 1, K, nchunk, wave, lane);
+    stage_body<F, MI, RAGGED, true, true, 2, NB>(acc, ka, kb, r, src, lo, ring, xb, h + 2, K, nchunk, wave, lane);
   }
-  for (; h + 2 < he; ++h) stage_body<F, MI, RAGGED, true, true>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
-  if (h + 1 < he) stage_body<F, MI, RAGGED, false, true>(acc, ka, kb, r, src, lo, ring, xb, h++, K, nchunk, wave, lane);
-  stage_body<F, MI, RAGGED, false, false>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
+  for (; h + 2 < he; ++h)
+    stage_body<F, MI, RAGGED, true, true, -1, NB>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
+  if (h + 1 < he)
+    stage_body<F, MI, RAGGED, false, true, -1, NB>(acc, ka, kb, r, src, lo, ring, xb, h++, K, nchunk, wave, lane);
+  stage_body<F, MI, RAGGED, false, false, -1, NB>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
 
   // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]; y is written
   // once and not read back here, so the stores are nontemporal (about 1% faster than plain ones). A
@@ -597,7 +616,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
@@ -609,7 +628,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
@@ -655,11 +674,12 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
   }
 }
 
-// Grids of at most a quarter of the CUs (a kernel of its own, so that the prefill kernel above keeps its
-// code): tiles of 32 MI rows (MI = 4 or 6 when M fits one such band, else 8), tile t taking band t %
-// tiles_m and column tile t / tiles_m. ksplit > 0: workgroup t < ntiles takes stages 0 .. ksplit - 1 of
-// tile t, workgroup ntiles + t the rest, and both add into the zeroed y.
-template <int F, bool RAGGED, int MI>
+// Small grids (a kernel of its own, so that the prefill kernel above keeps its code): tiles of 32 MI rows
+// (MI = 4 or 6 when M fits one such band, else 8) and 128 NB columns (NB = 1: each wave owns 32 weight
+// rows, so twice the tiles of the 256-column tiling), tile t taking band t % tiles_m and column tile
+// t / tiles_m. ksplit > 0: workgroup t < ntiles takes stages 0 .. ksplit - 1 of tile t, workgroup ntiles + t
+// the rest, and both add into the zeroed y.
+template <int F, bool RAGGED, int MI, int NB>
 __global__ __launch_bounds__(GM_THREADS) void gemm_small_kernel(const uint8_t* __restrict__ qp,
                                                                 const uint8_t* __restrict__ sp,
                                                                 const uint16_t* __restrict__ x,
@@ -675,8 +695,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_small_kernel(const uint8_t* _
     hb = second ? ksplit : 0;
     he = second ? he : ksplit;
   }
-  gemm_tile<F, MI, RAGGED>(ring, qp, sp, x, y, M, N, K, nchunk, (t % tiles_m) * 32 * MI, (t / tiles_m) * GM_BN, gscale,
-                           hb, he, ksplit > 0);
+  gemm_tile<F, MI, RAGGED, NB>(ring, qp, sp, x, y, M, N, K, nchunk, (t % tiles_m) * 32 * MI, (t / tiles_m) * 128 * NB,
+                               gscale, hb, he, ksplit > 0);
 }
 
 // y = 0 before the parts of a split K add into it (a kernel, not a memset, so that the call can be
@@ -685,13 +705,22 @@ __global__ void gemm_zero_kernel(float* __restrict__ y, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) y[i] = 0.f;
 }
 
-template <int F, bool RAGGED, int MI>
+template <int F, bool RAGGED, int MI, int NB>
 static int launch_gemm_small(hipStream_t st, int grid, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                              int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit) {
   static Fp4LdsLimit lds_limit;
-  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI>), GM_LDS);
-  return fp4_launch(gemm_small_kernel<F, RAGGED, MI>, dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K,
+  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI, NB>), GM_LDS);
+  return fp4_launch(gemm_small_kernel<F, RAGGED, MI, NB>, dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K,
                     nchunk, tiles_m, ntiles, g, ksplit);
+}
+
+template <int F, bool RAGGED, int NB>
+static int launch_gemm_small_mi(int band_rows, hipStream_t st, int grid, const uint8_t* q, const uint8_t* s,
+                                const uint16_t* x, float* y, int M, int N, int K, int nchunk, int tiles_m, int ntiles,
+                                float g, int ksplit) {
+  if (band_rows == 128) return launch_gemm_small<F, RAGGED, 4, NB>(st, grid, q, s, x, y, M, N, K, nchunk, 1, ntiles, g, ksplit);
+  if (band_rows) return launch_gemm_small<F, RAGGED, 6, NB>(st, grid, q, s, x, y, M, N, K, nchunk, 1, ntiles, g, ksplit);
+  return launch_gemm_small<F, RAGGED, 8, NB>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
 }
 
 template <int F, bool RAGGED>
@@ -713,18 +742,24 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   }
   if (tu.gemm_short == 0) ns = 0;  // tuning override: 256-row tiles only
   const int nbig = (int)(U - (int64_t)(GM_SHORT_BANDS * GM_SHORT_ROWS / GM_BM) * ns);
-  // Grids of at most a quarter of the CUs split K in two (at a multiple of the 3-stage ring period, each
-  // part at least 6 stages) so that twice the workgroups run; y is zeroed first and both parts add into
-  // it. On larger grids zeroing and adding y costs more than the extra workgroups gain (prefill N =
-  // 14336 at M = 512, 112 tiles: 91 us split against 79 us whole).
+  // Grids of 256-column tiles that fill at most half the CUs take 128-column tiles (twice the tiles, each
+  // wave owning 32 weight rows) where twice the grid still fits one round.
+  const bool narrow = ns == 0 && 2 * U <= cus && tu.gemm_narrow != 0;  // tuning override: 0 = 256 columns
+  const int NBsel = narrow ? 1 : 2;
+  const int64_t Ut = (int64_t)tiles_m * ((N + 128 * NBsel - 1) / (128 * NBsel));
+  // Grids of at most half the CUs (in tiles of the width chosen above) split K in two (at a multiple of
+  // the 3-stage ring period, each part at least 6 stages) so that twice the workgroups run; y is zeroed
+  // first and both parts add into it. On larger grids zeroing and adding y costs more than the extra
+  // workgroups gain (prefill N = 14336 at M = 512, 112 tiles of 256 columns: 91 us split against 79 us
+  // whole).
   int ksplit = 0;
   const int H = 2 * nchunk;
-  if (ns == 0 && 4 * U <= cus && H >= 12) ksplit = 3 * (H / 6);
+  if (ns == 0 && 2 * Ut <= cus && H >= 12) ksplit = 3 * (H / 6);
   if (tu.gemm_split == 0) ksplit = 0;  // tuning override: whole K per workgroup
   // one band: tiles only as high as M needs, 128 or 192 rows
   int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
   if (tu.gemm_band_rows == 0) band_rows = 0;  // tuning override: 256-row tiles
-  if (ksplit == 0 && band_rows == 0) {
+  if (ksplit == 0 && band_rows == 0 && !narrow) {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
     return fp4_launch(gemm_kernel<F, RAGGED>, dim3(nbig + GM_SHORT_BANDS * ns), dim3(GM_THREADS), GM_LDS, st, q, s, x,
@@ -736,10 +771,10 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
     const int rc = fp4_launch(gemm_zero_kernel, dim3(zb), dim3(256), 0, st, y, total);
     if (rc) return rc;
   }
-  const int grid = ksplit ? 2 * (int)U : (int)U;
-  if (band_rows == 128) return launch_gemm_small<F, RAGGED, 4>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
-  if (band_rows) return launch_gemm_small<F, RAGGED, 6>(st, grid, q, s, x, y, M, N, K, nchunk, 1, (int)U, g, ksplit);
-  return launch_gemm_small<F, RAGGED, 8>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)U, g, ksplit);
+  const int grid = ksplit ? 2 * (int)Ut : (int)Ut;
+  if (narrow)
+    return launch_gemm_small_mi<F, RAGGED, 1>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)Ut, g, ksplit);
+  return launch_gemm_small_mi<F, RAGGED, 2>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)Ut, g, ksplit);
 }
 
 template <int F>

@@ -50,6 +50,7 @@ struct Fp4Tuning {
   int gemm_short;      // FP4_GEMM_SHORT=0: 256-row tiles only
   int gemm_split;      // FP4_GEMM_SPLIT=0: whole K per workgroup
   int gemm_band_rows;  // FP4_GEMM_BAND_ROWS=0: 256-row tiles at M <= 192
+  int gemm_narrow;     // FP4_GEMM_NARROW=0: no 128-column tiles on small grids
   int quant_exhaustive;  // FP4_QUANT_EXHAUSTIVE=1: the ROCmFP4 packer scores every candidate (no pruning)
 };
 const Fp4Tuning& fp4_tuning();

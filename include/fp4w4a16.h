@@ -32,7 +32,7 @@
  *    raised), filled on first use and never changed afterwards; the tuning overrides read
  *    once from the environment at the first call (FP4_GEMV_WAVES, FP4_GEMV_U, FP4_GEMV_ONE,
  *    FP4_GEMV_RING, FP4_MIDM_WAVES, FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS,
- *    FP4_QUANT_EXHAUSTIVE; none
+ *    FP4_GEMM_NARROW, FP4_QUANT_EXHAUSTIVE; none
  *    set by default); and one 4-byte device word per GPU, a static device variable, that
  *    fp4_pack_layout uses when asked to validate (serialised by a per-device host lock).
  *    Apart from that word, which only the validation path touches, concurrent calls on

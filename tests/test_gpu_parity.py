@@ -488,6 +488,33 @@ def test_gemm_band_row_tiles(tmp_path):
         assert np.array_equal(y.view(np.uint32), ys[name].view(np.uint32)), name
 
 
+def test_gemm_narrow_tiles(tmp_path):
+    # Grids of 256-column tiles that fill at most half the CUs run 128-column tiles (each wave owns 32 weight
+    # rows). Against the oracle on sampled columns, and bitwise against the 256-column tiling (FP4_GEMM_NARROW=0
+    # in a child process): the same products in the same order, where both launches make the same K-split
+    # decision (no split at K = 640; both split at the other shapes, which have at most 64 tiles of 256
+    # columns). N = 1000 and 4350 leave a ragged last 128-column tile.
+    want = {}
+    for fmt in gc.FMTS:
+        for (m, n, k) in [(512, 4350, 2048), (300, 1000, 640), (700, 2304, 1024), (129, 1000, 1152)]:
+            _announce("gemm-narrow", fmt, m, n, k)
+            w, packed = gc.make_case(fmt, n, k, cfg=74, mat=m)
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(m, k, cfg=74, mat=m)
+            y = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+            torch.cuda.synchronize()
+            assert not torch.isnan(y).any()
+            cols = np.unique(np.concatenate([[0, 127, 128, n - 1], np.linspace(0, n - 1, 40).astype(int)]))
+            gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"gemm-narrow {fmt} M={m} {n}x{k}")
+            name = f"{fmt}_{m}_{n}_{k}"
+            gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
+            want[name] = y.cpu().numpy()
+    ys = gc.run_variant(tmp_path, {"FP4_GEMM_NARROW": "0"})
+    for name, y in want.items():
+        assert np.array_equal(y.view(np.uint32), ys[name].view(np.uint32)), name
+
+
 def test_gemm_split_in_graph():
     # The split-K GEMM enqueues a zero-fill kernel and the product: captured in a graph (on torch's capture
     # stream) and replayed several times, with eager work and synchronizations between the replays, every
