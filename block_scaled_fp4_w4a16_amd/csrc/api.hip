@@ -31,7 +31,8 @@ const Fp4Tuning& fp4_tuning() {
   static const Fp4Tuning t = {env_int("FP4_GEMV_WAVES"), env_int("FP4_GEMV_U"),      env_int("FP4_GEMV_ONE"),
                               env_int("FP4_GEMV_RING"),  env_int("FP4_MIDM_WAVES"),  env_int("FP4_GEMM_SHORT"),
                               env_int("FP4_GEMM_SPLIT"), env_int("FP4_GEMM_BAND_ROWS"),
-                              env_int("FP4_GEMM_NARROW"),  env_int("FP4_QUANT_EXHAUSTIVE")};
+                              env_int("FP4_GEMM_NARROW"),  env_int("FP4_QUANT_EXHAUSTIVE"),
+                              env_int("FP4_ONE_BATCH")};
   return t;
 }
 

@@ -310,7 +310,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
   // With few x rows (XPF) a batch's x is loaded ahead of its weights and held in registers until
   // they are issued, and the next batch's x is prefetched together with its weights. With many rows
   // that would cost too many registers: x is then loaded and committed at the top of each batch.
-  constexpr bool XPF = XStage<U, MX>::NX <= 2;
+  constexpr bool XPF = XStage<U, MX>::NX <= (ONE ? 6 : 2);
   XStage<U, XPF ? MX : 1> xst;
   if constexpr (XPF) {
     if (wave < nchunk) {
@@ -758,26 +758,60 @@ static int pick_waves(int nwg, int min_chunks, int M, int wmax) {
   return W;
 }
 
-// Fills in the workgroup ranges, picks the variant and wave count, and launches. Every item has N, K >= 1.
-template <int F, int MAXI>
-static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
-  // With more than 4 x rows a workgroup takes two tiles (they share the staged x) when there are enough
-  // tiles for one such workgroup per CU; otherwise one.
-  int total_tiles = 0;
-  for (int i = 0; i < b.count; ++i) total_tiles += (b.it[i].N + TILE_N - 1) / TILE_N;
-  const int T = (M > 4 && total_tiles >= 2 * 256) ? 2 : 1;
-  int nwg = 0, min_chunks = 1 << 30, max_chunks = 0;
+// One tile per workgroup: fills in the workgroup ranges; returns the workgroup count.
+template <int MAXI>
+static int fill_ranges(GemvBatch<MAXI>& b, int T, int& min_chunks, int& max_chunks) {
+  int nwg = 0;
+  min_chunks = 1 << 30;
+  max_chunks = 0;
   for (int i = 0; i < b.count; ++i) {
     GemvItem& it = b.it[i];
     it.nchunk = (it.K + CHUNK_K - 1) / CHUNK_K;
     it.wg0 = nwg;
     b.start[i] = nwg;
-    const int ntiles = (it.N + TILE_N - 1) / TILE_N;
-    nwg += (ntiles + T - 1) / T;
+    nwg += ((it.N + TILE_N - 1) / TILE_N + T - 1) / T;
     min_chunks = min_chunks < it.nchunk ? min_chunks : it.nchunk;
     max_chunks = max_chunks > it.nchunk ? max_chunks : it.nchunk;
   }
   for (int i = b.count; i < MAXI; ++i) b.start[i] = 0x7fffffff;
+  return nwg;
+}
+
+// 2 <= M <= 8: every chunk of a wave in one batch, as at M = 1 (x first, then all of the wave's weight
+// units, so a wave waits about one memory latency rather than one per batch). Wave count as at M = 1;
+// with more than 4 rows of x the grid must also fit the chip in one round (the staged x of U chunks per
+// wave then limits the workgroups per CU). Returns -1 where it does not apply (then nothing is launched).
+template <int F, int MAXI>
+static int try_one_batch(GemvBatch<MAXI>& b, int M, hipStream_t st) {
+  if (M < 2 || M > 8 || fp4_tuning().one_batch == 0) return -1;
+  int min_chunks, max_chunks;
+  const int nwg = fill_ranges(b, 1, min_chunks, max_chunks);
+  int W = pick_waves<GemvLaunch<F, 1, 4, 4, 4, MAXI, 4, true>>(nwg, min_chunks, 1, 16);
+  if (W == 16 && (max_chunks + 7) / 8 <= 4) W = 8;
+  const int U = (max_chunks + W - 1) / W;
+  if (M == 2) return U > 4 ? -1 : U <= 3 ? GemvLaunch<F, 1, 2, 3, 2, MAXI, 2, true>::launch(b, nwg, W, M, st)
+                                         : GemvLaunch<F, 1, 2, 4, 2, MAXI, 2, true>::launch(b, nwg, W, M, st);
+  if (M == 3) return U > 4 ? -1 : U <= 3 ? GemvLaunch<F, 1, 4, 3, 3, MAXI, 3, true>::launch(b, nwg, W, M, st)
+                                         : GemvLaunch<F, 1, 4, 4, 3, MAXI, 3, true>::launch(b, nwg, W, M, st);
+  if (M == 4) return U > 4 ? -1 : U <= 3 ? GemvLaunch<F, 1, 4, 3, 4, MAXI, 4, true>::launch(b, nwg, W, M, st)
+                                         : GemvLaunch<F, 1, 4, 4, 4, MAXI, 4, true>::launch(b, nwg, W, M, st);
+  using L8 = GemvLaunch<F, 1, 4, 3, 8, MAXI, 0, true>;
+  if (U > 3 || (int64_t)nwg > (int64_t)L8::resident(W, M) * fp4_device_cus()) return -1;
+  return L8::launch(b, nwg, W, M, st);
+}
+
+// Fills in the workgroup ranges, picks the variant and wave count, and launches. Every item has N, K >= 1.
+template <int F, int MAXI>
+static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
+  const int one = try_one_batch<F, MAXI>(b, M, st);
+  if (one != -1) return one;
+  // With more than 4 x rows a workgroup takes two tiles (they share the staged x) when there are enough
+  // tiles for one such workgroup per CU; otherwise one.
+  int total_tiles = 0;
+  for (int i = 0; i < b.count; ++i) total_tiles += (b.it[i].N + TILE_N - 1) / TILE_N;
+  const int T = (M > 4 && total_tiles >= 2 * 256) ? 2 : 1;
+  int min_chunks, max_chunks;
+  const int nwg = fill_ranges(b, T, min_chunks, max_chunks);
   // Batches of two chunk slots when the wave count that would be picked leaves at most two chunks per
   // wave (no load slots that read nothing), else four.
   const int wmax = (M > 4) ? 8 : 16;  // keep the staged x (W * U * M * 256 B) inside the LDS
@@ -807,7 +841,8 @@ static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     if (U == 3) return O3::launch(b, nwg, W, M, st);
     if (U == 4) return O4::launch(b, nwg, W, M, st);
     return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
-  } else if (M == 2) {
+  }
+  if (M == 2) {
     using L4 = GemvLaunch<F, 1, 2, 4, 2, MAXI, 2>;
     return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
   } else if (M == 3) {
@@ -912,9 +947,21 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   if (M == 0) return 0;
   rc = check_item(fmt, M, N, K, q, s, x_bf16, y);
   if (rc) return rc;
+  GemvBatch<1> b;
+  b.count = 1;
+  b.it[0] = GemvItem{(const uint8_t*)q, (const uint8_t*)s, (const uint16_t*)x_bf16, y, (int)N, (int)K, 0, 0,
+                     global_scale, 0};
   if (M >= 5 && fmt != Q4_0) {
-    // from 5 rows of x on, decoding each weight once into scaled bf16 operands (the mid-M kernel) is
-    // faster than folding the scales per group and per x row
+    // From 5 rows of x on: the one-batch GEMV where its grid fits the chip in one round, else the mid-M
+    // kernel (each weight decoded once into scaled bf16 operands, chunks in a chain per wave), which is
+    // faster than the GEMV's batch loop
+    int one = -1;
+    switch (fmt) {
+      case NVFP4: one = try_one_batch<NVFP4, 1>(b, (int)M, (hipStream_t)stream); break;
+      case DUAL:  one = try_one_batch<DUAL, 1>(b, (int)M, (hipStream_t)stream); break;
+      default:    one = try_one_batch<FAST, 1>(b, (int)M, (hipStream_t)stream); break;
+    }
+    if (one != -1) return one;
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* qq = (const uint8_t*)q;
     const uint8_t* ss = (const uint8_t*)s;
@@ -925,10 +972,6 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
       default:    return dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
     }
   }
-  GemvBatch<1> b;
-  b.count = 1;
-  b.it[0] = GemvItem{(const uint8_t*)q, (const uint8_t*)s, (const uint16_t*)x_bf16, y, (int)N, (int)K, 0, 0,
-                     global_scale, 0};
   return dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
 }
 

@@ -52,6 +52,7 @@ struct Fp4Tuning {
   int gemm_band_rows;  // FP4_GEMM_BAND_ROWS=0: 256-row tiles at M <= 192
   int gemm_narrow;     // FP4_GEMM_NARROW=0: no 128-column tiles on small grids
   int quant_exhaustive;  // FP4_QUANT_EXHAUSTIVE=1: the ROCmFP4 packer scores every candidate (no pruning)
+  int one_batch;       // FP4_ONE_BATCH=0: no one-batch GEMV for 2 <= M <= 8 (batch loop, or mid-M kernel from M = 5)
 };
 const Fp4Tuning& fp4_tuning();
 

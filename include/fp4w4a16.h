@@ -32,7 +32,7 @@
  *    raised), filled on first use and never changed afterwards; the tuning overrides read
  *    once from the environment at the first call (FP4_GEMV_WAVES, FP4_GEMV_U, FP4_GEMV_ONE,
  *    FP4_GEMV_RING, FP4_MIDM_WAVES, FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS,
- *    FP4_GEMM_NARROW, FP4_QUANT_EXHAUSTIVE; none
+ *    FP4_GEMM_NARROW, FP4_QUANT_EXHAUSTIVE, FP4_ONE_BATCH; none
  *    set by default); and one 4-byte device word per GPU, a static device variable, that
  *    fp4_pack_layout uses when asked to validate (serialised by a per-device host lock).
  *    Apart from that word, which only the validation path touches, concurrent calls on
@@ -133,8 +133,10 @@ int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q, const void
  * design page, sections 01 and 02). Streams each nibble and scale byte
  * once, decodes to exact bf16 levels, contracts against x on the matrix cores, applies
  * the group scales to the FP32 partial sums, reduces the K split inside the workgroup and
- * multiplies by g. From M = 5 on (NVFP4, Dual, FAST) it runs the w4a16_midm kernel instead,
- * which decodes each weight once into exact bf16 level*scale shared by all rows of x.
+ * multiplies by g. Up to M = 8 a wave issues all of its loads at once where that fits the chip
+ * in one round of workgroups. Otherwise, from M = 5 on (NVFP4, Dual, FAST), it runs the
+ * w4a16_midm kernel, which decodes each weight once into exact bf16 level*scale shared by
+ * all rows of x.
  * q/s are fp4_pack_layout output (device); x is M x K bf16 bit patterns and y M x N fp32,
  * both row-major on the device. Deterministic (no atomics). Errors: FP4_ERR_ARG,
  * FP4_ERR_SHAPE (M < 0, N or K), FP4_ERR_UNSUPPORTED (M > 16, K > 2^24), FP4_ERR_ALIGN,

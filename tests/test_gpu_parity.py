@@ -77,7 +77,7 @@ def test_dequant_all_codes_and_scales(fmt):
 # ------------------------------------------------------------------ GEMV (M <= 16)
 
 @pytest.mark.parametrize("fmt", gc.FMTS_ALL)
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16])
 def test_gemv_small_shapes(fmt, m):
     for (n, k) in [(48, 256), (37, 160), (256, 1536)]:
         _announce("gemv", fmt, m, n, k)
@@ -124,6 +124,26 @@ def test_gemv_ring_forced(tmp_path):
     ys = gc.run_variant(tmp_path, {"FP4_GEMV_RING": "1"})
     for name, (fmt, packed, x_bits) in cases.items():
         gc.check_product(fmt, packed, x_bits, torch.from_numpy(ys[name]), label=f"gemv-ring {name}")
+
+
+def test_gemv_one_batch_off(tmp_path):
+    # With FP4_ONE_BATCH=0 (child process) 2 <= M <= 8 takes the batch loop (M <= 4) or the mid-M kernel
+    # instead of the one-batch GEMV: the paths that the shape rules still pick where one batch does not
+    # fit, on the shapes of the default-path test above
+    cases = {}
+    for fmt in gc.FMTS_ALL:
+        for m in (2, 3, 4, 5, 8):
+            for (n, k) in [(37, 160), (256, 1536)]:
+                _announce("gemv-one-batch-off", fmt, m, n, k)
+                w, packed = gc.make_case(fmt, n, k, cfg=52, mat=n)
+                pw = gc.upload(fmt, n, k, packed)
+                x_bits = synth.activations(m, k, cfg=52, mat=k)
+                name = f"{fmt}_{m}_{n}_{k}"
+                gc.save_case(tmp_path, name, "gemv", fmt, m, n, k, pw, x_bits)
+                cases[name] = (fmt, packed, x_bits)
+    ys = gc.run_variant(tmp_path, {"FP4_ONE_BATCH": "0"})
+    for name, (fmt, packed, x_bits) in cases.items():
+        gc.check_product(fmt, packed, x_bits, torch.from_numpy(ys[name]), label=f"gemv-one-batch-off {name}")
 
 
 def test_gemv_ring_full_grid():

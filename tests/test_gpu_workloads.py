@@ -50,7 +50,7 @@ def test_decode_sweep_one_layer():
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "rocmfp4_dual", "rocmfp4_fast", "q4_0"])
-@pytest.mark.parametrize("m", [1, 9, 16, 33, 64])
+@pytest.mark.parametrize("m", [1, 4, 6, 9, 16, 33, 64])
 def test_spec_verify(fmt, m):
     if fmt == "q4_0" and m > 16:
         pytest.skip("Q4_0 runs through the GEMV only (M <= 16)")
@@ -64,3 +64,29 @@ def test_prefill_m2048(fmt):
     n = synth.WORKLOADS[4]["shapes"][0][0]
     cols = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, n - 1], rng.choice(n, 57, replace=False)]))
     _run(fmt, 4, 0, 2048, cols=cols)
+
+
+def test_decode_sweep_layer_grouped_launches():
+    # one 4B-class layer at full size through the launch patterns the sweep benchmark times: q|k|v as
+    # one grouped launch on one x, o alone, gate|up as one grouped launch on one x, down alone; then
+    # the same seven products as one device-list launch. Every output column against the oracle.
+    fmt, cfg = "nvfp4", 2
+    shapes = synth.WORKLOADS[cfg]["shapes"][:7]
+    print("CASE decode-sweep layer grouped launches", shapes, flush=True)
+    packed, pws = [], []
+    for mat, (n, k) in enumerate(shapes):
+        p = pack.pack(fmt, synth.workload_weights(cfg, mat))
+        packed.append(p)
+        pws.append(gc.upload(fmt, n, k, p))
+    # one x per consumer: q, k and v read the same x, so do gate and up
+    x_of = (0, 0, 0, 3, 4, 4, 6)
+    xb = {j: synth.workload_activations(cfg, j, 1) for j in set(x_of)}
+    xt = {j: gc.x_tensor(v) for j, v in xb.items()}
+    for label, groups in (("decode order", ((0, 1, 2), (3,), (4, 5), (6,))), ("device list", (tuple(range(7)),))):
+        ys = [torch.full((1, n), float("nan"), device="cuda") for (n, _) in shapes]
+        for grp in groups:
+            fp4.w4a16_gemv_batched(fmt, 1, [(pws[i].q, pws[i].s, pws[i].global_scale, xt[x_of[i]], ys[i],
+                                             shapes[i][0], shapes[i][1]) for i in grp])
+        torch.cuda.synchronize()
+        for i, (n, k) in enumerate(shapes):
+            gc.check_product(fmt, packed[i], xb[x_of[i]], ys[i], label=f"{label} {n}x{k}")
