@@ -700,9 +700,15 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_small_kernel(const uint8_t* _
 }
 
 // y = 0 before the parts of a split K add into it (a kernel, not a memset, so that the call can be
-// captured in a graph).
-__global__ void gemm_zero_kernel(float* __restrict__ y, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) y[i] = 0.f;
+// captured in a graph). One 16-byte store per thread where y is 16-byte aligned and the element count a
+// multiple of 4 (n4 = n / 4 stores); otherwise (n4 = 0) one element per thread.
+__global__ void gemm_zero_kernel(float* __restrict__ y, int64_t n, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n4 > 0) {
+    if (i < n4) reinterpret_cast<f32x4*>(y)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (i < n) {
+    y[i] = 0.f;
+  }
 }
 
 template <int F, bool RAGGED, int MI, int NB>
@@ -767,8 +773,9 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   }
   if (ksplit) {
     const int64_t total = (int64_t)M * N;
-    const int zb = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    const int rc = fp4_launch(gemm_zero_kernel, dim3(zb), dim3(256), 0, st, y, total);
+    const int64_t n4 = (total % 4 == 0 && fp4_aligned(y, 16)) ? total / 4 : 0;
+    const int64_t threads = n4 > 0 ? n4 : total;
+    const int rc = fp4_launch(gemm_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, y, total, n4);
     if (rc) return rc;
   }
   const int grid = ksplit ? 2 * (int)Ut : (int)Ut;
