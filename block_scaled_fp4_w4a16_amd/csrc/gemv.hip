@@ -664,18 +664,18 @@ __global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restri
           xa[4 * v] = w4[0]; xa[4 * v + 1] = w4[1]; xa[4 * v + 2] = w4[2]; xa[4 * v + 3] = w4[3];
         }
         unit_mac<F, 4>(acc[t][0], wr[t], xa);
-        continue;
-      }
-      bf16x8 b[4];
-      decode_scaled<F>(wr[t], b);
+      } else {
+        bf16x8 b[4];
+        decode_scaled<F>(wr[t], b);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = min(mb * 16 + m16, M - 1);  // rows past M repeat a valid row; never stored
-        const uint8_t* xr = xs + (g * M + row) * 64;
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row = min(mb * 16 + m16, M - 1);  // rows past M repeat a valid row; never stored
+          const uint8_t* xr = xs + (g * M + row) * 64;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + 16 * j);
-          acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[t][mb], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + 16 * j);
+            acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[t][mb], 0, 0, 0);
+          }
         }
       }
     }
@@ -974,15 +974,16 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   b.count = 1;
   b.it[0] = GemvItem{(const uint8_t*)q, (const uint8_t*)s, (const uint16_t*)x_bf16, y, (int)N, (int)K, 0, 0,
                      global_scale, 0};
-  if (M >= 5 && fmt != Q4_0) {
+  if (M >= 5) {
     // From 5 rows of x on: the one-batch GEMV where its grid fits the chip in one round, else the mid-M
-    // kernel (each weight decoded once into scaled bf16 operands, chunks in a chain per wave), which is
-    // faster than the GEMV's batch loop
+    // kernel (chunks in a chain per wave; with M <= 16 one block of x rows and the scales folded per group,
+    // which also covers Q4_0), both faster than the GEMV's batch loop
     int one = -1;
     switch (fmt) {
       case NVFP4: one = try_one_batch<NVFP4, 1>(b, (int)M, (hipStream_t)stream); break;
       case DUAL:  one = try_one_batch<DUAL, 1>(b, (int)M, (hipStream_t)stream); break;
-      default:    one = try_one_batch<FAST, 1>(b, (int)M, (hipStream_t)stream); break;
+      case FAST:  one = try_one_batch<FAST, 1>(b, (int)M, (hipStream_t)stream); break;
+      default:    one = try_one_batch<Q4_0, 1>(b, (int)M, (hipStream_t)stream); break;
     }
     if (one != -1) return one;
     hipStream_t st = (hipStream_t)stream;
@@ -992,7 +993,9 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
     switch (fmt) {
       case NVFP4: return dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
       case DUAL:  return dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
-      default:    return dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
+      case FAST:  return dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
+      default:    if (fp4_tuning().one_batch != 0)  // M <= 16 here: one block of x rows
+                    return dispatch_midm_mb<Q4_0, 1>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
     }
   }
   return dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);

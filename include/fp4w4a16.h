@@ -134,9 +134,9 @@ int fp4_pack_layout(int fmt, int64_t N, int64_t K, const void* src_q, const void
  * once, decodes to exact bf16 levels, contracts against x on the matrix cores, applies
  * the group scales to the FP32 partial sums, reduces the K split inside the workgroup and
  * multiplies by g. Up to M = 8 a wave issues all of its loads at once where that fits the chip
- * in one round of workgroups. Otherwise, from M = 5 on (NVFP4, Dual, FAST), it runs the
- * w4a16_midm kernel, which decodes each weight once into exact bf16 level*scale shared by
- * all rows of x.
+ * in one round of workgroups. Otherwise, from M = 5 on, it runs the mid-M kernel of
+ * w4a16_midm (each wave's chunks in a chain); for Q4_0 only its one-block form (M <= 16), in
+ * which the scales are folded per group as in the GEMV.
  * q/s are fp4_pack_layout output (device); x is M x K bf16 bit patterns and y M x N fp32,
  * both row-major on the device. Deterministic (no atomics). Errors: FP4_ERR_ARG,
  * FP4_ERR_SHAPE (M < 0, N or K), FP4_ERR_UNSUPPORTED (M > 16, K > 2^24), FP4_ERR_ALIGN,
