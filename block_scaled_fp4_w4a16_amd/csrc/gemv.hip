@@ -603,18 +603,19 @@ __device__ __forceinline__ void decode_scaled(const WeightRegs<F>& w, bf16x8 (&b
 }
 
 // Dynamic LDS: [W waves][4 lane groups][M rows][64 B] of staged x (one chunk per wave); after the K loop
-// the same space holds the cross-wave reduction buffer [W][T][MB][64 lanes][4] floats.
-template <int F, int MB, int T, int WMAX = 8>
-__global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
-                                                   const uint16_t* __restrict__ x, float* __restrict__ y, int N,
-                                                   int K, float gscale, int mw) {
+// the same space holds the cross-wave reduction buffer [W][T][MB][64 lanes][4] floats. wg0 is the
+// matrix's first workgroup (grouped launches).
+template <int F, int MB, int T>
+__device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
+                                          const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K,
+                                          float gscale, int mw, int wg0) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int M = mw & 0xff, W = mw >> 8;
   const int ntiles = (N + TILE_N - 1) / TILE_N, nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4, m16 = lane & 15;
-  const int tile0 = blockIdx.x * T;
+  const int tile0 = ((int)blockIdx.x - wg0) * T;
   const int tiles_here = min(T, ntiles - tile0);
   Srcs src;
   src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
@@ -704,6 +705,30 @@ __global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restri
       y[(int64_t)mrow * N + col] = sum * gscale;
     }
   }
+}
+
+template <int F, int MB, int T, int WMAX = 8>
+__global__ __launch_bounds__(64 * WMAX) void midm_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
+                                                   const uint16_t* __restrict__ x, float* __restrict__ y, int N,
+                                                   int K, float gscale, int mw) {
+  midm_body<F, MB, T>(qp, sp, x, y, N, K, gscale, mw, 0);
+}
+
+// Several matrices with one block of x rows (5 <= M <= 16) in one launch; the workgroup finds its matrix
+// as the grouped GEMV does.
+template <int F, int MAXI, int WMAX>
+__global__ __launch_bounds__(64 * WMAX) void midm_group_kernel(int st1, int st2, int st3, int mw,
+                                                               const GemvBatch<MAXI> batch) {
+  const int b = (int)blockIdx.x;
+  int item = 0;
+  if constexpr (MAXI <= 4) {
+    item = (b >= st1 ? 1 : 0) + (b >= st2 ? 1 : 0) + (b >= st3 ? 1 : 0);
+  } else {
+#pragma unroll
+    for (int i = 1; i < MAXI; ++i) item += b >= batch.start[i] ? 1 : 0;  // starts ascend
+  }
+  const GemvItem& it = batch.it[item];
+  midm_body<F, 1, 1>(it.q, it.s, it.x, it.y, it.N, it.K, it.g, mw, it.wg0);
 }
 
 // Workgroups of W waves of kernel `k` that one compute unit holds at once, with `lds` bytes of dynamic
@@ -820,6 +845,57 @@ static int try_one_batch(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   return L8::launch(b, nwg, W, M, st);
 }
 
+// The grouped mid-M kernel (one block of x rows) for a launch of one or more matrices, 5 <= M <= 16: wave
+// count as for one matrix (the most, up to 16, that give every wave two chunks of the shortest K and keep
+// the grid resident in one round).
+template <int F, int MAXI, int WMAX>
+struct MidmGroupLaunch {
+  static const void* fn() { return reinterpret_cast<const void*>(&midm_group_kernel<F, MAXI, WMAX>); }
+  static size_t lds(int W, int M) {
+    const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * 64 * 4 * sizeof(float);
+    return stage > red ? stage : red;
+  }
+  static int resident(int W, int M) {    // workgroups per CU (per device, wave count and M)
+    static std::atomic<int> cache[64][5][17];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int wi = 0;
+    while ((1 << wi) < W) ++wi;
+    int r = cache[dev][wi][M].load(std::memory_order_relaxed);
+    if (r <= 0) {
+      static Fp4LdsLimit lds_limit;
+      lds_limit.ensure(fn(), GEMV_LDS_MAX);
+      r = resident_per_cu(fn(), W, lds(W, M));
+      cache[dev][wi][M].store(r, std::memory_order_relaxed);
+    }
+    return r;
+  }
+  static int launch(const GemvBatch<MAXI>& b, int nwg, int W, int M, hipStream_t st) {
+    static Fp4LdsLimit lds_limit;
+    lds_limit.ensure(fn(), GEMV_LDS_MAX);
+    const int inf = 0x7fffffff;
+    return fp4_launch(midm_group_kernel<F, MAXI, WMAX>, dim3(nwg), dim3(64 * W), lds(W, M), st,
+                      MAXI > 1 ? b.start[1 % MAXI] : inf, MAXI > 2 ? b.start[2 % MAXI] : inf,
+                      MAXI > 3 ? b.start[3 % MAXI] : inf, M | (W << 8), b);
+  }
+};
+
+template <int F, int MAXI>
+static int dispatch_midm_group(GemvBatch<MAXI>& b, int M, hipStream_t st) {
+  int min_chunks, max_chunks;
+  const int nwg = fill_ranges(b, 1, min_chunks, max_chunks);
+  const int cus = fp4_device_cus();
+  int W = 16;
+  while (W > 1 && (min_chunks < 2 * W ||
+                   (int64_t)nwg > (int64_t)cus * (W > 8 ? MidmGroupLaunch<F, MAXI, 16>::resident(W, M)
+                                                        : MidmGroupLaunch<F, MAXI, 8>::resident(W, M))))
+    W >>= 1;
+  const int tw = fp4_tuning().midm_waves;  // tuning override
+  if (tw > 0 && tw <= 16) W = tw;
+  if (W > 8) return MidmGroupLaunch<F, MAXI, 16>::launch(b, nwg, W, M, st);
+  return MidmGroupLaunch<F, MAXI, 8>::launch(b, nwg, W, M, st);
+}
+
 // Fills in the workgroup ranges, picks the variant and wave count, and launches. Every item has N, K >= 1.
 template <int F, int MAXI>
 static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
@@ -874,6 +950,8 @@ static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   } else if (M == 4) {
     using L4 = GemvLaunch<F, 1, 4, 4, 4, MAXI, 4>;
     return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
+  } else if (fp4_tuning().one_batch != 0) {
+    return dispatch_midm_group<F, MAXI>(b, M, st);
   } else if (T == 2) {
     using L = GemvLaunch<F, 2, 4, 2, 16, MAXI, 0>;
     return L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
