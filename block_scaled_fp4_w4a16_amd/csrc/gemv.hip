@@ -901,16 +901,11 @@ template <int F, int MAXI>
 static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   const int one = try_one_batch<F, MAXI>(b, M, st);
   if (one != -1) return one;
-  // With more than 4 x rows a workgroup takes two tiles (they share the staged x) when there are enough
-  // tiles for one such workgroup per CU; otherwise one.
-  int total_tiles = 0;
-  for (int i = 0; i < b.count; ++i) total_tiles += (b.it[i].N + TILE_N - 1) / TILE_N;
-  const int T = (M > 4 && total_tiles >= 2 * 256) ? 2 : 1;
+  // From 5 rows of x on: the mid-M kernel's one-block form, per item
+  if (M > 4) return dispatch_midm_group<F, MAXI>(b, M, st);
   int min_chunks, max_chunks;
-  const int nwg = fill_ranges(b, T, min_chunks, max_chunks);
-  // Batches of two chunk slots when the wave count that would be picked leaves at most two chunks per
-  // wave (no load slots that read nothing), else four.
-  const int wmax = (M > 4) ? 8 : 16;  // keep the staged x (W * U * M * 256 B) inside the LDS
+  const int nwg = fill_ranges(b, 1, min_chunks, max_chunks);
+  const int wmax = 16;
   if (M == 1) {
     // One batch of U chunk slots per wave when W * U covers the longest K (no prefetch registers);
     // U is the fewest slots that do at the picked wave count.
@@ -950,15 +945,8 @@ static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   } else if (M == 4) {
     using L4 = GemvLaunch<F, 1, 4, 4, 4, MAXI, 4>;
     return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
-  } else if (fp4_tuning().one_batch != 0) {
-    return dispatch_midm_group<F, MAXI>(b, M, st);
-  } else if (T == 2) {
-    using L = GemvLaunch<F, 2, 4, 2, 16, MAXI, 0>;
-    return L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
-  } else {
-    using L = GemvLaunch<F, 1, 4, 2, 16, MAXI, 0>;
-    return L::launch(b, nwg, pick_waves<L>(nwg, min_chunks, M, wmax), M, st);
   }
+  return -6;  // not reached: M <= 4 is handled above
 }
 
 template <int MAXI>
@@ -1072,8 +1060,7 @@ extern "C" int w4a16_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void* 
       case NVFP4: return dispatch_midm<NVFP4>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
       case DUAL:  return dispatch_midm<DUAL>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
       case FAST:  return dispatch_midm<FAST>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
-      default:    if (fp4_tuning().one_batch != 0)  // M <= 16 here: one block of x rows
-                    return dispatch_midm_mb<Q4_0, 1>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
+      default:    return dispatch_midm_mb<Q4_0, 1>((int)M, st, qq, ss, xx, y, (int)N, (int)K, global_scale);
     }
   }
   return dispatch_fmt(fmt, b, (int)M, (hipStream_t)stream);
