@@ -43,6 +43,7 @@ __host__ __device__ constexpr int gm_scale_parts(int f, int nb) {
 __host__ __device__ constexpr int gm_loads_per_stage(int f, int mi, int nb = 2) { return mi + nb + gm_scale_parts(f, nb); }
 constexpr int GM_SHORT_ROWS = 192;   // rows of an MI = 6 tile
 constexpr int GM_SHORT_BANDS = 8;    // MI = 6 tiles cover rows 0 .. 8 * 192 - 1 of their columns
+constexpr int64_t GM_SPLIT_MAX_OUT = 5 << 19;  // most outputs (M N) for which a small grid splits K in two
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -760,7 +761,9 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   // whole).
   int ksplit = 0;
   const int H = 2 * nchunk;
-  if (ns == 0 && 2 * Ut <= cus && H >= 12) ksplit = 3 * (H / 6);
+  // The two parts add into y with FP32 atomics, whose cost grows with M N: measured on 14336 x 4096, M = 256
+  // (3.7 M outputs) the split took 51.0 us against 47.9 us whole, at M = 160 (2.3 M) 36.3 against 40.3 us.
+  if (ns == 0 && 2 * Ut <= cus && H >= 12 && (int64_t)M * N <= GM_SPLIT_MAX_OUT) ksplit = 3 * (H / 6);
   if (tu.gemm_split == 0) ksplit = 0;  // tuning override: whole K per workgroup
   // one band: tiles only as high as M needs, 128 or 192 rows
   int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;

@@ -458,7 +458,8 @@ def test_gemm_short_tiles(tmp_path):
 
 
 def test_gemm_split_k(tmp_path):
-    # Grids of at most a quarter of the CUs split K in two parts that add into the zeroed y: against the
+    # Small grids (at most half as many tiles as CUs, and not too many outputs) split K in two parts that
+    # add into the zeroed y: against the
     # oracle, repeatable to the bit (two addends onto zero give the same sum in either order), and the
     # whole-K launch (FP4_GEMM_SPLIT=0, in a child process) within the tolerance too.
     cases = {}
