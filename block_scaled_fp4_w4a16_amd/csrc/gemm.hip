@@ -41,6 +41,18 @@ __host__ __device__ constexpr int gm_scale_parts(int f, int nb) {
   return 2 * nb * (unit_s(f) / 4) / 64 > 1 ? 2 * nb * (unit_s(f) / 4) / 64 : 1;
 }
 __host__ __device__ constexpr int gm_loads_per_stage(int f, int mi, int nb = 2) { return mi + nb + gm_scale_parts(f, nb); }
+// Stage layout per tile shape: x, then each wave's weight pieces, then each wave's scale bytes. 256-column
+// tiles (NB = 2) keep the layout above whatever MI (32 KiB of x, 2 KiB of weights and 512 B of scales per
+// wave: 42 KiB); 128-column tiles (NB = 1) take only what they use (32 MI rows of x, 1 KiB and 256 B per
+// wave), so a ring of 128-row tiles fits in 63 KiB and two workgroups can share a CU.
+__host__ __device__ constexpr int gm_x_bytes(int mi, int nb) { return nb == 2 ? GM_X_BYTES : mi * 32 * GM_ROW_BYTES; }
+__host__ __device__ constexpr int gm_w_wave(int nb) { return 1024 * nb; }
+__host__ __device__ constexpr int gm_s_wave(int nb) { return 256 * nb; }
+__host__ __device__ constexpr int gm_stage_bytes(int mi, int nb) {
+  return gm_x_bytes(mi, nb) + GM_WAVES * (gm_w_wave(nb) + gm_s_wave(nb));
+}
+__host__ __device__ constexpr int gm_lds(int mi, int nb) { return GM_RING * gm_stage_bytes(mi, nb); }
+static_assert(gm_stage_bytes(8, 2) == GM_STAGE_BYTES && gm_stage_bytes(6, 2) == GM_STAGE_BYTES, "prefill layout");
 constexpr int GM_SHORT_ROWS = 192;   // rows of an MI = 6 tile
 constexpr int GM_SHORT_BANDS = 8;    // MI = 6 tiles cover rows 0 .. 8 * 192 - 1 of their columns
 constexpr int64_t GM_SPLIT_MAX_OUT = 5 << 19;  // most outputs (M N) for which a small grid splits K in two
@@ -76,10 +88,10 @@ __device__ __forceinline__ int x_swizzle(int row) { return (row & 7) ^ ((row >> 
 
 // x of stage h: global -> LDS ring slot, one 16-byte direct load per slot. Slot S of the stage holds row
 // S / 8, physical segment S % 8 = sigma ^ x_swizzle(row).
-template <int F, int MI, bool RAGGED>
+template <int F, int MI, bool RAGGED, int NB = 2>
 __device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h, int K, int wave, int lane) {
   const int c = h >> 1, hh = h & 1;
-  uint8_t* base = ring + (h % GM_RING) * GM_STAGE_BYTES;
+  uint8_t* base = ring + (h % GM_RING) * gm_stage_bytes(MI, NB);
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int first = (wave * MI + i) * 64;                  // first slot of this instruction (uniform)
@@ -94,17 +106,18 @@ __device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h
 
 // Weights of stage h: the two lane pieces 2 hh, 2 hh + 1 of a unit are 512 contiguous bytes, so the wave's four
 // tiles take 2 KiB (two 16-byte direct loads per lane), plus the scale bytes of the same four tiles.
-template <int F, int NB = 2>
+template <int F, int MI, int NB = 2>
 __device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h, int nchunk, int wave, int lane) {
   const int c = h >> 1, hh = h & 1;
-  uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
+  constexpr int XB = gm_x_bytes(MI, NB), WB = GM_WAVES * gm_w_wave(NB);
+  uint8_t* stage = ring + (h % GM_RING) * gm_stage_bytes(MI, NB);
 #pragma unroll
   for (int part = 0; part < NB; ++part) {
     const int tt = 2 * part + (lane >> 5);
     const uint32_t off = (uint32_t)(tt * nchunk + c) * UNIT_Q + 512 * hh + (lane & 31) * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16, off, 0,
-        0, 0);
+        src.q, (__attribute__((address_space(3))) void*)(stage + XB + wave * gm_w_wave(NB) + part * 1024), 16, off,
+        0, 0, 0);
   }
   constexpr int us = unit_s(F);                   // 128 (16-weight groups) or 64 (FAST) bytes per unit
   constexpr int lanes_per_tile = us / 4;          // 4-byte loads
@@ -115,8 +128,8 @@ __device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h
     const int tt = idx / lanes_per_tile;
     const uint32_t off = (uint32_t)(tt * nchunk + c) * us + (idx % lanes_per_tile) * 4;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256), 4,
-        off, 0, 0, 0);
+        src.s, (__attribute__((address_space(3))) void*)(stage + XB + WB + wave * gm_s_wave(NB) + part * 256), 4, off,
+        0, 0, 0);
   }
 }
 
@@ -152,7 +165,8 @@ template <int F, int MI, int P, int NB = 2>
 __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
                                                  int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
-  uint8_t* stage = ring + (h % GM_RING) * GM_STAGE_BYTES;
+  constexpr int XB = gm_x_bytes(MI, NB), WB = GM_WAVES * gm_w_wave(NB);
+  uint8_t* stage = ring + (h % GM_RING) * gm_stage_bytes(MI, NB);
   const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
   const uint32_t xrow8 = (uint32_t)K * 16u;                 // 8 rows of bf16
 #pragma unroll
@@ -166,7 +180,7 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
 #pragma unroll
     for (int part = 0; part < NB; ++part)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16,
+          src.q, (__attribute__((address_space(3))) void*)(stage + XB + wave * gm_w_wave(NB) + part * 1024), 16,
           o.w + (uint32_t)(part * 2 * nchunk * UNIT_Q), ws, 0, 0);
   }
   if constexpr (P == 2) {
@@ -175,8 +189,8 @@ __device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadO
 #pragma unroll
     for (int part = 0; part < parts; ++part)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256),
-          4, o.s + (uint32_t)(part * 2 * nchunk * us), ss, 0, 0);
+          src.s, (__attribute__((address_space(3))) void*)(stage + XB + WB + wave * gm_s_wave(NB) + part * 256), 4,
+          o.s + (uint32_t)(part * 2 * nchunk * us), ss, 0, 0);
   }
 }
 
@@ -187,6 +201,7 @@ template <int F, int MI, int I, int NB = 2>
 __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOffs& o, uint8_t* stage, int h, int K,
                                                 int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
+  constexpr int XB = gm_x_bytes(MI, NB), WB = GM_WAVES * gm_w_wave(NB);
   if constexpr (I < MI) {
     const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
     const uint32_t xrow8 = (uint32_t)K * 16u;               // 8 rows of bf16
@@ -196,15 +211,15 @@ __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOf
   } else if constexpr (I < MI + NB) {
     constexpr int part = I - MI;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src.q, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + wave * 2048 + part * 1024), 16,
+        src.q, (__attribute__((address_space(3))) void*)(stage + XB + wave * gm_w_wave(NB) + part * 1024), 16,
         o.w + (uint32_t)(part * 2 * nchunk * UNIT_Q), c * UNIT_Q + 512 * hh, 0, 0);
   } else {
     constexpr int us = unit_s(F), parts = gm_scale_parts(F, NB);
     constexpr int part = I - MI - NB;
     if constexpr (part < parts)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          src.s, (__attribute__((address_space(3))) void*)(stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + part * 256),
-          4, o.s + (uint32_t)(part * 2 * nchunk * us), c * us, 0, 0);
+          src.s, (__attribute__((address_space(3))) void*)(stage + XB + WB + wave * gm_s_wave(NB) + part * 256), 4,
+          o.s + (uint32_t)(part * 2 * nchunk * us), c * us, 0, 0);
   }
 }
 
@@ -213,8 +228,8 @@ template <int F, int MI, bool RAGGED, int NB = 2>
 __device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
                                             int nchunk, int wave, int lane) {
   if constexpr (RAGGED) {
-    issue_x<F, MI, RAGGED>(src, ring, h, K, wave, lane);
-    issue_w<F, NB>(src, ring, h, nchunk, wave, lane);
+    issue_x<F, MI, RAGGED, NB>(src, ring, h, K, wave, lane);
+    issue_w<F, MI, NB>(src, ring, h, nchunk, wave, lane);
   } else {
     issue_stage_part<F, MI, 0, NB>(src, o, ring, h, K, nchunk, wave);
     issue_stage_part<F, MI, 1, NB>(src, o, ring, h, K, nchunk, wave);
@@ -222,17 +237,18 @@ __device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& 
   }
 }
 
-template <int NB = 2>
+template <int MI, int NB = 2>
 __device__ __forceinline__ void read_w(WRegs& r, const uint8_t* stage, int F_spr, int F_us, int wave, int lane) {
+  constexpr int XB = gm_x_bytes(MI, NB), WB = GM_WAVES * gm_w_wave(NB);
   const int kh = lane >> 5;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int rl = 32 * j + (lane & 31);
     const int t = rl >> 4, n = rl & 15;
-    const uint8_t* wb = stage + GM_X_BYTES + wave * 2048 + t * 512 + n * 16 + 8 * kh;
+    const uint8_t* wb = stage + XB + wave * gm_w_wave(NB) + t * 512 + n * 16 + 8 * kh;
     r.w[j][0] = *reinterpret_cast<const u32x2*>(wb);
     r.w[j][1] = *reinterpret_cast<const u32x2*>(wb + 256);
-    const uint8_t* sb = stage + GM_X_BYTES + GM_W_BYTES + wave * 512 + t * F_us + n * F_spr;
+    const uint8_t* sb = stage + XB + WB + wave * gm_s_wave(NB) + t * F_us + n * F_spr;
     if (F_spr == 4) r.sc[j] = *reinterpret_cast<const uint16_t*>(sb + 2 * kh);
     else r.sc[j] = *reinterpret_cast<const uint32_t*>(sb + 4 * kh);
   }
@@ -341,13 +357,14 @@ struct XBase {
   uint32_t v[GM_RING][4];
 };
 
+template <int MI, int NB>
 __device__ __forceinline__ void x_bases(XBase& xb, int lane) {
   const int r = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int slot = 0; slot < GM_RING; ++slot)
 #pragma unroll
     for (int S = 0; S < 4; ++S)
-      xb.v[slot][S] = (uint32_t)(slot * GM_STAGE_BYTES + r * GM_ROW_BYTES + 16 * ((4 * kh + S) ^ x_swizzle(r)));
+      xb.v[slot][S] = (uint32_t)(slot * gm_stage_bytes(MI, NB) + r * GM_ROW_BYTES + 16 * ((4 * kh + S) ^ x_swizzle(r)));
 }
 
 // x fragment i (rows 32 i .. 32 i + 31) at per-lane offset `base` of fragment 0.
@@ -493,7 +510,8 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
   const int s0 = SLOT >= 0 ? SLOT : h % GM_RING;
   const int s1 = SLOT >= 0 ? (SLOT + 1) % GM_RING : (s0 == GM_RING - 1 ? 0 : s0 + 1);
   const int s2 = SLOT >= 0 ? (SLOT + 2) % GM_RING : (s1 == GM_RING - 1 ? 0 : s1 + 1);
-  const StageLoads L{&src, &lo, ring, ring + s2 * GM_STAGE_BYTES, h + 2, K, nchunk, wave, lane};
+  constexpr int SB = gm_stage_bytes(MI, NB);
+  const StageLoads L{&src, &lo, ring, ring + s2 * SB, h + 2, K, nchunk, wave, lane};
   // this stage's and the next stage's per-lane fragment offsets (registers when the slot is known)
   uint32_t xc[4], xn[4];
 #pragma unroll
@@ -502,8 +520,8 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
       xc[S] = xb.v[SLOT][S];
       xn[S] = xb.v[(SLOT + 1) % GM_RING][S];
     } else {
-      xc[S] = xb.v[0][S] + (uint32_t)(s0 * GM_STAGE_BYTES);
-      xn[S] = xb.v[0][S] + (uint32_t)(s1 * GM_STAGE_BYTES);
+      xc[S] = xb.v[0][S] + (uint32_t)(s0 * SB);
+      xn[S] = xb.v[0][S] + (uint32_t)(s1 * SB);
     }
   }
   kstep<F, MI, RAGGED, 0, LOAD, NB>(acc, ka, kb, r, ring, xc, L);
@@ -512,14 +530,14 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
   // k-step 3: MFMAs from kb; the operands of stage h + 1's k-step 0 go to ka
   mfma_group<MI, 0, NB>(acc, kb);
   __builtin_amdgcn_sched_barrier(0);
-  const uint8_t* next = ring + s1 * GM_STAGE_BYTES;
+  const uint8_t* next = ring + s1 * SB;
   if constexpr (MORE) {
     // outstanding direct loads, oldest first: stage h + 1, then stage h + 2 if issued
     if constexpr (LOAD) wait_vmcnt<LPS>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads of stage h are done
     workgroup_barrier();
-    read_w<NB>(r, next, scales_per_row_chunk(F), unit_s(F), wave, lane);
+    read_w<MI, NB>(r, next, scales_per_row_chunk(F), unit_s(F), wave, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
   BDec d[2];
@@ -589,9 +607,9 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
   workgroup_barrier();
   WRegs r;
   KOps<MI> ka, kb;
-  read_w<NB>(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
+  read_w<MI, NB>(r, ring, scales_per_row_chunk(F), unit_s(F), wave, lane);
   XBase xb;
-  x_bases(xb, lane);
+  x_bases<MI, NB>(xb, lane);
   prep_all0<F, MI, NB>(ka, r, ring, xb.v[0][0]);
 
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
@@ -716,16 +734,17 @@ template <int F, bool RAGGED, int MI, int NB>
 static int launch_gemm_small(hipStream_t st, int grid, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                              int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit) {
   static Fp4LdsLimit lds_limit;
-  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI, NB>), GM_LDS);
-  return fp4_launch(gemm_small_kernel<F, RAGGED, MI, NB>, dim3(grid), dim3(GM_THREADS), GM_LDS, st, q, s, x, y, M, N, K,
-                    nchunk, tiles_m, ntiles, g, ksplit);
+  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI, NB>), gm_lds(MI, NB));
+  return fp4_launch(gemm_small_kernel<F, RAGGED, MI, NB>, dim3(grid), dim3(GM_THREADS), gm_lds(MI, NB), st, q, s, x, y,
+                    M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
 }
 
 template <int F, bool RAGGED, int NB>
 static int launch_gemm_small_mi(int band_rows, hipStream_t st, int grid, const uint8_t* q, const uint8_t* s,
                                 const uint16_t* x, float* y, int M, int N, int K, int nchunk, int tiles_m, int ntiles,
                                 float g, int ksplit) {
-  if (band_rows == 128) return launch_gemm_small<F, RAGGED, 4, NB>(st, grid, q, s, x, y, M, N, K, nchunk, 1, ntiles, g, ksplit);
+  if (band_rows == 128)
+    return launch_gemm_small<F, RAGGED, 4, NB>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
   if (band_rows) return launch_gemm_small<F, RAGGED, 6, NB>(st, grid, q, s, x, y, M, N, K, nchunk, 1, ntiles, g, ksplit);
   return launch_gemm_small<F, RAGGED, 8, NB>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
 }
@@ -753,21 +772,33 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   // wave owning 32 weight rows) where twice the grid still fits one round.
   const bool narrow = ns == 0 && 2 * U <= cus && tu.gemm_narrow != 0;  // tuning override: 0 = 256 columns
   const int NBsel = narrow ? 1 : 2;
-  const int64_t Ut = (int64_t)tiles_m * ((N + 128 * NBsel - 1) / (128 * NBsel));
-  // Grids of at most half the CUs (in tiles of the width chosen above) split K in two (at a multiple of
+  const int64_t tiles_nb = (N + 128 * NBsel - 1) / (128 * NBsel);
+  // Tile height: one band of 128 or 192 rows when M fits it. Above 192 rows, 128-column grids take 128-row
+  // tiles over ceil(M / 128) bands where that grid still fits one workgroup per CU (twice the workgroups of
+  // 256-row tiles; their compact ring also lets two share a CU): 14336 x 4096 at M = 256 38.1 us against
+  // 47.8 us, 9728 x 2560 at M = 256 22.9 against 32.4 us. With more bands than that, 256-row tiles win
+  // (M = 512: 62.3 against 66.9 us).
+  int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
+  int bands = 1;
+  if (band_rows == 0 && narrow && (int64_t)((M + 127) / 128) * tiles_nb <= cus) {
+    band_rows = 128;
+    bands = (M + 127) / 128;
+  }
+  if (tu.gemm_band_rows == 0) {  // tuning override: 256-row tiles
+    band_rows = 0;
+    bands = tiles_m;
+  }
+  const int rows_m = band_rows ? bands : tiles_m;  // bands of the grid
+  const int64_t Ut = (int64_t)rows_m * tiles_nb;
+  // Grids of at most half the CUs (in tiles of the shape chosen above) split K in two (at a multiple of
   // the 3-stage ring period, each part at least 6 stages) so that twice the workgroups run; y is zeroed
-  // first and both parts add into it. On larger grids zeroing and adding y costs more than the extra
-  // workgroups gain (prefill N = 14336 at M = 512, 112 tiles of 256 columns: 91 us split against 79 us
-  // whole).
+  // first and both parts add into it with FP32 atomics, whose cost grows with M N: on 14336 x 4096, M = 256
+  // (3.7 M outputs) the split took 51.0 us against 47.9 us whole, at M = 160 (2.3 M) 36.3 against 40.3 us.
+  // At M = 512 (112 tiles of 256 columns) the split had been 91 us against 79 us whole.
   int ksplit = 0;
   const int H = 2 * nchunk;
-  // The two parts add into y with FP32 atomics, whose cost grows with M N: measured on 14336 x 4096, M = 256
-  // (3.7 M outputs) the split took 51.0 us against 47.9 us whole, at M = 160 (2.3 M) 36.3 against 40.3 us.
   if (ns == 0 && 2 * Ut <= cus && H >= 12 && (int64_t)M * N <= GM_SPLIT_MAX_OUT) ksplit = 3 * (H / 6);
   if (tu.gemm_split == 0) ksplit = 0;  // tuning override: whole K per workgroup
-  // one band: tiles only as high as M needs, 128 or 192 rows
-  int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
-  if (tu.gemm_band_rows == 0) band_rows = 0;  // tuning override: 256-row tiles
   if (ksplit == 0 && band_rows == 0 && !narrow) {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
@@ -783,8 +814,8 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   }
   const int grid = ksplit ? 2 * (int)Ut : (int)Ut;
   if (narrow)
-    return launch_gemm_small_mi<F, RAGGED, 1>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)Ut, g, ksplit);
-  return launch_gemm_small_mi<F, RAGGED, 2>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, (int)Ut, g, ksplit);
+    return launch_gemm_small_mi<F, RAGGED, 1>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut, g, ksplit);
+  return launch_gemm_small_mi<F, RAGGED, 2>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut, g, ksplit);
 }
 
 template <int F>

@@ -487,13 +487,13 @@ def test_gemm_split_k(tmp_path):
 
 
 def test_gemm_band_row_tiles(tmp_path):
-    # M <= 128 runs 128-row tiles and M <= 192 192-row tiles: the same products in the same order as the
-    # 256-row tiling whose padding rows they skip (FP4_GEMM_BAND_ROWS=0, in a child process), so the outputs
-    # are bitwise equal (K = 1152 also takes the two-way split).
+    # M <= 128 runs 128-row tiles, M <= 192 192-row tiles, and larger M on a small grid 128-row tiles over
+    # several bands: the same products in the same order as the 256-row tiling (FP4_GEMM_BAND_ROWS=0, in a
+    # child process), so the outputs are bitwise equal (K = 1152 also takes the two-way split on both sides).
     n, k = 600, 1152
     want = {}
     for fmt in gc.FMTS:
-        for m in (65, 128, 129, 192):
+        for m in (65, 128, 129, 192, 200, 256):
             _announce("gemm-band-rows", fmt, m, n, k)
             w, packed = gc.make_case(fmt, n, k, cfg=70, mat=m)
             pw = gc.upload(fmt, n, k, packed)
@@ -512,10 +512,10 @@ def test_gemm_band_row_tiles(tmp_path):
 
 def test_gemm_narrow_tiles(tmp_path):
     # Grids of 256-column tiles that fill at most half the CUs run 128-column tiles (each wave owns 32 weight
-    # rows). Against the oracle on sampled columns, and bitwise against the 256-column tiling (FP4_GEMM_NARROW=0
-    # in a child process): the same products in the same order, where both launches make the same K-split
-    # decision (no split at K = 640; both split at the other shapes, which have at most 64 tiles of 256
-    # columns). N = 1000 and 4350 leave a ragged last 128-column tile.
+    # rows), over 128-row bands where that grid fits the CUs. Against the oracle on sampled columns, and,
+    # with K whole on both sides (FP4_GEMM_SPLIT=0, child processes: the two tilings may decide the split
+    # differently), bitwise against the 256-column tiling (FP4_GEMM_NARROW=0): the same products in the same
+    # order. N = 1000 and 4350 leave a ragged last 128-column tile.
     want = {}
     for fmt in gc.FMTS:
         for (m, n, k) in [(512, 4350, 2048), (300, 1000, 640), (700, 2304, 1024), (129, 1000, 1152)]:
@@ -532,9 +532,10 @@ def test_gemm_narrow_tiles(tmp_path):
             name = f"{fmt}_{m}_{n}_{k}"
             gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
             want[name] = y.cpu().numpy()
-    ys = gc.run_variant(tmp_path, {"FP4_GEMM_NARROW": "0"})
-    for name, y in want.items():
-        assert np.array_equal(y.view(np.uint32), ys[name].view(np.uint32)), name
+    narrow = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0"})
+    wide = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0", "FP4_GEMM_NARROW": "0"})
+    for name in want:
+        assert np.array_equal(narrow[name].view(np.uint32), wide[name].view(np.uint32)), name
 
 
 def test_gemm_split_in_graph():
