@@ -327,9 +327,10 @@ def test_gemv_batched_small_counts(count):
         assert torch.equal(y1, y)
 
 
-def test_gemv_batched_many_items_and_repeatability():
-    # the full item count; every item a different matrix; outputs bitwise repeatable
-    fmt, m = "nvfp4", 2
+@pytest.mark.parametrize("fmt,m", [("nvfp4", 2), ("rocmfp4_fast", 9), ("q4_0", 16)])
+def test_gemv_batched_many_items_and_repeatability(fmt, m):
+    # the full item count; every item a different matrix; outputs bitwise repeatable (M = 2: the GEMV's
+    # one-batch form; 9 and 16: the grouped mid-M kernel)
     _announce("gemv-batched-max", fmt, m)
     items, cases = [], []
     for i in range(fp4.GEMV_MAX_ITEMS):
