@@ -269,7 +269,7 @@ def test_gemv_m0_is_noop():
 # ------------------------------------------------------------------ batched GEMV
 
 @pytest.mark.parametrize("fmt", gc.FMTS_ALL)
-@pytest.mark.parametrize("m", [1, 3, 9, 16])
+@pytest.mark.parametrize("m", [1, 3, 6, 9, 16])
 def test_gemv_batched_matches_oracle(fmt, m):
     # matrices of different N and K (ragged tiles and chunks), two of them sharing one x, with
     # canaries around every y
@@ -325,6 +325,29 @@ def test_gemv_batched_small_counts(count):
         fp4.w4a16_gemv(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y1)
         torch.cuda.synchronize()
         assert torch.equal(y1, y)
+
+
+@pytest.mark.parametrize("m", [1, 3, 6])
+@pytest.mark.parametrize("longest_k", [9728, 14464])
+def test_gemv_batched_long_k(m, longest_k):
+    # two matrices of K = 9728 (76 chunks: 5 chunk slots per wave at 16 waves, the one-batch form at
+    # M <= 4) and, in the second case, one of K = 14464 (113 chunks: more slots than one batch holds,
+    # so the whole group takes the prefetching batch loop); M = 6 takes the grouped mid-M kernel
+    fmt = "rocmfp4_dual"
+    shapes = [(48, 9728), (37, 9728)] + ([(16, 14464)] if longest_k > 9728 else [])
+    _announce("gemv-batched-long-k", fmt, m, shapes)
+    items, cases = [], []
+    for i, (n, k) in enumerate(shapes):
+        w, packed = gc.make_case(fmt, n, k, cfg=62, mat=i)
+        pw = gc.upload(fmt, n, k, packed)
+        x_bits = synth.activations(m, k, cfg=62, mat=i)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        items.append((pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y, n, k))
+        cases.append((packed, x_bits, y, n, k))
+    fp4.w4a16_gemv_batched(fmt, m, items)
+    torch.cuda.synchronize()
+    for packed, x_bits, y, n, k in cases:
+        gc.check_product(fmt, packed, x_bits, y, label=f"batched-long-k M={m} {n}x{k}")
 
 
 @pytest.mark.parametrize("fmt,m", [("nvfp4", 2), ("rocmfp4_fast", 9), ("q4_0", 16)])
@@ -537,6 +560,28 @@ def test_gemm_narrow_tiles(tmp_path):
     wide = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0", "FP4_GEMM_NARROW": "0"})
     for name in want:
         assert np.array_equal(narrow[name].view(np.uint32), wide[name].view(np.uint32)), name
+
+
+def test_gemm_small_grid_stage_counts():
+    # The small-grid kernels (128-column tiles of 128, 192 and 256 rows) over K of 2 to 24 stages (K = 672
+    # ragged): a K loop with no full ring period, the single-stage remainder and both peeled last stages; from
+    # 12 stages K also splits in two parts at stage 3 floor(H / 6) of H. Against the oracle on sampled
+    # columns.
+    shapes = ([(65, 1000, k) for k in (128, 256, 384, 512, 672, 768, 1024, 1536)] +
+              [(150, 600, k) for k in (256, 896, 1152)] + [(300, 11008, k) for k in (128, 640)])
+    for fmt in gc.FMTS:
+        for (m, n, k) in shapes:
+            _announce("gemm-stage-counts", fmt, m, n, k)
+            w, packed = gc.make_case(fmt, n, k, cfg=75, mat=k + m)
+            del w
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(m, k, cfg=75, mat=k + m)
+            y = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+            torch.cuda.synchronize()
+            assert not torch.isnan(y).any()
+            cols = np.unique(np.concatenate([[0, 127, 128, n - 1], np.linspace(0, n - 1, 24).astype(int)]))
+            gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"gemm-stages {fmt} M={m} {n}x{k}")
 
 
 def test_gemm_split_in_graph():
