@@ -86,12 +86,11 @@ __device__ __forceinline__ int stage_k(int c, int hh, int sigma) {
 // the MFMA operand reads (8 or 16 lanes per LDS access, consecutive rows) have no bank conflicts.
 __device__ __forceinline__ int x_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// x of stage h: global -> LDS ring slot, one 16-byte direct load per slot. Slot S of the stage holds row
-// S / 8, physical segment S % 8 = sigma ^ x_swizzle(row).
+// x of stage h: global -> its LDS ring slot `base`, one 16-byte direct load per slot. Slot S of the stage
+// holds row S / 8, physical segment S % 8 = sigma ^ x_swizzle(row).
 template <int F, int MI, bool RAGGED, int NB = 2>
-__device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h, int K, int wave, int lane) {
+__device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* base, int h, int K, int wave, int lane) {
   const int c = h >> 1, hh = h & 1;
-  uint8_t* base = ring + (h % GM_RING) * gm_stage_bytes(MI, NB);
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int first = (wave * MI + i) * 64;                  // first slot of this instruction (uniform)
@@ -107,10 +106,9 @@ __device__ __forceinline__ void issue_x(const GemmSrc& src, uint8_t* ring, int h
 // Weights of stage h: the two lane pieces 2 hh, 2 hh + 1 of a unit are 512 contiguous bytes, so the wave's four
 // tiles take 2 KiB (two 16-byte direct loads per lane), plus the scale bytes of the same four tiles.
 template <int F, int MI, int NB = 2>
-__device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* ring, int h, int nchunk, int wave, int lane) {
+__device__ __forceinline__ void issue_w(const GemmSrc& src, uint8_t* stage, int h, int nchunk, int wave, int lane) {
   const int c = h >> 1, hh = h & 1;
   constexpr int XB = gm_x_bytes(MI, NB), WB = GM_WAVES * gm_w_wave(NB);
-  uint8_t* stage = ring + (h % GM_RING) * gm_stage_bytes(MI, NB);
 #pragma unroll
   for (int part = 0; part < NB; ++part) {
     const int tt = 2 * part + (lane >> 5);
@@ -162,11 +160,10 @@ __device__ __forceinline__ void load_offsets(LoadOffs& o, int K, int nchunk, int
 // has two), then in part 1 the weight pieces and in part 2 the scale bytes. Spreading a stage's loads over
 // three k-steps keeps each burst of vector-memory issue short.
 template <int F, int MI, int P, int NB = 2>
-__device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
+__device__ __forceinline__ void issue_stage_part(const GemmSrc& src, const LoadOffs& o, uint8_t* stage, int h, int K,
                                                  int nchunk, int wave) {
   const int c = h >> 1, hh = h & 1;
   constexpr int XB = gm_x_bytes(MI, NB), WB = GM_WAVES * gm_w_wave(NB);
-  uint8_t* stage = ring + (h % GM_RING) * gm_stage_bytes(MI, NB);
   const int xs = 2 * (c * CHUNK_K + hh * (F == FAST ? 16 : 8));
   const uint32_t xrow8 = (uint32_t)K * 16u;                 // 8 rows of bf16
 #pragma unroll
@@ -223,17 +220,17 @@ __device__ __forceinline__ void issue_stage_one(const GemmSrc& src, const LoadOf
   }
 }
 
-// All of stage h's loads: the three parts, or the per-slot path when K is ragged.
+// All of stage h's loads into its ring slot `stage`: the three parts, or the per-slot path when K is ragged.
 template <int F, int MI, bool RAGGED, int NB = 2>
-__device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& o, uint8_t* ring, int h, int K,
+__device__ __forceinline__ void issue_stage(const GemmSrc& src, const LoadOffs& o, uint8_t* stage, int h, int K,
                                             int nchunk, int wave, int lane) {
   if constexpr (RAGGED) {
-    issue_x<F, MI, RAGGED, NB>(src, ring, h, K, wave, lane);
-    issue_w<F, MI, NB>(src, ring, h, nchunk, wave, lane);
+    issue_x<F, MI, RAGGED, NB>(src, stage, h, K, wave, lane);
+    issue_w<F, MI, NB>(src, stage, h, nchunk, wave, lane);
   } else {
-    issue_stage_part<F, MI, 0, NB>(src, o, ring, h, K, nchunk, wave);
-    issue_stage_part<F, MI, 1, NB>(src, o, ring, h, K, nchunk, wave);
-    issue_stage_part<F, MI, 2, NB>(src, o, ring, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 0, NB>(src, o, stage, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 1, NB>(src, o, stage, h, K, nchunk, wave);
+    issue_stage_part<F, MI, 2, NB>(src, o, stage, h, K, nchunk, wave);
   }
 }
 
@@ -431,7 +428,6 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[MI][2], const KOps<MI>&
 struct StageLoads {
   const GemmSrc* src;
   const LoadOffs* o;
-  uint8_t* ring;
   uint8_t* dst;  // ring slot of stage h
   int h, K, nchunk, wave, lane;
 };
@@ -454,7 +450,7 @@ template <int F, int MI, bool RAGGED, int S, int G, int NB = 2>
 __device__ __forceinline__ void issue_part(const StageLoads& L) {
   if constexpr (RAGGED) {
     if constexpr (S == 0 && G == 1)
-      issue_stage<F, MI, true, NB>(*L.src, *L.o, L.ring, L.h, L.K, L.nchunk, L.wave, L.lane);
+      issue_stage<F, MI, true, NB>(*L.src, *L.o, L.dst, L.h, L.K, L.nchunk, L.wave, L.lane);
   } else {
     if constexpr (S < 3 && (G & 1)) issue_point<F, MI, S * (MI / 2) + (G >> 1), NB>(L);
   }
@@ -501,17 +497,18 @@ __device__ __forceinline__ void prep_all0(KOps<MI>& k, const WRegs& r, const uin
 
 // Stage h of the K loop (see the kernel). LOAD: the stage issues stage h + 2's loads; MORE: there is a
 // stage h + 1, whose k-step 0 operands this stage prepares into ka. SLOT = h % 3 when known at compile
-// time (the ring offsets are then constants), else -1.
-template <int F, int MI, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1, int NB = 2>
+// time (the ring offsets are then constants), else -1. With SETS = 2 wave sets sharing the K range, h
+// counts this set's own stages (ring slots), and the stage of K that it stands for is h0 + 2 h.
+template <int F, int MI, bool RAGGED, bool LOAD, bool MORE, int SLOT = -1, int NB = 2, int SETS = 1>
 __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, KOps<MI>& kb, WRegs& r,
                                            const GemmSrc& src, const LoadOffs& lo, uint8_t* ring, const XBase& xb, int h, int K,
-                                           int nchunk, int wave, int lane) {
+                                           int nchunk, int wave, int lane, int h0 = 0) {
   constexpr int LPS = gm_loads_per_stage(F, MI, NB);
   const int s0 = SLOT >= 0 ? SLOT : h % GM_RING;
   const int s1 = SLOT >= 0 ? (SLOT + 1) % GM_RING : (s0 == GM_RING - 1 ? 0 : s0 + 1);
   const int s2 = SLOT >= 0 ? (SLOT + 2) % GM_RING : (s1 == GM_RING - 1 ? 0 : s1 + 1);
   constexpr int SB = gm_stage_bytes(MI, NB);
-  const StageLoads L{&src, &lo, ring, ring + s2 * SB, h + 2, K, nchunk, wave, lane};
+  const StageLoads L{&src, &lo, ring + s2 * SB, h0 + SETS * (h + 2), K, nchunk, wave, lane};
   // this stage's and the next stage's per-lane fragment offsets (registers when the slot is known)
   uint32_t xc[4], xn[4];
 #pragma unroll
@@ -566,13 +563,18 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
   }
 }
 
-// One tile of y: rows m0 .. m0 + 32 MI - 1, columns n0 .. n0 + 128 NB - 1 (see the kernel).
-template <int F, int MI, bool RAGGED, int NB = 2>
+// One tile of y: rows m0 .. m0 + 32 MI - 1, columns n0 .. n0 + 128 NB - 1 (see the kernel). SETS = 2: two
+// sets of 4 waves (two waves per SIMD), each with a ring of its own, share the tile's K range: set s takes
+// stages hb + s, hb + s + 2, ... (he - hb even), and set 1's sums are added to set 0's through LDS at the end
+// (in that order, so the result does not depend on timing).
+template <int F, int MI, bool RAGGED, int NB = 2, int SETS = 1>
 __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                           const uint16_t* __restrict__ x, float* __restrict__ y, int M, int N, int K,
                                           int nchunk, int m0, int n0, float gscale, int hb, int he, bool add_out) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave: keeps descriptors scalar
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave: keeps descriptors scalar
+  const int wave = SETS == 1 ? wid : (wid & (GM_WAVES - 1));
+  const int set = SETS == 1 ? 0 : (wid >> 2);
   const int wrow0 = n0 + 32 * NB * wave;       // this wave's 32 NB weight rows (2 NB tiles of 16)
   const int ntiles = (N + TILE_N - 1) / TILE_N;
 
@@ -600,9 +602,17 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
   // Stages hb .. he - 1 (all of K, or one part of a split K); hb is a multiple of the ring period, so
   // stage h sits in ring slot h % 3 as when hb = 0.
   constexpr int LPS = gm_loads_per_stage(F, MI, NB);
-  issue_stage<F, MI, RAGGED, NB>(src, lo, ring, hb, K, nchunk, wave, lane);
-  if (hb + 1 < he) issue_stage<F, MI, RAGGED, NB>(src, lo, ring, hb + 1, K, nchunk, wave, lane);
-  if (hb + 1 < he) wait_vmcnt<LPS>();
+  constexpr int SB = gm_stage_bytes(MI, NB);
+  // With two sets, this set's stages are counted from 0 (stage v of the set is stage h0 + 2 v of K) and it
+  // uses its own ring; with one, v is the stage of K itself (h0 = 0).
+  const int h0 = SETS == 1 ? 0 : hb + set;
+  const int vb = SETS == 1 ? hb : 0, ve = SETS == 1 ? he : (he - hb) / 2;
+  if constexpr (SETS == 2) ring += set * gm_lds(MI, NB);
+  issue_stage<F, MI, RAGGED, NB>(src, lo, ring + (vb % GM_RING) * SB, h0 + SETS * vb, K, nchunk, wave, lane);
+  if (vb + 1 < ve)
+    issue_stage<F, MI, RAGGED, NB>(src, lo, ring + ((vb + 1) % GM_RING) * SB, h0 + SETS * (vb + 1), K, nchunk, wave,
+                                   lane);
+  if (vb + 1 < ve) wait_vmcnt<LPS>();
   else wait_vmcnt<0>();
   workgroup_barrier();
   WRegs r;
@@ -614,18 +624,47 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
 
   // Every stage but the last two issues the loads of stage h + 2; the last has no next stage. The stage
   // body is compiled for each case, so the loop has no per-group branches.
-  int h = hb;
+  int h = vb;
   // three stages per iteration (the ring period), so that every ring offset is a constant
-  for (; h + 4 < he; h += 3) {
-    stage_body<F, MI, RAGGED, true, true, 0, NB>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
-    stage_body<F, MI, RAGGED, true, true, 1, NB>(acc, ka, kb, r, src, lo, ring, xb, h + 1, K, nchunk, wave, lane);
-    stage_body<F, MI, RAGGED, true, true, 2, NB>(acc, ka, kb, r, src, lo, ring, xb, h + 2, K, nchunk, wave, lane);
+  for (; h + 4 < ve; h += 3) {
+    stage_body<F, MI, RAGGED, true, true, 0, NB, SETS>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane, h0);
+    stage_body<F, MI, RAGGED, true, true, 1, NB, SETS>(acc, ka, kb, r, src, lo, ring, xb, h + 1, K, nchunk, wave, lane,
+                                                       h0);
+    stage_body<F, MI, RAGGED, true, true, 2, NB, SETS>(acc, ka, kb, r, src, lo, ring, xb, h + 2, K, nchunk, wave, lane,
+                                                       h0);
   }
-  for (; h + 2 < he; ++h)
-    stage_body<F, MI, RAGGED, true, true, -1, NB>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
-  if (h + 1 < he)
-    stage_body<F, MI, RAGGED, false, true, -1, NB>(acc, ka, kb, r, src, lo, ring, xb, h++, K, nchunk, wave, lane);
-  stage_body<F, MI, RAGGED, false, false, -1, NB>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane);
+  for (; h + 2 < ve; ++h)
+    stage_body<F, MI, RAGGED, true, true, -1, NB, SETS>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane, h0);
+  if (h + 1 < ve)
+    stage_body<F, MI, RAGGED, false, true, -1, NB, SETS>(acc, ka, kb, r, src, lo, ring, xb, h++, K, nchunk, wave, lane,
+                                                         h0);
+  stage_body<F, MI, RAGGED, false, false, -1, NB, SETS>(acc, ka, kb, r, src, lo, ring, xb, h, K, nchunk, wave, lane, h0);
+
+  if constexpr (SETS == 2) {
+    // set 1 hands its sums to set 0 through LDS (the rings are free once every wave has passed the barrier
+    // after its last LDS read): [wave][i][j][e][lane] floats, 256 contiguous bytes per (i, j, e)
+    ring -= set * gm_lds(MI, NB);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    workgroup_barrier();
+    float* red = reinterpret_cast<float*>(ring) + (size_t)wave * (MI * NB * 16 * 64) + lane;
+    if (set == 1) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) red[((i * NB + j) * 16 + e) * 64] = acc[i][j][e];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    workgroup_barrier();
+    if (set == 1) return;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += red[((i * NB + j) * 16 + e) * 64];
+  }
 
   // epilogue: acc[i][j][e] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]; y is written
   // once and not read back here, so the stores are nontemporal (about 1% faster than plain ones). A
@@ -698,8 +737,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
 // rows, so twice the tiles of the 256-column tiling), tile t taking band t % tiles_m and column tile
 // t / tiles_m. ksplit > 0: workgroup t < ntiles takes stages 0 .. ksplit - 1 of tile t, workgroup ntiles + t
 // the rest, and both add into the zeroed y.
-template <int F, bool RAGGED, int MI, int NB>
-__global__ __launch_bounds__(GM_THREADS) void gemm_small_kernel(const uint8_t* __restrict__ qp,
+template <int F, bool RAGGED, int MI, int NB, int SETS = 1>
+__global__ __launch_bounds__(GM_THREADS * SETS) void gemm_small_kernel(const uint8_t* __restrict__ qp,
                                                                 const uint8_t* __restrict__ sp,
                                                                 const uint16_t* __restrict__ x,
                                                                 float* __restrict__ y, int M, int N, int K,
@@ -714,8 +753,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_small_kernel(const uint8_t* _
     hb = second ? ksplit : 0;
     he = second ? he : ksplit;
   }
-  gemm_tile<F, MI, RAGGED, NB>(ring, qp, sp, x, y, M, N, K, nchunk, (t % tiles_m) * 32 * MI, (t / tiles_m) * 128 * NB,
-                               gscale, hb, he, ksplit > 0);
+  gemm_tile<F, MI, RAGGED, NB, SETS>(ring, qp, sp, x, y, M, N, K, nchunk, (t % tiles_m) * 32 * MI,
+                                     (t / tiles_m) * 128 * NB, gscale, hb, he, ksplit > 0);
 }
 
 // y = 0 before the parts of a split K add into it (a kernel, not a memset, so that the call can be
@@ -730,19 +769,24 @@ __global__ void gemm_zero_kernel(float* __restrict__ y, int64_t n, int64_t n4) {
   }
 }
 
-template <int F, bool RAGGED, int MI, int NB>
+template <int F, bool RAGGED, int MI, int NB, int SETS = 1>
 static int launch_gemm_small(hipStream_t st, int grid, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                              int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit) {
   static Fp4LdsLimit lds_limit;
-  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI, NB>), gm_lds(MI, NB));
-  return fp4_launch(gemm_small_kernel<F, RAGGED, MI, NB>, dim3(grid), dim3(GM_THREADS), gm_lds(MI, NB), st, q, s, x, y,
-                    M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
+  constexpr int lds = SETS * gm_lds(MI, NB);
+  lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI, NB, SETS>), lds);
+  return fp4_launch(gemm_small_kernel<F, RAGGED, MI, NB, SETS>, dim3(grid), dim3(GM_THREADS * SETS), lds, st, q, s, x,
+                    y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
 }
 
 template <int F, bool RAGGED, int NB>
-static int launch_gemm_small_mi(int band_rows, hipStream_t st, int grid, const uint8_t* q, const uint8_t* s,
+static int launch_gemm_small_mi(int band_rows, bool sets2, hipStream_t st, int grid, const uint8_t* q, const uint8_t* s,
                                 const uint16_t* x, float* y, int M, int N, int K, int nchunk, int tiles_m, int ntiles,
                                 float g, int ksplit) {
+  if constexpr (NB == 1) {
+    if (sets2 && band_rows == 128)
+      return launch_gemm_small<F, RAGGED, 4, 1, 2>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
+  }
   if (band_rows == 128)
     return launch_gemm_small<F, RAGGED, 4, NB>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
   if (band_rows) return launch_gemm_small<F, RAGGED, 6, NB>(st, grid, q, s, x, y, M, N, K, nchunk, 1, ntiles, g, ksplit);
@@ -799,6 +843,15 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   const int H = 2 * nchunk;
   if (ns == 0 && 2 * Ut <= cus && H >= 12 && (int64_t)M * N <= GM_SPLIT_MAX_OUT) ksplit = 3 * (H / 6);
   if (tu.gemm_split == 0) ksplit = 0;  // tuning override: whole K per workgroup
+  // 128-row bands of 128-column tiles (a 63 KiB ring) run two sets of 4 waves per workgroup, each over every
+  // other stage with a ring of its own (two waves per SIMD; each weight still decoded once per workgroup).
+  // The sets need an even number of stages in each part of K. With them a stage costs about 0.7 us per
+  // workgroup and the split's zero fill and atomics about 7.5 us per million outputs, so K splits only while
+  // that is below a quarter of the stages' time (M N <= 23000 H): 14336 x 4096 at M = 128 26.4 us whole
+  // against 28.9 us split, at M = 65 21.3 us split against 25.5 us whole.
+  const bool sets2 = narrow && band_rows == 128 && tu.gemm_sets != 1;  // tuning override: 1 = one set
+  if (sets2 && ksplit) ksplit = (int64_t)M * N <= 23000LL * H ? 2 * (H / 4) : 0;
+  if (sets2 && tu.gemm_split == 1 && ns == 0 && 2 * Ut <= cus && H >= 12) ksplit = 2 * (H / 4);  // tuning override
   if (ksplit == 0 && band_rows == 0 && !narrow) {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
@@ -814,8 +867,10 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   }
   const int grid = ksplit ? 2 * (int)Ut : (int)Ut;
   if (narrow)
-    return launch_gemm_small_mi<F, RAGGED, 1>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut, g, ksplit);
-  return launch_gemm_small_mi<F, RAGGED, 2>(band_rows, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut, g, ksplit);
+    return launch_gemm_small_mi<F, RAGGED, 1>(band_rows, sets2, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut,
+                                              g, ksplit);
+  return launch_gemm_small_mi<F, RAGGED, 2>(band_rows, false, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut, g,
+                                            ksplit);
 }
 
 template <int F>

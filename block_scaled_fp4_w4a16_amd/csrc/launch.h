@@ -48,11 +48,12 @@ struct Fp4Tuning {
   int gemv_ring;       // FP4_GEMV_RING=0/1: never / whenever it applies, the long-K ring kernel
   int midm_waves;      // FP4_MIDM_WAVES: waves per mid-M workgroup
   int gemm_short;      // FP4_GEMM_SHORT=0: 256-row tiles only
-  int gemm_split;      // FP4_GEMM_SPLIT=0: whole K per workgroup
+  int gemm_split;      // FP4_GEMM_SPLIT=0: whole K per workgroup; =1: two-set tiles split K wherever the grid allows
   int gemm_band_rows;  // FP4_GEMM_BAND_ROWS=0: 256-row tiles at M <= 192
   int gemm_narrow;     // FP4_GEMM_NARROW=0: no 128-column tiles on small grids
   int quant_exhaustive;  // FP4_QUANT_EXHAUSTIVE=1: the ROCmFP4 packer scores every candidate (no pruning)
   int one_batch;       // FP4_ONE_BATCH=0: no one-batch GEMV for 2 <= M <= 8 (batch loop, or mid-M kernel from M = 5)
+  int gemm_sets;       // FP4_GEMM_SETS=1: one set of 4 waves per workgroup on 128-row small-grid tiles too
 };
 const Fp4Tuning& fp4_tuning();
 

@@ -512,8 +512,9 @@ def test_gemm_split_k(tmp_path):
 
 def test_gemm_band_row_tiles(tmp_path):
     # M <= 128 runs 128-row tiles, M <= 192 192-row tiles, and larger M on a small grid 128-row tiles over
-    # several bands: the same products in the same order as the 256-row tiling (FP4_GEMM_BAND_ROWS=0, in a
-    # child process), so the outputs are bitwise equal (K = 1152 also takes the two-way split on both sides).
+    # several bands. Against the oracle as launched; and with one wave set per workgroup (FP4_GEMM_SETS=1, child
+    # processes) the same products in the same order as the 256-row tiling (FP4_GEMM_BAND_ROWS=0), so those
+    # outputs are bitwise equal (K = 1152 also takes the two-way split on both sides).
     n, k = 600, 1152
     want = {}
     for fmt in gc.FMTS:
@@ -529,17 +530,19 @@ def test_gemm_band_row_tiles(tmp_path):
             name = f"{fmt}_{m}"
             gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
             want[name] = y.cpu().numpy()
-    ys = gc.run_variant(tmp_path, {"FP4_GEMM_BAND_ROWS": "0"})
-    for name, y in want.items():
-        assert np.array_equal(y.view(np.uint32), ys[name].view(np.uint32)), name
+    bands = gc.run_variant(tmp_path, {"FP4_GEMM_SETS": "1"})
+    ys = gc.run_variant(tmp_path, {"FP4_GEMM_SETS": "1", "FP4_GEMM_BAND_ROWS": "0"})
+    for name in want:
+        assert np.array_equal(bands[name].view(np.uint32), ys[name].view(np.uint32)), name
 
 
 def test_gemm_narrow_tiles(tmp_path):
     # Grids of 256-column tiles that fill at most half the CUs run 128-column tiles (each wave owns 32 weight
     # rows), over 128-row bands where that grid fits the CUs. Against the oracle on sampled columns, and,
-    # with K whole on both sides (FP4_GEMM_SPLIT=0, child processes: the two tilings may decide the split
-    # differently), bitwise against the 256-column tiling (FP4_GEMM_NARROW=0): the same products in the same
-    # order. N = 1000 and 4350 leave a ragged last 128-column tile.
+    # with K whole and one wave set per workgroup on both sides (FP4_GEMM_SPLIT=0, FP4_GEMM_SETS=1, child
+    # processes: the two tilings may decide the split differently), bitwise against the 256-column tiling
+    # (FP4_GEMM_NARROW=0): the same products in the same order. N = 1000 and 4350 leave a ragged last
+    # 128-column tile.
     want = {}
     for fmt in gc.FMTS:
         for (m, n, k) in [(512, 4350, 2048), (300, 1000, 640), (700, 2304, 1024), (129, 1000, 1152)]:
@@ -556,10 +559,44 @@ def test_gemm_narrow_tiles(tmp_path):
             name = f"{fmt}_{m}_{n}_{k}"
             gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
             want[name] = y.cpu().numpy()
-    narrow = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0"})
-    wide = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0", "FP4_GEMM_NARROW": "0"})
+    narrow = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0", "FP4_GEMM_SETS": "1"})
+    wide = gc.run_variant(tmp_path, {"FP4_GEMM_SPLIT": "0", "FP4_GEMM_NARROW": "0", "FP4_GEMM_SETS": "1"})
     for name in want:
         assert np.array_equal(narrow[name].view(np.uint32), wide[name].view(np.uint32)), name
+
+
+def test_gemm_two_wave_sets(tmp_path):
+    # 128-row small-grid tiles run two sets of 4 waves over alternate stages, set 1's sums added to set 0's at
+    # the end. K from 2 stages (one per set) up, ragged K = 672, split and whole K: against the oracle as
+    # launched, bitwise repeatable, and against the oracle again with one set (FP4_GEMM_SETS=1), with K forced
+    # whole (FP4_GEMM_SPLIT=0) and with the split forced wherever the grid allows (FP4_GEMM_SPLIT=1).
+    shapes = [(65, 1000, 128), (65, 1000, 256), (100, 600, 1152), (128, 2304, 1024), (256, 600, 672),
+              (200, 1000, 640), (97, 14336, 256)]
+    cases = {}
+    for fmt in gc.FMTS:
+        for (m, n, k) in shapes:
+            _announce("gemm-sets", fmt, m, n, k)
+            w, packed = gc.make_case(fmt, n, k, cfg=76, mat=k + m)
+            del w
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(m, k, cfg=76, mat=k + m)
+            x = gc.x_tensor(x_bits)
+            ys = []
+            for _ in range(2):
+                y = torch.full((m, n), float("nan"), device="cuda")
+                fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+                ys.append(y)
+            torch.cuda.synchronize()
+            assert torch.equal(ys[0], ys[1])
+            cols = np.unique(np.concatenate([[0, 127, 128, n - 1], np.linspace(0, n - 1, 24).astype(int)]))
+            gc.check_product(fmt, packed, x_bits, ys[0], cols=cols, label=f"gemm-sets {fmt} M={m} {n}x{k}")
+            name = f"{fmt}_{m}_{n}_{k}"
+            gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
+            cases[name] = (fmt, packed, x_bits, cols)
+    for env in ({"FP4_GEMM_SETS": "1"}, {"FP4_GEMM_SPLIT": "0"}, {"FP4_GEMM_SPLIT": "1"}):
+        ys = gc.run_variant(tmp_path, env)
+        for name, (fmt, packed, x_bits, cols) in cases.items():
+            gc.check_product(fmt, packed, x_bits, torch.from_numpy(ys[name]), cols=cols, label=f"{env} {name}")
 
 
 def test_gemm_small_grid_stage_counts():
