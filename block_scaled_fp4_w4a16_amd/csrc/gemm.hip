@@ -817,17 +817,20 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   const bool narrow = ns == 0 && 2 * U <= cus && tu.gemm_narrow != 0;  // tuning override: 0 = 256 columns
   const int NBsel = narrow ? 1 : 2;
   const int64_t tiles_nb = (N + 128 * NBsel - 1) / (128 * NBsel);
-  // Tile height: one band of 128 or 192 rows when M fits it. Above 192 rows, 128-column grids take 128-row
-  // tiles over ceil(M / 128) bands where that grid still fits one workgroup per CU (twice the workgroups of
-  // 256-row tiles; their compact ring also lets two share a CU): 14336 x 4096 at M = 256 38.1 us against
-  // 47.8 us, 9728 x 2560 at M = 256 22.9 against 32.4 us. With more bands than that, 256-row tiles win
-  // (M = 512: 62.3 against 66.9 us).
-  int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS) ? GM_SHORT_ROWS : 0;
+  // Tile height: one band of 128 or 192 rows when M fits it. Above that, 128-column grids take 128-row tiles
+  // over ceil(M / 128) bands where that grid still fits one workgroup per CU (twice the workgroups of 256-row
+  // tiles): 14336 x 4096 at M = 256 38.1 us against 47.8 us, 9728 x 2560 at M = 256 22.9 against 32.4 us,
+  // both with one wave set. With more bands than that, 256-row tiles win (M = 512: 62.3 against 66.9 us).
+  // With two wave sets per 128-row tile (below), 128-row bands also beat one 192-row band for 128 < M <= 192
+  // (14336 x 4096 at M = 160 30.4 against 36.8 us, 9728 x 2560 at M = 192 18.9 against 26.0 us).
+  const bool sets_ok = tu.gemm_sets != 1;
+  int band_rows = (M <= 128) ? 128 : (M <= GM_SHORT_ROWS && !(sets_ok && narrow)) ? GM_SHORT_ROWS : 0;
   int bands = 1;
   if (band_rows == 0 && narrow && (int64_t)((M + 127) / 128) * tiles_nb <= cus) {
     band_rows = 128;
     bands = (M + 127) / 128;
   }
+  if (band_rows == 0 && M <= GM_SHORT_ROWS) band_rows = GM_SHORT_ROWS;
   if (tu.gemm_band_rows == 0) {  // tuning override: 256-row tiles
     band_rows = 0;
     bands = tiles_m;
@@ -849,7 +852,9 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   // workgroup and the split's zero fill and atomics about 7.5 us per million outputs, so K splits only while
   // that is below a quarter of the stages' time (M N <= 23000 H): 14336 x 4096 at M = 128 26.4 us whole
   // against 28.9 us split, at M = 65 21.3 us split against 25.5 us whole.
-  const bool sets2 = narrow && band_rows == 128 && tu.gemm_sets != 1;  // tuning override: 1 = one set
+  // (256-row tiles with two sets, each with a 2-slot ring to fit 148 KiB, were slower: 14336 x 4096 at
+  // M = 512 64.1 against 58.7 us.)
+  const bool sets2 = narrow && band_rows == 128 && sets_ok;  // tuning override FP4_GEMM_SETS=1: one set
   if (sets2 && ksplit) ksplit = (int64_t)M * N <= 23000LL * H ? 2 * (H / 4) : 0;
   if (sets2 && tu.gemm_split == 1 && ns == 0 && 2 * Ut <= cus && H >= 12) ksplit = 2 * (H / 4);  // tuning override
   if (ksplit == 0 && band_rows == 0 && !narrow) {

@@ -567,11 +567,12 @@ def test_gemm_narrow_tiles(tmp_path):
 
 def test_gemm_two_wave_sets(tmp_path):
     # 128-row small-grid tiles run two sets of 4 waves over alternate stages, set 1's sums added to set 0's at
-    # the end. K from 2 stages (one per set) up, ragged K = 672, split and whole K: against the oracle as
-    # launched, bitwise repeatable, and against the oracle again with one set (FP4_GEMM_SETS=1), with K forced
-    # whole (FP4_GEMM_SPLIT=0) and with the split forced wherever the grid allows (FP4_GEMM_SPLIT=1).
+    # the end (also two 128-row bands for 128 < M <= 192). K from 2 stages (one per set) up, ragged K = 672,
+    # split and whole K: against the oracle as launched, bitwise repeatable, and against the oracle again with
+    # one set (FP4_GEMM_SETS=1), with K forced whole (FP4_GEMM_SPLIT=0) and with the split forced wherever the
+    # grid allows (FP4_GEMM_SPLIT=1).
     shapes = [(65, 1000, 128), (65, 1000, 256), (100, 600, 1152), (128, 2304, 1024), (256, 600, 672),
-              (200, 1000, 640), (97, 14336, 256)]
+              (200, 1000, 640), (97, 14336, 256), (160, 2304, 1152), (192, 1000, 384)]
     cases = {}
     for fmt in gc.FMTS:
         for (m, n, k) in shapes:
@@ -605,7 +606,7 @@ def test_gemm_small_grid_stage_counts():
     # 12 stages K also splits in two parts at stage 3 floor(H / 6) of H. Against the oracle on sampled
     # columns.
     shapes = ([(65, 1000, k) for k in (128, 256, 384, 512, 672, 768, 1024, 1536)] +
-              [(150, 600, k) for k in (256, 896, 1152)] + [(300, 11008, k) for k in (128, 640)])
+              [(150, 600, k) for k in (256, 896, 1152)] + [(300, 11008, k) for k in (128, 256, 384, 640, 1024)])
     for fmt in gc.FMTS:
         for (m, n, k) in shapes:
             _announce("gemm-stage-counts", fmt, m, n, k)
