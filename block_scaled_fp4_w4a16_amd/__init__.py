@@ -47,6 +47,9 @@ _SIGS = {
     "w4a16_gemm": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "w4a16_midm": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "w4a16_matmul": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
+    "w4a16_gemm_ws": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p, ctypes.c_size_t, _p]),
+    "w4a16_matmul_ws": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p, ctypes.c_size_t, _p]),
+    "w4a16_gemm_workspace_bytes": (_i64, [_c, _i64, _i64, _i64]),
     "fp4_dequant_f32": (_c, [_c, _i64, _i64, _p, _p, _f, _p, _p]),
     "fp4_quantize_nvfp4": (_c, [_i64, _i64, _p, _p, _p, _p, _p]),
     "fp4_quantize_rocmfp4": (_c, [_c, _i64, _i64, _p, _p, _p, _p]),
@@ -211,7 +214,47 @@ def w4a16_gemv_batched(fmt, M, items, stream=None):
         _check(lib().w4a16_gemv_batched(f, M, len(items), arr, _stream(stream)), "w4a16_gemv_batched")
 
 
-def w4a16_gemm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
+def w4a16_gemm_workspace_bytes(fmt, M, N, K, device=None) -> int:
+    """Workspace bytes w4a16_gemm_ws would use for this shape on `device` (default: the current one)."""
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        n = int(lib().w4a16_gemm_workspace_bytes(_fmt(fmt), M, N, K))
+    _check(n if n < 0 else 0, "w4a16_gemm_workspace_bytes")
+    return n
+
+
+def _product_ws(name, fmt, M, N, K, q, s, global_scale, x, y, stream, workspace):
+    """A product entry point that takes a workspace: `workspace` (a uint8 CUDA tensor) or, by default, one
+    of the size the library asks for, allocated here from torch's caching allocator on the launch stream."""
+    if x.dtype != torch.bfloat16 or y.dtype != torch.float32:
+        raise TypeError("x must be bfloat16 and y float32")
+    if x.numel() < M * K or y.numel() < M * N:
+        raise ValueError("x or y is smaller than M x K / M x N")
+    f = _fmt(fmt)
+    dev = _device(q, s, x, y)
+    if M > 0 and N > 0 and K > 0:
+        _check_planes(f, N, K, q, s)
+    with torch.cuda.device(dev):
+        st = _stream(stream)
+        if workspace is None and M > 64:
+            nbytes = w4a16_gemm_workspace_bytes(f, M, N, K, dev)
+            if nbytes > 0:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+                if stream is not None:
+                    # the kernels run on `stream`, not necessarily the one the allocator recorded
+                    ext = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(st)
+                    workspace.record_stream(ext)
+        ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), _nbytes(workspace))
+        _check(getattr(lib(), name)(f, M, N, K, _ptr(q), _ptr(s), float(global_scale), _ptr(x), _ptr(y), ws_ptr,
+                                    ws_bytes, st), name)
+
+
+def w4a16_gemm(fmt, M, N, K, q, s, global_scale, x, y, stream=None, workspace=None):
+    """The prefill product through w4a16_gemm_ws (K parts in a workspace where the launch rules split K)."""
+    _product_ws("w4a16_gemm_ws", fmt, M, N, K, q, s, global_scale, x, y, stream, workspace)
+
+
+def w4a16_gemm_noworkspace(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
+    """The C entry point w4a16_gemm itself (no workspace: at most the two-part atomic split)."""
     _product("w4a16_gemm", fmt, M, N, K, q, s, global_scale, x, y, stream)
 
 
@@ -219,8 +262,9 @@ def w4a16_midm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
     _product("w4a16_midm", fmt, M, N, K, q, s, global_scale, x, y, stream)
 
 
-def w4a16_matmul(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
-    _product("w4a16_matmul", fmt, M, N, K, q, s, global_scale, x, y, stream)
+def w4a16_matmul(fmt, M, N, K, q, s, global_scale, x, y, stream=None, workspace=None):
+    """Dispatch on M through w4a16_matmul_ws (the prefill path with a workspace)."""
+    _product_ws("w4a16_matmul_ws", fmt, M, N, K, q, s, global_scale, x, y, stream, workspace)
 
 
 def fp4_dequant_f32(fmt, N, K, q, s, global_scale, w, stream=None):

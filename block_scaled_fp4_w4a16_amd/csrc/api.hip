@@ -32,7 +32,7 @@ const Fp4Tuning& fp4_tuning() {
                               env_int("FP4_GEMV_RING"),  env_int("FP4_MIDM_WAVES"),  env_int("FP4_GEMM_SHORT"),
                               env_int("FP4_GEMM_SPLIT"), env_int("FP4_GEMM_BAND_ROWS"),
                               env_int("FP4_GEMM_NARROW"),  env_int("FP4_QUANT_EXHAUSTIVE"),
-                              env_int("FP4_ONE_BATCH"),  env_int("FP4_GEMM_SETS")};
+                              env_int("FP4_ONE_BATCH"),  env_int("FP4_GEMM_SETS"),   env_int("FP4_GEMM_PARTS")};
   return t;
 }
 

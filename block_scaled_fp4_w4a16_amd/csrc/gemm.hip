@@ -570,7 +570,8 @@ __device__ __forceinline__ void stage_body(f32x16 (&acc)[MI][2], KOps<MI>& ka, K
 template <int F, int MI, bool RAGGED, int NB = 2, int SETS = 1>
 __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                           const uint16_t* __restrict__ x, float* __restrict__ y, int M, int N, int K,
-                                          int nchunk, int m0, int n0, float gscale, int hb, int he, bool add_out) {
+                                          int nchunk, int m0, int n0, float gscale, int hb, int he, bool add_out,
+                                          bool keep = false) {
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave: keeps descriptors scalar
   const int wave = SETS == 1 ? wid : (wid & (GM_WAVES - 1));
@@ -683,6 +684,19 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ring, const uint8_t* __restri
         }
     return;
   }
+  if (keep) {  // a partial sum of a K part, read back soon by the combining kernel: plain stores
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int col = wrow0 + 32 * j + (lane & 31);
+          if (row < M && col < N) y[(int64_t)row * N + col] = acc[i][j][e] * gscale;
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -736,25 +750,34 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(const uint8_t* __restr
 // (MI = 4 or 6 when M fits one such band, else 8) and 128 NB columns (NB = 1: each wave owns 32 weight
 // rows, so twice the tiles of the 256-column tiling), tile t taking band t % tiles_m and column tile
 // t / tiles_m. ksplit > 0: workgroup t < ntiles takes stages 0 .. ksplit - 1 of tile t, workgroup ntiles + t
-// the rest, and both add into the zeroed y.
+// the rest, and both add into the zeroed y. ksplit = -P (two-set tiles only): workgroup p ntiles + t takes
+// chunks [p C / P, (p + 1) C / P) of tile t (C chunks) and writes its g-scaled sum to plane p of the
+// workspace ws (P planes of M x N floats); gemm_combine_kernel then adds the planes into y.
 template <int F, bool RAGGED, int MI, int NB, int SETS = 1>
 __global__ __launch_bounds__(GM_THREADS * SETS) void gemm_small_kernel(const uint8_t* __restrict__ qp,
                                                                 const uint8_t* __restrict__ sp,
                                                                 const uint16_t* __restrict__ x,
                                                                 float* __restrict__ y, int M, int N, int K,
                                                                 int nchunk, int tiles_m, int ntiles, float gscale,
-                                                                int ksplit) {
+                                                                int ksplit, float* __restrict__ ws) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   int t = (int)blockIdx.x;
   int hb = 0, he = 2 * nchunk;
+  float* out = y;
   if (ksplit > 0) {
     const bool second = t >= ntiles;
     if (second) t -= ntiles;
     hb = second ? ksplit : 0;
     he = second ? he : ksplit;
+  } else if (SETS == 2 && ksplit < 0) {
+    const int parts = -ksplit, p = t / ntiles;
+    t -= p * ntiles;
+    hb = 2 * (int)((int64_t)p * nchunk / parts);
+    he = 2 * (int)((int64_t)(p + 1) * nchunk / parts);
+    out = ws + (int64_t)p * M * N;
   }
-  gemm_tile<F, MI, RAGGED, NB, SETS>(ring, qp, sp, x, y, M, N, K, nchunk, (t % tiles_m) * 32 * MI,
-                                     (t / tiles_m) * 128 * NB, gscale, hb, he, ksplit > 0);
+  gemm_tile<F, MI, RAGGED, NB, SETS>(ring, qp, sp, x, out, M, N, K, nchunk, (t % tiles_m) * 32 * MI,
+                                     (t / tiles_m) * 128 * NB, gscale, hb, he, ksplit > 0, SETS == 2 && ksplit < 0);
 }
 
 // y = 0 before the parts of a split K add into it (a kernel, not a memset, so that the call can be
@@ -769,23 +792,49 @@ __global__ void gemm_zero_kernel(float* __restrict__ y, int64_t n, int64_t n4) {
   }
 }
 
+// y = plane 0 + plane 1 + ... + plane P - 1 of the workspace (n floats each), added in that order, so the
+// result does not depend on which K part finished first. Four elements per thread (16-byte loads and store)
+// where n is a multiple of 4 and ws and y are 16-byte aligned (n4 = n / 4), else one.
+__global__ void gemm_combine_kernel(const float* __restrict__ ws, float* __restrict__ y, int64_t n, int64_t n4,
+                                    int parts) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n4 > 0) {
+    if (i >= n4) return;
+    f32x4 a = reinterpret_cast<const f32x4*>(ws)[i];
+    for (int p = 1; p < parts; ++p) {
+      const f32x4 b = reinterpret_cast<const f32x4*>(ws + (int64_t)p * n)[i];
+      a[0] += b[0];
+      a[1] += b[1];
+      a[2] += b[2];
+      a[3] += b[3];
+    }
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(y) + i);
+  } else if (i < n) {
+    float a = ws[i];
+    for (int p = 1; p < parts; ++p) a += ws[(int64_t)p * n + i];
+    y[i] = a;
+  }
+}
+
 template <int F, bool RAGGED, int MI, int NB, int SETS = 1>
 static int launch_gemm_small(hipStream_t st, int grid, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
-                             int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit) {
+                             int M, int N, int K, int nchunk, int tiles_m, int ntiles, float g, int ksplit,
+                             float* ws = nullptr) {
   static Fp4LdsLimit lds_limit;
   constexpr int lds = SETS * gm_lds(MI, NB);
   lds_limit.ensure(reinterpret_cast<const void*>(&gemm_small_kernel<F, RAGGED, MI, NB, SETS>), lds);
   return fp4_launch(gemm_small_kernel<F, RAGGED, MI, NB, SETS>, dim3(grid), dim3(GM_THREADS * SETS), lds, st, q, s, x,
-                    y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
+                    y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit, ws);
 }
 
 template <int F, bool RAGGED, int NB>
 static int launch_gemm_small_mi(int band_rows, bool sets2, hipStream_t st, int grid, const uint8_t* q, const uint8_t* s,
                                 const uint16_t* x, float* y, int M, int N, int K, int nchunk, int tiles_m, int ntiles,
-                                float g, int ksplit) {
+                                float g, int ksplit, float* ws = nullptr) {
   if constexpr (NB == 1) {
     if (sets2 && band_rows == 128)
-      return launch_gemm_small<F, RAGGED, 4, 1, 2>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
+      return launch_gemm_small<F, RAGGED, 4, 1, 2>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit,
+                                                   ws);
   }
   if (band_rows == 128)
     return launch_gemm_small<F, RAGGED, 4, NB>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
@@ -793,9 +842,15 @@ static int launch_gemm_small_mi(int band_rows, bool sets2, hipStream_t st, int g
   return launch_gemm_small<F, RAGGED, 8, NB>(st, grid, q, s, x, y, M, N, K, nchunk, tiles_m, ntiles, g, ksplit);
 }
 
-template <int F, bool RAGGED>
-static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
-                          int N, int K, float g) {
+// Launch shape of a GEMM call (the rules below), shared by the launch and by the workspace query.
+struct GemmPlan {
+  int nchunk, tiles_m, ns, nbig, band_rows, rows_m, ksplit, parts;
+  int64_t Ut;
+  bool narrow, sets2;
+};
+
+static GemmPlan plan_gemm(int M, int N, int K, size_t ws_bytes) {
+  GemmPlan P{};
   const int nchunk = (K + CHUNK_K - 1) / CHUNK_K;
   const int tiles_m = (M + GM_BM - 1) / GM_BM;
   const int tiles_n = (N + GM_BN - 1) / GM_BN;
@@ -857,11 +912,61 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
   const bool sets2 = narrow && band_rows == 128 && sets_ok;  // tuning override FP4_GEMM_SETS=1: one set
   if (sets2 && ksplit) ksplit = (int64_t)M * N <= 23000LL * H ? 2 * (H / 4) : 0;
   if (sets2 && tu.gemm_split == 1 && ns == 0 && 2 * Ut <= cus && H >= 12) ksplit = 2 * (H / 4);  // tuning override
-  if (ksplit == 0 && band_rows == 0 && !narrow) {
+  // With a workspace, two-set grids that leave CUs idle split K into P parts instead (one round of Ut P
+  // workgroups, at least one chunk each, at most 16 parts): each part writes its g-scaled sum to a plane of
+  // the workspace and a second kernel adds the planes in a fixed order. P minimises a time model (ns):
+  // 700 per stage of a set, H / (2 P) stages, plus 2000 for the second launch, the planes' traffic
+  // ((P + 1) M N 4 bytes at 4 bytes per 1/1000 ns) and 400 per part. It replaces the two-part atomic split.
+  // Measured (NVFP4, P swept): 2560 x 9728 at M = 128 20.3-20.9 us for P = 8-12 against 42.3 us before,
+  // at M = 65 17.3-17.5 us for P = 8-10 against 29.4; 4096 x 4096 at M = 128 18.9 us at P = 4, 20.7 at 8.
+  int parts = 1;
+  if (sets2 && ns == 0 && tu.gemm_split != 0 && ws_bytes > 0) {
+    int pmax = (int)(cus / Ut);
+    if (pmax > nchunk) pmax = nchunk;
+    if (pmax > 16) pmax = 16;
+    double best = 700.0 * H / 2;
+    for (int p = 2; p <= pmax; ++p) {
+      if ((double)p * M * N * 4 > (double)ws_bytes) break;
+      const double t = 700.0 * H / (2.0 * p) + 2000.0 + (p + 1) * (double)M * N / 1000.0 + 400.0 * p;
+      if (t < best) {
+        best = t;
+        parts = p;
+      }
+    }
+    const int tp = tu.gemm_parts;  // tuning override: that many parts where they fit
+    if (tp >= 1 && tp <= pmax && (double)tp * M * N * 4 <= (double)ws_bytes) parts = tp;
+    if (parts > 1) ksplit = 0;
+  }
+  P.nchunk = nchunk;
+  P.tiles_m = tiles_m;
+  P.ns = ns;
+  P.nbig = nbig;
+  P.band_rows = band_rows;
+  P.rows_m = rows_m;
+  P.ksplit = ksplit;
+  P.parts = parts;
+  P.Ut = Ut;
+  P.narrow = narrow;
+  P.sets2 = sets2;
+  return P;
+}
+
+// Workspace bytes the K parts of a call would use (0: the call takes none).
+static size_t gemm_workspace_bytes(int M, int N, int K) {
+  const GemmPlan P = plan_gemm(M, N, K, ~(size_t)0);
+  return P.parts > 1 ? (size_t)P.parts * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+template <int F, bool RAGGED>
+static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M,
+                          int N, int K, float g, float* ws, size_t ws_bytes) {
+  const GemmPlan P = plan_gemm(M, N, K, ws ? ws_bytes : 0);
+  const int nchunk = P.nchunk, ksplit = P.ksplit;
+  if (ksplit == 0 && P.parts == 1 && P.band_rows == 0 && !P.narrow) {
     static Fp4LdsLimit lds_limit;
     lds_limit.ensure(reinterpret_cast<const void*>(&gemm_kernel<F, RAGGED>), GM_LDS);
-    return fp4_launch(gemm_kernel<F, RAGGED>, dim3(nbig + GM_SHORT_BANDS * ns), dim3(GM_THREADS), GM_LDS, st, q, s, x,
-                      y, M, N, K, nchunk, tiles_m, ns, nbig, g);
+    return fp4_launch(gemm_kernel<F, RAGGED>, dim3(P.nbig + GM_SHORT_BANDS * P.ns), dim3(GM_THREADS), GM_LDS, st, q,
+                      s, x, y, M, N, K, nchunk, P.tiles_m, P.ns, P.nbig, g);
   }
   if (ksplit) {
     const int64_t total = (int64_t)M * N;
@@ -870,53 +975,93 @@ static int launch_gemm_t(hipStream_t st, const uint8_t* q, const uint8_t* s, con
     const int rc = fp4_launch(gemm_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, y, total, n4);
     if (rc) return rc;
   }
-  const int grid = ksplit ? 2 * (int)Ut : (int)Ut;
-  if (narrow)
-    return launch_gemm_small_mi<F, RAGGED, 1>(band_rows, sets2, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut,
-                                              g, ksplit);
-  return launch_gemm_small_mi<F, RAGGED, 2>(band_rows, false, st, grid, q, s, x, y, M, N, K, nchunk, rows_m, (int)Ut, g,
-                                            ksplit);
+  if (P.parts > 1) {  // K parts into the workspace planes, then their sum into y
+    const int grid = P.parts * (int)P.Ut;
+    int rc = launch_gemm_small_mi<F, RAGGED, 1>(P.band_rows, true, st, grid, q, s, x, y, M, N, K, nchunk, P.rows_m,
+                                                (int)P.Ut, g, -P.parts, ws);
+    if (rc) return rc;
+    const int64_t total = (int64_t)M * N;
+    const int64_t n4 = (total % 4 == 0 && fp4_aligned(y, 16) && fp4_aligned(ws, 16)) ? total / 4 : 0;
+    const int64_t threads = n4 > 0 ? n4 : total;
+    return fp4_launch(gemm_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, ws, y, total, n4,
+                      P.parts);
+  }
+  const int grid = ksplit ? 2 * (int)P.Ut : (int)P.Ut;
+  if (P.narrow)
+    return launch_gemm_small_mi<F, RAGGED, 1>(P.band_rows, P.sets2, st, grid, q, s, x, y, M, N, K, nchunk, P.rows_m,
+                                              (int)P.Ut, g, ksplit);
+  return launch_gemm_small_mi<F, RAGGED, 2>(P.band_rows, false, st, grid, q, s, x, y, M, N, K, nchunk, P.rows_m,
+                                            (int)P.Ut, g, ksplit);
 }
 
 template <int F>
 static int launch_gemm(hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y, int M, int N,
-                       int K, float g) {
-  if (K % CHUNK_K == 0) return launch_gemm_t<F, false>(st, q, s, x, y, M, N, K, g);
-  return launch_gemm_t<F, true>(st, q, s, x, y, M, N, K, g);
+                       int K, float g, float* ws, size_t ws_bytes) {
+  if (K % CHUNK_K == 0) return launch_gemm_t<F, false>(st, q, s, x, y, M, N, K, g, ws, ws_bytes);
+  return launch_gemm_t<F, true>(st, q, s, x, y, M, N, K, g, ws, ws_bytes);
 }
 
 }  // namespace fp4
 
 using namespace fp4;
 
-extern "C" int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
-                          float global_scale, const void* x_bf16, float* y, void* stream) {
+// Arguments of a GEMM call: 0 or a negative status.
+static int check_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   if (!fp4_valid_format(fmt)) return -1;
   if (M < 0) return -2;
   if (fmt == Q4_0) return -4;  // its FP16-scaled weights are not exact in bf16; Q4_0 runs through the GEMV
   int rc = fp4_check_nk(fmt, N, K);
   if (rc) return rc;
-  if (M == 0) return 0;
   if (M > (1LL << 30)) return -4;
   if (K > (1LL << 22)) return -4;  // tile offsets are 32-bit buffer offsets: 256 rows x K x 2 bytes < 2^31
-  if (!q || !s || !x_bf16 || !y) return -1;
-  if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(x_bf16, 16) || !fp4_aligned(y, 4)) return -3;
   const int64_t grid = ((M + GM_BM - 1) / GM_BM) * ((N + GM_BN - 1) / GM_BN);
   if (grid > 0x7fffffffLL) return -4;
+  return 0;
+}
+
+extern "C" int64_t w4a16_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  const int rc = check_gemm(fmt, M, N, K);
+  if (rc) return rc;
+  if (M == 0) return 0;
+  return (int64_t)gemm_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+extern "C" int w4a16_gemm_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                             float global_scale, const void* x_bf16, float* y, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const int rc = check_gemm(fmt, M, N, K);
+  if (rc) return rc;
+  if (M == 0) return 0;
+  if (!q || !s || !x_bf16 || !y) return -1;
+  if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(x_bf16, 16) || !fp4_aligned(y, 4)) return -3;
+  if (workspace && !fp4_aligned(workspace, 16)) return -3;
   hipStream_t st = (hipStream_t)stream;
   const uint8_t* qq = (const uint8_t*)q;
   const uint8_t* ss = (const uint8_t*)s;
   const uint16_t* xx = (const uint16_t*)x_bf16;
+  float* ws = (float*)workspace;
+  const size_t wb = workspace ? workspace_bytes : 0;
   switch (fmt) {
-    case NVFP4: return launch_gemm<NVFP4>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale);
-    case DUAL:  return launch_gemm<DUAL>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale);
-    default:    return launch_gemm<FAST>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale);
+    case NVFP4: return launch_gemm<NVFP4>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale, ws, wb);
+    case DUAL:  return launch_gemm<DUAL>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale, ws, wb);
+    default:    return launch_gemm<FAST>(st, qq, ss, xx, y, (int)M, (int)N, (int)K, global_scale, ws, wb);
   }
+}
+
+extern "C" int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                          float global_scale, const void* x_bf16, float* y, void* stream) {
+  return w4a16_gemm_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, nullptr, 0, stream);
+}
+
+extern "C" int w4a16_matmul_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                               float global_scale, const void* x_bf16, float* y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (M >= 0 && M <= 16) return w4a16_gemv(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
+  if (M <= 64) return w4a16_midm(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
+  return w4a16_gemm_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, workspace, workspace_bytes, stream);
 }
 
 extern "C" int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                             float global_scale, const void* x_bf16, float* y, void* stream) {
-  if (M >= 0 && M <= 16) return w4a16_gemv(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
-  if (M <= 64) return w4a16_midm(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
-  return w4a16_gemm(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
+  return w4a16_matmul_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, nullptr, 0, stream);
 }

@@ -54,6 +54,7 @@ struct Fp4Tuning {
   int quant_exhaustive;  // FP4_QUANT_EXHAUSTIVE=1: the ROCmFP4 packer scores every candidate (no pruning)
   int one_batch;       // FP4_ONE_BATCH=0: no one-batch GEMV for 2 <= M <= 8 (batch loop, or mid-M kernel from M = 5)
   int gemm_sets;       // FP4_GEMM_SETS=1: one set of 4 waves per workgroup on 128-row small-grid tiles too
+  int gemm_parts;      // FP4_GEMM_PARTS: K parts of a two-set grid with a workspace, where they fit (1: none)
 };
 const Fp4Tuning& fp4_tuning();
 

@@ -32,8 +32,8 @@
  *    raised), filled on first use and never changed afterwards; the tuning overrides read
  *    once from the environment at the first call (FP4_GEMV_WAVES, FP4_GEMV_U, FP4_GEMV_ONE,
  *    FP4_GEMV_RING, FP4_MIDM_WAVES, FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS,
- *    FP4_GEMM_NARROW, FP4_QUANT_EXHAUSTIVE, FP4_ONE_BATCH; none
- *    set by default); and one 4-byte device word per GPU, a static device variable, that
+ *    FP4_GEMM_NARROW, FP4_QUANT_EXHAUSTIVE, FP4_ONE_BATCH, FP4_GEMM_SETS, FP4_GEMM_PARTS;
+ *    none set by default); and one 4-byte device word per GPU, a static device variable, that
  *    fp4_pack_layout uses when asked to validate (serialised by a per-device host lock).
  *    Apart from that word, which only the validation path touches, concurrent calls on
  *    different streams share no mutable state.
@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP4W4A16_ABI_VERSION 2
+#define FP4W4A16_ABI_VERSION 3
 
 /* Weight formats. */
 enum {
@@ -173,20 +173,47 @@ int w4a16_gemv_batched(int fmt, int64_t M, int count, const fp4_gemv_item* items
  * Prefill-shaped product, any M >= 1, intended for M >= 64 (a prompt of many tokens against
  * the same packed weights; W as defined at the top: EdgeRock-4B-NVFP4 card, description;
  * ROCmFP4 design page, sections 01 and 02, and the technical-boundaries note that the levels
- * are exact integers, which lets level*scale be exact in bf16): stages x tiles
- * and packed weight tiles, dequantizes each weight tile once into LDS as exact bf16
- * level*scale, contracts with bf16 MFMA in FP32 and multiplies by g in the epilogue.
- * When y has few 256x256 tiles (at most a quarter of the device's compute units) and K spans
- * at least 6 chunks of 128, K is split in two: the call enqueues a kernel that zeroes y, then
- * the product, whose two halves add their g-scaled sums into y with FP32 atomics. Two addends
+ * are exact integers, which lets level*scale be exact in bf16): stages x tiles and packed
+ * weight tiles in LDS, decodes each weight once per workgroup into exact bf16 level*scale
+ * MFMA operands, contracts with bf16 MFMA in FP32 and multiplies by g in the epilogue. For
+ * M <= 128 (192) the tiles may be 128 (192) rows high; 128-row tiles of small grids run two
+ * wave sets over alternate stages of K whose two sums are added in a fixed order.
+ * When y has few tiles (at most half the device's compute units) and K spans at least 6
+ * chunks of 128, K may be split in two: the call enqueues a kernel that zeroes y, then the
+ * product, whose two halves add their g-scaled sums into y with FP32 atomics. Two addends
  * onto zero give the same sum in either order, so the result is still bit-reproducible; it
- * differs from the whole-K sum only by rounding. Both kernels run on `stream`. For M <= 128 (192)
- * the tiles are 128 (192) rows high: same products, same order, same bits as 256-row tiles.
+ * differs from the whole-K sum only by rounding. Both kernels run on `stream`.
  * Q4_0 gives FP4_ERR_UNSUPPORTED (its level*scale is not exact in bf16). Other errors:
  * FP4_ERR_ARG, FP4_ERR_SHAPE, FP4_ERR_UNSUPPORTED (K > 2^22), FP4_ERR_ALIGN, FP4_ERR_HIP.
+ * Equivalent to w4a16_gemm_ws with no workspace.
  */
 int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                float global_scale, const void* x_bf16, float* y, void* stream);
+
+/*
+ * w4a16_gemm with a caller workspace (device memory, 16-byte aligned, owned by the caller and
+ * used only while the call's kernels run on `stream`; it needs no initial contents). Grids that
+ * leave compute units idle (the small-N prefill shapes, e.g. a 2560 x 9728 projection at
+ * M = 65..256: the band between the decode and prefill shapes of the Nanbeige4.2-3B-NVFP4A16
+ * card's serving notes) split K into P parts (2 <= P <= 16) instead of the two-part atomic split:
+ * each part writes its g-scaled sum to plane p of the workspace (P planes of M x N floats) and a
+ * second kernel on `stream` adds the planes into y in the order p = 0 .. P - 1, so the result is
+ * bit-reproducible and differs from the whole-K sum only by rounding. workspace_bytes at least
+ * w4a16_gemm_workspace_bytes() gives the split the launch rules choose; a smaller workspace gives
+ * the largest split that fits (possibly none, as w4a16_gemm); NULL means none. Errors as
+ * w4a16_gemm, and FP4_ERR_ALIGN for a misaligned workspace. Calls that share a workspace must be
+ * ordered on one stream.
+ */
+int w4a16_gemm_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                  float global_scale, const void* x_bf16, float* y, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes that w4a16_gemm_ws would use for this shape on the current device (0 when it
+ * would not split K into parts), or a negative status for arguments w4a16_gemm would reject
+ * (pointers aside). At most 64 KiB per compute unit of the device.
+ */
+int64_t w4a16_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /*
  * Mid-sized M, 1 <= M <= 64 (the band between the decode and prefill shapes,
@@ -199,9 +226,12 @@ int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const vo
                float global_scale, const void* x_bf16, float* y, void* stream);
 
 /* Dispatch on M: M <= 16 -> w4a16_gemv, 17 <= M <= 64 -> w4a16_midm, otherwise
- * w4a16_gemm. */
+ * w4a16_gemm (w4a16_matmul_ws: w4a16_gemm_ws with the workspace; the smaller M take none). */
 int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                  float global_scale, const void* x_bf16, float* y, void* stream);
+int w4a16_matmul_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                    float global_scale, const void* x_bf16, float* y, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * Dequantize the kernel layout to FP32 W[N][K] (the pages' dequant-at-load, EdgeRock card,

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert fp4.fp4_abi_version() == 2
+    assert fp4.fp4_abi_version() == 3
     for st in (OK, ARG, SHAPE, ALIGN, UNSUP, INVALID_SCALE, HIP, 12345):
         assert isinstance(fp4.fp4_status_string(st), str) and fp4.fp4_status_string(st)
     # every status has its own text
@@ -46,7 +46,7 @@ def test_header_declares_status_codes():
     for name, value in (("FP4_OK", 0), ("FP4_ERR_ARG", -1), ("FP4_ERR_SHAPE", -2), ("FP4_ERR_ALIGN", -3),
                         ("FP4_ERR_UNSUPPORTED", -4), ("FP4_ERR_INVALID_SCALE", -5), ("FP4_ERR_HIP", -6)):
         assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
-    assert re.search(r"FP4W4A16_ABI_VERSION\s+2\b", text)
+    assert re.search(r"FP4W4A16_ABI_VERSION\s+3\b", text)
     assert re.search(r"int fp4_pack_layout\([^)]*int validate, void\* stream\)", text)
 
 
@@ -110,6 +110,46 @@ def test_product_argument_errors(fn):
         assert call(M=17) == UNSUP
     if fn == "w4a16_midm":
         assert call(M=65) == UNSUP
+
+
+@pytest.mark.parametrize("fn", ["w4a16_gemm_ws", "w4a16_matmul_ws"])
+def test_workspace_product_argument_errors(fn):
+    f = getattr(_raw(), fn)
+    M = 128  # the prefill path (w4a16_matmul_ws dispatches to it above M = 64)
+
+    def call(fmt=NVFP4, K=64, x=FAKE, ws=FAKE, wsb=1 << 20):
+        return f(fmt, M, 16, K, FAKE, FAKE, 1.0, x, FAKE, ws, wsb, None)
+
+    assert call(fmt=7) == ARG
+    assert call(K=40) == SHAPE
+    assert call(x=FAKE + 8) == ALIGN
+    assert call(ws=FAKE + 4) == ALIGN          # the workspace must be 16-byte aligned
+    assert call(fmt=Q4_0) == UNSUP
+    assert f(NVFP4, 0, 16, 64, None, None, 1.0, None, None, None, 0, None) == OK
+
+
+def test_workspace_bytes_query():
+    r = _raw()
+    q = r.w4a16_gemm_workspace_bytes
+    assert q(7, 128, 2560, 9728) == ARG
+    assert q(Q4_0, 128, 2560, 9728) == UNSUP
+    assert q(NVFP4, 128, 2560, 40) == SHAPE
+    assert q(NVFP4, -1, 2560, 9728) == SHAPE
+    assert q(NVFP4, 0, 2560, 9728) == 0
+    cus = 256  # without a GPU the library plans for a 256-CU device
+    # the prefill shape fills the device: no K parts
+    assert q(NVFP4, 2048, 14336, 4096) == 0
+    # a 2560 x 9728 projection at M = 128 has 20 tiles of 128 x 128: the split rule takes 9 K parts (180 CUs)
+    assert q(NVFP4, 128, 2560, 9728) == 9 * 128 * 2560 * 4
+    # the parts' planes never exceed 64 KiB per CU (one round of 128 x 128 tiles)
+    worst = 0
+    for m in (65, 96, 128, 160, 192, 256, 300, 512):
+        for n in (128, 1000, 2560, 4096, 9728, 14336):
+            for k in (128, 1024, 2560, 4096, 9728):
+                b = q(DUAL, m, n, k)
+                assert b >= 0 and b % (4 * m * n) == 0
+                worst = max(worst, b)
+    assert 0 < worst <= cus * 64 * 1024
 
 
 @pytest.mark.parametrize("validate", [0, 1])

@@ -482,10 +482,10 @@ def test_gemm_short_tiles(tmp_path):
 
 
 def test_gemm_split_k(tmp_path):
-    # Small grids (at most half as many tiles as CUs, and not too many outputs) split K in two parts that
-    # add into the zeroed y: against the
-    # oracle, repeatable to the bit (two addends onto zero give the same sum in either order), and the
-    # whole-K launch (FP4_GEMM_SPLIT=0, in a child process) within the tolerance too.
+    # Without a workspace (the C entry point w4a16_gemm), small grids (at most half as many tiles as CUs,
+    # and not too many outputs) split K in two parts that add into the zeroed y: against the oracle,
+    # repeatable to the bit (two addends onto zero give the same sum in either order), and the whole-K
+    # launch (FP4_GEMM_SPLIT=0, in a child process) within the tolerance too.
     cases = {}
     for fmt in gc.FMTS:
         for (m, n, k) in [(100, 600, 1152), (256, 512, 2048), (257, 37, 4000)]:
@@ -497,7 +497,7 @@ def test_gemm_split_k(tmp_path):
             ys = []
             for _ in range(3):
                 y = torch.full((m, n), float("nan"), device="cuda")
-                fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+                fp4.w4a16_gemm_noworkspace(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
                 ys.append(y)
             torch.cuda.synchronize()
             gc.check_product(fmt, packed, x_bits, ys[0], label=f"gemm-split {fmt} M={m} {n}x{k}")
@@ -569,8 +569,9 @@ def test_gemm_two_wave_sets(tmp_path):
     # 128-row small-grid tiles run two sets of 4 waves over alternate stages, set 1's sums added to set 0's at
     # the end (also two 128-row bands for 128 < M <= 192). K from 2 stages (one per set) up, ragged K = 672,
     # split and whole K: against the oracle as launched, bitwise repeatable, and against the oracle again with
-    # one set (FP4_GEMM_SETS=1), with K forced whole (FP4_GEMM_SPLIT=0) and with the split forced wherever the
-    # grid allows (FP4_GEMM_SPLIT=1).
+    # one set (FP4_GEMM_SETS=1), with K forced whole (FP4_GEMM_SPLIT=0), with the two-part atomic split
+    # forced wherever the grid allows (FP4_GEMM_SPLIT=1, FP4_GEMM_PARTS=1) and with two K parts in the
+    # workspace (FP4_GEMM_PARTS=2).
     shapes = [(65, 1000, 128), (65, 1000, 256), (100, 600, 1152), (128, 2304, 1024), (256, 600, 672),
               (200, 1000, 640), (97, 14336, 256), (160, 2304, 1152), (192, 1000, 384)]
     cases = {}
@@ -594,10 +595,45 @@ def test_gemm_two_wave_sets(tmp_path):
             name = f"{fmt}_{m}_{n}_{k}"
             gc.save_case(tmp_path, name, "gemm", fmt, m, n, k, pw, x_bits)
             cases[name] = (fmt, packed, x_bits, cols)
-    for env in ({"FP4_GEMM_SETS": "1"}, {"FP4_GEMM_SPLIT": "0"}, {"FP4_GEMM_SPLIT": "1"}):
+    for env in ({"FP4_GEMM_SETS": "1"}, {"FP4_GEMM_SPLIT": "0"}, {"FP4_GEMM_SPLIT": "1", "FP4_GEMM_PARTS": "1"},
+                {"FP4_GEMM_PARTS": "2"}):
         ys = gc.run_variant(tmp_path, env)
         for name, (fmt, packed, x_bits, cols) in cases.items():
             gc.check_product(fmt, packed, x_bits, torch.from_numpy(ys[name]), cols=cols, label=f"{env} {name}")
+
+
+def test_gemm_k_parts():
+    # Grids that leave CUs idle (small N, long K) split K into P parts written to a workspace and added in a
+    # fixed order by a second kernel: the 2560 x 9728 projection at M = 65, 128 and 200 (20 or 40 tiles), the
+    # 9728 x 2560 one at M = 96, 4096 x 4096 at M = 128 and a ragged K. Against the oracle on sampled columns
+    # with the workspace the library asks for, bitwise repeatable; with a workspace for two planes only (the
+    # largest split that fits), and with none (the C entry point w4a16_gemm), against the oracle too.
+    shapes = [(65, 2560, 9728), (128, 2560, 9728), (200, 2560, 9728), (96, 9728, 2560), (128, 4096, 4096),
+              (100, 1000, 4000)]
+    for fmt in gc.FMTS:
+        for (m, n, k) in shapes:
+            _announce("gemm-k-parts", fmt, m, n, k)
+            assert fp4.w4a16_gemm_workspace_bytes(fmt, m, n, k) > 2 * m * n * 4   # more than two parts
+            w, packed = gc.make_case(fmt, n, k, cfg=77, mat=k + m)
+            del w
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(m, k, cfg=77, mat=k + m)
+            x = gc.x_tensor(x_bits)
+            cols = np.unique(np.concatenate([[0, 127, 128, n - 1], np.linspace(0, n - 1, 24).astype(int)]))
+            ys = []
+            for _ in range(2):
+                y = torch.full((m, n), float("nan"), device="cuda")
+                fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+                ys.append(y)
+            small = torch.empty(2 * m * n * 4, dtype=torch.uint8, device="cuda")
+            y2 = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y2, workspace=small)
+            y0 = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_gemm_noworkspace(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y0)
+            torch.cuda.synchronize()
+            assert torch.equal(ys[0], ys[1])
+            for lab, yy in (("parts", ys[0]), ("two planes", y2), ("no workspace", y0)):
+                gc.check_product(fmt, packed, x_bits, yy, cols=cols, label=f"gemm-k-parts {lab} {fmt} M={m} {n}x{k}")
 
 
 def test_gemm_small_grid_stage_counts():
@@ -622,22 +658,27 @@ def test_gemm_small_grid_stage_counts():
             gc.check_product(fmt, packed, x_bits, y, cols=cols, label=f"gemm-stages {fmt} M={m} {n}x{k}")
 
 
-def test_gemm_split_in_graph():
-    # The split-K GEMM enqueues a zero-fill kernel and the product: captured in a graph (on torch's capture
-    # stream) and replayed several times, with eager work and synchronizations between the replays, every
-    # replay gives the eager result bit for bit.
+@pytest.mark.parametrize("entry", ["w4a16_gemm_noworkspace", "w4a16_gemm"])
+def test_gemm_split_in_graph(entry):
+    # The split-K GEMM enqueues a zero-fill kernel and the product (no workspace), or the K parts into a
+    # workspace (allocated by the binding inside the capture) and the kernel that adds them: captured in a
+    # graph (on torch's capture stream) and replayed several times, with eager work and synchronizations
+    # between the replays, every replay gives the eager result bit for bit.
     fmt, m, n, k = "rocmfp4_fast", 128, 512, 2048
-    _announce("gemm-split-graph", fmt, m, n, k)
+    _announce("gemm-split-graph", entry, fmt, m, n, k)
+    fn = getattr(fp4, entry)
     w, packed = gc.make_case(fmt, n, k, cfg=71)
     pw = gc.upload(fmt, n, k, packed)
     x = gc.x_tensor(synth.activations(m, k, cfg=71))
+    if entry == "w4a16_gemm":
+        assert fp4.w4a16_gemm_workspace_bytes(fmt, m, n, k) > 0   # the K-parts path
     y_eager = torch.full((m, n), float("nan"), device="cuda")
-    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_eager)
+    fn(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_eager)
     torch.cuda.synchronize()
     y = torch.full((m, n), float("nan"), device="cuda")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+        fn(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
     for rep in range(4):
         y.fill_(float("nan") if rep % 2 else 7.0)
         junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
