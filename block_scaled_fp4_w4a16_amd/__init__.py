@@ -50,6 +50,7 @@ _SIGS = {
     "w4a16_gemm_ws": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p, ctypes.c_size_t, _p]),
     "w4a16_matmul_ws": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p, ctypes.c_size_t, _p]),
     "w4a16_gemm_workspace_bytes": (_i64, [_c, _i64, _i64, _i64]),
+    "w4a16_gemm_noalloc": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "fp4_dequant_f32": (_c, [_c, _i64, _i64, _p, _p, _f, _p, _p]),
     "fp4_quantize_nvfp4": (_c, [_i64, _i64, _p, _p, _p, _p, _p]),
     "fp4_quantize_rocmfp4": (_c, [_c, _i64, _i64, _p, _p, _p, _p]),
@@ -256,6 +257,10 @@ def w4a16_gemm(fmt, M, N, K, q, s, global_scale, x, y, stream=None, workspace=No
 def w4a16_gemm_noworkspace(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
     """The C entry point w4a16_gemm itself (no workspace: at most the two-part atomic split)."""
     _product("w4a16_gemm", fmt, M, N, K, q, s, global_scale, x, y, stream)
+
+
+def w4a16_gemm_noalloc(fmt, M, N, K, q, s, global_scale, x, y, stream=None):
+    _product("w4a16_gemm_noalloc", fmt, M, N, K, q, s, global_scale, x, y, stream)
 
 
 def w4a16_midm(fmt, M, N, K, q, s, global_scale, x, y, stream=None):

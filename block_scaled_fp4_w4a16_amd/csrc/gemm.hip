@@ -1065,3 +1065,40 @@ extern "C" int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void
                             float global_scale, const void* x_bf16, float* y, void* stream) {
   return w4a16_matmul_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, nullptr, 0, stream);
 }
+
+// The GEMM without a caller workspace and without allocating: its K-part planes live in `scratch`, a
+// file-scope device array of FP4_GEMM_SCRATCH_BYTES on every GPU the library runs on. The K parts of one
+// call fill at most one round of 128 x 128 tiles (parts x tiles <= CUs), so their planes hold at most
+// 16384 floats per CU: 16 MiB covers every split on a 256-CU device. In host code `scratch` names a host
+// stand-in, not device memory: the device address comes from hipGetSymbolAddress, taken once per device
+// (on the first call there, with that device current) and kept per device.
+static __device__ __align__(256) float scratch[FP4_GEMM_SCRATCH_BYTES / sizeof(float)];
+static std::atomic<float*> scratch_addr[64];
+
+static int scratch_of_current_device(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -6;
+  float* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return -6;
+    p = static_cast<float*>(a);
+    scratch_addr[dev].store(p, std::memory_order_release);  // a racing first call stores the same address
+  }
+  *out = p;
+  return 0;
+}
+
+extern "C" int w4a16_gemm_noalloc(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                                  float global_scale, const void* x_bf16, float* y, void* stream) {
+  const int rc = check_gemm(fmt, M, N, K);
+  if (rc) return rc;
+  if (M == 0) return 0;
+  if (!q || !s || !x_bf16 || !y) return -1;
+  if (!fp4_aligned(q, 16) || !fp4_aligned(s, 16) || !fp4_aligned(x_bf16, 16) || !fp4_aligned(y, 4)) return -3;
+  if (gemm_workspace_bytes((int)M, (int)N, (int)K) > FP4_GEMM_SCRATCH_BYTES) return -4;
+  float* ws = nullptr;
+  const int rs = scratch_of_current_device(&ws);
+  if (rs) return rs;
+  return w4a16_gemm_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, ws, FP4_GEMM_SCRATCH_BYTES, stream);
+}

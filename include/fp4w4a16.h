@@ -33,10 +33,11 @@
  *    once from the environment at the first call (FP4_GEMV_WAVES, FP4_GEMV_U, FP4_GEMV_ONE,
  *    FP4_GEMV_RING, FP4_MIDM_WAVES, FP4_GEMM_SHORT, FP4_GEMM_SPLIT, FP4_GEMM_BAND_ROWS,
  *    FP4_GEMM_NARROW, FP4_QUANT_EXHAUSTIVE, FP4_ONE_BATCH, FP4_GEMM_SETS, FP4_GEMM_PARTS;
- *    none set by default); and one 4-byte device word per GPU, a static device variable, that
- *    fp4_pack_layout uses when asked to validate (serialised by a per-device host lock).
- *    Apart from that word, which only the validation path touches, concurrent calls on
- *    different streams share no mutable state.
+ *    none set by default); one 4-byte device word per GPU, a static device variable, that
+ *    fp4_pack_layout uses when asked to validate (serialised by a per-device host lock); and
+ *    the static device array of w4a16_gemm_noalloc (FP4_GEMM_SCRATCH_BYTES per GPU), which
+ *    only that entry point touches. Apart from those two, concurrent calls on different
+ *    streams share no mutable state.
  *  - Shapes: W is N x K (N outputs, K inputs); x is M x K bf16 row-major; y is M x N
  *    fp32 row-major. K must be a multiple of 16 (NVFP4) or 32 (ROCmFP4). M = 0 is a
  *    no-op. x and the planes must be 16-byte aligned; y must be 4-byte aligned and must
@@ -214,6 +215,21 @@ int w4a16_gemm_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const
  * (pointers aside). At most 64 KiB per compute unit of the device.
  */
 int64_t w4a16_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+
+/*
+ * For callers that cannot allocate device memory (code under graph capture, serving loops,
+ * harnesses that forbid allocation): w4a16_gemm_ws with the workspace taken from a static device
+ * array of FP4_GEMM_SCRATCH_BYTES on each GPU (its address is looked up once per device, on the
+ * first call there; no allocation, ever). Outputs equal w4a16_gemm_ws's with a workspace of
+ * w4a16_gemm_workspace_bytes(). Shapes whose split would need more than FP4_GEMM_SCRATCH_BYTES
+ * (only possible on devices with more than 256 compute units) give FP4_ERR_UNSUPPORTED and
+ * nothing runs. Every call on a GPU uses that GPU's one array: calls that overlap in time on one
+ * GPU (on different streams, or from different threads without ordering) race on it and may give
+ * wrong results; order them on one stream. Other errors as w4a16_gemm.
+ */
+#define FP4_GEMM_SCRATCH_BYTES (16u << 20)
+int w4a16_gemm_noalloc(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
+                       float global_scale, const void* x_bf16, float* y, void* stream);
 
 /*
  * Mid-sized M, 1 <= M <= 64 (the band between the decode and prefill shapes,

@@ -76,7 +76,7 @@ def _raw():
     return fp4.lib()
 
 
-@pytest.mark.parametrize("fn", ["w4a16_gemv", "w4a16_midm", "w4a16_gemm", "w4a16_matmul"])
+@pytest.mark.parametrize("fn", ["w4a16_gemv", "w4a16_midm", "w4a16_gemm", "w4a16_matmul", "w4a16_gemm_noalloc"])
 def test_product_argument_errors(fn):
     f = getattr(_raw(), fn)
     good = dict(fmt=NVFP4, M=1, N=16, K=64, q=FAKE, s=FAKE, g=1.0, x=FAKE, y=FAKE, st=None)
@@ -88,7 +88,7 @@ def test_product_argument_errors(fn):
     assert call(fmt=7) == ARG
     assert call(fmt=0) == ARG
     assert call(fmt=5) == ARG
-    if fn in ("w4a16_midm", "w4a16_gemm"):
+    if fn in ("w4a16_midm", "w4a16_gemm", "w4a16_gemm_noalloc"):
         assert call(fmt=Q4_0) == UNSUP          # Q4_0 runs through the GEMV only
     else:
         assert call(fmt=Q4_0, K=48) == SHAPE   # Q4_0 needs K % 32 == 0
@@ -141,7 +141,8 @@ def test_workspace_bytes_query():
     assert q(NVFP4, 2048, 14336, 4096) == 0
     # a 2560 x 9728 projection at M = 128 has 20 tiles of 128 x 128: the split rule takes 9 K parts (180 CUs)
     assert q(NVFP4, 128, 2560, 9728) == 9 * 128 * 2560 * 4
-    # the parts' planes never exceed 64 KiB per CU (one round of 128 x 128 tiles)
+    # the parts' planes never exceed 64 KiB per CU (one round of 128 x 128 tiles), so the 16 MiB static
+    # scratch of the no-allocation entry point covers every split on a 256-CU device
     worst = 0
     for m in (65, 96, 128, 160, 192, 256, 300, 512):
         for n in (128, 1000, 2560, 4096, 9728, 14336):
