@@ -241,11 +241,12 @@ def bench_gemv(fp4, torch, synth, name: str, steps: int, warmup: int, reps: int,
                 y=y0.cpu().numpy(), x_bits=x_bits, w_np=w_np, global_scale=pw.global_scale)
 
 
-def bench_gemm(fp4, torch, synth, fmt: str, m: int, steps: int, warmup: int, reps: int, probes, pw=None):
-    n, k = synth.WORKLOADS[4]["shapes"][0]
+def bench_gemm(fp4, torch, synth, fmt: str, m: int, steps: int, warmup: int, reps: int, probes, pw=None, cfg=4,
+               mat=0):
+    n, k = synth.WORKLOADS[cfg]["shapes"][mat]
     if pw is None:
-        pw = pack_on_gpu(fp4, torch, fmt, synth.workload_weights(4, 0))
-    x_bits = synth.workload_activations(4, 0, m)
+        pw = pack_on_gpu(fp4, torch, fmt, synth.workload_weights(cfg, mat))
+    x_bits = synth.workload_activations(cfg, mat, m)
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
 
@@ -259,7 +260,7 @@ def bench_gemm(fp4, torch, synth, fmt: str, m: int, steps: int, warmup: int, rep
     torch.cuda.synchronize()
     flops = 2.0 * m * n * k
     return dict(fmt=fmt, m=m, n=n, k=k, t=t, tflops=flops / t["median_s"] / 1e12, pw=pw, x_bits=x_bits,
-                y=y.cpu().numpy())
+                y=y.cpu().numpy(), ws_bytes=fp4.w4a16_gemm_workspace_bytes(fmt, m, n, k))
 
 
 def bench_read_probe(torch, probes, nbytes: int, steps: int, warmup: int, reps: int):
@@ -549,7 +550,7 @@ def main():
             log(f"gemm {fmt} M=2048: {gemm[fmt]['t']['median_s'] * 1e6:.1f} us/launch median, "
                 f"{gemm[fmt]['tflops']:.1f} TFLOP/s "
                 f"({time.time() - t0:.1f}s)")
-    gemm_small = {}
+    gemm_small, gemm_small_n = {}, {}
     if "gemm_small" in only:
         t0 = time.time()
         pw = gemm["rocmfp4_fast"]["pw"] if "rocmfp4_fast" in gemm else None
@@ -557,10 +558,13 @@ def main():
             r = bench_gemm(fp4, torch, synth, "rocmfp4_fast", m, 200, 100, reps, probes, pw=pw)
             pw = r["pw"]
             gemm_small[m] = r
+        # small N and long K (the 2560 x 9728 down projection of the verify workload): K parts in a workspace
+        r = bench_gemm(fp4, torch, synth, "rocmfp4_fast", 128, 200, 100, reps, probes, cfg=3, mat=1)
+        gemm_small_n = {128: r}
         log(f"gemm FAST small M ({time.time() - t0:.1f}s)")
     for r in gemm.values():
         r.pop("pw", None)
-    for r in gemm_small.values():
+    for r in list(gemm_small.values()) + list(gemm_small_n.values()):
         r.pop("pw", None)
 
     sw = None
@@ -598,6 +602,12 @@ def main():
                 cpu[f"rocmfp4_fast_prefill_m{m}"] = oracle_sample("rocmfp4_fast", w_pref, sample_rows(r["n"], 64),
                                                                   r["x_bits"], r["y"], threads, budget, time_it=False)
             del w_pref
+            if gemm_small_n:
+                w_down = synth.workload_weights(3, 1)
+                for m, r in gemm_small_n.items():
+                    cpu[f"rocmfp4_fast_down_m{m}"] = oracle_sample("rocmfp4_fast", w_down, sample_rows(r["n"], 64),
+                                                                   r["x_bits"], r["y"], threads, budget, time_it=False)
+                del w_down
         if sw is not None:
             layer = synth.DECODE_4B_LAYER
             for mode in ("grouped", "device_list"):
@@ -698,6 +708,13 @@ def main():
                 "TFLOP/s": gated(round(r["tflops"], 2), f"rocmfp4_fast_prefill_m{m}"),
                 "frac": round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4), "timing": timing_fields(r["t"]),
                 "parity": parity_of(f"rocmfp4_fast_prefill_m{m}")} for m, r in gemm_small.items()}
+    if gemm_small_n:
+        line["gemm_small_n"] = {
+            f"rocmfp4_fast_down_m{m}_k{r['k']}_n{r['n']}": {
+                "TFLOP/s": gated(round(r["tflops"], 2), f"rocmfp4_fast_down_m{m}"),
+                "frac": round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4), "timing": timing_fields(r["t"]),
+                "k_parts": r["ws_bytes"] // (4 * m * r["n"]) if r["ws_bytes"] else 1,
+                "parity": parity_of(f"rocmfp4_fast_down_m{m}")} for m, r in gemm_small_n.items()}
     if sw:
         g = sw["grouped"]
         gbs = sw["bytes"] / g["median_s"] / 1e9
