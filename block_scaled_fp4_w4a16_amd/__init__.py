@@ -50,6 +50,7 @@ _SIGS = {
     "w4a16_gemm_ws": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p, ctypes.c_size_t, _p]),
     "w4a16_matmul_ws": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p, ctypes.c_size_t, _p]),
     "w4a16_gemm_workspace_bytes": (_i64, [_c, _i64, _i64, _i64]),
+    "w4a16_matmul_workspace_bytes": (_i64, [_c, _i64, _i64, _i64]),
     "w4a16_gemm_noalloc": (_c, [_c, _i64, _i64, _i64, _p, _p, _f, _p, _p, _p]),
     "fp4_dequant_f32": (_c, [_c, _i64, _i64, _p, _p, _f, _p, _p]),
     "fp4_quantize_nvfp4": (_c, [_i64, _i64, _p, _p, _p, _p, _p]),
@@ -215,12 +216,21 @@ def w4a16_gemv_batched(fmt, M, items, stream=None):
         _check(lib().w4a16_gemv_batched(f, M, len(items), arr, _stream(stream)), "w4a16_gemv_batched")
 
 
+def _workspace_bytes(name, fmt, M, N, K, device=None) -> int:
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        n = int(getattr(lib(), name)(_fmt(fmt), M, N, K))
+    _check(n if n < 0 else 0, name)
+    return n
+
+
 def w4a16_gemm_workspace_bytes(fmt, M, N, K, device=None) -> int:
     """Workspace bytes w4a16_gemm_ws would use for this shape on `device` (default: the current one)."""
-    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
-        n = int(lib().w4a16_gemm_workspace_bytes(_fmt(fmt), M, N, K))
-    _check(n if n < 0 else 0, "w4a16_gemm_workspace_bytes")
-    return n
+    return _workspace_bytes("w4a16_gemm_workspace_bytes", fmt, M, N, K, device)
+
+
+def w4a16_matmul_workspace_bytes(fmt, M, N, K, device=None) -> int:
+    """Workspace bytes w4a16_matmul_ws can use for this shape on `device` (0: it takes none)."""
+    return _workspace_bytes("w4a16_matmul_workspace_bytes", fmt, M, N, K, device)
 
 
 def _product_ws(name, fmt, M, N, K, q, s, global_scale, x, y, stream, workspace):
@@ -236,8 +246,9 @@ def _product_ws(name, fmt, M, N, K, q, s, global_scale, x, y, stream, workspace)
         _check_planes(f, N, K, q, s)
     with torch.cuda.device(dev):
         st = _stream(stream)
-        if workspace is None and M > 64:
-            nbytes = w4a16_gemm_workspace_bytes(f, M, N, K, dev)
+        if workspace is None and M > 0:
+            query = "w4a16_gemm_workspace_bytes" if name == "w4a16_gemm_ws" else "w4a16_matmul_workspace_bytes"
+            nbytes = _workspace_bytes(query, f, M, N, K, dev)
             if nbytes > 0:
                 workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
                 if stream is not None:

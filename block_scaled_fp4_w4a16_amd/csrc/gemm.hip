@@ -1053,11 +1053,33 @@ extern "C" int w4a16_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void* 
   return w4a16_gemm_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, nullptr, 0, stream);
 }
 
+// 48 <= M <= 64 on matrices of at least 20 M weights: with K parts in a workspace the GEMM beats the mid-M
+// kernel (NVFP4, one run each: 2560 x 9728 at M = 48 16.2 against 17.6 us, M = 64 17.2 against 22.2; 9728 x
+// 2560 at M = 64 16.4 against 19.6; 14336 x 4096 at M = 64 21.6 against 35.6), while on 4096 x 4096 the mid-M
+// kernel stays faster (M = 64 12.1 against 14.9 us).
+static bool matmul_gemm_band(int fmt, int64_t M, int64_t N, int64_t K) {
+  return M >= 48 && M <= 64 && fmt != Q4_0 && N * K >= (20LL << 20);
+}
+
+extern "C" int64_t w4a16_matmul_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (M > 64 || matmul_gemm_band(fmt, M, N, K)) return w4a16_gemm_workspace_bytes(fmt, M, N, K);
+  if (!fp4_valid_format(fmt)) return -1;
+  if (M < 0) return -2;
+  return fp4_check_nk(fmt, N, K);
+}
+
 extern "C" int w4a16_matmul_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                                float global_scale, const void* x_bf16, float* y, void* workspace,
                                size_t workspace_bytes, void* stream) {
   if (M >= 0 && M <= 16) return w4a16_gemv(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
-  if (M <= 64) return w4a16_midm(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
+  if (M <= 64) {
+    if (workspace && matmul_gemm_band(fmt, M, N, K) && check_gemm(fmt, M, N, K) == 0) {
+      const size_t need = gemm_workspace_bytes((int)M, (int)N, (int)K);
+      if (need > 0 && workspace_bytes >= need)
+        return w4a16_gemm_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, workspace, workspace_bytes, stream);
+    }
+    return w4a16_midm(fmt, M, N, K, q, s, global_scale, x_bf16, y, stream);
+  }
   return w4a16_gemm_ws(fmt, M, N, K, q, s, global_scale, x_bf16, y, workspace, workspace_bytes, stream);
 }
 

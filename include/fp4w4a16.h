@@ -242,12 +242,16 @@ int w4a16_midm(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const vo
                float global_scale, const void* x_bf16, float* y, void* stream);
 
 /* Dispatch on M: M <= 16 -> w4a16_gemv, 17 <= M <= 64 -> w4a16_midm, otherwise
- * w4a16_gemm (w4a16_matmul_ws: w4a16_gemm_ws with the workspace; the smaller M take none). */
+ * w4a16_gemm. w4a16_matmul_ws: the same with w4a16_gemm_ws above 64, and for 48 <= M <= 64 on
+ * matrices of at least 20 M weights (N K >= 20 * 2^20, not Q4_0) the GEMM with K parts too when the
+ * workspace holds them (there it is faster than the mid-M kernel); w4a16_matmul_workspace_bytes gives
+ * the workspace it can use (0: none), or a negative status for arguments it would reject. */
 int w4a16_matmul(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                  float global_scale, const void* x_bf16, float* y, void* stream);
 int w4a16_matmul_ws(int fmt, int64_t M, int64_t N, int64_t K, const void* q, const void* s,
                     float global_scale, const void* x_bf16, float* y, void* workspace,
                     size_t workspace_bytes, void* stream);
+int64_t w4a16_matmul_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /*
  * Dequantize the kernel layout to FP32 W[N][K] (the pages' dequant-at-load, EdgeRock card,

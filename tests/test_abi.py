@@ -153,6 +153,20 @@ def test_workspace_bytes_query():
     assert 0 < worst <= cus * 64 * 1024
 
 
+def test_matmul_workspace_bytes_query():
+    r = _raw()
+    qm, qg = r.w4a16_matmul_workspace_bytes, r.w4a16_gemm_workspace_bytes
+    assert qm(7, 56, 2560, 9728) == ARG
+    assert qm(NVFP4, 56, 2560, 40) == SHAPE
+    assert qm(NVFP4, 8, 2560, 9728) == 0              # the GEMV takes no workspace
+    assert qm(NVFP4, 47, 2560, 9728) == 0             # nor the mid-M kernel
+    assert qm(Q4_0, 56, 2560, 9728) == 0
+    assert qm(NVFP4, 56, 4096, 4096) == 0             # 16 M weights: the mid-M kernel
+    for m in (48, 56, 64, 128):                       # the GEMM's K parts
+        assert qm(NVFP4, m, 2560, 9728) == qg(NVFP4, m, 2560, 9728) > 0
+    assert qm(Q4_0, 128, 2560, 9728) == UNSUP
+
+
 @pytest.mark.parametrize("validate", [0, 1])
 def test_pack_layout_argument_errors(validate):
     # argument checks come before the validation pass, so these fail on the host with or without it

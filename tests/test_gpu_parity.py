@@ -716,6 +716,34 @@ def test_matmul_dispatch(m):
     gc.check_product(fmt, packed, x_bits, y, label=f"matmul M={m}")
 
 
+def test_matmul_gemm_band():
+    # 48 <= M <= 64 on matrices of at least 20 M weights: with a workspace that holds its K parts,
+    # w4a16_matmul_ws runs the GEMM (the binding provides the workspace); with a smaller one, the mid-M kernel
+    # (bitwise what w4a16_midm gives). Both against the oracle on sampled columns.
+    for fmt in ("nvfp4", "rocmfp4_dual"):
+        for (m, n, k) in [(48, 2560, 9728), (64, 9728, 2560)]:
+            _announce("matmul-gemm-band", fmt, m, n, k)
+            need = fp4.w4a16_matmul_workspace_bytes(fmt, m, n, k)
+            assert need == fp4.w4a16_gemm_workspace_bytes(fmt, m, n, k) > 0
+            w, packed = gc.make_case(fmt, n, k, cfg=79, mat=m)
+            del w
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(m, k, cfg=79, mat=m)
+            x = gc.x_tensor(x_bits)
+            y = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_matmul(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y)
+            y_small = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_matmul(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_small,
+                             workspace=torch.empty(need // 2, dtype=torch.uint8, device="cuda"))
+            y_midm = torch.full((m, n), float("nan"), device="cuda")
+            fp4.w4a16_midm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, x, y_midm)
+            torch.cuda.synchronize()
+            assert torch.equal(y_small, y_midm)
+            cols = np.unique(np.concatenate([[0, n - 1], np.linspace(0, n - 1, 24).astype(int)]))
+            for lab, yy in (("gemm", y), ("midm", y_small)):
+                gc.check_product(fmt, packed, x_bits, yy, cols=cols, label=f"matmul-band {lab} {fmt} M={m} {n}x{k}")
+
+
 def _random_shapes(fmt, count, seed):
     # Seeded shapes across all three product paths (GEMV M <= 16, mid-M 17..64, GEMM above), with ragged
     # N (any value) and K (any multiple of the format's block), so tile and chunk tails land anywhere.
