@@ -9,7 +9,10 @@ The same JSON line carries every other workload, each with its own roofline frac
     Dual and FAST (M = 9 is one token plus eight n-gram drafts);
   * the prefill GEMM, M = 2048, K = 4096, N = 14336, in FAST and NVFP4 (TFLOP/s), and the same matrix at
     M = 128, 256, 512;
-  * a plain streaming read of the same byte counts (the ceiling launch cost and memory latency leave).
+  * a plain streaming read of the same byte counts (the ceiling launch cost and memory latency leave);
+  * context: the M = 1 GEMV on two large matrices (a 70B-class gate/up projection 28672 x 8192 and its down
+    projection 8192 x 28672, NVFP4 and Dual, 132 MB each), where launch cost and latency are amortised, with
+    a plain read of the same bytes beside each.
 
 A step of a GEMV workload is one launch over one packed matrix. Weights are drawn by `synth`, packed on
 the GPU by the library's own packers and replicated into distinct copies totalling >= 1 GiB, so every
@@ -66,7 +69,11 @@ for _f in SPEC_FMTS + ("q4_0",):
         for _m in SPEC_MS:
             WORKLOADS[f"{_f}_{_shape}_m{_m}"] = (3, _mat, _f, _m)
 
-SECTIONS = ("headline", "nvfp4_2048", "spec", "gemm", "gemm_small", "sweep", "read_probe", "packers")
+SECTIONS = ("headline", "nvfp4_2048", "spec", "gemm", "gemm_small", "sweep", "read_probe", "packers", "gemv_large")
+# M = 1 GEMV context on large matrices: (N, K); weights N(0, 0.02) drawn on the GPU (synth.device_weights)
+LARGE_SHAPES = ((28672, 8192), (8192, 28672))
+LARGE_FMTS = ("nvfp4", "rocmfp4_dual")
+LARGE_CFG = 5
 
 
 def algorithmic_bytes(fmt: str, n: int, k: int) -> int:
@@ -239,6 +246,35 @@ def bench_gemv(fp4, torch, synth, name: str, steps: int, warmup: int, reps: int,
     del qs, ss
     return dict(name=name, fmt=fmt, n=n, k=k, m=m, copies=copies, bytes=algorithmic_bytes(fmt, n, k), t=t,
                 y=y0.cpu().numpy(), x_bits=x_bits, w_np=w_np, global_scale=pw.global_scale)
+
+
+def bench_gemv_large(fp4, torch, synth, fmt: str, n: int, k: int, steps: int, warmup: int, reps: int, probes):
+    """M = 1 GEMV on a large matrix (context: launch cost amortised), with a plain read of the same bytes."""
+    mat = n + k
+    w = synth.device_weights(n, k, cfg=LARGE_CFG, mat=mat)
+    pw = fp4.PackedWeight.quantize(fmt, w)
+    del w
+    plane_bytes = pw.q.numel() + pw.s.numel()
+    copies = max(2, -(-COLD_BYTES // plane_bytes))
+    qs = [pw.q] + [pw.q.clone() for _ in range(copies - 1)]
+    ss = [pw.s] + [pw.s.clone() for _ in range(copies - 1)]
+    x_bits = synth.activations(1, k, cfg=LARGE_CFG, mat=mat)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    ys = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _ in range(min(copies, 8))]
+
+    def launch(i):
+        fp4.w4a16_gemv(fmt, 1, n, k, qs[i % copies], ss[i % copies], pw.global_scale, x, ys[i % len(ys)])
+
+    t = time_steps(torch, launch, copies, steps, warmup, reps, probes)
+    y0 = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    fp4.w4a16_gemv(fmt, 1, n, k, qs[0], ss[0], pw.global_scale, x, y0)
+    torch.cuda.synchronize()
+    del qs, ss, pw
+    torch.cuda.empty_cache()
+    nbytes = algorithmic_bytes(fmt, n, k)
+    tr = bench_read_probe(torch, probes, nbytes, steps, warmup, reps)
+    return dict(name=f"{fmt}_{n}x{k}_m1", fmt=fmt, n=n, k=k, m=1, mat=mat, copies=copies, bytes=nbytes, t=t,
+                t_read=tr, y=y0.cpu().numpy(), x_bits=x_bits)
 
 
 def bench_gemm(fp4, torch, synth, fmt: str, m: int, steps: int, warmup: int, reps: int, probes, pw=None, cfg=4,
@@ -542,6 +578,16 @@ def main():
             read_probe[b] = bench_read_probe(torch, probes, b, args.steps, args.warmup, reps)
         log(f"read probe: {len(sizes)} sizes ({time.time() - t0:.1f}s)")
 
+    gemv_large = {}
+    if "gemv_large" in only:
+        t0 = time.time()
+        for (n, k) in LARGE_SHAPES:
+            for fmt in LARGE_FMTS:
+                r = bench_gemv_large(fp4, torch, synth, fmt, n, k, 200, 100, reps, probes)
+                gemv_large[r["name"]] = r
+        log(f"large-matrix GEMV: " + ", ".join(f"{nm} {r['t']['median_s'] * 1e6:.2f} us" for nm, r in gemv_large.items())
+            + f" ({time.time() - t0:.1f}s)")
+
     gemm = {}
     if "gemm" in only:
         for fmt in ("rocmfp4_fast", "nvfp4"):
@@ -608,6 +654,11 @@ def main():
                     cpu[f"rocmfp4_fast_down_m{m}"] = oracle_sample("rocmfp4_fast", w_down, sample_rows(r["n"], 64),
                                                                    r["x_bits"], r["y"], threads, budget, time_it=False)
                 del w_down
+        for name, r in gemv_large.items():
+            w = synth.device_weights(r["n"], r["k"], cfg=LARGE_CFG, mat=r["mat"]).cpu().numpy()
+            cpu[name] = oracle_sample(r["fmt"], w, sample_rows(r["n"], 64), r["x_bits"], r["y"], threads, budget,
+                                      time_it=False)
+            del w
         if sw is not None:
             layer = synth.DECODE_4B_LAYER
             for mode in ("grouped", "device_list"):
@@ -686,6 +737,20 @@ def main():
         workloads[name] = entry
     if workloads:
         line["gemv_workloads"] = workloads
+    if gemv_large:
+        line["gemv_large"] = {
+            "what": "context: the M = 1 GEMV on large matrices (launch cost and latency amortised), N(0, 0.02) weights "
+                    "packed on the GPU, a plain streaming read of the same bytes beside each",
+            "results": {}}
+        for name, r in gemv_large.items():
+            gbs = r["bytes"] / r["t"]["median_s"] / 1e9
+            rl = hbm_roofline(r["bytes"], r["t"])
+            rl["vs_read_probe"] = round(r["t_read"]["median_s"] / r["t"]["median_s"], 4)
+            line["gemv_large"]["results"][name] = {
+                "fmt": r["fmt"], "N": r["n"], "K": r["k"], "M": 1, "bytes_per_launch": r["bytes"],
+                "GB/s": gated(round(gbs, 2), name), "roofline": rl, "timing": timing_fields(r["t"]),
+                "read_probe_GB/s": round(r["bytes"] / r["t_read"]["median_s"] / 1e9, 2),
+                "parity": parity_of(name), "cold_copies": r["copies"]}
     if read_probe:
         line["read_probe"] = {
             "what": "plain streaming read of the same bytes per launch (16-byte nontemporal loads), cold copies",
