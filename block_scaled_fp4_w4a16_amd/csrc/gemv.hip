@@ -269,14 +269,21 @@ struct GemvBatch {
   GemvItem it[MAXI];
 };
 
+// How a launch's waves cover K. BATCH_LOOP: batches of U chunk slots, the next prefetched during the
+// current one. The others take all of a wave's chunks in one batch (wave w: chunks w, w + W, ...,
+// w + (U - 1) W) and differ in which slots may lie past the last chunk (such a slot reads zeros):
+// ONE_CHECKED any (each slot is tested), ONE_LAST only the last one ((U - 1) W <= nchunk for every
+// matrix), ONE_FULL none (nchunk = U W for every matrix).
+enum OneBatch { BATCH_LOOP = 0, ONE_CHECKED = 1, ONE_LAST = 2, ONE_FULL = 3 };
+
 // Dynamic LDS: [W waves][U chunks][4 lane groups][M rows][64 B] of staged x, then the
 // cross-wave reduction buffer: [W][T][64 lanes][4] floats, or with M <= 4 fixed at compile time only the
 // stored C rows, [W][T][M][16] floats.
 // MC > 0 fixes M = MC at compile time (the x address arithmetic then reduces to shifts and masks);
-// MC = 0 takes M from mw (at most MX). mw = M | W << 8, W = waves per workgroup. ONE: every wave's
-// chunks fit in one batch (nchunk <= U * W for every matrix of the launch), so there is no next batch
-// to prefetch. wg0 is the matrix's first workgroup.
-template <int F, int T, int RU, int U, int MX, int MC, bool ONE>
+// MC = 0 takes M from mw (at most MX). mw = M | W << 8, W = waves per workgroup. ONE (a OneBatch
+// value) other than BATCH_LOOP: every wave's chunks fit in one batch (nchunk <= U * W for every matrix of
+// the launch), so there is no next batch to prefetch. wg0 is the matrix's first workgroup.
+template <int F, int T, int RU, int U, int MX, int MC, int ONE>
 __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ sp,
                                           const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K,
                                           float gscale, int wg0, int mw) {
@@ -310,7 +317,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
   // With few x rows (XPF) a batch's x is loaded ahead of its weights and held in registers until
   // they are issued, and the next batch's x is prefetched together with its weights. With many rows
   // that would cost too many registers: x is then loaded and committed at the top of each batch.
-  constexpr bool XPF = XStage<U, MX>::NX <= (ONE ? 6 : 2);
+  constexpr bool XPF = XStage<U, MX>::NX <= (ONE != BATCH_LOOP ? 6 : 2);
   XStage<U, XPF ? MX : 1> xst;
   if constexpr (XPF) {
     if (wave < nchunk) {
@@ -323,7 +330,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
     }
   }
   bool have = XPF;  // wr already holds this batch's weights
-  for (int c0 = wave; c0 < nchunk; c0 += ONE ? nchunk : W * U) {
+  for (int c0 = wave; c0 < nchunk; c0 += ONE != BATCH_LOOP ? nchunk : W * U) {
     if constexpr (XPF) {
       stage_x_commit<F, U, MX, (MC > 0)>(xs, xst, M, lane);
     } else {
@@ -332,15 +339,18 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
     }
     // the next batch (x first, then weights) goes out before this batch is computed
     WeightRegs<F> nx[U][T];
-    const int c1 = ONE ? nchunk : c0 + W * U;
-    have = !ONE && c1 < nchunk;
+    const int c1 = ONE != BATCH_LOOP ? nchunk : c0 + W * U;
+    have = ONE == BATCH_LOOP && c1 < nchunk;
     if (have) {
       if constexpr (XPF) stage_x_issue<F, U, MX, (MC > 0)>(xst, src, M, K, c1, W, nchunk, lane);
       load_batch<F, T, U>(nx, src, c1, W, nchunk, lane, n);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c0 + u * W < nchunk) {
+      // Slots the launch guarantees to hold a chunk are computed without a test: straight-line code
+      // lets the compiler interleave one unit's decode with the previous unit's MFMAs.
+      const bool sure = ONE == ONE_FULL || (ONE == ONE_LAST && u < U - 1);
+      if (sure || c0 + u * W < nchunk) {
         // this lane's 32 x values of chunk slot u, read from the wave's staging area just before use
         uint32_t xa[16];
         const u32x4* src = reinterpret_cast<const u32x4*>(xs + ((u * 4 + g) * M + xm) * 64);
@@ -532,7 +542,7 @@ struct RingLaunch {
 // preload at wave start, so a wave does not first wait on the kernel-argument memory; W comes in mw, so
 // no dispatch-packet field is read either.
 // One matrix: everything the body needs is preloaded.
-template <int F, int T, int RU, int U, int MX, int MC, bool ONE>
+template <int F, int T, int RU, int U, int MX, int MC, int ONE>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                                                     int N, int K, float g, int mw) {
   gemv_body<F, T, RU, U, MX, MC, ONE>(q, s, x, y, N, K, g, 0, mw);
@@ -541,7 +551,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t* q, const uint
 // Several matrices: with at most 4 the starts of matrices 1..3 are preloaded (INT_MAX where unused), so
 // the workgroup's matrix is known at once and its fields take one read of the argument memory; with
 // more the starts are searched in the GemvBatch.
-template <int F, int T, int RU, int U, int MX, int MAXI, int MC, bool ONE>
+template <int F, int T, int RU, int U, int MX, int MAXI, int MC, int ONE>
 __global__ __launch_bounds__(1024) void gemv_group_kernel(int st1, int st2, int st3, int mw, const GemvBatch<MAXI> batch) {
   const int b = (int)blockIdx.x;
   int item = 0;
@@ -740,7 +750,7 @@ static int resident_per_cu(const void* k, int W, size_t lds) {
   return b;
 }
 
-template <int F, int T, int RU, int U, int MX, int MAXI, int MC, bool ONE = false>
+template <int F, int T, int RU, int U, int MX, int MAXI, int MC, int ONE = BATCH_LOOP>
 struct GemvLaunch {
   static const void* fn() {
     if constexpr (MAXI == 1) return reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX, MC, ONE>);
@@ -835,26 +845,26 @@ static int try_one_batch(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   if (M < 2 || M > 8 || fp4_tuning().one_batch == 0) return -1;
   int min_chunks, max_chunks;
   const int nwg = fill_ranges(b, 1, min_chunks, max_chunks);
-  int W = pick_waves<GemvLaunch<F, 1, 4, 4, 4, MAXI, 4, true>>(nwg, min_chunks, 1, 16);
+  int W = pick_waves<GemvLaunch<F, 1, 4, 4, 4, MAXI, 4, ONE_CHECKED>>(nwg, min_chunks, 1, 16);
   if (W == 16 && (max_chunks + 7) / 8 <= 4) W = 8;
   const int U = (max_chunks + W - 1) / W;
   if (M <= 4 && U > 6) return -1;
-  if (M == 2) return U <= 3 ? GemvLaunch<F, 1, 2, 3, 2, MAXI, 2, true>::launch(b, nwg, W, M, st)
-                   : U == 4 ? GemvLaunch<F, 1, 2, 4, 2, MAXI, 2, true>::launch(b, nwg, W, M, st)
-                            : GemvLaunch<F, 1, 2, 6, 2, MAXI, 2, true>::launch(b, nwg, W, M, st);
-  if (M == 3) return U <= 3 ? GemvLaunch<F, 1, 4, 3, 3, MAXI, 3, true>::launch(b, nwg, W, M, st)
-                   : U == 4 ? GemvLaunch<F, 1, 4, 4, 3, MAXI, 3, true>::launch(b, nwg, W, M, st)
-                            : GemvLaunch<F, 1, 4, 6, 3, MAXI, 3, true>::launch(b, nwg, W, M, st);
-  if (M == 4) return U <= 3 ? GemvLaunch<F, 1, 4, 3, 4, MAXI, 4, true>::launch(b, nwg, W, M, st)
-                   : U == 4 ? GemvLaunch<F, 1, 4, 4, 4, MAXI, 4, true>::launch(b, nwg, W, M, st)
-                            : GemvLaunch<F, 1, 4, 6, 4, MAXI, 4, true>::launch(b, nwg, W, M, st);
+  if (M == 2) return U <= 3 ? GemvLaunch<F, 1, 2, 3, 2, MAXI, 2, ONE_CHECKED>::launch(b, nwg, W, M, st)
+                   : U == 4 ? GemvLaunch<F, 1, 2, 4, 2, MAXI, 2, ONE_CHECKED>::launch(b, nwg, W, M, st)
+                            : GemvLaunch<F, 1, 2, 6, 2, MAXI, 2, ONE_CHECKED>::launch(b, nwg, W, M, st);
+  if (M == 3) return U <= 3 ? GemvLaunch<F, 1, 4, 3, 3, MAXI, 3, ONE_CHECKED>::launch(b, nwg, W, M, st)
+                   : U == 4 ? GemvLaunch<F, 1, 4, 4, 3, MAXI, 3, ONE_CHECKED>::launch(b, nwg, W, M, st)
+                            : GemvLaunch<F, 1, 4, 6, 3, MAXI, 3, ONE_CHECKED>::launch(b, nwg, W, M, st);
+  if (M == 4) return U <= 3 ? GemvLaunch<F, 1, 4, 3, 4, MAXI, 4, ONE_CHECKED>::launch(b, nwg, W, M, st)
+                   : U == 4 ? GemvLaunch<F, 1, 4, 4, 4, MAXI, 4, ONE_CHECKED>::launch(b, nwg, W, M, st)
+                            : GemvLaunch<F, 1, 4, 6, 4, MAXI, 4, ONE_CHECKED>::launch(b, nwg, W, M, st);
   if (U > 3) return -1;
   // M fixed at compile time here too (x loads and addressing for exactly M rows: 5-8% faster than a
   // runtime M bounded by 8)
-  if (M == 5) return one_batch_fit<GemvLaunch<F, 1, 4, 3, 5, MAXI, 5, true>>(b, nwg, W, M, st);
-  if (M == 6) return one_batch_fit<GemvLaunch<F, 1, 4, 3, 6, MAXI, 6, true>>(b, nwg, W, M, st);
-  if (M == 7) return one_batch_fit<GemvLaunch<F, 1, 4, 3, 7, MAXI, 7, true>>(b, nwg, W, M, st);
-  return one_batch_fit<GemvLaunch<F, 1, 4, 3, 8, MAXI, 8, true>>(b, nwg, W, M, st);
+  if (M == 5) return one_batch_fit<GemvLaunch<F, 1, 4, 3, 5, MAXI, 5, ONE_CHECKED>>(b, nwg, W, M, st);
+  if (M == 6) return one_batch_fit<GemvLaunch<F, 1, 4, 3, 6, MAXI, 6, ONE_CHECKED>>(b, nwg, W, M, st);
+  if (M == 7) return one_batch_fit<GemvLaunch<F, 1, 4, 3, 7, MAXI, 7, ONE_CHECKED>>(b, nwg, W, M, st);
+  return one_batch_fit<GemvLaunch<F, 1, 4, 3, 8, MAXI, 8, ONE_CHECKED>>(b, nwg, W, M, st);
 }
 
 // The grouped mid-M kernel (one block of x rows) for a launch of one or more matrices, 5 <= M <= 16: wave
@@ -915,6 +925,20 @@ static int dispatch_midm_group(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   return dispatch_midm_group_mx<F, MAXI, 16>(b, M, st);
 }
 
+// M = 1, one batch of U slots per wave. One matrix: straight-line slots (ONE_FULL where U W = nchunk,
+// else ONE_LAST, which U = ceil(nchunk / W) always allows; a tuning override of U that breaks it takes the
+// checked form). Several matrices: ONE_FULL when every one has U W chunks, else every slot is tested.
+template <int F, int U, int MAXI>
+static int launch_one_m1(const GemvBatch<MAXI>& b, int nwg, int W, bool full, bool last, hipStream_t st) {
+  if constexpr (U <= 4) {
+    if (full) return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_FULL>::launch(b, nwg, W, 1, st);
+  }
+  if constexpr (MAXI == 1) {
+    if (last) return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_LAST>::launch(b, nwg, W, 1, st);
+  }
+  return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_CHECKED>::launch(b, nwg, W, 1, st);
+}
+
 // Fills in the workgroup ranges, picks the variant and wave count, and launches. Every item has N, K >= 1.
 template <int F, int MAXI>
 static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
@@ -929,9 +953,7 @@ static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     // One batch of U chunk slots per wave when W * U covers the longest K (no prefetch registers);
     // U is the fewest slots that do at the picked wave count.
     using L4 = GemvLaunch<F, 1, 1, 4, 1, MAXI, 1>;
-    using O2 = GemvLaunch<F, 1, 1, 2, 1, MAXI, 1, true>;
-    using O3 = GemvLaunch<F, 1, 1, 3, 1, MAXI, 1, true>;
-    using O4 = GemvLaunch<F, 1, 1, 4, 1, MAXI, 1, true>;
+    using O4 = GemvLaunch<F, 1, 1, 4, 1, MAXI, 1, ONE_CHECKED>;
     int W = pick_waves<O4>(nwg, min_chunks, M, wmax);
     // 8 waves of up to 4 chunks beat 16 waves of 2 (K = 4096: 3-10% faster, fewer waves to reduce)
     const Fp4Tuning& tu = fp4_tuning();
@@ -947,12 +969,15 @@ static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     if (ring) return RingLaunch<F, 3>::launch(b.it[0], RING_WAVES, st);
     if (batch_loop && U <= 2) return L2::launch(b, nwg, W, M, st);
     if (batch_loop && U <= 4) return L4::launch(b, nwg, W, M, st);
-    if (U <= 2) return O2::launch(b, nwg, W, M, st);
-    if (U == 3) return O3::launch(b, nwg, W, M, st);
-    if (U == 4) return O4::launch(b, nwg, W, M, st);
+    // which slots may be empty (OneBatch)
+    const bool full = min_chunks == max_chunks && U * W == max_chunks;
+    const bool last = (U - 1) * W <= min_chunks;
     // up to 6 slots in one batch (the 2560 x 9728 matrix: 5.90 -> 5.18 us against the batch loop)
-    if (U == 5) return GemvLaunch<F, 1, 1, 5, 1, MAXI, 1, true>::launch(b, nwg, W, M, st);
-    if (U == 6) return GemvLaunch<F, 1, 1, 6, 1, MAXI, 1, true>::launch(b, nwg, W, M, st);
+    if (U <= 2) return launch_one_m1<F, 2, MAXI>(b, nwg, W, full, last, st);
+    if (U == 3) return launch_one_m1<F, 3, MAXI>(b, nwg, W, full, last, st);
+    if (U == 4) return launch_one_m1<F, 4, MAXI>(b, nwg, W, full, last, st);
+    if (U == 5) return launch_one_m1<F, 5, MAXI>(b, nwg, W, full, last, st);
+    if (U == 6) return launch_one_m1<F, 6, MAXI>(b, nwg, W, full, last, st);
     return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
   }
   if (M == 2) {

@@ -79,7 +79,9 @@ def test_dequant_all_codes_and_scales(fmt):
 @pytest.mark.parametrize("fmt", gc.FMTS_ALL)
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16])
 def test_gemv_small_shapes(fmt, m):
-    for (n, k) in [(48, 256), (37, 160), (256, 1536)]:
+    # at M = 1: (48, 256), (37, 160), (256, 1536) and (24, 4096) fill every chunk slot of every wave;
+    # (40, 2560) leaves the last slot of half the waves past the last chunk
+    for (n, k) in [(48, 256), (37, 160), (256, 1536), (24, 4096), (40, 2560)]:
         _announce("gemv", fmt, m, n, k)
         w, packed = gc.make_case(fmt, n, k, cfg=52, mat=n)
         pw = gc.upload(fmt, n, k, packed)
@@ -125,6 +127,25 @@ def test_gemv_ring_forced(tmp_path):
     ys = gc.run_variant(tmp_path, {"FP4_GEMV_RING": "1"})
     for name, (fmt, packed, x_bits) in cases.items():
         gc.check_product(fmt, packed, x_bits, torch.from_numpy(ys[name]), label=f"gemv-ring {name}")
+
+
+def test_gemv_slot_override(tmp_path):
+    # FP4_GEMV_U=4 (child process) gives M = 1 more chunk slots per wave than the shape needs: with 20
+    # chunks (8 waves x 4 slots) slots before the last lie past the last chunk, so every slot is tested;
+    # with 12 chunks (4 waves x 4 slots) only the last slot of every wave is empty. Results must not change.
+    cases = {}
+    for fmt in gc.FMTS_ALL:
+        for (n, k) in [(40, 2560), (256, 1536)]:
+            _announce("gemv-slot-override", fmt, n, k)
+            w, packed = gc.make_case(fmt, n, k, cfg=53, mat=n)
+            pw = gc.upload(fmt, n, k, packed)
+            x_bits = synth.activations(1, k, cfg=53, mat=k)
+            name = f"{fmt}_{n}_{k}"
+            gc.save_case(tmp_path, name, "gemv", fmt, 1, n, k, pw, x_bits)
+            cases[name] = (fmt, packed, x_bits)
+    ys = gc.run_variant(tmp_path, {"FP4_GEMV_U": "4"})
+    for name, (fmt, packed, x_bits) in cases.items():
+        gc.check_product(fmt, packed, x_bits, torch.from_numpy(ys[name]), label=f"gemv-slot-override {name}")
 
 
 def test_gemv_one_batch_off(tmp_path):
