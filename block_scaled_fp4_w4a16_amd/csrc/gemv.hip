@@ -925,16 +925,18 @@ static int dispatch_midm_group(GemvBatch<MAXI>& b, int M, hipStream_t st) {
   return dispatch_midm_group_mx<F, MAXI, 16>(b, M, st);
 }
 
-// M = 1, one batch of U slots per wave. One matrix: straight-line slots (ONE_FULL where U W = nchunk,
-// else ONE_LAST, which U = ceil(nchunk / W) always allows; a tuning override of U that breaks it takes the
+// M = 1, one batch of U slots per wave (U here is the kernel's slot count, at least the slots the launch
+// needs). One matrix: straight-line slots (ONE_FULL where U W = nchunk, else ONE_LAST where (U - 1) W <=
+// nchunk, which U = ceil(nchunk / W) always allows; the U tuning override can break it and then takes the
 // checked form). Several matrices: ONE_FULL when every one has U W chunks, else every slot is tested.
 template <int F, int U, int MAXI>
-static int launch_one_m1(const GemvBatch<MAXI>& b, int nwg, int W, bool full, bool last, hipStream_t st) {
+static int launch_one_m1(const GemvBatch<MAXI>& b, int nwg, int W, int min_chunks, int max_chunks, hipStream_t st) {
   if constexpr (U <= 4) {
-    if (full) return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_FULL>::launch(b, nwg, W, 1, st);
+    if (min_chunks == max_chunks && U * W == max_chunks)
+      return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_FULL>::launch(b, nwg, W, 1, st);
   }
   if constexpr (MAXI == 1) {
-    if (last) return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_LAST>::launch(b, nwg, W, 1, st);
+    if ((U - 1) * W <= min_chunks) return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_LAST>::launch(b, nwg, W, 1, st);
   }
   return GemvLaunch<F, 1, 1, U, 1, MAXI, 1, ONE_CHECKED>::launch(b, nwg, W, 1, st);
 }
@@ -969,15 +971,12 @@ static int dispatch_gemv(GemvBatch<MAXI>& b, int M, hipStream_t st) {
     if (ring) return RingLaunch<F, 3>::launch(b.it[0], RING_WAVES, st);
     if (batch_loop && U <= 2) return L2::launch(b, nwg, W, M, st);
     if (batch_loop && U <= 4) return L4::launch(b, nwg, W, M, st);
-    // which slots may be empty (OneBatch)
-    const bool full = min_chunks == max_chunks && U * W == max_chunks;
-    const bool last = (U - 1) * W <= min_chunks;
     // up to 6 slots in one batch (the 2560 x 9728 matrix: 5.90 -> 5.18 us against the batch loop)
-    if (U <= 2) return launch_one_m1<F, 2, MAXI>(b, nwg, W, full, last, st);
-    if (U == 3) return launch_one_m1<F, 3, MAXI>(b, nwg, W, full, last, st);
-    if (U == 4) return launch_one_m1<F, 4, MAXI>(b, nwg, W, full, last, st);
-    if (U == 5) return launch_one_m1<F, 5, MAXI>(b, nwg, W, full, last, st);
-    if (U == 6) return launch_one_m1<F, 6, MAXI>(b, nwg, W, full, last, st);
+    if (U <= 2) return launch_one_m1<F, 2, MAXI>(b, nwg, W, min_chunks, max_chunks, st);
+    if (U == 3) return launch_one_m1<F, 3, MAXI>(b, nwg, W, min_chunks, max_chunks, st);
+    if (U == 4) return launch_one_m1<F, 4, MAXI>(b, nwg, W, min_chunks, max_chunks, st);
+    if (U == 5) return launch_one_m1<F, 5, MAXI>(b, nwg, W, min_chunks, max_chunks, st);
+    if (U == 6) return launch_one_m1<F, 6, MAXI>(b, nwg, W, min_chunks, max_chunks, st);
     return L4::launch(b, nwg, pick_waves<L4>(nwg, min_chunks, M, wmax), M, st);
   }
   if (M == 2) {
