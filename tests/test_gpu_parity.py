@@ -80,8 +80,9 @@ def test_dequant_all_codes_and_scales(fmt):
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16])
 def test_gemv_small_shapes(fmt, m):
     # at M = 1: (48, 256), (37, 160), (256, 1536) and (24, 4096) fill every chunk slot of every wave;
-    # (40, 2560) leaves the last slot of half the waves past the last chunk
-    for (n, k) in [(48, 256), (37, 160), (256, 1536), (24, 4096), (40, 2560)]:
+    # (40, 2560) leaves the last slot of half the waves past the last chunk; (20, 96) is one partial chunk
+    # on the two-slot kernel
+    for (n, k) in [(48, 256), (37, 160), (256, 1536), (24, 4096), (40, 2560), (20, 96)]:
         _announce("gemv", fmt, m, n, k)
         w, packed = gc.make_case(fmt, n, k, cfg=52, mat=n)
         pw = gc.upload(fmt, n, k, packed)
