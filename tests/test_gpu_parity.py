@@ -321,6 +321,30 @@ def test_gemv_batched_matches_oracle(fmt, m):
         assert torch.all(buf[:32] == 12345.0) and torch.all(buf[32 + m * n:] == 12345.0)
 
 
+@pytest.mark.parametrize("fmt", gc.FMTS_ALL)
+@pytest.mark.parametrize("count", [3, 5])
+def test_gemv_batched_equal_k(fmt, count):
+    # grouped M = 1 launches whose matrices all have K = 1536 (12 chunks: 4 waves of 3 slots, every slot
+    # holding a chunk, the straight-line form), with ragged N and one shared x; 3 matrices take the
+    # 4-entry item table, 5 the 32-entry one
+    m, k = 1, 1536
+    shapes = [(40, k), (24, k), (130, k), (16, k), (77, k)][:count]
+    _announce("gemv-batched-equal-k", fmt, count)
+    x_bits = synth.activations(m, k, cfg=62, mat=count)
+    x = gc.x_tensor(x_bits)
+    items, cases = [], []
+    for i, (n, kk) in enumerate(shapes):
+        w, packed = gc.make_case(fmt, n, kk, cfg=62, mat=10 * count + i)
+        pw = gc.upload(fmt, n, kk, packed)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        items.append((pw.q, pw.s, pw.global_scale, x, y, n, kk))
+        cases.append((packed, y, n))
+    fp4.w4a16_gemv_batched(fmt, m, items)
+    torch.cuda.synchronize()
+    for packed, y, n in cases:
+        gc.check_product(fmt, packed, x_bits, y, label=f"batched-equal-k {fmt} {count} {n}x{k}")
+
+
 @pytest.mark.parametrize("count", [1, 2, 3, 4])
 def test_gemv_batched_small_counts(count):
     # launches of up to four matrices pass a smaller item table; each output against the oracle, and a
