@@ -732,8 +732,8 @@ def main():
                  "timing": timing_fields(r["t"]), "parity": parity_of(name), "cold_copies": r["copies"]}
         if r["bytes"] in read_probe:
             entry["roofline"]["vs_read_probe"] = round(read_probe[r["bytes"]]["median_s"] / r["t"]["median_s"], 4)
-        if name == "nvfp4_2048x2048_m1":
-            entry["roofline"]["traffic"] = traffic_from_profiles("gemv.hip", name)
+        # counter traffic where profiles/ holds it for the current kernel source (else null)
+        entry["roofline"]["traffic"] = traffic_from_profiles("gemv.hip", name)
         workloads[name] = entry
     if workloads:
         line["gemv_workloads"] = workloads
