@@ -612,7 +612,36 @@ __device__ __forceinline__ void decode_scaled(const WeightRegs<F>& w, bf16x8 (&b
   }
 }
 
-// Dynamic LDS: [W waves][4 lane groups][M rows][64 B] of staged x (one chunk per wave); after the K loop
+// Staged x of the mid-M kernel: lane group g's M rows of 64 B start at g * midm_gs(M), row m at m * MIDM_RS
+// within them. With M even the groups would start on the same LDS banks (M * 64 a multiple of 128 B), and
+// a commit that writes one piece to each of the four groups (32-weight blocks) would hit one bank set four
+// times; 16 B after each group moves them apart (FAST 9728 x 2560 at M = 16: 7.80 -> 6.86 us). With M odd
+// the groups already alternate between two bank halves, and a pad there measured slightly slower.
+constexpr int MIDM_RS = 64;
+__host__ __device__ constexpr int midm_gs(int M) { return M * MIDM_RS + ((M & 1) ? 0 : 16); }
+
+// Commits the registers of one chunk's x (stage_x_issue with one slot) to the wave's staging area in the
+// layout above: lane (m, g) later reads its 32 bf16 of the chunk as 64 contiguous bytes.
+template <int F, int MX>
+__device__ __forceinline__ void midm_x_commit(uint8_t* xs, const XStage<1, MX>& st, int M, int lane) {
+  const int pieces = M * 16, gs = midm_gs(M);
+#pragma unroll
+  for (int i = 0; i < XStage<1, MX>::NX; ++i) {
+    const int p = 64 * i + lane;
+    if (p < pieces) {
+      const int m = p >> 4, qq = p & 15;
+      const int dst = m * MIDM_RS + (block32(F) ? ((qq & 3) * gs + 16 * (qq >> 2)) : (2 * (qq & 1) * gs + 8 * (qq >> 1)));
+      if constexpr (block32(F)) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
+        *reinterpret_cast<u32x4*>(xs + dst) = st.v[i];
+      } else {                          // k = 16 j + 4 g + t: halves go to lane groups 2 (qq & 1) and +1
+        *reinterpret_cast<u32x2*>(xs + dst) = u32x2{st.v[i][0], st.v[i][1]};
+        *reinterpret_cast<u32x2*>(xs + dst + gs) = u32x2{st.v[i][2], st.v[i][3]};
+      }
+    }
+  }
+}
+
+// Dynamic LDS: [W waves][4 lane groups][midm_gs(M) B] of staged x (one chunk per wave); after the K loop
 // the same space holds the cross-wave reduction buffer [W][T][MB][64 lanes][4] floats. wg0 is the
 // matrix's first workgroup (grouped launches).
 template <int F, int MB, int T, int MXB = 16 * MB>
@@ -632,7 +661,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
   src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
   src.s = make_rsrc(sp + (int64_t)tile0 * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
   src.x = make_rsrc(x, (uint32_t)(M * K) * 2u);
-  const size_t xw_bytes = (size_t)4 * M * 64;
+  const size_t xw_bytes = (size_t)4 * midm_gs(M);
   uint8_t* xs = smem + wave * xw_bytes;
   const uint32_t soff_lane = n * (unit_s(F) / TILE_N);
 
@@ -655,7 +684,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
                    (uint32_t)(t * nchunk + wave) * unit_s(F) + soff_lane);
   }
   for (int c = wave; c < nchunk; c += W) {
-    stage_x_commit<F, 1, MXR>(xs, xst, M, lane);
+    midm_x_commit<F, MXR>(xs, xst, M, lane);
     WeightRegs<F> nx[T];               // next units of this wave, in flight during these
     const int c1 = c + W;
     if (c1 < nchunk) {
@@ -668,7 +697,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if constexpr (MB == 1) {           // one block of x rows: unscaled levels, scales folded per group
-        const uint8_t* xr = xs + (g * M + min(m16, M - 1)) * 64;
+        const uint8_t* xr = xs + g * midm_gs(M) + min(m16, M - 1) * MIDM_RS;
         uint32_t xa[16];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -682,7 +711,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int row = min(mb * 16 + m16, M - 1);  // rows past M repeat a valid row; never stored
-          const uint8_t* xr = xs + (g * M + row) * 64;
+          const uint8_t* xr = xs + g * midm_gs(M) + row * MIDM_RS;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + 16 * j);
@@ -874,7 +903,7 @@ template <int F, int MAXI, int WMAX, int MXB>
 struct MidmGroupLaunch {
   static const void* fn() { return reinterpret_cast<const void*>(&midm_group_kernel<F, MAXI, WMAX, MXB>); }
   static size_t lds(int W, int M) {
-    const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * 64 * 4 * sizeof(float);
+    const size_t stage = (size_t)W * 4 * midm_gs(M), red = (size_t)W * 64 * 4 * sizeof(float);
     return stage > red ? stage : red;
   }
   static int resident(int W, int M) {    // workgroups per CU (per device, wave count and M)
@@ -1022,7 +1051,7 @@ template <int F, int MB, int T, int WMAX = 8, int MXB = 16 * MB>
 static int launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                        int M, int N, int K, float g) {
   const int ntiles = (N + TILE_N - 1) / TILE_N;
-  const size_t stage = (size_t)W * 4 * M * 64, red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
+  const size_t stage = (size_t)W * 4 * midm_gs(M), red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
   const size_t lds = stage > red ? stage : red;
   static Fp4LdsLimit lds_limit;
   lds_limit.ensure(reinterpret_cast<const void*>(&midm_kernel<F, MB, T, WMAX, MXB>), GEMV_LDS_MAX);
@@ -1049,7 +1078,7 @@ static int dispatch_midm_mb(int M, hipStream_t st, const uint8_t* q, const uint8
   // Waves per workgroup: the most that give every wave at least two chunks and keep the grid resident at
   // once (16 waves per CU with two 16-row blocks of x and one tile, 8 otherwise, at this kernel's register
   // use). Up to 16 with one block of x and one tile (the kernel then fits 128 VGPRs; the staged x of 16 waves
-  // is at most 64 KiB), else up to 8 (the staged x of 8 waves at M = 64 fills 128 KiB of LDS).
+  // is at most 66 KiB), else up to 8 (the staged x of 8 waves at M = 64 fills 129 KiB of LDS).
   const int resident = (MB <= 2 && T == 1 ? 16 : 8) * 256;
   const int wmax = (MB == 1 && T == 1) ? 16 : 8;
   int W = wmax;
