@@ -137,9 +137,15 @@ __device__ __forceinline__ void unit_mac(f32x4& acc, const WeightRegs<F>& w, con
   }
 }
 
+// Bytes from one lane group's staged x rows to the next (M rows of 64 B). With M even, M * 64 is a multiple
+// of 128 B and the four groups of a chunk would start on the same LDS banks: a commit that writes one piece
+// to each of them (32-weight blocks) would hit one bank set four times, so 16 B follow each group. With M
+// odd the groups already alternate between two bank halves, and a pad there measured slightly slower.
+__host__ __device__ constexpr int x_gs(int M) { return M * 64 + ((M & 1) ? 0 : 16); }
+
 // x staging. Each wave copies the x columns of the chunks it is about to process into its own LDS
 // region, in per-lane fragment order: for chunk slot u, lane group g and x row m, the 32 bf16 that lane
-// (m, g) feeds to the MFMAs of that chunk sit as 64 contiguous bytes. The copy is split in two so that
+// (m, g) feeds to the MFMAs of that chunk sit as 64 contiguous bytes at (4 u + g) x_gs(M) + 64 m. The copy is split in two so that
 // the weight loads can be issued in between: `issue` starts coalesced 16-byte global loads (a chunk
 // row of x is 16 pieces) into registers, `commit` writes them to LDS. Loads complete in order, so
 // committing waits only for x, never for the weight loads issued after it; no workgroup barrier is
@@ -183,13 +189,14 @@ __device__ __forceinline__ void stage_x_commit(uint8_t* xs, const XStage<U, MX>&
     const int p = WRAP ? (64 * i + lane) % pieces : 64 * i + lane;
     if (WRAP || p < pieces) {
       const int u = U == 1 ? 0 : p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
-      const int dst = (u * 4 * M + m) * 64 + (block32(F) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
-                                                           : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
+      const int gs = x_gs(M);
+      const int dst = u * 4 * gs + m * 64 + (block32(F) ? ((qq & 3) * gs + 16 * (qq >> 2))
+                                                        : (2 * (qq & 1) * gs + 8 * (qq >> 1)));
       if constexpr (block32(F)) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
         *reinterpret_cast<u32x4*>(xs + dst) = st.v[i];
       } else {                          // k = 16 j + 4 g + t: halves go to lane groups 2 (qq & 1) and +1
         *reinterpret_cast<u32x2*>(xs + dst) = u32x2{st.v[i][0], st.v[i][1]};
-        *reinterpret_cast<u32x2*>(xs + dst + M * 64) = u32x2{st.v[i][2], st.v[i][3]};
+        *reinterpret_cast<u32x2*>(xs + dst + gs) = u32x2{st.v[i][2], st.v[i][3]};
       }
     }
   }
@@ -216,13 +223,14 @@ __device__ __forceinline__ void stage_x_now(uint8_t* xs, const Srcs& src, int M,
       const int p = p0 + 64 * i + lane;
       if (p >= pieces) continue;
       const int u = p / (M * 16), rem = p - u * (M * 16), m = rem >> 4, qq = rem & 15;
-      const int dst = (u * 4 * M + m) * 64 + (block32(F) ? ((qq & 3) * M * 64 + 16 * (qq >> 2))
-                                                           : (2 * (qq & 1) * M * 64 + 8 * (qq >> 1)));
+      const int gs = x_gs(M);
+      const int dst = u * 4 * gs + m * 64 + (block32(F) ? ((qq & 3) * gs + 16 * (qq >> 2))
+                                                        : (2 * (qq & 1) * gs + 8 * (qq >> 1)));
       if constexpr (block32(F)) {
         *reinterpret_cast<u32x4*>(xs + dst) = v[i];
       } else {
         *reinterpret_cast<u32x2*>(xs + dst) = u32x2{v[i][0], v[i][1]};
-        *reinterpret_cast<u32x2*>(xs + dst + M * 64) = u32x2{v[i][2], v[i][3]};
+        *reinterpret_cast<u32x2*>(xs + dst + gs) = u32x2{v[i][2], v[i][3]};
       }
     }
   }
@@ -302,7 +310,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
   src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
   src.s = make_rsrc(sp + (int64_t)tile0 * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
   src.x = make_rsrc(x, (uint32_t)(M * K) * 2u);
-  const size_t xw_bytes = (size_t)U * 4 * M * 64;
+  const size_t xw_bytes = (size_t)U * 4 * x_gs(M);
   uint8_t* xs = smem + wave * xw_bytes;
   float* red = reinterpret_cast<float*>(smem + W * xw_bytes);
 
@@ -353,7 +361,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ qp, const 
       if (sure || c0 + u * W < nchunk) {
         // this lane's 32 x values of chunk slot u, read from the wave's staging area just before use
         uint32_t xa[16];
-        const u32x4* src = reinterpret_cast<const u32x4*>(xs + ((u * 4 + g) * M + xm) * 64);
+        const u32x4* src = reinterpret_cast<const u32x4*>(xs + (u * 4 + g) * x_gs(M) + xm * 64);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const u32x4 w4 = src[v];
@@ -612,36 +620,8 @@ __device__ __forceinline__ void decode_scaled(const WeightRegs<F>& w, bf16x8 (&b
   }
 }
 
-// Staged x of the mid-M kernel: lane group g's M rows of 64 B start at g * midm_gs(M), row m at m * MIDM_RS
-// within them. With M even the groups would start on the same LDS banks (M * 64 a multiple of 128 B), and
-// a commit that writes one piece to each of the four groups (32-weight blocks) would hit one bank set four
-// times; 16 B after each group moves them apart (FAST 9728 x 2560 at M = 16: 7.80 -> 6.86 us). With M odd
-// the groups already alternate between two bank halves, and a pad there measured slightly slower.
-constexpr int MIDM_RS = 64;
-__host__ __device__ constexpr int midm_gs(int M) { return M * MIDM_RS + ((M & 1) ? 0 : 16); }
-
-// Commits the registers of one chunk's x (stage_x_issue with one slot) to the wave's staging area in the
-// layout above: lane (m, g) later reads its 32 bf16 of the chunk as 64 contiguous bytes.
-template <int F, int MX>
-__device__ __forceinline__ void midm_x_commit(uint8_t* xs, const XStage<1, MX>& st, int M, int lane) {
-  const int pieces = M * 16, gs = midm_gs(M);
-#pragma unroll
-  for (int i = 0; i < XStage<1, MX>::NX; ++i) {
-    const int p = 64 * i + lane;
-    if (p < pieces) {
-      const int m = p >> 4, qq = p & 15;
-      const int dst = m * MIDM_RS + (block32(F) ? ((qq & 3) * gs + 16 * (qq >> 2)) : (2 * (qq & 1) * gs + 8 * (qq >> 1)));
-      if constexpr (block32(F)) {        // k = 32 j + 8 g + t: fragment j = qq / 4 of lane group qq % 4
-        *reinterpret_cast<u32x4*>(xs + dst) = st.v[i];
-      } else {                          // k = 16 j + 4 g + t: halves go to lane groups 2 (qq & 1) and +1
-        *reinterpret_cast<u32x2*>(xs + dst) = u32x2{st.v[i][0], st.v[i][1]};
-        *reinterpret_cast<u32x2*>(xs + dst + gs) = u32x2{st.v[i][2], st.v[i][3]};
-      }
-    }
-  }
-}
-
-// Dynamic LDS: [W waves][4 lane groups][midm_gs(M) B] of staged x (one chunk per wave); after the K loop
+// Dynamic LDS: [W waves][4 lane groups][x_gs(M) B] of staged x (one chunk per wave; the pad that x_gs adds
+// for even M took FAST 9728 x 2560 at M = 16 from 7.80 to 6.86 us); after the K loop
 // the same space holds the cross-wave reduction buffer [W][T][MB][64 lanes][4] floats. wg0 is the
 // matrix's first workgroup (grouped launches).
 template <int F, int MB, int T, int MXB = 16 * MB>
@@ -661,7 +641,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
   src.q = make_rsrc(qp + (int64_t)tile0 * nchunk * UNIT_Q, (uint32_t)(tiles_here * nchunk * UNIT_Q));
   src.s = make_rsrc(sp + (int64_t)tile0 * nchunk * unit_s(F), (uint32_t)(tiles_here * nchunk * unit_s(F)));
   src.x = make_rsrc(x, (uint32_t)(M * K) * 2u);
-  const size_t xw_bytes = (size_t)4 * midm_gs(M);
+  const size_t xw_bytes = (size_t)4 * x_gs(M);
   uint8_t* xs = smem + wave * xw_bytes;
   const uint32_t soff_lane = n * (unit_s(F) / TILE_N);
 
@@ -684,7 +664,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
                    (uint32_t)(t * nchunk + wave) * unit_s(F) + soff_lane);
   }
   for (int c = wave; c < nchunk; c += W) {
-    midm_x_commit<F, MXR>(xs, xst, M, lane);
+    stage_x_commit<F, 1, MXR>(xs, xst, M, lane);
     WeightRegs<F> nx[T];               // next units of this wave, in flight during these
     const int c1 = c + W;
     if (c1 < nchunk) {
@@ -697,7 +677,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if constexpr (MB == 1) {           // one block of x rows: unscaled levels, scales folded per group
-        const uint8_t* xr = xs + g * midm_gs(M) + min(m16, M - 1) * MIDM_RS;
+        const uint8_t* xr = xs + g * x_gs(M) + min(m16, M - 1) * 64;
         uint32_t xa[16];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -711,7 +691,7 @@ __device__ __forceinline__ void midm_body(const uint8_t* __restrict__ qp, const 
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int row = min(mb * 16 + m16, M - 1);  // rows past M repeat a valid row; never stored
-          const uint8_t* xr = xs + g * midm_gs(M) + row * MIDM_RS;
+          const uint8_t* xr = xs + g * x_gs(M) + row * 64;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(xr + 16 * j);
@@ -785,7 +765,7 @@ struct GemvLaunch {
     if constexpr (MAXI == 1) return reinterpret_cast<const void*>(&gemv_kernel<F, T, RU, U, MX, MC, ONE>);
     else return reinterpret_cast<const void*>(&gemv_group_kernel<F, T, RU, U, MX, MAXI, MC, ONE>);
   }
-  static size_t lds(int W, int M) { return (size_t)W * U * 4 * M * 64 + (size_t)W * T * 64 * 4 * sizeof(float); }
+  static size_t lds(int W, int M) { return (size_t)W * U * 4 * x_gs(M) + (size_t)W * T * 64 * 4 * sizeof(float); }
   // workgroups resident per CU for W = 1, 2, 4, 8, 16 at this M (computed once per M class)
   static int resident(int W, int M) {
     static std::atomic<int> cache[64][5][17];
@@ -903,7 +883,7 @@ template <int F, int MAXI, int WMAX, int MXB>
 struct MidmGroupLaunch {
   static const void* fn() { return reinterpret_cast<const void*>(&midm_group_kernel<F, MAXI, WMAX, MXB>); }
   static size_t lds(int W, int M) {
-    const size_t stage = (size_t)W * 4 * midm_gs(M), red = (size_t)W * 64 * 4 * sizeof(float);
+    const size_t stage = (size_t)W * 4 * x_gs(M), red = (size_t)W * 64 * 4 * sizeof(float);
     return stage > red ? stage : red;
   }
   static int resident(int W, int M) {    // workgroups per CU (per device, wave count and M)
@@ -1051,7 +1031,7 @@ template <int F, int MB, int T, int WMAX = 8, int MXB = 16 * MB>
 static int launch_midm(int W, hipStream_t st, const uint8_t* q, const uint8_t* s, const uint16_t* x, float* y,
                        int M, int N, int K, float g) {
   const int ntiles = (N + TILE_N - 1) / TILE_N;
-  const size_t stage = (size_t)W * 4 * midm_gs(M), red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
+  const size_t stage = (size_t)W * 4 * x_gs(M), red = (size_t)W * T * MB * 64 * 4 * sizeof(float);
   const size_t lds = stage > red ? stage : red;
   static Fp4LdsLimit lds_limit;
   lds_limit.ensure(reinterpret_cast<const void*>(&midm_kernel<F, MB, T, WMAX, MXB>), GEMV_LDS_MAX);
