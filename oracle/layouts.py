@@ -1,9 +1,9 @@
 """Canonical byte layouts of the packed weights, and their sizes.
 
 Sources:
-* EdgeRock-4B-NVFP4 model card (description; package section): NVFP4 keeps
-  packed 4-bit data plus scales, one E4M3 scale per 16 values, one FP32 global
-  scale per matrix.
+* EdgeRock-4B-NVFP4 model card (description; package section): an NVFP4
+  matrix is stored as 4-bit codes, an E4M3 byte for every group of 16 weights
+  and a single FP32 factor for the whole matrix.
 * ROCmFP4 design page, format comparison table: 32 weights per block; Dual
   carries two UE4M3 bytes (one per 16-weight half) in 18 bytes = 4.50 bits per
   weight; FAST carries one UE4M3 byte in 17 bytes = 4.25 bits per weight; stock

@@ -1,8 +1,8 @@
 """Packers that turn fp32 weights into canonical packed bytes (CPU oracle, FP64 decisions).
 
 NVFP4 - data-free round-to-nearest (Nanbeige4.2-3B-NVFP4A16 card, "Creation": the
-NVFP4A16 scheme applied data-free, i.e. RTN; EdgeRock-4B-NVFP4 card: E2M1 values,
-E4M3 scale per 16, FP32 global scale per matrix):
+NVFP4A16 scheme applied data-free, i.e. RTN; EdgeRock-4B-NVFP4 card: E2M1 codes,
+an E4M3 byte for each group of 16 weights, one FP32 factor for the matrix):
   1. amax = max |W|; g = fl32(amax / (6 * 448))  (the global scale maps the largest
      block scale to the E4M3 maximum 448 and the largest weight to E2M1's 6);
   2. per 16-weight block: s = E4M3 RNE of max|w_block| / (6 g)  (FP64 divide);
