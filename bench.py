@@ -299,6 +299,36 @@ def bench_gemm(fp4, torch, synth, fmt: str, m: int, steps: int, warmup: int, rep
                 y=y.cpu().numpy(), ws_bytes=fp4.w4a16_gemm_workspace_bytes(fmt, m, n, k))
 
 
+def bench_dense_bf16_gemm(torch, m: int, n: int, k: int, steps: int, warmup: int, reps: int):
+    """Context for the GEMM: y = x W^T of the same shape on plain bf16 weights stored N x K, as a linear
+    layer holds them (torch.nn.functional.linear, i.e. the ROCm BLAS library; no dequantization, bf16
+    output), timed eagerly with events around `steps` back-to-back launches."""
+    import torch.nn.functional as tnf
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    x = torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((n, k), generator=g, device="cuda") * 0.02).to(torch.bfloat16)  # N x K, contiguous
+    y = tnf.linear(x, w)
+    for _ in range(warmup):
+        y = tnf.linear(x, w)
+    torch.cuda.synchronize()
+    samples = []
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            y = tnf.linear(x, w)
+        end.record()
+        torch.cuda.synchronize()
+        samples.append(start.elapsed_time(end) / 1e3 / steps)
+    del x, w, y
+    torch.cuda.empty_cache()
+    med = float(np.median(samples))
+    return dict(median_s=med, min_s=float(min(samples)), max_s=float(max(samples)), samples_s=samples,
+                launches_per_graph=0, graph_replays_per_rep=0, reps=reps, steps=steps)
+
+
 def bench_read_probe(torch, probes, nbytes: int, steps: int, warmup: int, reps: int):
     """The plain streaming read of `nbytes` per launch over >= 1 GiB of distinct slices."""
     slot = -(-nbytes // 256) * 256
@@ -588,7 +618,7 @@ def main():
         log(f"large-matrix GEMV: " + ", ".join(f"{nm} {r['t']['median_s'] * 1e6:.2f} us" for nm, r in gemv_large.items())
             + f" ({time.time() - t0:.1f}s)")
 
-    gemm = {}
+    gemm, gemm_dense = {}, None
     if "gemm" in only:
         for fmt in ("rocmfp4_fast", "nvfp4"):
             t0 = time.time()
@@ -596,6 +626,9 @@ def main():
             log(f"gemm {fmt} M=2048: {gemm[fmt]['t']['median_s'] * 1e6:.1f} us/launch median, "
                 f"{gemm[fmt]['tflops']:.1f} TFLOP/s "
                 f"({time.time() - t0:.1f}s)")
+        t0 = time.time()
+        gemm_dense = bench_dense_bf16_gemm(torch, 2048, 14336, 4096, args.gemm_steps, args.gemm_warmup, reps)
+        log(f"dense bf16 linear M=2048: {gemm_dense['median_s'] * 1e6:.1f} us/launch median ({time.time() - t0:.1f}s)")
     gemm_small, gemm_small_n = {}, {}
     if "gemm_small" in only:
         t0 = time.time()
@@ -767,6 +800,13 @@ def main():
                              "unit": "TFLOP/s", "frac": round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
                              "traffic": traffic_from_profiles("gemm.hip", f"{fmt}_prefill_m2048")},
                 "timing": timing_fields(r["t"]), "parity": parity_of(key)}
+    if gemm_dense is not None:
+        tf = 2.0 * 2048 * 14336 * 4096 / gemm_dense["median_s"] / 1e12
+        line["gemm_dense_bf16_context"] = {
+            "what": "y = x W^T of the prefill shape on plain bf16 weights stored N x K (torch.nn.functional.linear, "
+                    "ROCm BLAS library, no dequantization, bf16 output): context for the W4A16 GEMM, not a product "
+                    "of this library",
+            "TFLOP/s": round(tf, 2), "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "timing": timing_fields(gemm_dense)}
     if gemm_small:
         line["gemm_small_m"] = {
             f"rocmfp4_fast_m{m}_k4096_n14336": {
