@@ -8,7 +8,8 @@ The same JSON line carries every other workload, each with its own roofline frac
   * speculative verify / small batch: gate 9728 x 2560 and down 2560 x 9728 at M = 1, 9, 16 in NVFP4,
     Dual and FAST (M = 9 is one token plus eight n-gram drafts);
   * the prefill GEMM, M = 2048, K = 4096, N = 14336, in FAST and NVFP4 (TFLOP/s), and the same matrix at
-    M = 128, 256, 512;
+    M = 128, 256, 512; beside it, as context, the ROCm BLAS library's plain bf16 product of the same shape
+    (a linear layer's y = x W^T, no dequantization), timed eagerly;
   * a plain streaming read of the same byte counts (the ceiling launch cost and memory latency leave);
   * context: the M = 1 GEMV on two large matrices (a 70B-class gate/up projection 28672 x 8192 and its down
     projection 8192 x 28672, NVFP4 and Dual, 132 MB each), where launch cost and latency are amortised, with
