@@ -110,6 +110,11 @@ def test_product_argument_errors(fn):
         assert call(M=17) == UNSUP
     if fn == "w4a16_midm":
         assert call(M=65) == UNSUP
+    # K limits (32-bit buffer offsets): 2^24 for the GEMV and mid-M kernels, 2^22 for the GEMM
+    if fn in ("w4a16_gemv", "w4a16_midm", "w4a16_matmul"):
+        assert call(K=(1 << 24) + 16) == UNSUP
+    else:
+        assert call(M=128, K=(1 << 22) + 16) == UNSUP
 
 
 @pytest.mark.parametrize("fn", ["w4a16_gemm_ws", "w4a16_matmul_ws"])

@@ -110,6 +110,46 @@ def test_gemv_long_k_batches(fmt, m):
         gc.check_product(fmt, packed, x_bits, y, label=f"gemv-long-k {fmt} M={m} K={k}")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "rocmfp4_fast", "q4_0"])
+def test_very_long_k(fmt):
+    # K = 2^20 + 32 (8193 chunks, the last partial) through a single 16-row tile: the GEMV's batch loop
+    # and the mid-M chain then run hundreds of steps per wave, and the x and plane offsets reach 2^21.
+    n, k = 16, (1 << 20) + 32
+    w, packed = gc.make_case(fmt, n, k, cfg=65, mat=0)
+    pw = gc.upload(fmt, n, k, packed)
+    for m in (1, 2, 9, 16):
+        _announce("gemv-very-long-k", fmt, m, n, k)
+        x_bits = synth.activations(m, k, cfg=65, mat=m)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        fp4.w4a16_gemv(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+        torch.cuda.synchronize()
+        gc.check_product(fmt, packed, x_bits, y, label=f"gemv-very-long-k {fmt} M={m}")
+    if fmt == "q4_0":
+        return  # the matrix-core paths do not take Q4_0
+    m = 33
+    _announce("midm-very-long-k", fmt, m, n, k)
+    x_bits = synth.activations(m, k, cfg=65, mat=m)
+    y = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_midm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    gc.check_product(fmt, packed, x_bits, y, label=f"midm-very-long-k {fmt} M={m}")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "rocmfp4_fast"])
+def test_gemm_very_long_k(fmt):
+    # K = 2^20 + 32 on a one-tile grid (N = 32 of a 256-column tile, M = 65 of a 256-row one): 16385
+    # stages through the ring, with the small-grid K split.
+    m, n, k = 65, 32, (1 << 20) + 32
+    _announce("gemm-very-long-k", fmt, m, n, k)
+    w, packed = gc.make_case(fmt, n, k, cfg=66, mat=0)
+    pw = gc.upload(fmt, n, k, packed)
+    x_bits = synth.activations(m, k, cfg=66, mat=m)
+    y = torch.full((m, n), float("nan"), device="cuda")
+    fp4.w4a16_gemm(fmt, m, n, k, pw.q, pw.s, pw.global_scale, gc.x_tensor(x_bits), y)
+    torch.cuda.synchronize()
+    gc.check_product(fmt, packed, x_bits, y, label=f"gemm-very-long-k {fmt}")
+
+
 def test_gemv_ring_forced(tmp_path):
     # The long-K ring kernel (M = 1), switched on for small grids (FP4_GEMV_RING=1, in a child process: the
     # library reads its tuning overrides once per process): a ragged last tile, a partial last 128-wide chunk,
