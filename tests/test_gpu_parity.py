@@ -77,7 +77,7 @@ def test_dequant_all_codes_and_scales(fmt):
 # ------------------------------------------------------------------ GEMV (M <= 16)
 
 @pytest.mark.parametrize("fmt", gc.FMTS_ALL)
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16])
+@pytest.mark.parametrize("m", list(range(1, 17)))
 def test_gemv_small_shapes(fmt, m):
     # at M = 1: (48, 256), (37, 160), (256, 1536) and (24, 4096) fill every chunk slot of every wave;
     # (40, 2560) leaves the last slot of half the waves past the last chunk; (20, 96) is one partial chunk
