@@ -511,7 +511,7 @@ def test_midm_repeatable():
 # ------------------------------------------------------------------ GEMM
 
 @pytest.mark.parametrize("fmt", gc.FMTS)
-@pytest.mark.parametrize("m", [1, 17, 63, 64, 100, 257])
+@pytest.mark.parametrize("m", [1, 17, 63, 64, 65, 100, 127, 128, 129, 191, 192, 193, 255, 256, 257, 383, 384, 511, 512, 513])
 def test_gemm_shapes(fmt, m):
     for (n, k) in [(200, 384), (37, 160)]:
         _announce("gemm", fmt, m, n, k)
